@@ -1,0 +1,236 @@
+"""Plain CPU oracle for the forward pass of a top-k routed MoE SwiGLU FFN layer.
+
+TEST INFRASTRUCTURE.  Only the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or run this module.  It shares
+no code with the HIP path and imports nothing from it.
+
+Everything is computed in float64 from the (bf16-rounded, exactly widened)
+input values, except where a floating-point value decides an integer: the
+top-k choice is taken on the logits rounded to float32, the precision the
+routing kernel holds them in.
+
+Pages cited (no page has a usable title line, so each is named by its address):
+
+* P1  cf-1.com/news/5914943
+* P2  hotelren.com/news/5904824
+* P3  devpress.csdn.net/awstech/6a91abf42b83d06f0ec71b09.html
+* P4  2kiu.com/news/2885792
+* P5  hotelren.com/news/3071227
+
+Readings of points the pages leave open (each also listed in the design notes):
+
+* gate weights are a softmax over the k selected logits (P1 §2.1, P5 §4.1);
+  P3 §4.1's "softmax over all N, keep top-k, renormalise" gives the same values;
+* ties go to the lower expert index and slot order is (logit desc, index asc)
+  (P4 §5.3);
+* capacity C = floor((T*k)/N * CF) with the operation order of P4 §3.1's
+  formula; CF <= 0 means "no limit" (C = T);
+* the first C tokens in token order keep their place at an expert (P4 §3.1);
+  a dropped assignment contributes nothing and the surviving weights are not
+  renormalised, so a fully dropped token has y = 0 and only the caller's
+  residual carries it (P1 §2.3 tip);
+* the expert FFN is SwiGLU, FFN(x) = (silu(x W1) * (x W3)) W2 with
+  silu(z) = z / (1 + exp(-z)), W1 being the gated branch, no biases (P4 §2.2
+  names SwiGLU; the formula is the standard GLU-variant one);
+* aux = N * sum_e f_e * P_e with f_e = counts_e / (T*k) from the router's
+  pre-drop assignments and P_e the mean over tokens of the full-N softmax of
+  the logits (P1 §2.3, P2 §3.2); the 0.01-style coefficient is the caller's.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "router_logits", "select_topk", "gate_weights", "expert_counts", "capacity",
+    "dispatch", "silu", "swiglu_ffn", "aux_loss", "moe_forward", "moe_forward_per_token",
+]
+
+
+def router_logits(hidden, w_router, bias=None) -> np.ndarray:
+    """Router linear layer: logits[t, e] = sum_i hidden[t, i] * W_router[i, e] (+ bias[e]).
+
+    P1 §2.1 (router scores every expert with one small linear layer, W_router
+    [hidden_dim, num_experts]); P4 §3.1 (the einsum 'bsd,de->bse'); optional
+    bias per P3 §4.1 (nn.Linear with bias) and P4 §5.2 (per-expert offset).
+    """
+    L = np.asarray(hidden, np.float64) @ np.asarray(w_router, np.float64)
+    if bias is not None:
+        L = L + np.asarray(bias, np.float64)[None, :]
+    return L
+
+
+def select_topk(logits, k: int) -> np.ndarray:
+    """Indices [T, k] of the k largest logits per token, in slot order.
+
+    P1 §2.1 / §2.2 (top-k experts by router score, k = 2 typical); P4 §5.3
+    (equal logits are ranked by ascending expert id).  The decision is made on
+    the float32-rounded logits.
+    """
+    L32 = np.asarray(logits).astype(np.float32)
+    T, N = L32.shape
+    if not 1 <= k <= N:
+        raise ValueError("need 1 <= k <= N")
+    ids = np.broadcast_to(np.arange(N), (T, N))
+    order = np.lexsort((ids, -L32.astype(np.float64)), axis=-1)   # primary: -logit, then id
+    return order[:, :k].astype(np.int64)
+
+
+def gate_weights(logits, idx) -> np.ndarray:
+    """Softmax over the k selected logits of each token (P1 §2.1 code; P5 §4.1)."""
+    sel = np.take_along_axis(np.asarray(logits, np.float64), idx, axis=1)
+    m = sel.max(axis=1, keepdims=True)
+    e = np.exp(sel - m)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def expert_counts(idx, N: int) -> np.ndarray:
+    """tokens_per_expert before any capacity drop (P1 §2.3)."""
+    return np.bincount(np.asarray(idx).ravel(), minlength=N).astype(np.int64)
+
+
+def capacity(T: int, k: int, N: int, capacity_factor: float) -> int:
+    """Expert capacity C = floor((T*k)/N * CF) (P4 §3.1; worked example P5 §2.2).
+
+    CF <= 0 stands for "no capacity limit": C = T, which no expert can exceed
+    since a token never picks the same expert twice.
+    """
+    if capacity_factor is None or capacity_factor <= 0:
+        return int(T)
+    return int(math.floor((T * k) / N * float(capacity_factor)))
+
+
+def dispatch(idx, N: int, C: int) -> dict:
+    """Per-expert queues after the capacity cut.
+
+    Tokens are visited in order t = 0..T-1; at each selected expert the token
+    takes the next place, and it keeps its place only if fewer than C tokens
+    came before it (P4 §3.1 "keep the first capacity tokens per expert").
+    Kept rows are laid out expert-major, token-ascending inside an expert.
+    """
+    idx = np.asarray(idx)
+    T, k = idx.shape
+    place = np.empty((T, k), np.int64)
+    running = np.zeros(N, np.int64)
+    for t in range(T):
+        for j in range(k):
+            e = idx[t, j]
+            place[t, j] = running[e]
+            running[e] += 1
+    keep = place < C
+    kept = np.array([min(int(running[e]), C) for e in range(N)], np.int64)
+    offsets = np.zeros(N + 1, np.int64)
+    offsets[1:] = np.cumsum(kept)
+    slot_row = np.where(keep, offsets[idx] + place, -1)
+    perm_src = np.empty(int(offsets[-1]), np.int64)
+    for t in range(T):
+        for j in range(k):
+            if keep[t, j]:
+                perm_src[slot_row[t, j]] = t
+    return {"place": place, "keep": keep, "kept": kept, "offsets": offsets,
+            "slot_row": slot_row, "perm_src": perm_src}
+
+
+def silu(z):
+    """silu(z) = z * sigmoid(z) = z / (1 + exp(-z))."""
+    z = np.asarray(z, np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def swiglu_ffn(x, w1, w3, w2) -> np.ndarray:
+    """One expert: (silu(x W1) * (x W3)) W2 (P4 §2.2 names SwiGLU experts)."""
+    x = np.asarray(x, np.float64)
+    h1 = x @ np.asarray(w1, np.float64)
+    h3 = x @ np.asarray(w3, np.float64)
+    return (silu(h1) * h3) @ np.asarray(w2, np.float64)
+
+
+def aux_loss(logits, counts, k: int) -> float:
+    """Load-balancing loss N * sum_e f_e * P_e (P1 §2.3; P2 §3.2).
+
+    P_e: mean over tokens of the softmax over all N logits.  f_e: share of
+    the T*k router assignments that went to expert e, before capacity drop,
+    so that sum_e f_e = 1 and a uniform router scores exactly 1.
+    """
+    L = np.asarray(logits, np.float64)
+    T, N = L.shape
+    m = L.max(axis=1, keepdims=True)
+    ex = np.exp(L - m)
+    probs = ex / ex.sum(axis=1, keepdims=True)
+    P = probs.mean(axis=0)
+    f = np.asarray(counts, np.float64) / float(T * k)
+    return float(N * np.sum(f * P))
+
+
+def moe_forward(hidden, w_router, w1, w3, w2, k: int, capacity_factor: float = 0.0,
+                bias=None, tokens=None) -> dict:
+    """The layer forward, per expert (the page's gather -> FFN -> weighted add loop).
+
+    ``w1[e]``, ``w3[e]``, ``w2[e]`` are indexed one expert at a time, so the
+    caller may hand in lazy per-expert views.  If ``tokens`` is given, routing,
+    counts, dispatch and aux cover every token but the expert FFN and the
+    combine are evaluated only for those tokens (``y`` then has one row per
+    listed token).
+
+    P1 §2.1 (route, top-k, softmax, weighted sum), P3 §4.1 (per-expert loop;
+    its shortcut that weights every expert by the sum of both gate values is
+    not reproduced), P1 §2.3 (aux, capacity).
+    """
+    hidden = np.asarray(hidden)
+    T, d = hidden.shape
+    L = router_logits(hidden, w_router, bias)
+    N = L.shape[1]
+    idx = select_topk(L, k)
+    w = gate_weights(L, idx)
+    counts = expert_counts(idx, N)
+    C = capacity(T, k, N, capacity_factor)
+    disp = dispatch(idx, N, C)
+    slot_row, offsets, perm_src = disp["slot_row"], disp["offsets"], disp["perm_src"]
+
+    tok = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
+    want = np.zeros(T, bool)
+    want[tok] = True
+    A = int(offsets[-1])
+    y_perm = np.full((A, d), np.nan)
+    for e in range(N):
+        rows = np.arange(offsets[e], offsets[e + 1])
+        rows = rows[want[perm_src[rows]]]
+        if rows.size == 0:
+            continue
+        y_perm[rows] = swiglu_ffn(hidden[perm_src[rows]], w1[e], w3[e], w2[e])
+    y = np.zeros((tok.size, d))
+    for n, t in enumerate(tok):
+        for j in range(k):
+            r = slot_row[t, j]
+            if r >= 0:
+                y[n] += w[t, j] * y_perm[r]
+    return {"logits": L, "topk_idx": idx, "topk_w": w, "counts": counts, "capacity": C,
+            "kept": disp["kept"], "offsets": offsets, "slot_row": slot_row, "perm_src": perm_src,
+            "y_perm": y_perm, "y": y, "tokens": tok, "aux": aux_loss(L, counts, k)}
+
+
+def moe_forward_per_token(hidden, w_router, w1, w3, w2, k: int, capacity_factor: float = 0.0,
+                          bias=None) -> np.ndarray:
+    """Brute force for tiny inputs: y_t = sum over kept slots j of w_tj * FFN_{i_tj}(x_t).
+
+    One token and one slot at a time, with its own running per-expert counter
+    for the capacity cut; no permutation, no grouping.
+    """
+    hidden = np.asarray(hidden, np.float64)
+    T, d = hidden.shape
+    L = router_logits(hidden, w_router, bias)
+    N = L.shape[1]
+    idx = select_topk(L, k)
+    w = gate_weights(L, idx)
+    C = capacity(T, k, N, capacity_factor)
+    seen = [0] * N
+    y = np.zeros((T, d))
+    for t in range(T):
+        for j in range(k):
+            e = int(idx[t, j])
+            if seen[e] < C:
+                y[t] += w[t, j] * swiglu_ffn(hidden[t:t + 1], w1[e], w3[e], w2[e])[0]
+            seen[e] += 1
+    return y

@@ -1,0 +1,174 @@
+/*
+ * moe.h -- C ABI of libmoe_mi355x.so: the forward pass of a top-k routed
+ * Mixture-of-Experts SwiGLU FFN layer on one MI355X (gfx950).
+ *
+ * Pages cited (named by address; none has a usable title line):
+ *   P1 cf-1.com/news/5914943            P2 hotelren.com/news/5904824
+ *   P3 devpress.csdn.net/awstech/6a91abf42b83d06f0ec71b09.html
+ *   P4 2kiu.com/news/2885792            P5 hotelren.com/news/3071227
+ *
+ * The layer (P1 §2.1, P1 §2.3, P4 §2.2, P4 §3.1):
+ *   logits  = hidden . W_router (+ bias)                          moe_route
+ *   top-k per token, softmax over the k selected logits           moe_route
+ *   per-expert counts, capacity cut, expert-contiguous permute    moe_permute
+ *   per-expert SwiGLU FFN as one grouped GEMM pair                moe_expert_ffn
+ *   weighted combine back to token order                          moe_combine
+ *   load-balancing loss N * sum_e f_e * P_e                       moe_aux_loss
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer argument is a DEVICE pointer owned by the caller, to a
+ *     contiguous row-major array; the library never allocates, frees, keeps
+ *     or synchronises.  `stream` is a hipStream_t passed as void* (NULL = the
+ *     null stream); all work is enqueued on it asynchronously.
+ *   - Argument errors are detected on the host before anything is enqueued
+ *     and leave every output untouched.  MOE_ERR_HIP reports a launch error;
+ *     a fault inside a kernel surfaces at the caller's next synchronisation.
+ *   - dtype MOE_BF16: hidden, weights, x_perm, the SwiGLU activations and y
+ *     are bfloat16 (raw 16-bit patterns); accumulation is fp32.  MOE_F32: all
+ *     of them are fp32.  logits, topk_w, y_perm and aux are always fp32.
+ *   - Limits: 1 <= k <= N <= 256; T >= 1; d and f multiples of 64 (bf16:
+ *     f a multiple of 128); T * k < 2^31.  Outside them: MOE_ERR_UNSUPPORTED.
+ *   - Inputs must be finite; behaviour on NaN/Inf inputs is unspecified.
+ *   - Calls on one stream are ordered; calls that share outputs or workspace
+ *     on different streams race.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, k outside [1, N], NaN capacity factor */
+  MOE_ERR_UNSUPPORTED = 2, /* shape or dtype outside the limits above */
+  MOE_ERR_WORKSPACE = 3,   /* workspace smaller than moe_workspace_size() */
+  MOE_ERR_HIP = 4          /* HIP launch error */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum {
+  MOE_OP_ROUTE = 0,
+  MOE_OP_PERMUTE = 1,
+  MOE_OP_EXPERT_FFN = 2,
+  MOE_OP_COMBINE = 3,
+  MOE_OP_AUX_LOSS = 4
+} moe_op;
+
+/* Human-readable name of a status code (static string). */
+const char* moe_status_string(moe_status s);
+
+/* Bytes of device workspace `op` needs for these sizes (0 if none).  Returns
+ * 0 for an unknown op as well.  For MOE_OP_EXPERT_FFN, T*k is the row capacity
+ * (max_rows) of x_perm / y_perm. */
+size_t moe_workspace_size(moe_op op, int T, int d, int N, int k, int f, moe_dtype dt);
+
+/*
+ * moe_route -- router linear layer, top-k, gate weights, pre-drop counts.
+ *   P1 §2.1 (a small linear layer scores every expert, the top-k scores are
+ *   kept and softmax-normalised), P4 §3.1 (logits = hidden . router_w with
+ *   router_w [D, E]), P4 §5.3 (equal logits rank by ascending expert id),
+ *   P1 §2.3 (tokens_per_expert).
+ *
+ *   hidden    [T, d]   dtype dt
+ *   w_router  [d, N]   dtype dt
+ *   bias      [N] fp32 per-expert logit offset, or NULL for none
+ *   logits    [T, N] fp32 out: hidden . w_router (+ bias), fp32 accumulation
+ *   topk_idx  [T, k] int32 out: expert ids ordered by (logit desc, id asc)
+ *   topk_w    [T, k] fp32 out: softmax over the k selected logits
+ *   counts    [N] int32 out: number of tokens that chose each expert (before
+ *             any capacity drop); sum(counts) = T*k
+ */
+moe_status moe_route(const void* hidden, const void* w_router, const float* bias, int T, int d,
+                     int N, int k, moe_dtype dt, float* logits, int32_t* topk_idx, float* topk_w,
+                     int32_t* counts, void* stream);
+
+/*
+ * moe_permute -- capacity cut and permutation into expert-contiguous rows.
+ *   P4 §3.1 (capacity = int((B*S*k)/E * CF); each expert keeps its first
+ *   `capacity` tokens), P5 §2.2 (worked capacity example), P1 §2.3 tip
+ *   (tokens over capacity skip the MoE FFN and ride the residual), P3 §4.1
+ *   (scatter tokens into per-expert queues instead of a per-expert loop).
+ *
+ *   capacity_factor > 0: C = floor((T*k)/N * capacity_factor), computed in
+ *   double on the host; <= 0: no limit (C = T).  Tokens take places at an
+ *   expert in token order; (t, j) is kept iff its place is < C.  Kept rows
+ *   are expert-major, token-ascending within an expert.
+ *
+ *   hidden    [T, d] dtype dt
+ *   topk_idx  [T, k] int32 (from moe_route; ids outside [0, N) are ignored)
+ *   x_perm    [T*k, d] dtype dt out: rows [0, offsets[N]) = gathered hidden
+ *             rows (the rest are not written)
+ *   perm_src  [T*k] int32 out: token of each kept row (rows >= offsets[N] not written)
+ *   slot_row  [T, k] int32 out: row in x_perm of (t, j), or -1 if dropped
+ *   kept      [N] int32 out: min(count_e, C)
+ *   offsets   [N+1] int32 out: exclusive prefix sum of kept; offsets[N] = rows used
+ *   ws        device workspace of moe_workspace_size(MOE_OP_PERMUTE, ...) bytes
+ */
+moe_status moe_permute(const void* hidden, const int32_t* topk_idx, int T, int d, int N, int k,
+                       float capacity_factor, moe_dtype dt, void* x_perm, int32_t* perm_src,
+                       int32_t* slot_row, int32_t* kept, int32_t* offsets, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/*
+ * moe_expert_ffn -- every expert's SwiGLU FFN over its rows, as two grouped
+ * GEMMs (P1 §3.3 grouped GEMM; P4 §3.3 one kernel for all experts indexed by
+ * expert id; P4 §5.4 all experts' weights in one tensor sliced by id; P4 §2.2
+ * SwiGLU experts):  y_perm[r] = (silu(x_perm[r] W1_e) * (x_perm[r] W3_e)) W2_e
+ * for every row r in [offsets[e], offsets[e+1]), silu(z) = z / (1 + e^-z).
+ * Equivalent to moe_expert_up followed by moe_expert_down with the
+ * activations held in `ws`.
+ *
+ *   x_perm    [max_rows, d] dtype dt
+ *   offsets   [N+1] int32 (from moe_permute; offsets[N] <= max_rows)
+ *   w1, w3    [N, d, f] dtype dt;  w2 [N, f, d] dtype dt
+ *   y_perm    [max_rows, d] fp32 out (rows >= offsets[N] not written)
+ *   ws        moe_workspace_size(MOE_OP_EXPERT_FFN, T, d, N, k, f, dt) bytes
+ *             with T*k = max_rows
+ */
+moe_status moe_expert_ffn(const void* x_perm, const int32_t* offsets, const void* w1,
+                          const void* w3, const void* w2, int N, int d, int f, int max_rows,
+                          moe_dtype dt, float* y_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* First grouped GEMM with the SwiGLU epilogue fused:
+ *   act[r] = silu(x_perm[r] W1_e) * (x_perm[r] W3_e), act [max_rows, f] dtype dt. */
+moe_status moe_expert_up(const void* x_perm, const int32_t* offsets, const void* w1,
+                         const void* w3, int N, int d, int f, int max_rows, moe_dtype dt,
+                         void* act, void* stream);
+
+/* Second grouped GEMM: y_perm[r] = act[r] W2_e, y_perm fp32. */
+moe_status moe_expert_down(const void* act, const int32_t* offsets, const void* w2, int N, int d,
+                           int f, int max_rows, moe_dtype dt, float* y_perm, void* stream);
+
+/*
+ * moe_combine -- weighted combine back to token order (P1 §2.1: the output
+ * is the gate-weighted sum of the selected experts' outputs; P3 §4.1 gather).
+ *   y[t] = sum over j = 0..k-1 with slot_row[t, j] >= 0 of
+ *          topk_w[t, j] * y_perm[slot_row[t, j]]
+ *   summed in slot order in fp32, then stored in dtype dt.  Dropped slots
+ *   contribute nothing (weights are not renormalised); the residual is NOT
+ *   added (the caller adds hidden + y).
+ */
+moe_status moe_combine(const float* y_perm, const int32_t* slot_row, const float* topk_w, int T,
+                       int d, int k, moe_dtype dt, void* y, void* stream);
+
+/*
+ * moe_aux_loss -- load-balancing loss (P1 §2.3; P2 §3.2):
+ *   aux = N * sum_e f_e * P_e,  f_e = counts[e] / (T*k)  (pre-drop),
+ *   P_e = (1/T) sum_t softmax(logits[t, :])_e  (softmax over all N).
+ *   Equals 1 when routing is uniform.  The caller applies its coefficient.
+ *
+ *   logits [T, N] fp32, counts [N] int32 (from moe_route), aux: 1 fp32 out.
+ */
+moe_status moe_aux_loss(const float* logits, const int32_t* counts, int T, int N, int k,
+                        float* aux, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

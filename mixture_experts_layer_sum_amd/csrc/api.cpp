@@ -1,0 +1,166 @@
+// C ABI of libmoe_mi355x.so: argument validation on the host (before any HIP
+// call), then the launchers of each step.  Declarations and the contract of
+// every entry point are in include/moe.h.
+#include "moe.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "internal.hpp"
+
+namespace {
+
+constexpr int kMaxExperts = 256;
+
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+inline bool dtype_ok(moe_dtype dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+inline int elem_bytes(moe_dtype dt) { return dt == MOE_BF16 ? 2 : 4; }
+inline moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Shared shape checks.  Order: invalid (nonsense) arguments first, then
+// unsupported-but-meaningful ones.
+moe_status check_tnk(int T, int N, int k) {
+  if (T < 1 || N < 1 || k < 1 || k > N) return MOE_ERR_INVALID_ARG;
+  if (N > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(T) * k >= (int64_t{1} << 31)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status check_d(int d) {
+  if (d < 1) return MOE_ERR_INVALID_ARG;
+  if (d % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status check_expert_shape(int N, int d, int f, int max_rows, moe_dtype dt) {
+  if (N < 1 || d < 1 || f < 1 || max_rows < 1) return MOE_ERR_INVALID_ARG;
+  if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
+  if (N > kMaxExperts || d % 64 != 0 || f % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (dt == MOE_BF16 && (d % 256 != 0 || f % 128 != 0)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// Capacity C = floor((T*k)/N * CF) in double, CF <= 0 meaning "no limit".
+int capacity_of(int T, int k, int N, float cf) {
+  if (!(cf > 0.f)) return T;
+  const double c = std::floor((static_cast<double>(T) * k) / N * static_cast<double>(cf));
+  if (c >= static_cast<double>(T)) return T;
+  return static_cast<int>(c);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape or dtype outside the supported limits";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP launch error";
+  }
+  return "unknown moe_status";
+}
+
+size_t moe_workspace_size(moe_op op, int T, int d, int N, int k, int f, moe_dtype dt) {
+  if (T < 1 || N < 1 || k < 1) return 0;
+  switch (op) {
+    case MOE_OP_PERMUTE: return moe::permute_ws_bytes(T, N);
+    case MOE_OP_EXPERT_FFN:
+      if (f < 1 || !dtype_ok(dt)) return 0;
+      return static_cast<size_t>(T) * k * static_cast<size_t>(f) * elem_bytes(dt);
+    case MOE_OP_AUX_LOSS: return moe::aux_ws_bytes(T, N);
+    default: return 0;
+  }
+}
+
+moe_status moe_route(const void* hidden, const void* w_router, const float* bias, int T, int d,
+                     int N, int k, moe_dtype dt, float* logits, int32_t* topk_idx, float* topk_w,
+                     int32_t* counts, void* stream) {
+  if (!hidden || !w_router || !logits || !topk_idx || !topk_w || !counts) return MOE_ERR_INVALID_ARG;
+  moe_status s = check_tnk(T, N, k);
+  if (s != MOE_OK) return s;
+  if ((s = check_d(d)) != MOE_OK) return s;
+  if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_route(hidden, w_router, bias, T, d, N, k, dt == MOE_BF16, logits,
+                                      topk_idx, topk_w, counts, as_stream(stream)));
+}
+
+moe_status moe_permute(const void* hidden, const int32_t* topk_idx, int T, int d, int N, int k,
+                       float capacity_factor, moe_dtype dt, void* x_perm, int32_t* perm_src,
+                       int32_t* slot_row, int32_t* kept, int32_t* offsets, void* ws,
+                       size_t ws_bytes, void* stream) {
+  if (!hidden || !topk_idx || !x_perm || !perm_src || !slot_row || !kept || !offsets)
+    return MOE_ERR_INVALID_ARG;
+  if (std::isnan(capacity_factor)) return MOE_ERR_INVALID_ARG;
+  moe_status s = check_tnk(T, N, k);
+  if (s != MOE_OK) return s;
+  if ((s = check_d(d)) != MOE_OK) return s;
+  if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
+  const size_t need = moe::permute_ws_bytes(T, N);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (!ws) return MOE_ERR_INVALID_ARG;
+  const int C = capacity_of(T, k, N, capacity_factor);
+  return hip_status(moe::launch_permute(hidden, topk_idx, T, d, N, k, C, elem_bytes(dt), x_perm,
+                                        perm_src, slot_row, kept, offsets, ws, as_stream(stream)));
+}
+
+moe_status moe_expert_up(const void* x_perm, const int32_t* offsets, const void* w1,
+                         const void* w3, int N, int d, int f, int max_rows, moe_dtype dt,
+                         void* act, void* stream) {
+  if (!x_perm || !offsets || !w1 || !w3 || !act) return MOE_ERR_INVALID_ARG;
+  moe_status s = check_expert_shape(N, d, f, max_rows, dt);
+  if (s != MOE_OK) return s;
+  return hip_status(moe::launch_expert_up(x_perm, offsets, w1, w3, N, d, f, max_rows,
+                                          dt == MOE_BF16, act, as_stream(stream)));
+}
+
+moe_status moe_expert_down(const void* act, const int32_t* offsets, const void* w2, int N, int d,
+                           int f, int max_rows, moe_dtype dt, float* y_perm, void* stream) {
+  if (!act || !offsets || !w2 || !y_perm) return MOE_ERR_INVALID_ARG;
+  moe_status s = check_expert_shape(N, d, f, max_rows, dt);
+  if (s != MOE_OK) return s;
+  return hip_status(moe::launch_expert_down(act, offsets, w2, N, d, f, max_rows, dt == MOE_BF16,
+                                            y_perm, as_stream(stream)));
+}
+
+moe_status moe_expert_ffn(const void* x_perm, const int32_t* offsets, const void* w1,
+                          const void* w3, const void* w2, int N, int d, int f, int max_rows,
+                          moe_dtype dt, float* y_perm, void* ws, size_t ws_bytes, void* stream) {
+  if (!x_perm || !offsets || !w1 || !w3 || !w2 || !y_perm) return MOE_ERR_INVALID_ARG;
+  moe_status s = check_expert_shape(N, d, f, max_rows, dt);
+  if (s != MOE_OK) return s;
+  const size_t need = static_cast<size_t>(max_rows) * static_cast<size_t>(f) * elem_bytes(dt);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (!ws) return MOE_ERR_INVALID_ARG;
+  hipError_t e = moe::launch_expert_up(x_perm, offsets, w1, w3, N, d, f, max_rows, dt == MOE_BF16,
+                                       ws, as_stream(stream));
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(moe::launch_expert_down(ws, offsets, w2, N, d, f, max_rows, dt == MOE_BF16,
+                                            y_perm, as_stream(stream)));
+}
+
+moe_status moe_combine(const float* y_perm, const int32_t* slot_row, const float* topk_w, int T,
+                       int d, int k, moe_dtype dt, void* y, void* stream) {
+  if (!y_perm || !slot_row || !topk_w || !y) return MOE_ERR_INVALID_ARG;
+  if (T < 1 || k < 1) return MOE_ERR_INVALID_ARG;
+  if (k > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  moe_status s = check_d(d);
+  if (s != MOE_OK) return s;
+  if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_combine(y_perm, slot_row, topk_w, T, d, k, dt == MOE_BF16, y,
+                                        as_stream(stream)));
+}
+
+moe_status moe_aux_loss(const float* logits, const int32_t* counts, int T, int N, int k,
+                        float* aux, void* ws, size_t ws_bytes, void* stream) {
+  if (!logits || !counts || !aux) return MOE_ERR_INVALID_ARG;
+  moe_status s = check_tnk(T, N, k);
+  if (s != MOE_OK) return s;
+  if (ws_bytes < moe::aux_ws_bytes(T, N)) return MOE_ERR_WORKSPACE;
+  if (!ws) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_aux(logits, counts, T, N, k, aux, ws, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,142 @@
+// Weighted combine back to token order, and the load-balancing loss.
+//
+// Combine -- cf-1.com/news/5914943 §2.1: the layer output is the gate-weighted
+// sum of the selected experts' outputs; devpress.csdn.net/awstech/6a91abf4...
+// §4.1: gather the expert results back to token order.  Summed in slot order
+// in fp32; dropped slots add nothing and nothing is renormalised.
+//
+// Aux loss -- cf-1.com/news/5914943 §2.3 and hotelren.com/news/5904824 §3.2:
+// aux = N * sum_e f_e * P_e with f_e the share of router assignments at e
+// (pre-drop counts / (T*k)) and P_e the mean full-N softmax probability.
+// All reductions run in a fixed order (no float atomics), so the result is
+// bitwise reproducible.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace moe {
+
+// One block per token; each thread owns 4 consecutive columns.
+template <bool BF16>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_perm,
+                                                      const int32_t* __restrict__ slot_row,
+                                                      const float* __restrict__ topk_w, int d,
+                                                      int k, void* __restrict__ y) {
+  __shared__ int srow[256];
+  __shared__ float sw[256];
+  const int t = blockIdx.x;
+  for (int j = threadIdx.x; j < k; j += blockDim.x) {
+    srow[j] = slot_row[(size_t)t * k + j];
+    sw[j] = topk_w[(size_t)t * k + j];
+  }
+  __syncthreads();
+  const int nv = d >> 2;
+  for (int v = threadIdx.x; v < nv; v += blockDim.x) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+      const int r = srow[j];
+      if (r < 0) continue;
+      const float wj = sw[j];
+      const float4 x = reinterpret_cast<const float4*>(y_perm + (size_t)r * d)[v];
+      acc.x = fmaf(wj, x.x, acc.x);
+      acc.y = fmaf(wj, x.y, acc.y);
+      acc.z = fmaf(wj, x.z, acc.z);
+      acc.w = fmaf(wj, x.w, acc.w);
+    }
+    if (BF16) {
+      reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + (size_t)t * d)[v] =
+          make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
+    } else {
+      reinterpret_cast<float4*>(static_cast<float*>(y) + (size_t)t * d)[v] = acc;
+    }
+  }
+}
+
+hipError_t launch_combine(const float* y_perm, const int32_t* slot_row, const float* topk_w, int T,
+                          int d, int k, bool bf16, void* y, hipStream_t stream) {
+  if (bf16)
+    hipLaunchKernelGGL(combine_kernel<true>, dim3(T), dim3(256), 0, stream, y_perm, slot_row,
+                       topk_w, d, k, y);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, dim3(T), dim3(256), 0, stream, y_perm, slot_row,
+                       topk_w, d, k, y);
+  return hipGetLastError();
+}
+
+constexpr int kAuxTok = 256;   // tokens per block (64 per wave)
+
+// part[b][e] = sum over the block's tokens of softmax(logits[t])_e, in token order.
+__global__ __launch_bounds__(256) void aux_partial_kernel(const float* __restrict__ logits, int T,
+                                                          int N, float* __restrict__ part) {
+  __shared__ float red[4][256];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  const int tb = blockIdx.x * kAuxTok + w * 64;
+  for (int i = 0; i < 64; ++i) {
+    const int t = tb + i;
+    if (t >= T) break;
+    const float* L = logits + (size_t)t * N;
+    float v[4];
+    float m = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int e = lane + 64 * c;
+      v[c] = (e < N) ? L[e] : -INFINITY;
+      m = fmaxf(m, v[c]);
+    }
+    m = wave_max(m);
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      v[c] = (lane + 64 * c < N) ? __expf(v[c] - m) : 0.f;
+      s += v[c];
+    }
+    s = wave_sum(s);
+    const float inv = 1.f / s;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] += v[c] * inv;
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) red[w][lane + 64 * c] = acc[c];
+  __syncthreads();
+  for (int e = threadIdx.x; e < N; e += 256)
+    part[(size_t)blockIdx.x * N + e] = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
+}
+
+// Single block: P_e = sum_b part[b][e] / T, then aux = N * sum_e f_e P_e.
+__global__ __launch_bounds__(256) void aux_final_kernel(const float* __restrict__ part, int nb,
+                                                        const int32_t* __restrict__ counts, int T,
+                                                        int N, int k, float* __restrict__ aux) {
+  __shared__ float red[256];
+  const int e = threadIdx.x;
+  float term = 0.f;
+  if (e < N) {
+    double s = 0.0;
+    for (int b = 0; b < nb; ++b) s += part[(size_t)b * N + e];
+    const double P = s / T;
+    const double fe = static_cast<double>(counts[e]) / (static_cast<double>(T) * k);
+    term = static_cast<float>(fe * P);
+  }
+  red[e] = term;
+  __syncthreads();
+  for (int s = 128; s >= 1; s >>= 1) {
+    if (e < s) red[e] += red[e + s];
+    __syncthreads();
+  }
+  if (e == 0) aux[0] = red[0] * static_cast<float>(N);
+}
+
+size_t aux_ws_bytes(int T, int N) {
+  const size_t nb = (static_cast<size_t>(T) + kAuxTok - 1) / kAuxTok;
+  return nb * static_cast<size_t>(N) * sizeof(float);
+}
+
+hipError_t launch_aux(const float* logits, const int32_t* counts, int T, int N, int k, float* aux,
+                      void* ws, hipStream_t stream) {
+  const int nb = (T + kAuxTok - 1) / kAuxTok;
+  float* part = static_cast<float*>(ws);
+  hipLaunchKernelGGL(aux_partial_kernel, dim3(nb), dim3(256), 0, stream, logits, T, N, part);
+  hipLaunchKernelGGL(aux_final_kernel, dim3(1), dim3(256), 0, stream, part, nb, counts, T, N, k, aux);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,35 @@
+// Launchers behind the C ABI (one per step of the layer).  Each enqueues its
+// kernels on `stream` and returns hipGetLastError(); the API layer has
+// already validated every argument.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_route(const void* hidden, const void* w_router, const float* bias, int T, int d,
+                        int N, int k, bool bf16, float* logits, int32_t* topk_idx, float* topk_w,
+                        int32_t* counts, hipStream_t stream);
+
+size_t permute_ws_bytes(int T, int N);
+hipError_t launch_permute(const void* hidden, const int32_t* topk_idx, int T, int d, int N, int k,
+                          int C, int elem_bytes, void* x_perm, int32_t* perm_src,
+                          int32_t* slot_row, int32_t* kept, int32_t* offsets, void* ws,
+                          hipStream_t stream);
+
+hipError_t launch_expert_up(const void* x_perm, const int32_t* offsets, const void* w1,
+                            const void* w3, int N, int d, int f, int max_rows, bool bf16,
+                            void* act, hipStream_t stream);
+hipError_t launch_expert_down(const void* act, const int32_t* offsets, const void* w2, int N,
+                              int d, int f, int max_rows, bool bf16, float* y_perm,
+                              hipStream_t stream);
+
+hipError_t launch_combine(const float* y_perm, const int32_t* slot_row, const float* topk_w, int T,
+                          int d, int k, bool bf16, void* y, hipStream_t stream);
+
+size_t aux_ws_bytes(int T, int N);
+hipError_t launch_aux(const float* logits, const int32_t* counts, int T, int N, int k, float* aux,
+                      void* ws, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,222 @@
+"""Thin ctypes binding over libmoe_mi355x.so (the C ABI in include/moe.h).
+
+Argument marshalling only: torch tensors supply device memory and the current
+HIP stream; every step of the layer runs in the library's HIP kernels.  There
+is no fallback: if the library is missing or fails to load, importing this
+module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_EXPERT_FFN, MOE_OP_COMBINE, MOE_OP_AUX_LOSS = range(5)
+
+# Every symbol include/moe.h declares, with (restype, argtypes).
+_P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "moe_status_string": (ctypes.c_char_p, [_I]),
+    "moe_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
+    "moe_route": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
+    "moe_permute": (_I, [_P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "moe_expert_ffn": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
+    "moe_expert_up": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
+    "moe_expert_down": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
+    "moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P]),
+    "moe_aux_loss": (_I, [_P, _P, _I, _I, _I, _P, _P, _Z, _P]),
+}
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run __graft_entry__.build() "
+                          "(or python -m mixture_experts_layer_sum_amd.build)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    return lib
+
+
+_lib = load_library()
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_lib.moe_status_string(status).decode()}")
+
+
+def _check(status: int, where: str):
+    if status != MOE_OK:
+        raise MoEError(status, where)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float32:
+        return MOE_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("expected a contiguous device tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def workspace_size(op: int, T: int, d: int, N: int, k: int, f: int, dtype: torch.dtype) -> int:
+    return int(_lib.moe_workspace_size(op, T, d, N, k, f,
+                                       MOE_BF16 if dtype == torch.bfloat16 else MOE_F32))
+
+
+def _empty(shape, dtype, device, out):
+    return torch.empty(shape, dtype=dtype, device=device) if out is None else out
+
+
+def moe_route(hidden, w_router, k, bias=None, logits=None, topk_idx=None, topk_w=None,
+              counts=None, stream=None):
+    T, d = hidden.shape
+    N = w_router.shape[1]
+    dev = hidden.device
+    logits = _empty((T, N), torch.float32, dev, logits)
+    topk_idx = _empty((T, k), torch.int32, dev, topk_idx)
+    topk_w = _empty((T, k), torch.float32, dev, topk_w)
+    counts = _empty((N,), torch.int32, dev, counts)
+    _check(_lib.moe_route(_ptr(hidden), _ptr(w_router), _ptr(bias), T, d, N, k, _dt(hidden),
+                          _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _stream(stream)),
+           "moe_route")
+    return logits, topk_idx, topk_w, counts
+
+
+def moe_permute(hidden, topk_idx, N, capacity_factor=0.0, x_perm=None, perm_src=None,
+                slot_row=None, kept=None, offsets=None, ws=None, stream=None):
+    T, d = hidden.shape
+    k = topk_idx.shape[1]
+    dev = hidden.device
+    x_perm = _empty((T * k, d), hidden.dtype, dev, x_perm)
+    perm_src = _empty((T * k,), torch.int32, dev, perm_src)
+    slot_row = _empty((T, k), torch.int32, dev, slot_row)
+    kept = _empty((N,), torch.int32, dev, kept)
+    offsets = _empty((N + 1,), torch.int32, dev, offsets)
+    if ws is None:
+        ws = torch.empty(max(1, workspace_size(MOE_OP_PERMUTE, T, d, N, k, 1, hidden.dtype)),
+                         dtype=torch.uint8, device=dev)
+    _check(_lib.moe_permute(_ptr(hidden), _ptr(topk_idx), T, d, N, k, float(capacity_factor),
+                            _dt(hidden), _ptr(x_perm), _ptr(perm_src), _ptr(slot_row), _ptr(kept),
+                            _ptr(offsets), _ptr(ws), ws.numel(), _stream(stream)), "moe_permute")
+    return x_perm, perm_src, slot_row, kept, offsets
+
+
+def moe_expert_up(x_perm, offsets, w1, w3, act=None, stream=None):
+    max_rows, d = x_perm.shape
+    N, _, f = w1.shape
+    act = _empty((max_rows, f), x_perm.dtype, x_perm.device, act)
+    _check(_lib.moe_expert_up(_ptr(x_perm), _ptr(offsets), _ptr(w1), _ptr(w3), N, d, f, max_rows,
+                              _dt(x_perm), _ptr(act), _stream(stream)), "moe_expert_up")
+    return act
+
+
+def moe_expert_down(act, offsets, w2, y_perm=None, stream=None):
+    max_rows, f = act.shape
+    N, _, d = w2.shape
+    y_perm = _empty((max_rows, d), torch.float32, act.device, y_perm)
+    _check(_lib.moe_expert_down(_ptr(act), _ptr(offsets), _ptr(w2), N, d, f, max_rows, _dt(act),
+                                _ptr(y_perm), _stream(stream)), "moe_expert_down")
+    return y_perm
+
+
+def moe_expert_ffn(x_perm, offsets, w1, w3, w2, y_perm=None, ws=None, stream=None):
+    max_rows, d = x_perm.shape
+    N, _, f = w1.shape
+    dev = x_perm.device
+    y_perm = _empty((max_rows, d), torch.float32, dev, y_perm)
+    if ws is None:
+        ws = torch.empty(workspace_size(MOE_OP_EXPERT_FFN, max_rows, d, N, 1, f, x_perm.dtype),
+                         dtype=torch.uint8, device=dev)
+    _check(_lib.moe_expert_ffn(_ptr(x_perm), _ptr(offsets), _ptr(w1), _ptr(w3), _ptr(w2), N, d, f,
+                               max_rows, _dt(x_perm), _ptr(y_perm), _ptr(ws), ws.numel(),
+                               _stream(stream)), "moe_expert_ffn")
+    return y_perm
+
+
+def moe_combine(y_perm, slot_row, topk_w, dtype, y=None, stream=None):
+    T, k = slot_row.shape
+    d = y_perm.shape[1]
+    y = _empty((T, d), dtype, y_perm.device, y)
+    _check(_lib.moe_combine(_ptr(y_perm), _ptr(slot_row), _ptr(topk_w), T, d, k,
+                            MOE_BF16 if dtype == torch.bfloat16 else MOE_F32, _ptr(y),
+                            _stream(stream)), "moe_combine")
+    return y
+
+
+def moe_aux_loss(logits, counts, k, aux=None, ws=None, stream=None):
+    T, N = logits.shape
+    dev = logits.device
+    aux = _empty((1,), torch.float32, dev, aux)
+    if ws is None:
+        ws = torch.empty(workspace_size(MOE_OP_AUX_LOSS, T, 1, N, k, 1, torch.float32),
+                         dtype=torch.uint8, device=dev)
+    _check(_lib.moe_aux_loss(_ptr(logits), _ptr(counts), T, N, k, _ptr(aux), _ptr(ws), ws.numel(),
+                             _stream(stream)), "moe_aux_loss")
+    return aux
+
+
+class MoEBuffers:
+    """Every output and workspace of one layer forward, allocated once."""
+
+    def __init__(self, T, d, N, k, f, dtype, device="cuda"):
+        self.T, self.d, self.N, self.k, self.f, self.dtype = T, d, N, k, f, dtype
+        e = lambda shape, dt: torch.empty(shape, dtype=dt, device=device)  # noqa: E731
+        self.logits = e((T, N), torch.float32)
+        self.topk_idx = e((T, k), torch.int32)
+        self.topk_w = e((T, k), torch.float32)
+        self.counts = e((N,), torch.int32)
+        self.x_perm = e((T * k, d), dtype)
+        self.perm_src = e((T * k,), torch.int32)
+        self.slot_row = e((T, k), torch.int32)
+        self.kept = e((N,), torch.int32)
+        self.offsets = e((N + 1,), torch.int32)
+        self.act = e((T * k, f), dtype)
+        self.y_perm = e((T * k, d), torch.float32)
+        self.y = e((T, d), dtype)
+        self.aux = e((1,), torch.float32)
+        self.ws_permute = e((max(1, workspace_size(MOE_OP_PERMUTE, T, d, N, k, f, dtype)),), torch.uint8)
+        self.ws_aux = e((max(1, workspace_size(MOE_OP_AUX_LOSS, T, d, N, k, f, dtype)),), torch.uint8)
+
+
+def moe_forward(hidden, w_router, w1, w3, w2, k, capacity_factor=0.0, bias=None,
+                bufs: Optional[MoEBuffers] = None, stream=None):
+    """Run the five steps on the current stream.  Returns the MoEBuffers holding every result.
+
+    ``y`` excludes the residual: the layer output with residual is hidden + y.
+    """
+    T, d = hidden.shape
+    N, _, f = w1.shape
+    if bufs is None:
+        bufs = MoEBuffers(T, d, N, k, f, hidden.dtype, hidden.device)
+    b = bufs
+    moe_route(hidden, w_router, k, bias, b.logits, b.topk_idx, b.topk_w, b.counts, stream)
+    moe_permute(hidden, b.topk_idx, N, capacity_factor, b.x_perm, b.perm_src, b.slot_row, b.kept,
+                b.offsets, b.ws_permute, stream)
+    moe_expert_up(b.x_perm, b.offsets, w1, w3, b.act, stream)
+    moe_expert_down(b.act, b.offsets, w2, b.y_perm, stream)
+    moe_combine(b.y_perm, b.slot_row, b.topk_w, hidden.dtype, b.y, stream)
+    moe_aux_loss(b.logits, b.counts, k, b.aux, b.ws_aux, stream)
+    return b

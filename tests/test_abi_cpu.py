@@ -1,0 +1,146 @@
+"""The C ABI on the host: the library loads without a GPU, exports every symbol
+include/moe.h declares, and rejects bad arguments before any HIP call.
+
+Only argument-validation paths are exercised here (fake non-null pointers are
+never dereferenced because validation fails first); nothing is launched.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+moe = pytest.importorskip("mixture_experts_layer_sum_amd.moe")
+lib = moe._lib
+
+OK, INV, UNS, WS = moe.MOE_OK, moe.MOE_ERR_INVALID_ARG, moe.MOE_ERR_UNSUPPORTED, moe.MOE_ERR_WORKSPACE
+BF16, F32 = moe.MOE_BF16, moe.MOE_F32
+P = ctypes.c_void_p(4096)          # fake device address: never dereferenced
+NUL = None
+S = ctypes.c_void_p(0)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_are_exported():
+    names = declared_functions()
+    assert {"moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_aux_loss"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(moe.SIGNATURES)
+
+
+def test_status_strings():
+    for s in range(5):
+        assert lib.moe_status_string(s).startswith(b"MOE_")
+    assert lib.moe_status_string(99) == b"unknown moe_status"
+
+
+def test_workspace_sizes():
+    assert lib.moe_workspace_size(moe.MOE_OP_ROUTE, 64, 128, 8, 2, 256, F32) == 0
+    assert lib.moe_workspace_size(moe.MOE_OP_COMBINE, 64, 128, 8, 2, 256, F32) == 0
+    # two int32 [chunks, N] tables, chunks of 256 tokens
+    assert lib.moe_workspace_size(moe.MOE_OP_PERMUTE, 257, 128, 8, 2, 256, F32) == 2 * 2 * 8 * 4
+    assert lib.moe_workspace_size(moe.MOE_OP_EXPERT_FFN, 64, 128, 8, 2, 256, BF16) == 64 * 2 * 256 * 2
+    assert lib.moe_workspace_size(moe.MOE_OP_EXPERT_FFN, 64, 128, 8, 2, 256, F32) == 64 * 2 * 256 * 4
+    assert lib.moe_workspace_size(moe.MOE_OP_AUX_LOSS, 256, 128, 8, 2, 256, F32) == 8 * 4
+    assert lib.moe_workspace_size(17, 64, 128, 8, 2, 256, F32) == 0
+    assert lib.moe_workspace_size(moe.MOE_OP_PERMUTE, 0, 128, 8, 2, 256, F32) == 0
+
+
+def route(**kw):
+    a = dict(hidden=P, w_router=P, bias=NUL, T=64, d=128, N=8, k=2, dt=BF16, logits=P,
+             topk_idx=P, topk_w=P, counts=P, stream=S)
+    a.update(kw)
+    return lib.moe_route(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hidden=NUL), INV), (dict(w_router=NUL), INV), (dict(logits=NUL), INV),
+    (dict(topk_idx=NUL), INV), (dict(topk_w=NUL), INV), (dict(counts=NUL), INV),
+    (dict(T=0), INV), (dict(T=-3), INV), (dict(N=0), INV), (dict(k=0), INV), (dict(k=9), INV),
+    (dict(d=0), INV), (dict(N=257, k=2), UNS), (dict(d=100), UNS), (dict(dt=2), UNS),
+    (dict(T=2 ** 30, k=2), UNS),
+])
+def test_route_rejects(kw, status):
+    assert route(**kw) == status
+
+
+def permute(**kw):
+    a = dict(hidden=P, topk_idx=P, T=300, d=128, N=8, k=2, cf=1.25, dt=BF16, x_perm=P,
+             perm_src=P, slot_row=P, kept=P, offsets=P, ws=P, ws_bytes=1 << 20, stream=S)
+    a.update(kw)
+    return lib.moe_permute(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hidden=NUL), INV), (dict(topk_idx=NUL), INV), (dict(x_perm=NUL), INV),
+    (dict(perm_src=NUL), INV), (dict(slot_row=NUL), INV), (dict(kept=NUL), INV),
+    (dict(offsets=NUL), INV), (dict(cf=math.nan), INV), (dict(k=0), INV), (dict(k=9), INV),
+    (dict(T=0), INV), (dict(d=96), UNS), (dict(N=300), UNS), (dict(dt=7), UNS),
+    (dict(ws_bytes=2 * 2 * 8 * 4 - 1), WS), (dict(ws=NUL), INV),
+])
+def test_permute_rejects(kw, status):
+    assert permute(**kw) == status
+
+
+def ffn(**kw):
+    a = dict(x_perm=P, offsets=P, w1=P, w3=P, w2=P, N=8, d=256, f=256, max_rows=128, dt=BF16,
+             y_perm=P, ws=P, ws_bytes=1 << 30, stream=S)
+    a.update(kw)
+    return lib.moe_expert_ffn(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x_perm=NUL), INV), (dict(offsets=NUL), INV), (dict(w1=NUL), INV), (dict(w3=NUL), INV),
+    (dict(w2=NUL), INV), (dict(y_perm=NUL), INV), (dict(N=0), INV), (dict(d=0), INV),
+    (dict(f=0), INV), (dict(max_rows=0), INV), (dict(N=257), UNS), (dict(d=320), UNS),
+    (dict(f=192), UNS), (dict(d=128, dt=BF16), UNS), (dict(f=64, dt=F32, d=64), WS),
+    (dict(dt=3), UNS), (dict(ws_bytes=128 * 256 * 2 - 1), WS), (dict(ws=NUL), INV),
+])
+def test_expert_ffn_rejects(kw, status):
+    if kw.get("dt") == F32 and kw.get("f") == 64:
+        # fp32 accepts d = f = 64; a too-small workspace is then the only error
+        kw = dict(kw, ws_bytes=128 * 64 * 4 - 1)
+    assert ffn(**kw) == status
+
+
+def test_expert_up_down_reject():
+    assert lib.moe_expert_up(NUL, P, P, P, 8, 256, 256, 64, BF16, P, S) == INV
+    assert lib.moe_expert_up(P, P, P, P, 8, 256, 200, 64, BF16, P, S) == UNS
+    assert lib.moe_expert_down(P, P, NUL, 8, 256, 256, 64, BF16, P, S) == INV
+    assert lib.moe_expert_down(P, P, P, 8, 128, 256, 64, BF16, P, S) == UNS
+
+
+@pytest.mark.parametrize("args,status", [
+    ((NUL, P, P, 64, 128, 2, BF16, P, S), INV), ((P, NUL, P, 64, 128, 2, BF16, P, S), INV),
+    ((P, P, NUL, 64, 128, 2, BF16, P, S), INV), ((P, P, P, 64, 128, 2, BF16, NUL, S), INV),
+    ((P, P, P, 0, 128, 2, BF16, P, S), INV), ((P, P, P, 64, 128, 0, BF16, P, S), INV),
+    ((P, P, P, 64, 130, 2, BF16, P, S), UNS), ((P, P, P, 64, 128, 2, 9, P, S), UNS),
+    ((P, P, P, 64, 128, 300, BF16, P, S), UNS),
+])
+def test_combine_rejects(args, status):
+    assert lib.moe_combine(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((NUL, P, 64, 8, 2, P, P, 1024, S), INV), ((P, NUL, 64, 8, 2, P, P, 1024, S), INV),
+    ((P, P, 64, 8, 2, NUL, P, 1024, S), INV), ((P, P, 64, 8, 9, P, P, 1024, S), INV),
+    ((P, P, 0, 8, 2, P, P, 1024, S), INV), ((P, P, 64, 300, 2, P, P, 1 << 20, S), UNS),
+    ((P, P, 64, 8, 2, P, P, 31, S), WS), ((P, P, 64, 8, 2, P, NUL, 1024, S), INV),
+])
+def test_aux_rejects(args, status):
+    assert lib.moe_aux_loss(*args) == status
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(ImportError):
+        moe.load_library(str(tmp_path / "nope.so"))

@@ -1,0 +1,303 @@
+"""Throughput of the top-k MoE SwiGLU layer forward on one MI355X.
+
+A step is one pass of the whole layer (route, permute, up GEMM + SwiGLU, down
+GEMM, combine, aux loss) over one batch of the Mixtral-shaped workload
+(T 8192 = batch 4 x seq 2048, d 4096, 8 experts, top-2, f 14336, bf16, no
+drop), with every input already resident in HBM and every buffer allocated
+before the timed region.  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Also reported in the same line:
+  roofline      the up-projection grouped GEMM (the dominant kernel): its
+                algorithmic flops per launch (4*A*d*f, A = routed rows) over
+                its mean duration from HIP events on the launch stream,
+                against the bf16 dense MFMA peak; HBM traffic per launch from
+                rocprofv3 FETCH_SIZE/WRITE_SIZE when a committed counter
+                summary matches the current kernel source, else null;
+  decode        the decode-shaped workload (T 256, d 4096, 128 experts, top-2,
+                f 1536): layer time and the algorithmic bytes it must read
+                (the weights of every expert that got a token, router weights,
+                hidden and y) per second, against the HBM peak;
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload.
+
+Helper modes for profiling (no timing claims):
+  --copy-calibration MiB   also run a plain device copy of that size (read once,
+                           written once) so rocprofv3 counters can be scaled
+  --summarize-rocprof DIR  turn rocprofv3 csv output into a short text summary
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+UP_KERNEL = "grouped_gemm_bf16_kernel<true>"
+GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_sum_amd", "csrc", "expert_gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "up_gemm_mixtral_T8192_traffic.json")
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def src_hash(path=GEMM_SRC):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def upload(inp):
+    import numpy as np
+    import torch
+
+    def t(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to("cuda").view(torch.bfloat16)
+        return torch.from_numpy(a).to("cuda")
+
+    return {k: t(getattr(inp, k)) for k in ("hidden", "w_router", "w1", "w3", "w2", "bias")}
+
+
+def time_layer(inp, dev, steps, warmup):
+    """Warm up, then time `steps` forwards; per-step HIP events bracket the GEMMs."""
+    import torch
+    from mixture_experts_layer_sum_amd import moe
+    T, d, N, k, f = inp.T, inp.d, inp.N, inp.k, inp.f
+    b = moe.MoEBuffers(T, d, N, k, f, dev["hidden"].dtype)
+    s = torch.cuda.current_stream()
+
+    def step(ev=None):
+        moe.moe_route(dev["hidden"], dev["w_router"], k, dev["bias"], b.logits, b.topk_idx, b.topk_w,
+                      b.counts)
+        moe.moe_permute(dev["hidden"], b.topk_idx, N, inp.capacity_factor, b.x_perm, b.perm_src,
+                        b.slot_row, b.kept, b.offsets, b.ws_permute)
+        if ev:
+            ev[0].record(s)
+        moe.moe_expert_up(b.x_perm, b.offsets, dev["w1"], dev["w3"], b.act)
+        if ev:
+            ev[1].record(s)
+        moe.moe_expert_down(b.act, b.offsets, dev["w2"], b.y_perm)
+        if ev:
+            ev[2].record(s)
+        moe.moe_combine(b.y_perm, b.slot_row, b.topk_w, dev["hidden"].dtype, b.y)
+        moe.moe_aux_loss(b.logits, b.counts, k, b.aux, b.ws_aux)
+
+    for _ in range(warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    up_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    down_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    kept = b.kept.cpu().numpy()
+    A = int(b.offsets[-1].item())
+    return {"elapsed_s": elapsed, "ms_per_step": 1e3 * elapsed / steps, "up_ms": up_ms,
+            "down_ms": down_ms, "A": A, "kept": kept, "aux": float(b.aux.item())}
+
+
+def layer_flops(inp, A):
+    return 2.0 * inp.T * inp.d * inp.N + 6.0 * inp.d * inp.f * A
+
+
+def layer_bytes(inp, kept):
+    s = 2 if inp.dtype == "bf16" else 4
+    active = int((kept > 0).sum())
+    return active * 3.0 * inp.d * inp.f * s + inp.d * inp.N * s + 2.0 * inp.T * inp.d * s
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            return int(info[0]["num_threads"]), info[0].get("internal_api", "blas")
+    except Exception:  # pragma: no cover - informational only
+        pass
+    return len(os.sched_getaffinity(0)), "unknown"
+
+
+def cpu_baseline(inp, sample_tokens):
+    """The oracle as it stands, on the first `sample_tokens` tokens of the same layer."""
+    import oracle.moe_oracle as O
+    from mixture_experts_layer_sum_amd import synth  # noqa: F401
+
+    class View:
+        def __init__(self, name):
+            self.name = name
+
+        def __getitem__(self, e):
+            return inp.expert_values(self.name, e)
+
+    S = min(sample_tokens, inp.T)
+    hid = inp.values("hidden")[:S]
+    t0 = time.perf_counter()
+    O.moe_forward(hid, inp.values("w_router"), View("w1"), View("w3"), View("w2"), inp.k,
+                  inp.capacity_factor, inp.bias)
+    dt = time.perf_counter() - t0
+    threads, api = blas_threads()
+    return {"value": S / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"full fp64 oracle forward (route, top-k, dispatch, per-expert SwiGLU, "
+                      f"combine, aux) of the first {S} of {inp.T} tokens with the same weights; "
+                      f"{dt:.1f} s; numpy BLAS {api}, {threads} threads"}
+
+
+def copy_calibration(mib):
+    import torch
+    n = mib * (1 << 20)
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {mib} MiB read + {mib} MiB written per copy, 3 copies")
+
+
+def traffic_entry():
+    """HBM bytes per launch of the up GEMM from committed counters, if they match this source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = json.load(open(TRAFFIC_FILE))
+    if rec.get("kernel_source_sha256_16") != src_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def summarize_rocprof(d, out):
+    """Short text summary of rocprofv3 csv output in directory `d`."""
+    import csv
+    lines = []
+    stats = sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True))
+    for p in stats:
+        rows = list(csv.DictReader(open(p)))
+        lines.append(f"kernel stats ({os.path.relpath(p, d)}):")
+        lines.append("| kernel | calls | avg us | min us | max us | % time |")
+        lines.append("|---|---|---|---|---|---|")
+        for r in rows:
+            lines.append(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs'])/1e3:.1f} | "
+                         f"{float(r['MinNs'])/1e3:.1f} | {float(r['MaxNs'])/1e3:.1f} | "
+                         f"{float(r['Percentage']):.2f} |")
+    cc = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))
+    for p in cc:
+        rows = list(csv.DictReader(open(p)))
+        agg = {}
+        for r in rows:
+            key = (r.get("Kernel_Name", "")[:90], r.get("Counter_Name", ""))
+            agg.setdefault(key, []).append(float(r.get("Counter_Value", 0) or 0))
+        lines.append(f"counters ({os.path.relpath(p, d)}), mean per dispatch:")
+        lines.append("| kernel | counter | dispatches | mean value |")
+        lines.append("|---|---|---|---|")
+        for (kname, cname), vals in sorted(agg.items()):
+            lines.append(f"| {kname} | {cname} | {len(vals)} | {sum(vals)/len(vals):.1f} |")
+    text = "\n".join(lines) + "\n"
+    if out:
+        with open(out, "a") as fh:
+            fh.write(text)
+    print(text)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=384)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB")
+    ap.add_argument("--summarize-rocprof", default=None, metavar="DIR")
+    ap.add_argument("--summary-out", default=None)
+    args = ap.parse_args()
+
+    if args.summarize_rocprof:
+        summarize_rocprof(args.summarize_rocprof, args.summary_out)
+        return 0
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this layer's path runs on a single MI355X; "
+              "a multi-GPU (expert-parallel) run is not built.", file=sys.stderr)
+        return 2
+
+    import torch
+    from mixture_experts_layer_sum_amd import moe, synth  # noqa: F401  (fails loudly if unbuilt)
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+
+    key = "mixtral"
+    w = synth.WORKLOADS[key]
+    log(f"generating {w.name}")
+    inp = synth.make_workload_inputs(key, seed=args.seed)
+    dev = upload(inp)
+    log("timing")
+    r = time_layer(inp, dev, args.steps, args.warmup)
+    A = r["A"]
+    up_flops = 4.0 * A * inp.d * inp.f
+    up_tflops = up_flops / (r["up_ms"] * 1e-3) / 1e12
+    total_flops = layer_flops(inp, A)
+    ms = r["ms_per_step"]
+    value = inp.T / (ms * 1e-3)
+    traffic = traffic_entry()
+    out = {
+        "metric": "MoE layer forward tokens/s (Mixtral-shaped layer)",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded Gaussian, bf16)",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "N": w.N, "k": w.k, "f": w.f,
+                   "capacity_factor": w.capacity_factor, "seed": args.seed},
+        "layer_tflops": total_flops / (ms * 1e-3) / 1e12,
+        "layer_pct_mfma_peak": 100.0 * total_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "kernel_ms": {"up_gemm_swiglu": r["up_ms"], "down_gemm": r["down_ms"],
+                      "other_steps": ms - r["up_ms"] - r["down_ms"]},
+        "roofline": {"kernel": UP_KERNEL, "bound": "mfma", "achieved": up_tflops,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": up_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": traffic, "work_per_launch": f"4*A*d*f = {up_flops:.4e} flop, A={A}"},
+    }
+    del dev
+    torch.cuda.empty_cache()
+
+    if not args.no_decode:
+        kd = "decode"
+        wd = synth.WORKLOADS[kd]
+        log(f"generating {wd.name}")
+        inpd = synth.make_workload_inputs(kd, seed=args.seed)
+        devd = upload(inpd)
+        rd = time_layer(inpd, devd, max(args.steps, 20), args.warmup)
+        by = layer_bytes(inpd, rd["kept"])
+        gbs = by / (rd["ms_per_step"] * 1e-3) / 1e9
+        out["decode"] = {"workload": wd.name, "ms_per_step": rd["ms_per_step"],
+                         "tokens_per_s": wd.T / (rd["ms_per_step"] * 1e-3),
+                         "active_experts": int((rd["kept"] > 0).sum()), "algorithmic_bytes": by,
+                         "GB_per_s": gbs, "pct_hbm_peak": 100.0 * gbs / PEAK_HBM_GBS,
+                         "up_ms": rd["up_ms"], "down_ms": rd["down_ms"]}
+        del devd
+        torch.cuda.empty_cache()
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -30,13 +30,40 @@
 
 namespace moe {
 
-constexpr int kBM = 256, kBN = 256, kBK = 64, kGemmThreads = 512;
+constexpr int kBM = 256, kBN = 256, kBK = 64, kGemmThreads = 256;
 constexpr int kLd = kBK + 8;   // bf16 per LDS row (16-byte pad breaks bank aliasing)
 constexpr int kGroupM = 8;
 
-// Locate row tile `mt` (tiles of `bm` rows numbered expert by expert).
-// Wave-uniform; returns false if mt is past the last tile.  Offsets are
-// clamped to [0, max_rows] and made non-decreasing.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma32(const uint4& a, const uint4& b, f32x16 acc) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+
+// Row tiles of `bm` rows are numbered expert by expert.  Offsets are clamped
+// to [0, max_rows] and made non-decreasing, so inconsistent offsets can never
+// address a row >= max_rows.  Wave-uniform.
+__device__ __forceinline__ int count_tiles(const int32_t* __restrict__ offsets, int N, int bm,
+                                           int max_rows) {
+  const int lane = threadIdx.x & 63;
+  int total = 0;
+  for (int b = 0; b < N; b += 64) {
+    const int e = b + lane;
+    int cnt = 0;
+    if (e < N) {
+      const int o0 = min(max(offsets[e], 0), max_rows);
+      const int o1 = min(max(offsets[e + 1], o0), max_rows);
+      cnt = (o1 - o0 + bm - 1) / bm;
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) cnt += __shfl_xor(cnt, m, 64);
+    total += cnt;
+  }
+  return total;
+}
+
+// Locate row tile `mt`; returns false if mt is past the last tile.
 __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, int N, int mt,
                                           int bm, int max_rows, int& e_out, int& r0, int& rend) {
   const int lane = threadIdx.x & 63;
@@ -45,7 +72,6 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
     const int e = b + lane;
     int o0 = 0, o1 = 0;
     if (e < N) {
-      // clamped so that inconsistent offsets can never address rows >= max_rows
       o0 = min(max(offsets[e], 0), max_rows);
       o1 = min(max(offsets[e + 1], o0), max_rows);
     }
@@ -61,8 +87,7 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
       const unsigned long long bal = __ballot(before + inc > mt);
       const int L = __ffsll(static_cast<long long>(bal)) - 1;
       const int exc = __shfl(inc - cnt, L, 64);
-      const int eo = b + L;
-      e_out = eo;
+      e_out = b + L;
       r0 = __shfl(o0, L, 64) + (mt - before - exc) * bm;
       rend = __shfl(o1, L, 64);
       return true;
@@ -72,141 +97,203 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
   return false;
 }
 
-__device__ __forceinline__ void tile_of_block(int mt_bound, int n_tiles, int& mt, int& nt,
-                                              bool& valid) {
-  const int G = gridDim.x;                 // a multiple of 8
-  const int per = G >> 3;
+// Block -> (row tile, column tile).  Blocks are dealt round-robin to the 8
+// XCDs, so block b runs on XCD b % 8: give XCD x the contiguous range
+// [x*per, (x+1)*per) of the real tiles (per = ceil(tiles / 8)), and inside a
+// range walk kGroupM row tiles for every column tile, so the blocks an XCD
+// runs at the same time share A rows and weight columns in its L2.
+__device__ __forceinline__ bool tile_of_block(int m_tiles, int n_tiles, int& mt, int& nt) {
+  const int total = m_tiles * n_tiles;
+  const int per = (total + 7) >> 3;
   const int b = blockIdx.x;
-  const int logical = (b & 7) * per + (b >> 3);
-  const int total = mt_bound * n_tiles;
-  valid = logical < total;
-  if (!valid) return;
+  const int local = b >> 3;
+  if (local >= per) return false;
+  const int logical = (b & 7) * per + local;
+  if (logical >= total) return false;
   const int span = kGroupM * n_tiles;
   const int grp = logical / span;
   const int first = grp * kGroupM;
-  const int gm = (mt_bound - first) < kGroupM ? (mt_bound - first) : kGroupM;
+  const int gm = (m_tiles - first) < kGroupM ? (m_tiles - first) : kGroupM;
   const int in = logical - grp * span;
   mt = first + in % gm;
   nt = in / gm;
+  return true;
 }
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
+
+__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// Transpose a 4(k) x 8(n) block of bf16 held as four 8-wide rows into eight
+// 4-wide columns (two packed dwords each) and store them k-contiguous in LDS.
+__device__ __forceinline__ void store_kmajor(uint16_t* dst, int ld, const uint4& r0,
+                                             const uint4& r1, const uint4& r2, const uint4& r3) {
+  const uint32_t a[4] = {r0.x, r0.y, r0.z, r0.w};
+  const uint32_t b[4] = {r1.x, r1.y, r1.z, r1.w};
+  const uint32_t c[4] = {r2.x, r2.y, r2.z, r2.w};
+  const uint32_t d[4] = {r3.x, r3.y, r3.z, r3.w};
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const uint2 even = make_uint2((a[m] & 0xFFFFu) | (b[m] << 16), (c[m] & 0xFFFFu) | (d[m] << 16));
+    const uint2 odd = make_uint2((a[m] >> 16) | (b[m] & 0xFFFF0000u), (c[m] >> 16) | (d[m] & 0xFFFF0000u));
+    *reinterpret_cast<uint2*>(dst + (2 * m) * ld) = even;
+    *reinterpret_cast<uint2*>(dst + (2 * m + 1) * ld) = odd;
+  }
+}
+
+// 256 x 256 block tile, 4 waves in 2 x 2, 128 x 128 per wave on 32x32x16 bf16
+// MFMAs (4 x 4 accumulators of 16 floats per lane, held in AGPRs).
+// Operand convention: lane l holds row/column (l % 32) and k values
+// 8*(l/32) .. 8*(l/32)+7 of a 16-deep k slice, for A and B alike.
+// Result: lane l, element r is D[8*(r/4) + 4*(l/32) + r%4][l % 32].
+// Global loads are raw buffer loads: rows past the tile's last valid row fall
+// outside the A descriptor's range and read as zero.
 template <bool UP>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
     const uint16_t* __restrict__ X, const int32_t* __restrict__ offsets, int N,
     const uint16_t* __restrict__ Wa, const uint16_t* __restrict__ Wb, int K, int Nout,
-    int n_tiles, int mt_bound, int max_rows, void* __restrict__ out) {
+    int n_tiles, int max_rows, void* __restrict__ out) {
   __shared__ __align__(16) uint16_t As[2][kBM * kLd];
   __shared__ __align__(16) uint16_t Bs[2][kBN * kLd];
 
+  const int m_tiles = count_tiles(offsets, N, kBM, max_rows);
   int mt, nt;
-  bool valid;
-  tile_of_block(mt_bound, n_tiles, mt, nt, valid);
-  if (!valid) return;
+  if (!tile_of_block(m_tiles, n_tiles, mt, nt)) return;
   int e, r0, rend;
   if (!find_tile(offsets, N, mt, kBM, max_rows, e, r0, rend)) return;
+  // the tile coordinates are block-uniform: keep them (and the descriptors
+  // built from them) in scalar registers
+  e = __builtin_amdgcn_readfirstlane(e);
+  r0 = __builtin_amdgcn_readfirstlane(r0);
+  rend = __builtin_amdgcn_readfirstlane(rend);
+  nt = __builtin_amdgcn_readfirstlane(nt);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = w & 3, wn = w >> 2;
-  const int g = lane >> 4, l16 = lane & 15;
-  // UP: block columns [n0, n0+128) of W1 and W3; DOWN: [n0, n0+256) of W2.
+  const int wm = w & 1, wn = w >> 1;
+  const int l32 = lane & 31, h = lane >> 5;
+  // UP: block columns [n0, n0+128) of W1 and of W3; DOWN: [n0, n0+256) of W2.
   const int n0 = UP ? nt * (kBN / 2) : nt * kBN;
 
-  // ---- global -> register mapping
-  // A: 256 rows x 8 chunks of 8 bf16; thread handles items tid + 512*i.
-  const uint16_t* a_src[4];
-  bool a_ok[4];
-  int a_lds[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int item = tid + kGemmThreads * i;
-    const int row = item >> 3, ch = item & 7;
-    const int gr = r0 + row;
-    a_ok[i] = gr < rend;
-    a_src[i] = X + (size_t)(a_ok[i] ? gr : r0) * K + 8 * ch;
-    a_lds[i] = row * kLd + 8 * ch;
-  }
-  // B: 4 k-rows x 8 columns per thread.
-  const int q = tid & 15;
-  int cg, bcol;
-  const uint16_t* wbase;
+  const int tile_rows = min(rend - r0, kBM);
+  const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(X + (size_t)r0 * K), 0, tile_rows * K * 2, kRsrcWord3);
   const size_t wexp = (size_t)e * K * Nout;
-  if (UP) {
-    cg = (tid >> 4) & 15;
-    const bool second = tid >= 256;
-    wbase = (second ? Wb : Wa) + wexp + n0 + 8 * cg;
-    bcol = (second ? 128 : 0) + 8 * cg;
-  } else {
-    cg = tid >> 4;  // 0..31
-    wbase = Wa + wexp + n0 + 8 * cg;
-    bcol = 8 * cg;
-  }
-  const uint16_t* b_src = wbase + (size_t)(4 * q) * Nout;
+  const int wbytes = K * Nout * 2;
+  const __amdgpu_buffer_rsrc_t b_rs0 =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Wa + wexp), 0, wbytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t b_rs1 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>((UP ? Wb : Wa) + wexp), 0, wbytes, kRsrcWord3);
 
-  uint4 ra[4], rb[4];
-  const uint4 z4 = make_uint4(0, 0, 0, 0);
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      ra[i] = a_ok[i] ? *reinterpret_cast<const uint4*>(a_src[i] + k0) : z4;
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      rb[r] = *reinterpret_cast<const uint4*>(b_src + (size_t)(k0 + r) * Nout);
-  };
-  auto lstore = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&As[st][a_lds[i]]) = ra[i];
-    const uint32_t* r32[4] = {reinterpret_cast<const uint32_t*>(&rb[0]),
-                              reinterpret_cast<const uint32_t*>(&rb[1]),
-                              reinterpret_cast<const uint32_t*>(&rb[2]),
-                              reinterpret_cast<const uint32_t*>(&rb[3])};
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int h = c >> 1;
-      uint32_t lo, hi;
-      if (c & 1) {
-        lo = (r32[0][h] >> 16) | (r32[1][h] & 0xFFFF0000u);
-        hi = (r32[2][h] >> 16) | (r32[3][h] & 0xFFFF0000u);
-      } else {
-        lo = (r32[0][h] & 0xFFFFu) | (r32[1][h] << 16);
-        hi = (r32[2][h] & 0xFFFFu) | (r32[3][h] << 16);
-      }
-      *reinterpret_cast<uint2*>(&Bs[st][(bcol + c) * kLd + 4 * q]) = make_uint2(lo, hi);
-    }
-  };
+  // A: 256 rows x 8 chunks of 8 bf16 = 2048 items; item tid + 256*i is row
+  // (tid/8) + 32*i, chunk tid%8.
+  const uint32_t a_voff = (uint32_t)(((tid >> 3) * K + 8 * (tid & 7)) * 2);
+  const uint32_t a_step = (uint32_t)(32 * K * 2);
+  const int a_lds = (tid >> 3) * kLd + 8 * (tid & 7);
+  // B: two 4(k) x 8(n) blocks per thread; q = k quad, cg = column group.
+  const int q = tid & 15;
+  const int cg0 = tid >> 4;
+  const int cg1 = UP ? cg0 : cg0 + 16;
+  const uint32_t b_voff0 = (uint32_t)(((4 * q) * Nout + n0 + 8 * cg0) * 2);
+  const uint32_t b_voff1 = (uint32_t)(((4 * q) * Nout + n0 + 8 * cg1) * 2);
+  const uint32_t b_row = (uint32_t)(Nout * 2);
+  const int bcol0 = 8 * cg0;
+  const int bcol1 = UP ? 128 + 8 * cg0 : 8 * cg1;
 
-  f32x4 acc[4][8];
+  uint4 pa0, pa1, pa2, pa3, pa4, pa5, pa6, pa7;
+  uint4 pb00, pb01, pb02, pb03, pb10, pb11, pb12, pb13;
+
+#define MOE_GLOAD(k0)                                                   \
+  do {                                                                  \
+    const uint32_t ks = (uint32_t)(k0) * 2;                             \
+    const uint32_t kb = (uint32_t)(k0) * b_row;                         \
+    pa0 = bload(a_rs, a_voff, ks);                                      \
+    pa1 = bload(a_rs, a_voff + a_step, ks);                             \
+    pa2 = bload(a_rs, a_voff + 2 * a_step, ks);                         \
+    pa3 = bload(a_rs, a_voff + 3 * a_step, ks);                         \
+    pa4 = bload(a_rs, a_voff + 4 * a_step, ks);                         \
+    pa5 = bload(a_rs, a_voff + 5 * a_step, ks);                         \
+    pa6 = bload(a_rs, a_voff + 6 * a_step, ks);                         \
+    pa7 = bload(a_rs, a_voff + 7 * a_step, ks);                         \
+    pb00 = bload(b_rs0, b_voff0, kb);                                   \
+    pb01 = bload(b_rs0, b_voff0 + b_row, kb);                           \
+    pb02 = bload(b_rs0, b_voff0 + 2 * b_row, kb);                       \
+    pb03 = bload(b_rs0, b_voff0 + 3 * b_row, kb);                       \
+    pb10 = bload(b_rs1, b_voff1, kb);                                   \
+    pb11 = bload(b_rs1, b_voff1 + b_row, kb);                           \
+    pb12 = bload(b_rs1, b_voff1 + 2 * b_row, kb);                       \
+    pb13 = bload(b_rs1, b_voff1 + 3 * b_row, kb);                       \
+  } while (0)
+
+#define MOE_LSTORE(st)                                                  \
+  do {                                                                  \
+    uint16_t* as_ = As[st] + a_lds;                                     \
+    *reinterpret_cast<uint4*>(as_) = pa0;                               \
+    *reinterpret_cast<uint4*>(as_ + 32 * kLd) = pa1;                    \
+    *reinterpret_cast<uint4*>(as_ + 64 * kLd) = pa2;                    \
+    *reinterpret_cast<uint4*>(as_ + 96 * kLd) = pa3;                    \
+    *reinterpret_cast<uint4*>(as_ + 128 * kLd) = pa4;                   \
+    *reinterpret_cast<uint4*>(as_ + 160 * kLd) = pa5;                   \
+    *reinterpret_cast<uint4*>(as_ + 192 * kLd) = pa6;                   \
+    *reinterpret_cast<uint4*>(as_ + 224 * kLd) = pa7;                   \
+    store_kmajor(Bs[st] + bcol0 * kLd + 4 * q, kLd, pb00, pb01, pb02, pb03); \
+    store_kmajor(Bs[st] + bcol1 * kLd + 4 * q, kLd, pb10, pb11, pb12, pb13); \
+  } while (0)
+
+  f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // this wave's rows / columns inside the block tile (LDS element offsets)
+  const int a_frag = (wm * 128 + l32) * kLd + 8 * h;
+  int b_frag[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int col = UP ? ((j < 2) ? (wn * 64 + 32 * j) : (128 + wn * 64 + 32 * (j - 2)))
+                       : (wn * 128 + 32 * j);
+    b_frag[j] = (col + l32) * kLd + 8 * h;
+  }
+
+#define MOE_COMPUTE(as_, bs_, s)                                                          \
+  do {                                                                                   \
+    uint4 fa[4], fb[4];                                                                  \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                        \
+        fa[i] = *reinterpret_cast<const uint4*>((as_) + a_frag + 32 * i * kLd + 16 * (s)); \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                        \
+        fb[j] = *reinterpret_cast<const uint4*>((bs_) + b_frag[j] + 16 * (s));           \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                        \
+        _Pragma("unroll") for (int j = 0; j < 4; ++j)                                    \
+            acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);                                 \
+  } while (0)
 
   const int nk = K / kBK;
-  gload(0);
-  lstore(0);
+  MOE_GLOAD(0);
+  MOE_LSTORE(0);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * kBK);
+    const bool more = kt + 1 < nk;
+    if (more) MOE_GLOAD((kt + 1) * kBK);
     const uint16_t* as = As[st];
     const uint16_t* bs = Bs[st];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      uint4 a[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const uint4*>(as + (wm * 64 + 16 * i + l16) * kLd + 32 * s + 8 * g);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int col = UP ? ((j < 4) ? (wn * 64 + 16 * j) : (128 + wn * 64 + 16 * (j - 4)))
-                           : (wn * 128 + 16 * j);
-        const uint4 b = *reinterpret_cast<const uint4*>(bs + (col + l16) * kLd + 32 * s + 8 * g);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i][j] = mfma16(a[i], b, acc[i][j]);
-      }
-    }
-    if (kt + 1 < nk) lstore(st ^ 1);
+    MOE_COMPUTE(as, bs, 0);
+    MOE_COMPUTE(as, bs, 1);
+    // the other stage was last read before the previous barrier: fill it now,
+    // while this stage's MFMAs are still in flight
+    if (more) MOE_LSTORE(st ^ 1);
+    MOE_COMPUTE(as, bs, 2);
+    MOE_COMPUTE(as, bs, 3);
     __syncthreads();
   }
+#undef MOE_GLOAD
+#undef MOE_LSTORE
+#undef MOE_COMPUTE
 
   // ---- epilogue
   if (UP) {
@@ -214,14 +301,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = r0 + wm * 64 + 16 * i + 4 * g + r;
+      for (int r = 0; r < 16; ++r) {
+        const int row = r0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
         if (row < rend) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float h1 = acc[i][j][r], h3 = acc[i][j + 4][r];
-            const float gv = h1 / (1.f + __expf(-h1)) * h3;
-            act[(size_t)row * Nout + n0 + wn * 64 + 16 * j + l16] = f32_to_bf16(gv);
+          for (int j = 0; j < 2; ++j) {
+            const float h1 = acc[i][j][r], h3 = acc[i][j + 2][r];
+            const float gv = h1 * __builtin_amdgcn_rcpf(1.f + __expf(-h1)) * h3;
+            act[(size_t)row * Nout + n0 + wn * 64 + 32 * j + l32] = f32_to_bf16(gv);
           }
         }
       }
@@ -230,12 +317,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = r0 + wm * 64 + 16 * i + 4 * g + r;
+      for (int r = 0; r < 16; ++r) {
+        const int row = r0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
         if (row < rend) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            y[(size_t)row * Nout + n0 + wn * 128 + 16 * j + l16] = acc[i][j][r];
+          for (int j = 0; j < 4; ++j)
+            y[(size_t)row * Nout + n0 + wn * 128 + 32 * j + l32] = acc[i][j][r];
         }
       }
   }
@@ -317,7 +404,7 @@ hipError_t launch_expert_up(const void* x_perm, const int32_t* offsets, const vo
     hipLaunchKernelGGL(grouped_gemm_bf16_kernel<true>, dim3(grid), dim3(kGemmThreads), 0, stream,
                        static_cast<const uint16_t*>(x_perm), offsets, N,
                        static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w3), d, f,
-                       n_tiles, mt_bound, max_rows, act);
+                       n_tiles, max_rows, act);
   } else {
     const int n_tiles = f / kFBN;
     const int mt_bound = (max_rows + kFBM - 1) / kFBM + N;
@@ -339,7 +426,7 @@ hipError_t launch_expert_down(const void* act, const int32_t* offsets, const voi
     hipLaunchKernelGGL(grouped_gemm_bf16_kernel<false>, dim3(grid), dim3(kGemmThreads), 0, stream,
                        static_cast<const uint16_t*>(act), offsets, N,
                        static_cast<const uint16_t*>(w2), static_cast<const uint16_t*>(nullptr), f,
-                       d, n_tiles, mt_bound, max_rows, static_cast<void*>(y_perm));
+                       d, n_tiles, max_rows, static_cast<void*>(y_perm));
   } else {
     const int n_tiles = d / kFBN;
     const int mt_bound = (max_rows + kFBM - 1) / kFBM + N;

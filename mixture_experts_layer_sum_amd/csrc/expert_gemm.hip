@@ -202,44 +202,51 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
   const int bcol0 = 8 * cg0;
   const int bcol1 = UP ? 128 + 8 * cg0 : 8 * cg1;
 
-  uint4 pa0, pa1, pa2, pa3, pa4, pa5, pa6, pa7;
-  uint4 pb00, pb01, pb02, pb03, pb10, pb11, pb12, pb13;
+  // Two register sets of one k-step each: the loads for step kt+2 are issued
+  // at the top of step kt and written to LDS in the middle of step kt+1, so
+  // they have about one and a half k-steps of MFMA work to arrive.
+#define MOE_REGSET(P)                                                   \
+  uint4 P##a0, P##a1, P##a2, P##a3, P##a4, P##a5, P##a6, P##a7;         \
+  uint4 P##b00, P##b01, P##b02, P##b03, P##b10, P##b11, P##b12, P##b13
+  MOE_REGSET(x);
+  MOE_REGSET(y);
+#undef MOE_REGSET
 
-#define MOE_GLOAD(k0)                                                   \
+#define MOE_GLOAD(P, k0)                                                \
   do {                                                                  \
     const uint32_t ks = (uint32_t)(k0) * 2;                             \
     const uint32_t kb = (uint32_t)(k0) * b_row;                         \
-    pa0 = bload(a_rs, a_voff, ks);                                      \
-    pa1 = bload(a_rs, a_voff + a_step, ks);                             \
-    pa2 = bload(a_rs, a_voff + 2 * a_step, ks);                         \
-    pa3 = bload(a_rs, a_voff + 3 * a_step, ks);                         \
-    pa4 = bload(a_rs, a_voff + 4 * a_step, ks);                         \
-    pa5 = bload(a_rs, a_voff + 5 * a_step, ks);                         \
-    pa6 = bload(a_rs, a_voff + 6 * a_step, ks);                         \
-    pa7 = bload(a_rs, a_voff + 7 * a_step, ks);                         \
-    pb00 = bload(b_rs0, b_voff0, kb);                                   \
-    pb01 = bload(b_rs0, b_voff0 + b_row, kb);                           \
-    pb02 = bload(b_rs0, b_voff0 + 2 * b_row, kb);                       \
-    pb03 = bload(b_rs0, b_voff0 + 3 * b_row, kb);                       \
-    pb10 = bload(b_rs1, b_voff1, kb);                                   \
-    pb11 = bload(b_rs1, b_voff1 + b_row, kb);                           \
-    pb12 = bload(b_rs1, b_voff1 + 2 * b_row, kb);                       \
-    pb13 = bload(b_rs1, b_voff1 + 3 * b_row, kb);                       \
+    P##a0 = bload(a_rs, a_voff, ks);                                    \
+    P##a1 = bload(a_rs, a_voff + a_step, ks);                           \
+    P##a2 = bload(a_rs, a_voff + 2 * a_step, ks);                       \
+    P##a3 = bload(a_rs, a_voff + 3 * a_step, ks);                       \
+    P##a4 = bload(a_rs, a_voff + 4 * a_step, ks);                       \
+    P##a5 = bload(a_rs, a_voff + 5 * a_step, ks);                       \
+    P##a6 = bload(a_rs, a_voff + 6 * a_step, ks);                       \
+    P##a7 = bload(a_rs, a_voff + 7 * a_step, ks);                       \
+    P##b00 = bload(b_rs0, b_voff0, kb);                                 \
+    P##b01 = bload(b_rs0, b_voff0 + b_row, kb);                         \
+    P##b02 = bload(b_rs0, b_voff0 + 2 * b_row, kb);                     \
+    P##b03 = bload(b_rs0, b_voff0 + 3 * b_row, kb);                     \
+    P##b10 = bload(b_rs1, b_voff1, kb);                                 \
+    P##b11 = bload(b_rs1, b_voff1 + b_row, kb);                         \
+    P##b12 = bload(b_rs1, b_voff1 + 2 * b_row, kb);                     \
+    P##b13 = bload(b_rs1, b_voff1 + 3 * b_row, kb);                     \
   } while (0)
 
-#define MOE_LSTORE(st)                                                  \
+#define MOE_LSTORE(P, st)                                               \
   do {                                                                  \
     uint16_t* as_ = As[st] + a_lds;                                     \
-    *reinterpret_cast<uint4*>(as_) = pa0;                               \
-    *reinterpret_cast<uint4*>(as_ + 32 * kLd) = pa1;                    \
-    *reinterpret_cast<uint4*>(as_ + 64 * kLd) = pa2;                    \
-    *reinterpret_cast<uint4*>(as_ + 96 * kLd) = pa3;                    \
-    *reinterpret_cast<uint4*>(as_ + 128 * kLd) = pa4;                   \
-    *reinterpret_cast<uint4*>(as_ + 160 * kLd) = pa5;                   \
-    *reinterpret_cast<uint4*>(as_ + 192 * kLd) = pa6;                   \
-    *reinterpret_cast<uint4*>(as_ + 224 * kLd) = pa7;                   \
-    store_kmajor(Bs[st] + bcol0 * kLd + 4 * q, kLd, pb00, pb01, pb02, pb03); \
-    store_kmajor(Bs[st] + bcol1 * kLd + 4 * q, kLd, pb10, pb11, pb12, pb13); \
+    *reinterpret_cast<uint4*>(as_) = P##a0;                             \
+    *reinterpret_cast<uint4*>(as_ + 32 * kLd) = P##a1;                  \
+    *reinterpret_cast<uint4*>(as_ + 64 * kLd) = P##a2;                  \
+    *reinterpret_cast<uint4*>(as_ + 96 * kLd) = P##a3;                  \
+    *reinterpret_cast<uint4*>(as_ + 128 * kLd) = P##a4;                 \
+    *reinterpret_cast<uint4*>(as_ + 160 * kLd) = P##a5;                 \
+    *reinterpret_cast<uint4*>(as_ + 192 * kLd) = P##a6;                 \
+    *reinterpret_cast<uint4*>(as_ + 224 * kLd) = P##a7;                 \
+    store_kmajor(Bs[st] + bcol0 * kLd + 4 * q, kLd, P##b00, P##b01, P##b02, P##b03); \
+    store_kmajor(Bs[st] + bcol1 * kLd + 4 * q, kLd, P##b10, P##b11, P##b12, P##b13); \
   } while (0)
 
   f32x16 acc[4][4];
@@ -260,40 +267,100 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
     b_frag[j] = (col + l32) * kLd + 8 * h;
   }
 
-#define MOE_COMPUTE(as_, bs_, s)                                                          \
-  do {                                                                                   \
-    uint4 fa[4], fb[4];                                                                  \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                        \
-        fa[i] = *reinterpret_cast<const uint4*>((as_) + a_frag + 32 * i * kLd + 16 * (s)); \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                        \
-        fb[j] = *reinterpret_cast<const uint4*>((bs_) + b_frag[j] + 16 * (s));           \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                        \
-        _Pragma("unroll") for (int j = 0; j < 4; ++j)                                    \
-            acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);                                 \
+  // Fragment registers, double-buffered: sub-step s+1's fragments are read
+  // from LDS while sub-step s's MFMAs run.
+  uint4 fa0[4], fb0[4], fa1[4], fb1[4];
+#define MOE_LOADF(F, st, s)                                                                  \
+  do {                                                                                      \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                           \
+        fa##F[i] = *reinterpret_cast<const uint4*>(As[st] + a_frag + 32 * i * kLd + 16 * (s)); \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                           \
+        fb##F[j] = *reinterpret_cast<const uint4*>(Bs[st] + b_frag[j] + 16 * (s));          \
+  } while (0)
+#define MOE_MMA(F)                                                                           \
+  do {                                                                                      \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                           \
+        _Pragma("unroll") for (int j = 0; j < 4; ++j)                                       \
+            acc[i][j] = mfma32(fa##F[i], fb##F[j], acc[i][j]);                              \
+  } while (0)
+#define MOE_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+  // One k-step reading LDS stage `st` (four 16-deep sub-steps).  Loads for
+  // step kt+2 go to register set L at the top; set S (step kt+1) is written to
+  // the other stage in the second sub-step; the barrier sits before the last
+  // sub-step's MFMAs so that the next stage's first fragments are read while
+  // they run.  The body has no branches (past the end, loads repeat the last
+  // k-step and the extra LDS writes and reads are never used), so the
+  // hardware wait counters only ever wait for the loads a step consumes.
+  // Interleaving hints for the scheduler (groups are emitted in this order):
+  // 0x008 MFMA, 0x020 VMEM read, 0x100 LDS read, 0x200 LDS write, 0x002 VALU.
+#define MOE_SG(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+#define MOE_PATTERN_LOAD()                                              \
+  _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {                    \
+    MOE_SG(0x008, 1); MOE_SG(0x020, 2); MOE_SG(0x100, 1);               \
+  }                                                                     \
+  _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) MOE_SG(0x008, 1)
+#define MOE_PATTERN_STORE()                                             \
+  _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {                    \
+    MOE_SG(0x008, 1); MOE_SG(0x100, 1); MOE_SG(0x002, 4); MOE_SG(0x200, 1); \
+  }                                                                     \
+  _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {                    \
+    MOE_SG(0x008, 1); MOE_SG(0x002, 4); MOE_SG(0x200, 1);               \
+  }
+#define MOE_PATTERN_READ()                                              \
+  _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {                    \
+    MOE_SG(0x008, 1); MOE_SG(0x100, 1);                                 \
+  }                                                                     \
+  _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) MOE_SG(0x008, 1)
+
+#define MOE_STEP(L, S, st)                                              \
+  do {                                                                  \
+    MOE_GLOAD(L, min(kt + 2, nk - 1) * kBK);                            \
+    MOE_LOADF(1, st, 1);                                                \
+    MOE_MMA(0);                                                         \
+    MOE_PATTERN_LOAD();                                                 \
+    MOE_FENCE();                                                        \
+    MOE_LOADF(0, st, 2);                                                \
+    MOE_LSTORE(S, (st) ^ 1);                                            \
+    MOE_MMA(1);                                                         \
+    MOE_PATTERN_STORE();                                                \
+    MOE_FENCE();                                                        \
+    MOE_LOADF(1, st, 3);                                                \
+    MOE_MMA(0);                                                         \
+    MOE_PATTERN_READ();                                                 \
+    MOE_FENCE();                                                        \
+    __syncthreads();                                                    \
+    MOE_FENCE();                                                        \
+    MOE_LOADF(0, (st) ^ 1, 0);                                          \
+    MOE_MMA(1);                                                         \
+    MOE_PATTERN_READ();                                                 \
+    MOE_FENCE();                                                        \
   } while (0)
 
   const int nk = K / kBK;
-  MOE_GLOAD(0);
-  MOE_LSTORE(0);
+  MOE_GLOAD(x, 0);
+  MOE_LSTORE(x, 0);
+  MOE_GLOAD(y, min(1, nk - 1) * kBK);
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) MOE_GLOAD((kt + 1) * kBK);
-    const uint16_t* as = As[st];
-    const uint16_t* bs = Bs[st];
-    MOE_COMPUTE(as, bs, 0);
-    MOE_COMPUTE(as, bs, 1);
-    // the other stage was last read before the previous barrier: fill it now,
-    // while this stage's MFMAs are still in flight
-    if (more) MOE_LSTORE(st ^ 1);
-    MOE_COMPUTE(as, bs, 2);
-    MOE_COMPUTE(as, bs, 3);
-    __syncthreads();
+  MOE_LOADF(0, 0, 0);
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    MOE_STEP(x, y, 0);      // step kt   (even): stage 0, loads kt+2 -> x, stores y (kt+1)
+    ++kt;
+    MOE_STEP(y, x, 1);      // step kt+1 (odd) : stage 1, loads kt+3 -> y, stores x (kt+2)
+    --kt;
   }
+  if (kt < nk) MOE_STEP(x, y, 0);
+#undef MOE_LOADF
+#undef MOE_MMA
+#undef MOE_FENCE
+#undef MOE_SG
+#undef MOE_PATTERN_LOAD
+#undef MOE_PATTERN_STORE
+#undef MOE_PATTERN_READ
 #undef MOE_GLOAD
 #undef MOE_LSTORE
-#undef MOE_COMPUTE
+#undef MOE_STEP
 
   // ---- epilogue
   if (UP) {

@@ -218,7 +218,7 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=384)
+    ap.add_argument("--cpu-tokens", type=int, default=3072)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB")
     ap.add_argument("--summarize-rocprof", default=None, metavar="DIR")
     ap.add_argument("--summary-out", default=None)

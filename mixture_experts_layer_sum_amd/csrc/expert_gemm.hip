@@ -10,28 +10,31 @@
 // up   : act[r, :] = silu(X[r] W1_e) * (X[r] W3_e)       (SwiGLU fused in the epilogue)
 // down : y_perm[r, :] = act[r] W2_e                        (fp32 out)
 //
-// bf16 path (MFMA): a block computes a 256-row x 256-column tile with 8 waves
-// (4 along rows x 2 along columns, 64 x 128 per wave, 16x16x32 bf16 MFMAs,
-// fp32 accumulators).  For `up` the 256 columns are 128 columns of W1 and
-// the same 128 columns of W3, so the epilogue has both halves of a SwiGLU
-// product in the same lane.  k advances 64 at a time through two LDS stages;
-// the next stage's global loads are in flight while the current one feeds the
-// MFMAs.  The weights are n-contiguous in memory while an MFMA B operand wants
-// 8 consecutive k per lane, so every thread loads a 4(k) x 8(n) block and
-// transposes it in registers before writing it to LDS k-contiguous.
+// bf16 path (MFMA): a block computes a 256-row x 256-column tile with 4 waves
+// (2 x 2, 128 x 128 per wave on 32x32x16 bf16 MFMAs, fp32 accumulators in
+// AGPRs).  For `up` the 256 columns are 128 columns of W1 and the same 128
+// columns of W3, so each lane holds both halves of its SwiGLU products.
+// k advances 64 at a time through two 64 KB LDS stages filled by direct
+// buffer -> LDS loads (no VGPRs in flight; every request is a whole 128-byte
+// line).  A (x_perm rows) is stored row-major and read with ds_read_b128; the
+// weights stay n-contiguous in LDS and the MFMA B operand (8 consecutive k per
+// lane) is assembled with the gfx950 transposing read ds_read_b64_tr_b16.
+// Both LDS layouts are XOR-swizzled per row so that the fragment reads are
+// bank-conflict free.  One barrier per k-step, placed after the last
+// fragment read of the current stage: the stage is refilled two steps ahead
+// while the last slice's MFMAs run.
 // The row tiles of all experts are numbered consecutively; a block finds its
 // expert with a wave-wide prefix scan of the per-expert tile counts read from
 // `offsets` on the device, so the host never needs the routing result.
-// Block ids are remapped so that each XCD (blocks are dealt round-robin to the
-// 8 XCDs) works on a contiguous range of tiles, grouped 8 row tiles at a time,
-// which keeps the A rows and weight columns it streams in its own L2.
+// Blocks are dealt round-robin to the 8 XCDs; each XCD gets a contiguous range
+// of the real tiles, walked 8 row tiles at a time per column tile, so the
+// blocks an XCD runs together share A rows and weight columns in its L2.
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace moe {
 
-constexpr int kBM = 256, kBN = 256, kBK = 64, kGemmThreads = 256;
-constexpr int kLd = kBK + 8;   // bf16 per LDS row (16-byte pad breaks bank aliasing)
+constexpr int kBM = 256, kBN = 256, kGemmThreads = 256;
 constexpr int kGroupM = 8;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -127,57 +130,120 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
-// Transpose a 4(k) x 8(n) block of bf16 held as four 8-wide rows into eight
-// 4-wide columns (two packed dwords each) and store them k-contiguous in LDS.
-__device__ __forceinline__ void store_kmajor(uint16_t* dst, int ld, const uint4& r0,
-                                             const uint4& r1, const uint4& r2, const uint4& r3) {
-  const uint32_t a[4] = {r0.x, r0.y, r0.z, r0.w};
-  const uint32_t b[4] = {r1.x, r1.y, r1.z, r1.w};
-  const uint32_t c[4] = {r2.x, r2.y, r2.z, r2.w};
-  const uint32_t d[4] = {r3.x, r3.y, r3.z, r3.w};
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kBK = 64;
+
+// Direct global -> LDS loads of one 64-deep k-step into the stage at `dst`
+// (32768 elements): A at element 0, B sub-tile q at 16384 + 8192 q.
+__device__ __forceinline__ void gemm_issue(uint16_t* __restrict__ dst, __amdgpu_buffer_rsrc_t a_rs,
+                                           __amdgpu_buffer_rsrc_t b_rs, const uint32_t* a_off,
+                                           const uint32_t* b_off, int w, int kstep, int Nout) {
+  const uint32_t ka = (uint32_t)kstep * (kBK * 2);
+  const uint32_t kb = (uint32_t)kstep * (uint32_t)(kBK * Nout * 2);
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const uint2 even = make_uint2((a[m] & 0xFFFFu) | (b[m] << 16), (c[m] & 0xFFFFu) | (d[m] << 16));
-    const uint2 odd = make_uint2((a[m] >> 16) | (b[m] & 0xFFFF0000u), (c[m] >> 16) | (d[m] & 0xFFFF0000u));
-    *reinterpret_cast<uint2*>(dst + (2 * m) * ld) = even;
-    *reinterpret_cast<uint2*>(dst + (2 * m + 1) * ld) = odd;
+  for (int i = 0; i < 8; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, (lds_void*)(dst + (8 * w + i) * 512), 16,
+                                             a_off[i] + ka, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rs, (lds_void*)(dst + 16384 + (8 * w + i) * 512), 16,
+                                             b_off[i] + kb, 0, 0, 0);
+}
+
+__device__ __forceinline__ void gemm_frags(const uint16_t* __restrict__ st, int s2,
+                                           const int (&a_rd)[4][4], const int (&b_rd)[4][4][2],
+                                           uint4 (&fa)[4], uint4 (&fb)[4]) {
+  const uint16_t* bs_ = st + 16384;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const uint4*>(st + a_rd[s2][i]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(bs_ + b_rd[s2][j][0]));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(bs_ + b_rd[s2][j][1]));
+    const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+    fb[j] = make_uint4(l2.x, l2.y, h2.x, h2.y);
   }
 }
 
-// 256 x 256 block tile, 4 waves in 2 x 2, 128 x 128 per wave on 32x32x16 bf16
-// MFMAs (4 x 4 accumulators of 16 floats per lane, held in AGPRs).
-// Operand convention: lane l holds row/column (l % 32) and k values
-// 8*(l/32) .. 8*(l/32)+7 of a 16-deep k slice, for A and B alike.
-// Result: lane l, element r is D[8*(r/4) + 4*(l/32) + r%4][l % 32].
-// Global loads are raw buffer loads: rows past the tile's last valid row fall
-// outside the A descriptor's range and read as zero.
+__device__ __forceinline__ void gemm_mma(const uint4 (&fa)[4], const uint4 (&fb)[4],
+                                         f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
+}
+
+// Wait until this wave's LDS reads are done and all of its direct loads have
+// landed, then meet the other waves.  One asm statement with a memory clobber
+// (no load in it), so that no LDS access moves across it.
+#define MOE_WAIT_BARRIER() asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory")
+
+// One 64-deep k-step.  On entry fa0/fb0 hold the first 16-deep slice of the
+// step (stage `cur`).  The barrier after the last fragment read of `cur`
+// certifies that every wave is done with it and that the next step has
+// landed in `nxt`; `cur` is then refilled two steps ahead while the last
+// slice's MFMAs run, and the next step's first slice is read from `nxt`.
+// `dst` is `cur`: a separate restrict parameter only so that the refill
+// carries its own alias scope and reading `nxt` does not wait for it.
+__device__ __forceinline__ void gemm_step(const uint16_t* __restrict__ cur, uint16_t* __restrict__ dst,
+                                          const uint16_t* __restrict__ nxt,
+                                          __amdgpu_buffer_rsrc_t a_rs, __amdgpu_buffer_rsrc_t b_rs,
+                                          const uint32_t* a_off, const uint32_t* b_off, int w,
+                                          int kstep, int Nout, const int (&a_rd)[4][4],
+                                          const int (&b_rd)[4][4][2], f32x16 (&acc)[4][4],
+                                          uint4 (&fa0)[4], uint4 (&fb0)[4]) {
+  uint4 fa1[4], fb1[4];
+  gemm_frags(cur, 1, a_rd, b_rd, fa1, fb1);
+  gemm_mma(fa0, fb0, acc);
+  gemm_frags(cur, 2, a_rd, b_rd, fa0, fb0);
+  gemm_mma(fa1, fb1, acc);
+  gemm_frags(cur, 3, a_rd, b_rd, fa1, fb1);
+  gemm_mma(fa0, fb0, acc);
+  MOE_WAIT_BARRIER();
+  gemm_issue(dst, a_rs, b_rs, a_off, b_off, w, kstep, Nout);
+  __builtin_amdgcn_sched_barrier(0);     // keep the refill right after the barrier
+  gemm_frags(nxt, 0, a_rd, b_rd, fa0, fb0);
+  gemm_mma(fa1, fb1, acc);
+}
+
+// LDS layout of one stage (64 KB):
+//   A  [256 rows][64 k]   rows of 8 x 16-byte chunks (one full 128-byte line
+//                          of x_perm per row); chunk c of row r sits at
+//                          position c ^ ((r >> 1) & 7)
+//   B  2 sub-tiles [64 k][128 n], rows of 16 chunks; chunk c of row k sits at
+//                          position c ^ (4 * (k & 3))
+// Both swizzles make the fragment reads conflict-free.
 template <bool UP>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
     const uint16_t* __restrict__ X, const int32_t* __restrict__ offsets, int N,
     const uint16_t* __restrict__ Wa, const uint16_t* __restrict__ Wb, int K, int Nout,
     int n_tiles, int max_rows, void* __restrict__ out) {
-  __shared__ __align__(16) uint16_t As[2][kBM * kLd];
-  __shared__ __align__(16) uint16_t Bs[2][kBN * kLd];
+  // two 64 KB stages as separate LDS objects: the compiler tracks in-flight
+  // direct loads per LDS object, so a read of one stage never waits on the
+  // refill of the other
+  __shared__ __align__(1024) uint16_t S0[32768], S1[32768];
 
   const int m_tiles = count_tiles(offsets, N, kBM, max_rows);
   int mt, nt;
   if (!tile_of_block(m_tiles, n_tiles, mt, nt)) return;
   int e, r0, rend;
   if (!find_tile(offsets, N, mt, kBM, max_rows, e, r0, rend)) return;
-  // the tile coordinates are block-uniform: keep them (and the descriptors
-  // built from them) in scalar registers
   e = __builtin_amdgcn_readfirstlane(e);
   r0 = __builtin_amdgcn_readfirstlane(r0);
   rend = __builtin_amdgcn_readfirstlane(rend);
   nt = __builtin_amdgcn_readfirstlane(nt);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w & 1, wn = w >> 1;
   const int l32 = lane & 31, h = lane >> 5;
-  // UP: block columns [n0, n0+128) of W1 and of W3; DOWN: [n0, n0+256) of W2.
   const int n0 = UP ? nt * (kBN / 2) : nt * kBN;
-
   const int tile_rows = min(rend - r0, kBM);
+
   const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(X + (size_t)r0 * K), 0, tile_rows * K * 2, kRsrcWord3);
   const size_t wexp = (size_t)e * K * Nout;
@@ -187,67 +253,23 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
   const __amdgpu_buffer_rsrc_t b_rs1 = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>((UP ? Wb : Wa) + wexp), 0, wbytes, kRsrcWord3);
 
-  // A: 256 rows x 8 chunks of 8 bf16 = 2048 items; item tid + 256*i is row
-  // (tid/8) + 32*i, chunk tid%8.
-  const uint32_t a_voff = (uint32_t)(((tid >> 3) * K + 8 * (tid & 7)) * 2);
-  const uint32_t a_step = (uint32_t)(32 * K * 2);
-  const int a_lds = (tid >> 3) * kLd + 8 * (tid & 7);
-  // B: two 4(k) x 8(n) blocks per thread; q = k quad, cg = column group.
-  const int q = tid & 15;
-  const int cg0 = tid >> 4;
-  const int cg1 = UP ? cg0 : cg0 + 16;
-  const uint32_t b_voff0 = (uint32_t)(((4 * q) * Nout + n0 + 8 * cg0) * 2);
-  const uint32_t b_voff1 = (uint32_t)(((4 * q) * Nout + n0 + 8 * cg1) * 2);
-  const uint32_t b_row = (uint32_t)(Nout * 2);
-  const int bcol0 = 8 * cg0;
-  const int bcol1 = UP ? 128 + 8 * cg0 : 8 * cg1;
-
-  // Two register sets of one k-step each: the loads for step kt+2 are issued
-  // at the top of step kt and written to LDS in the middle of step kt+1, so
-  // they have about one and a half k-steps of MFMA work to arrive.
-#define MOE_REGSET(P)                                                   \
-  uint4 P##a0, P##a1, P##a2, P##a3, P##a4, P##a5, P##a6, P##a7;         \
-  uint4 P##b00, P##b01, P##b02, P##b03, P##b10, P##b11, P##b12, P##b13
-  MOE_REGSET(x);
-  MOE_REGSET(y);
-#undef MOE_REGSET
-
-#define MOE_GLOAD(P, k0)                                                \
-  do {                                                                  \
-    const uint32_t ks = (uint32_t)(k0) * 2;                             \
-    const uint32_t kb = (uint32_t)(k0) * b_row;                         \
-    P##a0 = bload(a_rs, a_voff, ks);                                    \
-    P##a1 = bload(a_rs, a_voff + a_step, ks);                           \
-    P##a2 = bload(a_rs, a_voff + 2 * a_step, ks);                       \
-    P##a3 = bload(a_rs, a_voff + 3 * a_step, ks);                       \
-    P##a4 = bload(a_rs, a_voff + 4 * a_step, ks);                       \
-    P##a5 = bload(a_rs, a_voff + 5 * a_step, ks);                       \
-    P##a6 = bload(a_rs, a_voff + 6 * a_step, ks);                       \
-    P##a7 = bload(a_rs, a_voff + 7 * a_step, ks);                       \
-    P##b00 = bload(b_rs0, b_voff0, kb);                                 \
-    P##b01 = bload(b_rs0, b_voff0 + b_row, kb);                         \
-    P##b02 = bload(b_rs0, b_voff0 + 2 * b_row, kb);                     \
-    P##b03 = bload(b_rs0, b_voff0 + 3 * b_row, kb);                     \
-    P##b10 = bload(b_rs1, b_voff1, kb);                                 \
-    P##b11 = bload(b_rs1, b_voff1 + b_row, kb);                         \
-    P##b12 = bload(b_rs1, b_voff1 + 2 * b_row, kb);                     \
-    P##b13 = bload(b_rs1, b_voff1 + 3 * b_row, kb);                     \
-  } while (0)
-
-#define MOE_LSTORE(P, st)                                               \
-  do {                                                                  \
-    uint16_t* as_ = As[st] + a_lds;                                     \
-    *reinterpret_cast<uint4*>(as_) = P##a0;                             \
-    *reinterpret_cast<uint4*>(as_ + 32 * kLd) = P##a1;                  \
-    *reinterpret_cast<uint4*>(as_ + 64 * kLd) = P##a2;                  \
-    *reinterpret_cast<uint4*>(as_ + 96 * kLd) = P##a3;                  \
-    *reinterpret_cast<uint4*>(as_ + 128 * kLd) = P##a4;                 \
-    *reinterpret_cast<uint4*>(as_ + 160 * kLd) = P##a5;                 \
-    *reinterpret_cast<uint4*>(as_ + 192 * kLd) = P##a6;                 \
-    *reinterpret_cast<uint4*>(as_ + 224 * kLd) = P##a7;                 \
-    store_kmajor(Bs[st] + bcol0 * kLd + 4 * q, kLd, P##b00, P##b01, P##b02, P##b03); \
-    store_kmajor(Bs[st] + bcol1 * kLd + 4 * q, kLd, P##b10, P##b11, P##b12, P##b13); \
-  } while (0)
+  // ---- direct global -> LDS loads: wave w issues A instructions 4w..4w+3
+  // (16 rows each) and B instructions 4w..4w+3 (4 k-rows of one sub-tile each).
+  uint32_t a_off[8], b_off[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int a = 8 * w + i;                                  // A instruction: 8 rows
+    int row = 8 * a + (lane >> 3);
+    row = row < tile_rows ? row : tile_rows - 1;             // rows past the end repeat the last one
+    const int c = (lane & 7) ^ ((row >> 1) & 7);
+    a_off[i] = (uint32_t)((row * K + 8 * c) * 2);
+    const int b = 8 * w + i;                                  // B instruction: 4 k-rows of sub-tile b / 16
+    const int kr = 4 * (b & 15) + (lane >> 4);
+    const int cb = (lane & 15) ^ (4 * (kr & 3));
+    const int colbase = UP ? n0 : n0 + 128 * (b >> 4);
+    b_off[i] = (uint32_t)((kr * Nout + colbase + 8 * cb) * 2);
+  }
+  const __amdgpu_buffer_rsrc_t b_rs = (w >> 1) ? b_rs1 : b_rs0;   // wave-uniform
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -257,110 +279,55 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // this wave's rows / columns inside the block tile (LDS element offsets)
-  const int a_frag = (wm * 128 + l32) * kLd + 8 * h;
-  int b_frag[4];
+  // fragment addresses (element offsets inside a stage)
+  // A: row wm*128 + 32i + l32, chunk 2s + h  (s = 16-deep sub-step)
+  int a_rd[4][4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int col = UP ? ((j < 2) ? (wn * 64 + 32 * j) : (128 + wn * 64 + 32 * (j - 2)))
-                       : (wn * 128 + 32 * j);
-    b_frag[j] = (col + l32) * kLd + 8 * h;
+  for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wm * 128 + 32 * i + l32;
+      a_rd[s2][i] = row * 64 + 8 * ((2 * s2 + h) ^ ((row >> 1) & 7));
+    }
+  // B (transposing read): 16-lane group gq = lane / 16 covers columns
+  // 16*(gq & 1) .. +15 of the 32-column fragment and k rows 8*(gq >> 1) + 4t .. +3;
+  // lane i of the group points at row (i / 4), columns 4*(i % 4) .. +3.
+  int b_rd[4][4][2];
+  {
+    const int gq = lane >> 4, i16 = lane & 15;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = UP ? (j >> 1) : wn;
+      const int cb = UP ? (wn * 64 + 32 * (j & 1)) : (32 * j);
+      const int col = cb + 16 * (gq & 1) + 4 * (i16 & 3);
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int kr = 16 * s2 + 8 * (gq >> 1) + 4 * t + (i16 >> 2);
+          const int c = (col >> 3) ^ (4 * (kr & 3));
+          b_rd[s2][j][t] = q * (64 * 128) + kr * 128 + 8 * c + (col & 7);
+        }
+    }
   }
-
-  // Fragment registers, double-buffered: sub-step s+1's fragments are read
-  // from LDS while sub-step s's MFMAs run.
-  uint4 fa0[4], fb0[4], fa1[4], fb1[4];
-#define MOE_LOADF(F, st, s)                                                                  \
-  do {                                                                                      \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                           \
-        fa##F[i] = *reinterpret_cast<const uint4*>(As[st] + a_frag + 32 * i * kLd + 16 * (s)); \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                           \
-        fb##F[j] = *reinterpret_cast<const uint4*>(Bs[st] + b_frag[j] + 16 * (s));          \
-  } while (0)
-#define MOE_MMA(F)                                                                           \
-  do {                                                                                      \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                           \
-        _Pragma("unroll") for (int j = 0; j < 4; ++j)                                       \
-            acc[i][j] = mfma32(fa##F[i], fb##F[j], acc[i][j]);                              \
-  } while (0)
-#define MOE_FENCE() __builtin_amdgcn_sched_barrier(0)
-
-  // One k-step reading LDS stage `st` (four 16-deep sub-steps).  Loads for
-  // step kt+2 go to register set L at the top; set S (step kt+1) is written to
-  // the other stage in the second sub-step; the barrier sits before the last
-  // sub-step's MFMAs so that the next stage's first fragments are read while
-  // they run.  The body has no branches (past the end, loads repeat the last
-  // k-step and the extra LDS writes and reads are never used), so the
-  // hardware wait counters only ever wait for the loads a step consumes.
-  // Interleaving hints for the scheduler (groups are emitted in this order):
-  // 0x008 MFMA, 0x020 VMEM read, 0x100 LDS read, 0x200 LDS write, 0x002 VALU.
-#define MOE_SG(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
-#define MOE_PATTERN_LOAD()                                              \
-  _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {                    \
-    MOE_SG(0x008, 1); MOE_SG(0x020, 2); MOE_SG(0x100, 1);               \
-  }                                                                     \
-  _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) MOE_SG(0x008, 1)
-#define MOE_PATTERN_STORE()                                             \
-  _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {                    \
-    MOE_SG(0x008, 1); MOE_SG(0x100, 1); MOE_SG(0x002, 4); MOE_SG(0x200, 1); \
-  }                                                                     \
-  _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {                    \
-    MOE_SG(0x008, 1); MOE_SG(0x002, 4); MOE_SG(0x200, 1);               \
-  }
-#define MOE_PATTERN_READ()                                              \
-  _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {                    \
-    MOE_SG(0x008, 1); MOE_SG(0x100, 1);                                 \
-  }                                                                     \
-  _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) MOE_SG(0x008, 1)
-
-#define MOE_STEP(L, S, st)                                              \
-  do {                                                                  \
-    MOE_GLOAD(L, min(kt + 2, nk - 1) * kBK);                            \
-    MOE_LOADF(1, st, 1);                                                \
-    MOE_MMA(0);                                                         \
-    MOE_PATTERN_LOAD();                                                 \
-    MOE_FENCE();                                                        \
-    MOE_LOADF(0, st, 2);                                                \
-    MOE_LSTORE(S, (st) ^ 1);                                            \
-    MOE_MMA(1);                                                         \
-    MOE_PATTERN_STORE();                                                \
-    MOE_FENCE();                                                        \
-    MOE_LOADF(1, st, 3);                                                \
-    MOE_MMA(0);                                                         \
-    MOE_PATTERN_READ();                                                 \
-    MOE_FENCE();                                                        \
-    __syncthreads();                                                    \
-    MOE_FENCE();                                                        \
-    MOE_LOADF(0, (st) ^ 1, 0);                                          \
-    MOE_MMA(1);                                                         \
-    MOE_PATTERN_READ();                                                 \
-    MOE_FENCE();                                                        \
-  } while (0)
 
   const int nk = K / kBK;
-  MOE_GLOAD(x, 0);
-  MOE_LSTORE(x, 0);
-  MOE_GLOAD(y, min(1, nk - 1) * kBK);
-  __syncthreads();
-  MOE_LOADF(0, 0, 0);
+  gemm_issue(S0, a_rs, b_rs, a_off, b_off, w, 0, Nout);
+  gemm_issue(S1, a_rs, b_rs, a_off, b_off, w, min(1, nk - 1), Nout);
+  asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // step 0 landed
+  uint4 fa0[4], fb0[4];
+  gemm_frags(S0, 0, a_rd, b_rd, fa0, fb0);
+#define MOE_STEP(C, N)                                                                      \
+  gemm_step(C, C, N, a_rs, b_rs, a_off, b_off, w, min(kt + 2, nk - 1), Nout, a_rd, b_rd, acc, \
+            fa0, fb0)
   int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    MOE_STEP(x, y, 0);      // step kt   (even): stage 0, loads kt+2 -> x, stores y (kt+1)
-    ++kt;
-    MOE_STEP(y, x, 1);      // step kt+1 (odd) : stage 1, loads kt+3 -> y, stores x (kt+2)
-    --kt;
+  for (; kt + 2 <= nk; kt += 2) {
+    MOE_STEP(S0, S1); ++kt;
+    MOE_STEP(S1, S0); --kt;
   }
-  if (kt < nk) MOE_STEP(x, y, 0);
-#undef MOE_LOADF
-#undef MOE_MMA
-#undef MOE_FENCE
-#undef MOE_SG
-#undef MOE_PATTERN_LOAD
-#undef MOE_PATTERN_STORE
-#undef MOE_PATTERN_READ
-#undef MOE_GLOAD
-#undef MOE_LSTORE
+  if (kt < nk) MOE_STEP(S0, S1);
 #undef MOE_STEP
+  __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0): no LDS write in flight at exit
 
   // ---- epilogue
   if (UP) {

@@ -78,7 +78,7 @@ def time_layer(inp, dev, steps, warmup):
 
     def step(ev=None):
         moe.moe_route(dev["hidden"], dev["w_router"], k, dev["bias"], b.logits, b.topk_idx, b.topk_w,
-                      b.counts)
+                      b.counts, b.ws_route)
         moe.moe_permute(dev["hidden"], b.topk_idx, N, inp.capacity_factor, b.x_perm, b.perm_src,
                         b.slot_row, b.kept, b.offsets, b.ws_permute)
         if ev:
@@ -217,8 +217,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-main", action="store_true",
+                    help="profiling aid: time only the decode-shaped layer (no JSON line)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=3072)
+    ap.add_argument("--cpu-tokens", type=int, default=8192)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB")
     ap.add_argument("--summarize-rocprof", default=None, metavar="DIR")
     ap.add_argument("--summary-out", default=None)
@@ -237,6 +239,13 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         return 1
+
+    if args.no_main:
+        kd = "decode"
+        inpd = synth.make_workload_inputs(kd, seed=args.seed)
+        rd = time_layer(inpd, upload(inpd), max(args.steps, 20), args.warmup)
+        log(f"decode only: {rd['ms_per_step']:.3f} ms/step")
+        return 0
 
     key = "mixtral"
     w = synth.WORKLOADS[key]

@@ -26,8 +26,9 @@
  *   - dtype MOE_BF16: hidden, weights, x_perm, the SwiGLU activations and y
  *     are bfloat16 (raw 16-bit patterns); accumulation is fp32.  MOE_F32: all
  *     of them are fp32.  logits, topk_w, y_perm and aux are always fp32.
- *   - Limits: 1 <= k <= N <= 256; T >= 1; d and f multiples of 64 (bf16:
- *     f a multiple of 128); T * k < 2^31.  Outside them: MOE_ERR_UNSUPPORTED.
+ *   - Limits: 1 <= k <= N <= 256; T >= 1; d and f multiples of 64; for the
+ *     bf16 expert GEMMs also d a multiple of 256 and f of 128; T * k < 2^31.
+ *     Outside them: MOE_ERR_UNSUPPORTED.
  *   - Inputs must be finite; behaviour on NaN/Inf inputs is unspecified.
  *   - Calls on one stream are ordered; calls that share outputs or workspace
  *     on different streams race.
@@ -83,10 +84,13 @@ size_t moe_workspace_size(moe_op op, int T, int d, int N, int k, int f, moe_dtyp
  *   topk_w    [T, k] fp32 out: softmax over the k selected logits
  *   counts    [N] int32 out: number of tokens that chose each expert (before
  *             any capacity drop); sum(counts) = T*k
+ *   ws        device workspace of moe_workspace_size(MOE_OP_ROUTE, ...) bytes
+ *             (partial logits when the hidden dimension is split across
+ *             blocks; may be NULL when that size is 0)
  */
 moe_status moe_route(const void* hidden, const void* w_router, const float* bias, int T, int d,
                      int N, int k, moe_dtype dt, float* logits, int32_t* topk_idx, float* topk_w,
-                     int32_t* counts, void* stream);
+                     int32_t* counts, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_permute -- capacity cut and permutation into expert-contiguous rows.

@@ -66,6 +66,9 @@ const char* moe_status_string(moe_status s) {
 size_t moe_workspace_size(moe_op op, int T, int d, int N, int k, int f, moe_dtype dt) {
   if (T < 1 || N < 1 || k < 1) return 0;
   switch (op) {
+    case MOE_OP_ROUTE:
+      if (d < 1 || !dtype_ok(dt)) return 0;
+      return dt == MOE_BF16 ? moe::route_ws_bytes(T, d, N) : 0;
     case MOE_OP_PERMUTE: return moe::permute_ws_bytes(T, N);
     case MOE_OP_EXPERT_FFN:
       if (f < 1 || !dtype_ok(dt)) return 0;
@@ -77,14 +80,17 @@ size_t moe_workspace_size(moe_op op, int T, int d, int N, int k, int f, moe_dtyp
 
 moe_status moe_route(const void* hidden, const void* w_router, const float* bias, int T, int d,
                      int N, int k, moe_dtype dt, float* logits, int32_t* topk_idx, float* topk_w,
-                     int32_t* counts, void* stream) {
+                     int32_t* counts, void* ws, size_t ws_bytes, void* stream) {
   if (!hidden || !w_router || !logits || !topk_idx || !topk_w || !counts) return MOE_ERR_INVALID_ARG;
   moe_status s = check_tnk(T, N, k);
   if (s != MOE_OK) return s;
   if ((s = check_d(d)) != MOE_OK) return s;
   if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
+  const size_t need = dt == MOE_BF16 ? moe::route_ws_bytes(T, d, N) : 0;
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (need > 0 && !ws) return MOE_ERR_INVALID_ARG;
   return hip_status(moe::launch_route(hidden, w_router, bias, T, d, N, k, dt == MOE_BF16, logits,
-                                      topk_idx, topk_w, counts, as_stream(stream)));
+                                      topk_idx, topk_w, counts, ws, as_stream(stream)));
 }
 
 moe_status moe_permute(const void* hidden, const int32_t* topk_idx, int T, int d, int N, int k,

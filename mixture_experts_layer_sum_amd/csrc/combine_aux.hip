@@ -62,7 +62,7 @@ hipError_t launch_combine(const float* y_perm, const int32_t* slot_row, const fl
   return hipGetLastError();
 }
 
-constexpr int kAuxTok = 256;   // tokens per block (64 per wave)
+constexpr int kAuxTok = 64;    // tokens per block (16 per wave)
 
 // part[b][e] = sum over the block's tokens of softmax(logits[t])_e, in token order.
 __global__ __launch_bounds__(256) void aux_partial_kernel(const float* __restrict__ logits, int T,
@@ -70,8 +70,8 @@ __global__ __launch_bounds__(256) void aux_partial_kernel(const float* __restric
   __shared__ float red[4][256];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  const int tb = blockIdx.x * kAuxTok + w * 64;
-  for (int i = 0; i < 64; ++i) {
+  const int tb = blockIdx.x * kAuxTok + w * (kAuxTok / 4);
+  for (int i = 0; i < kAuxTok / 4; ++i) {
     const int t = tb + i;
     if (t >= T) break;
     const float* L = logits + (size_t)t * N;

@@ -362,6 +362,176 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
   }
 }
 
+// ---------------------------------------------------------------- few rows per expert
+// Decode-shaped batches give each expert only a handful of rows, so the work
+// is reading every active expert's weights once (HBM-bound).  One wave owns
+// one (expert, group of up to 16*MT rows, 64-column slice): it streams its
+// weight columns straight from global memory into registers -- every load is
+// a full 128-byte line -- and never touches LDS.
+//
+// MFMA 16x16x32 with a column-permuted B operand: lane l = 16g + j loads the
+// 8 k-rows k0+8g .. k0+8g+7 of 8 adjacent weight columns (one 16-byte vector
+// per row) and transposes the 8x8 block in registers, giving 8 B operands
+// (8 consecutive k each).  MFMA number c then produces, in output column j,
+// weight column base(j) + c.  For `up`, lanes j < 8 read W1 columns
+// n0 + 8j .. n0 + 8j + 7 and lanes j >= 8 the same columns of W3, so a
+// shuffle across 8 lanes brings both halves of a SwiGLU product together.
+// For `down`, lane j reads W2 columns n0 + 8j .. n0 + 8j + 7 (128 columns).
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+// Streaming 16-byte load (weights are read once): non-temporal hint.
+__device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
+  const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void transpose8x8(const uint4 (&r)[8], uint4 (&c)[8]) {
+  // r[kk] holds columns 0..7 of k-row kk; c[col] gets k-rows 0..7 of column col
+  uint32_t w[8][4];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    w[kk][0] = r[kk].x; w[kk][1] = r[kk].y; w[kk][2] = r[kk].z; w[kk][3] = r[kk].w;
+  }
+#pragma unroll
+  for (int col = 0; col < 8; ++col) {
+    const int h = col >> 1;
+    uint32_t o[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t lo = w[2 * m][h], hi = w[2 * m + 1][h];
+      o[m] = (col & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+    }
+    c[col] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+template <bool UP, int MT>
+__global__ __launch_bounds__(64) void grouped_gemm_bf16_rows_kernel(
+    const uint16_t* __restrict__ X, const int32_t* __restrict__ offsets, int N,
+    const uint16_t* __restrict__ Wa, const uint16_t* __restrict__ Wb, int K, int Nout,
+    int n_slices, int max_rows, void* __restrict__ out) {
+  constexpr int BM = 16 * MT;
+  const int mt = blockIdx.x / n_slices, ns = blockIdx.x - mt * n_slices;
+  int e, r0, rend;
+  if (!find_tile(offsets, N, mt, BM, max_rows, e, r0, rend)) return;
+  e = __builtin_amdgcn_readfirstlane(e);
+  r0 = __builtin_amdgcn_readfirstlane(r0);
+  rend = __builtin_amdgcn_readfirstlane(rend);
+
+  const int lane = threadIdx.x, j = lane & 15, g = lane >> 4;
+  const int n0 = ns * (UP ? 64 : 128);
+  const size_t wexp = (size_t)e * K * Nout;
+  const uint16_t* wsrc = UP ? ((j < 8 ? Wa : Wb) + wexp + n0 + 8 * (j & 7))
+                            : (Wa + wexp + n0 + 8 * j);
+  wsrc += (size_t)(8 * g) * Nout;
+  // A rows: row r0 + 16 t + j (clamped to the last valid row), k 8g .. 8g+7
+  const uint16_t* asrc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int row = min(r0 + 16 * t + j, rend - 1);
+    asrc[t] = X + (size_t)row * K + 8 * g;
+  }
+
+  f32x4 acc[MT][8];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const size_t rstride = (size_t)Nout;
+  uint4 wb[2][8], xa[2][MT];
+#define MOE_ROWS_LOAD(S, k0)                                                          \
+  do {                                                                               \
+    _Pragma("unroll") for (int kk = 0; kk < 8; ++kk)                                 \
+        wb[S][kk] = load_stream(wsrc + (size_t)((k0) + kk) * rstride);               \
+    _Pragma("unroll") for (int t = 0; t < MT; ++t)                                   \
+        xa[S][t] = *reinterpret_cast<const uint4*>(asrc[t] + (k0));                  \
+  } while (0)
+#define MOE_ROWS_MMA(S)                                                               \
+  do {                                                                               \
+    uint4 bf[8];                                                                     \
+    transpose8x8(wb[S], bf);                                                         \
+    _Pragma("unroll") for (int t = 0; t < MT; ++t)                                   \
+        _Pragma("unroll") for (int c = 0; c < 8; ++c)                                \
+            acc[t][c] = mfma16(xa[S][t], bf[c], acc[t][c]);                          \
+  } while (0)
+
+  const int nk = K / 32;                        // K is a multiple of 64: nk is even
+  MOE_ROWS_LOAD(0, 0);
+  for (int kt = 0; kt < nk; kt += 2) {
+    MOE_ROWS_LOAD(1, (kt + 1) * 32);
+    MOE_ROWS_MMA(0);
+    if (kt + 2 < nk) MOE_ROWS_LOAD(0, (kt + 2) * 32);
+    MOE_ROWS_MMA(1);
+  }
+#undef MOE_ROWS_LOAD
+#undef MOE_ROWS_MMA
+
+  // acc[t][c][r]: row r0 + 16t + 4g + r, weight column base(j) + c
+  if (UP) {
+    uint16_t* act = static_cast<uint16_t*>(out);
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const float mine = acc[t][c][r];
+          const float other = __shfl_xor(mine, 8, 64);    // W3 half for lanes j < 8
+          v[c] = mine * __builtin_amdgcn_rcpf(1.f + __expf(-mine)) * other;
+        }
+        const int row = r0 + 16 * t + 4 * g + r;
+        if (j < 8 && row < rend) {
+          const uint4 pk = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                      pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+          *reinterpret_cast<uint4*>(act + (size_t)row * Nout + n0 + 8 * j) = pk;
+        }
+      }
+  } else {
+    float* y = static_cast<float*>(out);
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = r0 + 16 * t + 4 * g + r;
+        if (row < rend) {
+          float4* dst = reinterpret_cast<float4*>(y + (size_t)row * Nout + n0 + 8 * j);
+          dst[0] = make_float4(acc[t][0][r], acc[t][1][r], acc[t][2][r], acc[t][3][r]);
+          dst[1] = make_float4(acc[t][4][r], acc[t][5][r], acc[t][6][r], acc[t][7][r]);
+        }
+      }
+  }
+}
+
+// Rows-per-expert threshold below which the streaming kernel is used.
+static int rows_mt(int max_rows, int N) {
+  const int avg = (max_rows + N - 1) / N;
+  if (avg > 48) return 0;              // big tiles
+  return avg <= 16 ? 1 : (avg <= 32 ? 2 : 4);
+}
+
+template <bool UP>
+static void launch_rows(int mt, const void* x, const int32_t* offsets, int N, const void* wa,
+                        const void* wb, int K, int Nout, int max_rows, void* out,
+                        hipStream_t stream) {
+  const int n_slices = Nout / (UP ? 64 : 128);
+  const int bm = 16 * mt;
+  const int m_bound = (max_rows + bm - 1) / bm + N;
+  const dim3 grid(m_bound * n_slices), block(64);
+  const auto* X = static_cast<const uint16_t*>(x);
+  const auto* A = static_cast<const uint16_t*>(wa);
+  const auto* B = static_cast<const uint16_t*>(wb);
+  if (mt == 1)
+    hipLaunchKernelGGL((grouped_gemm_bf16_rows_kernel<UP, 1>), grid, block, 0, stream, X, offsets,
+                       N, A, B, K, Nout, n_slices, max_rows, out);
+  else if (mt == 2)
+    hipLaunchKernelGGL((grouped_gemm_bf16_rows_kernel<UP, 2>), grid, block, 0, stream, X, offsets,
+                       N, A, B, K, Nout, n_slices, max_rows, out);
+  else
+    hipLaunchKernelGGL((grouped_gemm_bf16_rows_kernel<UP, 4>), grid, block, 0, stream, X, offsets,
+                       N, A, B, K, Nout, n_slices, max_rows, out);
+}
+
 // ---------------------------------------------------------------- fp32 (VALU)
 constexpr int kFBM = 64, kFBN = 64, kFBK = 16;
 
@@ -431,7 +601,9 @@ static int round8(int x) { return (x + 7) & ~7; }
 hipError_t launch_expert_up(const void* x_perm, const int32_t* offsets, const void* w1,
                             const void* w3, int N, int d, int f, int max_rows, bool bf16,
                             void* act, hipStream_t stream) {
-  if (bf16) {
+  if (bf16 && rows_mt(max_rows, N) > 0) {
+    launch_rows<true>(rows_mt(max_rows, N), x_perm, offsets, N, w1, w3, d, f, max_rows, act, stream);
+  } else if (bf16) {
     const int n_tiles = f / (kBN / 2);
     const int mt_bound = (max_rows + kBM - 1) / kBM + N;
     const int grid = round8(mt_bound * n_tiles);
@@ -453,7 +625,10 @@ hipError_t launch_expert_up(const void* x_perm, const int32_t* offsets, const vo
 hipError_t launch_expert_down(const void* act, const int32_t* offsets, const void* w2, int N,
                               int d, int f, int max_rows, bool bf16, float* y_perm,
                               hipStream_t stream) {
-  if (bf16) {
+  if (bf16 && rows_mt(max_rows, N) > 0) {
+    launch_rows<false>(rows_mt(max_rows, N), act, offsets, N, w2, nullptr, f, d, max_rows,
+                       static_cast<void*>(y_perm), stream);
+  } else if (bf16) {
     const int n_tiles = d / kBN;
     const int mt_bound = (max_rows + kBM - 1) / kBM + N;
     const int grid = round8(mt_bound * n_tiles);

@@ -8,9 +8,10 @@
 
 namespace moe {
 
+size_t route_ws_bytes(int T, int d, int N);   // bf16 router k-split partials (0 if none)
 hipError_t launch_route(const void* hidden, const void* w_router, const float* bias, int T, int d,
                         int N, int k, bool bf16, float* logits, int32_t* topk_idx, float* topk_w,
-                        int32_t* counts, hipStream_t stream);
+                        int32_t* counts, void* ws, hipStream_t stream);
 
 size_t permute_ws_bytes(int T, int N);
 hipError_t launch_permute(const void* hidden, const int32_t* topk_idx, int T, int d, int N, int k,

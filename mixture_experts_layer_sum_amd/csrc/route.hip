@@ -7,19 +7,17 @@
 // 2kiu.com/news/2885792 §5.3: equal logits are ranked by ascending expert id.
 // cf-1.com/news/5914943 §2.3: tokens_per_expert counts the router's choices.
 //
-// One block = 64 tokens, 4 waves; wave w owns tokens 16w..16w+15 of the block.
-// bf16: the logits tile is a chain of 16x16x32 MFMAs whose A operand (hidden
-// rows) streams from HBM straight into registers (each hidden element is used
-// by exactly one wave) and whose B operand (W_router, k-contiguous after an
-// in-register 4x8 transpose) is staged per k-chunk in LDS and shared by the
-// four waves.  The epilogue keeps the tile in LDS, and each wave runs k rounds
-// of a wave64 argmax reduction per token.
+// bf16: 16x16x32 MFMAs; a block's 8 waves split the hidden dimension and
+// their partial logits are summed in a fixed order (see router_bf16_kernel).
+// fp32: one block = 64 tokens, 4 waves, a plain fp32 dot product per
+// (token, expert).  Both end with the same epilogue: the logits tile stays in
+// LDS and one wave per token runs k rounds of a wave64 argmax reduction.
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace moe {
 
-constexpr int kRtTok = 64;
+constexpr int kRtTok = 64;        // fp32 router: tokens per block
 constexpr int kRtThreads = 256;
 
 __global__ void zero_i32_kernel(int32_t* __restrict__ p, int n) {
@@ -27,188 +25,287 @@ __global__ void zero_i32_kernel(int32_t* __restrict__ p, int n) {
   if (i < n) p[i] = 0;
 }
 
-// Top-k + softmax + histogram for the rows of one wave.  lg: LDS tile
-// [64][ldl] of fp32 logits (bias included).  Ordering: larger logit first,
-// lower expert id first among equal logits.
-__device__ __forceinline__ void topk_rows(const float* lg, int ldl, int t0, int T, int N, int k,
-                                          int32_t* __restrict__ topk_idx,
-                                          float* __restrict__ topk_w, int* hist) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int rr = 0; rr < 16; ++rr) {
-    const int r = w * 16 + rr;
-    const int t = t0 + r;
-    if (t >= T) break;
-    float v[4];
-    unsigned taken = 0;
+// Top-k + softmax + histogram of one token, by one wave.  lg: the token's N
+// fp32 logits (bias included) in LDS.  Ordering: larger logit first, lower
+// expert id first among equal logits.  k rounds of a wave64 argmax.
+__device__ __forceinline__ void topk_row(const float* lg, int t, int N, int k,
+                                         int32_t* __restrict__ topk_idx,
+                                         float* __restrict__ topk_w, int* hist) {
+  const int lane = threadIdx.x & 63;
+  float v[4];
+  unsigned taken = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int e = lane + 64 * c;
+    v[c] = (e < N) ? lg[e] : 0.f;
+    if (e >= N) taken |= 1u << c;
+  }
+  float sv[4] = {0.f, 0.f, 0.f, 0.f};
+  int si[4] = {0, 0, 0, 0};
+  float vmax = 0.f;
+  for (int jj = 0; jj < k; ++jj) {
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int e = lane + 64 * c;
-      v[c] = (e < N) ? lg[r * ldl + e] : 0.f;
-      if (e >= N) taken |= 1u << c;
-    }
-    float sv[4] = {0.f, 0.f, 0.f, 0.f};
-    int si[4] = {0, 0, 0, 0};
-    float vmax = 0.f;
-    for (int j = 0; j < k; ++j) {
-      float bv = -INFINITY;
-      int be = 0x7fffffff;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if (!(taken & (1u << c))) {
-          const int e = lane + 64 * c;
-          if (be == 0x7fffffff || v[c] > bv) { bv = v[c]; be = e; }
-        }
-      }
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) {
-        const float ov = __shfl_xor(bv, m, 64);
-        const int oe = __shfl_xor(be, m, 64);
-        if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-      }
-      if ((be & 63) == lane) taken |= 1u << (be >> 6);
-      if (j == 0) vmax = bv;
-      if ((j & 63) == lane) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          if (c == (j >> 6)) { sv[c] = bv; si[c] = be; }
+      if (!(taken & (1u << c))) {
+        const int e = lane + 64 * c;
+        if (be == 0x7fffffff || v[c] > bv) { bv = v[c]; be = e; }
       }
     }
-    float s = 0.f;
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if (lane + 64 * c < k) s += __expf(sv[c] - vmax);
-    s = wave_sum(s);
-    const float inv = 1.f / s;
+    for (int m = 32; m >= 1; m >>= 1) {
+      const float ov = __shfl_xor(bv, m, 64);
+      const int oe = __shfl_xor(be, m, 64);
+      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+    }
+    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    if (jj == 0) vmax = bv;
+    if ((jj & 63) == lane) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int j = lane + 64 * c;
-      if (j < k) {
-        topk_idx[(size_t)t * k + j] = si[c];
-        topk_w[(size_t)t * k + j] = __expf(sv[c] - vmax) * inv;
-        atomicAdd(&hist[si[c]], 1);
-      }
+      for (int c = 0; c < 4; ++c)
+        if (c == (jj >> 6)) { sv[c] = bv; si[c] = be; }
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    if (lane + 64 * c < k) s += __expf(sv[c] - vmax);
+  s = wave_sum(s);
+  const float inv = 1.f / s;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int jj = lane + 64 * c;
+    if (jj < k) {
+      topk_idx[(size_t)t * k + jj] = si[c];
+      topk_w[(size_t)t * k + jj] = __expf(sv[c] - vmax) * inv;
+      atomicAdd(&hist[si[c]], 1);
     }
   }
 }
 
-template <int NT>
-struct RouterCfg {
-  static constexpr int Npad = 16 * NT;
-  static constexpr int BK = NT <= 4 ? 256 : (NT == 8 ? 128 : 64);
-  static constexpr int ldw = BK + 8;                     // bf16 elements per LDS row of W^T
-  static constexpr int ldl = Npad + 1;                   // floats per LDS row of logits
-  static constexpr int w_bytes = Npad * ldw * 2;
-  static constexpr int l_bytes = kRtTok * ldl * 4;
-  static constexpr int smem = w_bytes > l_bytes ? w_bytes : l_bytes;
-};
+// Top-k for the 16 rows of one wave (fp32 router): rows 16w .. 16w+15 of lg.
+__device__ __forceinline__ void topk_rows(const float* lg, int ldl, int t0, int T, int N, int k,
+                                          int32_t* __restrict__ topk_idx,
+                                          float* __restrict__ topk_w, int* hist) {
+  const int w = threadIdx.x >> 6;
+  for (int rr = 0; rr < 16; ++rr) {
+    const int r = w * 16 + rr;
+    if (t0 + r >= T) break;
+    topk_row(lg + r * ldl, t0 + r, N, k, topk_idx, topk_w, hist);
+  }
+}
 
-template <int NT>
-__global__ __launch_bounds__(kRtThreads) void router_bf16_kernel(
+// 8x8 transpose of bf16: r[kk] holds columns 0..7 of k-row kk; c[col] gets
+// k-rows 0..7 of column col (an MFMA B operand).
+__device__ __forceinline__ void transpose8x8_rt(const uint4 (&r)[8], uint4 (&c)[8]) {
+  uint32_t w[8][4];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    w[kk][0] = r[kk].x; w[kk][1] = r[kk].y; w[kk][2] = r[kk].z; w[kk][3] = r[kk].w;
+  }
+#pragma unroll
+  for (int col = 0; col < 8; ++col) {
+    const int h = col >> 1;
+    uint32_t o[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t lo = w[2 * m][h], hi = w[2 * m + 1][h];
+      o[m] = (col & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+    }
+    c[col] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// bf16 router.  A block owns 16*MTR tokens; its 8 waves split the k range
+// (32-deep steps dealt round-robin) and each wave computes all expert columns
+// for all of the block's tokens with 16x16x32 MFMAs:
+//   A operand  lane 16g + j: token row j of a 16-token tile, k 8g .. 8g+7
+//   B operand  lane 16g + j loads k-rows 8g .. 8g+7 of W_router columns
+//              8j .. 8j+7 (+128 per pass) as 16-byte vectors and transposes
+//              them in registers; MFMA c then yields column 8j + c.
+// The eight partial tiles are summed in wave order through LDS (fixed order,
+// so the logits are reproducible), the bias is added, and each wave then runs
+// the top-k / softmax / histogram epilogue on its share of the tokens.
+// NW = LDS row width (expert columns kept); WAVES * MTR * NW <= 2048 (LDS).
+// U = k-steps whose loads are in flight together (register budget permitting).
+// With few token tiles the k range is also split across gridDim.y blocks:
+// each then writes its partial tile to `part_out` [gridDim.y][T][N] and
+// router_finish_kernel completes the tokens.
+template <int MTR, int NW, int WAVES, int U>
+__global__ __launch_bounds__(64 * WAVES) void router_bf16_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ wr,
     const float* __restrict__ bias, int T, int d, int N, int k, float* __restrict__ logits,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int32_t* __restrict__ counts) {
-  using C = RouterCfg<NT>;
-  constexpr int BK = C::BK, ldw = C::ldw, NS = BK / 32;
-  __shared__ __align__(16) unsigned char smem[C::smem];
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int32_t* __restrict__ counts,
+    float* __restrict__ part_out) {
+  constexpr int P = (NW + 127) / 128;          // 128-column passes
+  constexpr int ROWS = 16 * MTR;
+  constexpr int LD = NW + 1;
+  __shared__ float part[WAVES * ROWS * LD];
   __shared__ int hist[256];
-  uint16_t* Ws = reinterpret_cast<uint16_t*>(smem);
-  float* lg = reinterpret_cast<float*>(smem);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 15, g = lane >> 4;
+  const int t0 = blockIdx.x * ROWS;
+  for (int i = tid; i < 256; i += 64 * WAVES) hist[i] = 0;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int t0 = blockIdx.x * kRtTok;
-  const int g = lane >> 4, ml = lane & 15;
-  const int row = t0 + w * 16 + ml;
-  const bool rv = row < T;
-  const uint16_t* hrow = hidden + (size_t)(rv ? row : 0) * d + 8 * g;
-  for (int i = tid; i < 256; i += kRtThreads) hist[i] = 0;
-
-  f32x4 acc[NT];
+  const uint16_t* arow[MTR];
 #pragma unroll
-  for (int c = 0; c < NT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < MTR; ++m) arow[m] = hidden + (size_t)min(t0 + 16 * m + j, T - 1) * d + 8 * g;
+  const bool nvec = (N & 7) == 0;
+
+  f32x4 acc[MTR][P][8];
+#pragma unroll
+  for (int m = 0; m < MTR; ++m)
+#pragma unroll
+    for (int q = 0; q < P; ++q)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[m][q][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const uint4 z4 = make_uint4(0, 0, 0, 0);
-  uint4 a[NS];
-  {
-    const int klen = d < BK ? d : BK;
+  // this block's k range: steps [ks0, ks1) of 32, dealt round-robin to the waves
+  const int nks = d / 32;
+  const int per = (nks + gridDim.y - 1) / gridDim.y;
+  const int ks0 = blockIdx.y * per, ks1 = min(nks, ks0 + per);
+  // U k-steps per iteration, all of their loads issued before any MFMA; a step
+  // past the end re-reads the last one with a zero A operand (adds nothing)
+  for (int ks = ks0 + w; ks < ks1; ks += U * WAVES) {
+    uint4 av[U][MTR], wv[U][P][8];
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-      a[s] = (rv && 32 * s < klen) ? *reinterpret_cast<const uint4*>(hrow + 32 * s) : z4;
-  }
-  const bool nvec = (N & 7) == 0;
-  for (int k0 = 0; k0 < d; k0 += BK) {
-    const int klen = (d - k0) < BK ? (d - k0) : BK;
-    __syncthreads();
-    // Stage W_router rows [k0, k0+klen) transposed: Ws[n][kk] (k contiguous).
-    const int kq_n = klen >> 2, cg_n = C::Npad >> 3;
-    for (int it = tid; it < kq_n * cg_n; it += kRtThreads) {
-      const int kq = it % kq_n, cg = it / kq_n;
-      uint32_t r[4][4];
+    for (int u = 0; u < U; ++u) {
+      const int ksu = ks + u * WAVES;
+      const bool live = ksu < ks1;
+      const int k0 = 32 * (live ? ksu : ks);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int kk = k0 + 4 * kq + q;
-        const uint16_t* src = wr + (size_t)kk * N + 8 * cg;
-        if (nvec) {
-          uint4 x = (8 * cg < N) ? *reinterpret_cast<const uint4*>(src) : z4;
-          r[q][0] = x.x; r[q][1] = x.y; r[q][2] = x.z; r[q][3] = x.w;
-        } else {
-          uint16_t e8[8];
+      for (int m = 0; m < MTR; ++m)
+        av[u][m] = live ? *reinterpret_cast<const uint4*>(arow[m] + k0) : z4;
 #pragma unroll
-          for (int c = 0; c < 8; ++c) e8[c] = (8 * cg + c < N) ? src[c] : (uint16_t)0;
+      for (int q = 0; q < P; ++q) {
+        const int col = 128 * q + 8 * j;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) r[q][c] = e8[2 * c] | ((uint32_t)e8[2 * c + 1] << 16);
+        for (int kk = 0; kk < 8; ++kk) {
+          const uint16_t* src = wr + (size_t)(k0 + 8 * g + kk) * N + col;
+          if (nvec) {
+            wv[u][q][kk] = (col < N) ? *reinterpret_cast<const uint4*>(src) : z4;
+          } else {
+            uint32_t e2[4];
+#pragma unroll
+            for (int c2 = 0; c2 < 4; ++c2) {
+              const uint32_t lo = (col + 2 * c2 < N) ? src[2 * c2] : 0u;
+              const uint32_t hi = (col + 2 * c2 + 1 < N) ? src[2 * c2 + 1] : 0u;
+              e2[c2] = lo | (hi << 16);
+            }
+            wv[u][q][kk] = make_uint4(e2[0], e2[1], e2[2], e2[3]);
+          }
         }
       }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int q = 0; q < P; ++q) {
+        uint4 bf[8];
+        transpose8x8_rt(wv[u][q], bf);
+#pragma unroll
+        for (int m = 0; m < MTR; ++m)
+#pragma unroll
+          for (int c = 0; c < 8; ++c) acc[m][q][c] = mfma16(av[u][m], bf[c], acc[m][q][c]);
+      }
+  }
+  // partial tile of this wave: row 16m + 4g + r, column 128q + 8j + c
+  float* mine = part + w * ROWS * LD;
+#pragma unroll
+  for (int m = 0; m < MTR; ++m)
+#pragma unroll
+    for (int q = 0; q < P; ++q)
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const int h = c >> 1;
-        uint32_t lo, hi;
-        if (c & 1) {
-          lo = (r[0][h] >> 16) | (r[1][h] & 0xFFFF0000u);
-          hi = (r[2][h] >> 16) | (r[3][h] & 0xFFFF0000u);
-        } else {
-          lo = (r[0][h] & 0xFFFFu) | (r[1][h] << 16);
-          hi = (r[2][h] & 0xFFFFu) | (r[3][h] << 16);
-        }
-        *reinterpret_cast<uint2*>(Ws + (8 * cg + c) * ldw + 4 * kq) = make_uint2(lo, hi);
-      }
-    }
-    __syncthreads();
-    uint4 an[NS];
-    const int kn = k0 + BK;
-    const int klen_n = (d - kn) < BK ? (d - kn) : BK;
+        const int col = 128 * q + 8 * j + c;
+        if (col < NW) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-      an[s] = (rv && kn < d && 32 * s < klen_n) ? *reinterpret_cast<const uint4*>(hrow + kn + 32 * s) : z4;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      if (32 * s < klen) {
-#pragma unroll
-        for (int c = 0; c < NT; ++c) {
-          const uint4 b = *reinterpret_cast<const uint4*>(Ws + (16 * c + ml) * ldw + 32 * s + 8 * g);
-          acc[c] = mfma16(a[s], b, acc[c]);
+          for (int r = 0; r < 4; ++r) mine[(16 * m + 4 * g + r) * LD + col] = acc[m][q][c][r];
         }
       }
-    }
-#pragma unroll
-    for (int s = 0; s < NS; ++s) a[s] = an[s];
-  }
-  __syncthreads();   // every wave is done with Ws; reuse the space for the logits tile
-#pragma unroll
-  for (int c = 0; c < NT; ++c) {
-    const int col = 16 * c + ml;
-    const float b = (bias != nullptr && col < N) ? bias[col] : 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) lg[(w * 16 + 4 * g + r) * C::ldl + col] = acc[c][r] + b;
-  }
   __syncthreads();
-  for (int i = tid; i < kRtTok * N; i += kRtThreads) {
+  // fixed-order sum over the waves; with a k split the block's partial goes out
+  if (gridDim.y > 1) {
+    float* dst = part_out + (size_t)blockIdx.y * T * N;
+    for (int i = tid; i < ROWS * N; i += 64 * WAVES) {
+      const int r = i / N, e = i - r * N;
+      float v = part[r * LD + e];
+#pragma unroll
+      for (int ww = 1; ww < WAVES; ++ww) v += part[(ww * ROWS + r) * LD + e];
+      if (t0 + r < T) dst[(size_t)(t0 + r) * N + e] = v;
+    }
+    return;
+  }
+  // ... else bias, logits out; the sum lands in wave 0's tile
+  for (int i = tid; i < ROWS * N; i += 64 * WAVES) {
     const int r = i / N, e = i - r * N;
-    if (t0 + r < T) logits[(size_t)(t0 + r) * N + e] = lg[r * C::ldl + e];
+    float v = part[r * LD + e];
+#pragma unroll
+    for (int ww = 1; ww < WAVES; ++ww) v += part[(ww * ROWS + r) * LD + e];
+    v += (bias != nullptr) ? bias[e] : 0.f;
+    part[r * LD + e] = v;
+    if (t0 + r < T) logits[(size_t)(t0 + r) * N + e] = v;
   }
-  topk_rows(lg, C::ldl, t0, T, N, k, topk_idx, topk_w, hist);
   __syncthreads();
-  for (int e = tid; e < N; e += kRtThreads)
+  for (int r = w; r < ROWS; r += WAVES) {
+    if (t0 + r < T) topk_row(part + r * LD, t0 + r, N, k, topk_idx, topk_w, hist);
+  }
+  __syncthreads();
+  for (int e = tid; e < N; e += 64 * WAVES)
     if (hist[e]) atomicAdd(&counts[e], hist[e]);
+}
+
+// Completes the tokens of a k-split router: sums the KS partial tiles in
+// slice order, adds the bias, writes the logits and runs the top-k epilogue.
+// One block = 4 tokens, 4 waves (one token each).
+__global__ __launch_bounds__(256) void router_finish_kernel(const float* __restrict__ part, int KS,
+                                                            const float* __restrict__ bias, int T,
+                                                            int N, int k, float* __restrict__ logits,
+                                                            int32_t* __restrict__ topk_idx,
+                                                            float* __restrict__ topk_w,
+                                                            int32_t* __restrict__ counts) {
+  __shared__ float lg[4 * 257];
+  __shared__ int hist[256];
+  const int tid = threadIdx.x, w = tid >> 6;
+  const int t0 = blockIdx.x * 4;
+  hist[tid] = 0;
+  for (int i = tid; i < 4 * N; i += 256) {
+    const int r = i / N, e = i - r * N;
+    const int t = t0 + r;
+    if (t >= T) continue;
+    const float* src = part + (size_t)t * N + e;
+    const size_t slice = (size_t)T * N;
+    float v = 0.f;
+    for (int ks = 0; ks < KS; ++ks) v += src[ks * slice];
+    v += (bias != nullptr) ? bias[e] : 0.f;
+    lg[r * 257 + e] = v;
+    logits[(size_t)t * N + e] = v;
+  }
+  __syncthreads();
+  if (t0 + w < T) topk_row(lg + w * 257, t0 + w, N, k, topk_idx, topk_w, hist);
+  __syncthreads();
+  for (int e = tid; e < N; e += 256)
+    if (hist[e]) atomicAdd(&counts[e], hist[e]);
+}
+
+// Number of k slices for the bf16 router: enough blocks to cover the CUs when
+// the token tiles alone do not, each slice at least 256 deep.
+static int router_kslices(int T, int d, int N) {
+  const int rows = (N <= 64) ? (T >= 64 * 256 ? 64 : (T >= 32 * 256 ? 32 : 16))
+                             : (N <= 128 ? (T >= 32 * 256 ? 32 : 16) : 16);
+  const int tiles = (T + rows - 1) / rows;
+  int ks = 256 / tiles;
+  ks = ks < 1 ? 1 : ks;
+  const int maxks = d / 256 < 1 ? 1 : d / 256;
+  return ks > maxks ? maxks : ks;
+}
+
+size_t route_ws_bytes(int T, int d, int N) {
+  const int ks = router_kslices(T, d, N);
+  return ks > 1 ? static_cast<size_t>(ks) * T * N * sizeof(float) : 0;
 }
 
 // fp32: the same epilogue after a plain fp32 dot product per (token, expert).
@@ -243,7 +340,7 @@ __global__ __launch_bounds__(kRtThreads) void router_f32_kernel(
 
 hipError_t launch_route(const void* hidden, const void* w_router, const float* bias, int T, int d,
                         int N, int k, bool bf16, float* logits, int32_t* topk_idx, float* topk_w,
-                        int32_t* counts, hipStream_t stream) {
+                        int32_t* counts, void* ws, hipStream_t stream) {
   hipLaunchKernelGGL(zero_i32_kernel, dim3((N + 255) / 256), dim3(256), 0, stream, counts, N);
   const dim3 grid((T + kRtTok - 1) / kRtTok), block(kRtThreads);
   if (!bf16) {
@@ -254,16 +351,28 @@ hipError_t launch_route(const void* hidden, const void* w_router, const float* b
   }
   const auto* h = static_cast<const uint16_t*>(hidden);
   const auto* wr = static_cast<const uint16_t*>(w_router);
-  const int nt = (N + 15) / 16;
-#define MOE_ROUTER_CASE(NTV)                                                                   \
-  hipLaunchKernelGGL(router_bf16_kernel<NTV>, grid, block, 0, stream, h, wr, bias, T, d, N, k, \
-                     logits, topk_idx, topk_w, counts)
-  if (nt <= 1) MOE_ROUTER_CASE(1);
-  else if (nt <= 2) MOE_ROUTER_CASE(2);
-  else if (nt <= 4) MOE_ROUTER_CASE(4);
-  else if (nt <= 8) MOE_ROUTER_CASE(8);
-  else MOE_ROUTER_CASE(16);
-#undef MOE_ROUTER_CASE
+  // widest token tile the LDS allows for this N once there are enough tokens
+  // for about one block per CU; otherwise split k across blocks as well
+  const int KS = router_kslices(T, d, N);
+  float* part = static_cast<float*>(ws);
+#define MOE_ROUTER(MTR, NW, WV)                                                                \
+  hipLaunchKernelGGL((router_bf16_kernel<MTR, NW, WV, 1>),                                   \
+                     dim3((T + 16 * MTR - 1) / (16 * MTR), KS), dim3(64 * WV), 0, stream, h,  \
+                     wr, bias, T, d, N, k, logits, topk_idx, topk_w, counts, part)
+  if (N <= 64) {
+    if (T >= 64 * 256) MOE_ROUTER(4, 64, 8);
+    else if (T >= 32 * 256) MOE_ROUTER(2, 64, 8);
+    else MOE_ROUTER(1, 64, 8);
+  } else if (N <= 128) {
+    if (T >= 32 * 256) MOE_ROUTER(2, 128, 8);
+    else MOE_ROUTER(1, 128, 8);
+  } else {
+    MOE_ROUTER(1, 256, 8);
+  }
+  if (KS > 1)
+    hipLaunchKernelGGL(router_finish_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, part, KS,
+                       bias, T, N, k, logits, topk_idx, topk_w, counts);
+#undef MOE_ROUTER
   return hipGetLastError();
 }
 

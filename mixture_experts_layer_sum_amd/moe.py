@@ -25,7 +25,7 @@ _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 SIGNATURES = {
     "moe_status_string": (ctypes.c_char_p, [_I]),
     "moe_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
-    "moe_route": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
+    "moe_route": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P]),
     "moe_permute": (_I, [_P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "moe_expert_ffn": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
     "moe_expert_up": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
@@ -91,7 +91,7 @@ def _empty(shape, dtype, device, out):
 
 
 def moe_route(hidden, w_router, k, bias=None, logits=None, topk_idx=None, topk_w=None,
-              counts=None, stream=None):
+              counts=None, ws=None, stream=None):
     T, d = hidden.shape
     N = w_router.shape[1]
     dev = hidden.device
@@ -99,9 +99,12 @@ def moe_route(hidden, w_router, k, bias=None, logits=None, topk_idx=None, topk_w
     topk_idx = _empty((T, k), torch.int32, dev, topk_idx)
     topk_w = _empty((T, k), torch.float32, dev, topk_w)
     counts = _empty((N,), torch.int32, dev, counts)
+    if ws is None:
+        ws = torch.empty(max(1, workspace_size(MOE_OP_ROUTE, T, d, N, k, 1, hidden.dtype)),
+                         dtype=torch.uint8, device=dev)
     _check(_lib.moe_route(_ptr(hidden), _ptr(w_router), _ptr(bias), T, d, N, k, _dt(hidden),
-                          _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _stream(stream)),
-           "moe_route")
+                          _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(ws),
+                          ws.numel(), _stream(stream)), "moe_route")
     return logits, topk_idx, topk_w, counts
 
 
@@ -197,6 +200,7 @@ class MoEBuffers:
         self.y_perm = e((T * k, d), torch.float32)
         self.y = e((T, d), dtype)
         self.aux = e((1,), torch.float32)
+        self.ws_route = e((max(1, workspace_size(MOE_OP_ROUTE, T, d, N, k, f, dtype)),), torch.uint8)
         self.ws_permute = e((max(1, workspace_size(MOE_OP_PERMUTE, T, d, N, k, f, dtype)),), torch.uint8)
         self.ws_aux = e((max(1, workspace_size(MOE_OP_AUX_LOSS, T, d, N, k, f, dtype)),), torch.uint8)
 
@@ -212,7 +216,8 @@ def moe_forward(hidden, w_router, w1, w3, w2, k, capacity_factor=0.0, bias=None,
     if bufs is None:
         bufs = MoEBuffers(T, d, N, k, f, hidden.dtype, hidden.device)
     b = bufs
-    moe_route(hidden, w_router, k, bias, b.logits, b.topk_idx, b.topk_w, b.counts, stream)
+    moe_route(hidden, w_router, k, bias, b.logits, b.topk_idx, b.topk_w, b.counts, b.ws_route,
+              stream)
     moe_permute(hidden, b.topk_idx, N, capacity_factor, b.x_perm, b.perm_src, b.slot_row, b.kept,
                 b.offsets, b.ws_permute, stream)
     moe_expert_up(b.x_perm, b.offsets, w1, w3, b.act, stream)

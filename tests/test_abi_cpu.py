@@ -46,19 +46,24 @@ def test_status_strings():
 
 def test_workspace_sizes():
     assert lib.moe_workspace_size(moe.MOE_OP_ROUTE, 64, 128, 8, 2, 256, F32) == 0
+    # bf16 router: partial logits when few token tiles split the hidden dim
+    assert lib.moe_workspace_size(moe.MOE_OP_ROUTE, 8192, 4096, 8, 2, 256, BF16) == 0
+    assert lib.moe_workspace_size(moe.MOE_OP_ROUTE, 256, 4096, 128, 2, 256, BF16) == 16 * 256 * 128 * 4
     assert lib.moe_workspace_size(moe.MOE_OP_COMBINE, 64, 128, 8, 2, 256, F32) == 0
     # two int32 [chunks, N] tables, chunks of 256 tokens
     assert lib.moe_workspace_size(moe.MOE_OP_PERMUTE, 257, 128, 8, 2, 256, F32) == 2 * 2 * 8 * 4
     assert lib.moe_workspace_size(moe.MOE_OP_EXPERT_FFN, 64, 128, 8, 2, 256, BF16) == 64 * 2 * 256 * 2
     assert lib.moe_workspace_size(moe.MOE_OP_EXPERT_FFN, 64, 128, 8, 2, 256, F32) == 64 * 2 * 256 * 4
-    assert lib.moe_workspace_size(moe.MOE_OP_AUX_LOSS, 256, 128, 8, 2, 256, F32) == 8 * 4
+    # one fp32 [N] partial per 64 tokens
+    assert lib.moe_workspace_size(moe.MOE_OP_AUX_LOSS, 256, 128, 8, 2, 256, F32) == 4 * 8 * 4
+    assert lib.moe_workspace_size(moe.MOE_OP_AUX_LOSS, 65, 128, 8, 2, 256, F32) == 2 * 8 * 4
     assert lib.moe_workspace_size(17, 64, 128, 8, 2, 256, F32) == 0
     assert lib.moe_workspace_size(moe.MOE_OP_PERMUTE, 0, 128, 8, 2, 256, F32) == 0
 
 
 def route(**kw):
     a = dict(hidden=P, w_router=P, bias=NUL, T=64, d=128, N=8, k=2, dt=BF16, logits=P,
-             topk_idx=P, topk_w=P, counts=P, stream=S)
+             topk_idx=P, topk_w=P, counts=P, ws=P, ws_bytes=1 << 30, stream=S)
     a.update(kw)
     return lib.moe_route(*a.values())
 
@@ -68,7 +73,8 @@ def route(**kw):
     (dict(topk_idx=NUL), INV), (dict(topk_w=NUL), INV), (dict(counts=NUL), INV),
     (dict(T=0), INV), (dict(T=-3), INV), (dict(N=0), INV), (dict(k=0), INV), (dict(k=9), INV),
     (dict(d=0), INV), (dict(N=257, k=2), UNS), (dict(d=100), UNS), (dict(dt=2), UNS),
-    (dict(T=2 ** 30, k=2), UNS),
+    (dict(T=2 ** 30, k=2), UNS), (dict(T=256, d=4096, N=128, ws_bytes=0), WS),
+    (dict(T=256, d=4096, N=128, ws=NUL), INV),
 ])
 def test_route_rejects(kw, status):
     assert route(**kw) == status

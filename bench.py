@@ -25,6 +25,10 @@ Helper modes for profiling (no timing claims):
   --copy-calibration MiB   also run a plain device copy of that size (read once,
                            written once) so rocprofv3 counters can be scaled
   --summarize-rocprof DIR  turn rocprofv3 csv output into a short text summary
+  --write-traffic FETCH_DIR WRITE_DIR
+                           turn two rocprofv3 --pmc runs (FETCH_SIZE, then
+                           WRITE_SIZE, each with --copy-calibration) into the
+                           per-launch HBM traffic record of the grouped GEMMs
 """
 from __future__ import annotations
 
@@ -177,10 +181,110 @@ def traffic_entry():
     return rec.get("bytes_per_launch")
 
 
-def summarize_rocprof(d, out):
-    """Short text summary of rocprofv3 csv output in directory `d`."""
+def _counter_rows(d, counter):
+    import csv
+    rows = []
+    for p in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        rows += [r for r in csv.DictReader(open(p)) if r.get("Counter_Name") == counter]
+    if not rows:
+        raise SystemExit(f"no {counter} rows under {d}")
+    return rows
+
+
+def write_traffic(fetch_dir, write_dir, calib_mib, cmds):
+    """HBM bytes per launch of both grouped GEMMs from FETCH_SIZE / WRITE_SIZE (KiB per dispatch).
+
+    Each counter is scaled by what it reads for the calibration copy (`calib_mib` MiB read and
+    written once, the largest __amd_rocclr_copyBuffer dispatches in the same run).
+    """
+    from mixture_experts_layer_sum_amd import synth
+    w = synth.WORKLOADS["mixtral"]
+    A = w.T * w.k                      # no capacity limit: every assignment is a routed row
+    s = 2
+    algo = {"up": A * w.d * s + 2 * w.N * w.d * w.f * s + A * w.f * s,
+            "down": A * w.f * s + w.N * w.f * w.d * s + A * w.d * 4}
+    names = {"up": "grouped_gemm_bf16_kernel<true>", "down": "grouped_gemm_bf16_kernel<false>"}
+    calib_kib = calib_mib * 1024.0
+    per = {}
+    factor = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(d, counter)
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        big = [v for v in copies if v > 0.25 * calib_kib]
+        if not big:
+            raise SystemExit(f"no calibration copy found in {d}")
+        factor[counter] = calib_kib / (sum(big) / len(big))
+        for key, kname in names.items():
+            vals = [float(r["Counter_Value"]) for r in rows if kname in r["Kernel_Name"]]
+            per[(key, counter)] = sum(vals) / len(vals)
+    src = os.path.relpath(GEMM_SRC, ROOT)
+    recs = {}
+    for key in ("up", "down"):
+        rd = per[(key, "FETCH_SIZE")] * 1024 * factor["FETCH_SIZE"]
+        wr = per[(key, "WRITE_SIZE")] * 1024 * factor["WRITE_SIZE"]
+        recs[key] = {"kernel": names[key], "fetch_size_kib_per_dispatch": per[(key, "FETCH_SIZE")],
+                     "write_size_kib_per_dispatch": per[(key, "WRITE_SIZE")],
+                     "bytes_per_launch": rd + wr, "read_bytes_per_launch": rd,
+                     "write_bytes_per_launch": wr, "algorithmic_bytes_per_launch": algo[key]}
+    rec = dict(recs["up"])
+    rec.update({"workload": f"{w.name} (seed 0, A = {A} routed rows)", "kernel_source": src,
+                "kernel_source_sha256_16": src_hash(),
+                "copy_calibration": {"mib": calib_mib, "fetch_factor": factor["FETCH_SIZE"],
+                                     "write_factor": factor["WRITE_SIZE"]},
+                "down": recs["down"], "commands": cmds})
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(rec, fh, indent=2)
+        fh.write("\n")
+    md = [f"# HBM traffic of the grouped GEMMs, Mixtral-shaped layer (seed 0, A = {A} routed rows)",
+          "", "Commands (repo root, on one MI355X; one counter per run):", ""]
+    md += [f"    {c}" for c in cmds]
+    md += ["", f"Calibration in the same processes: a plain {calib_mib} MiB device copy "
+           f"(`--copy-calibration {calib_mib}`, torch `copy_`, runs as `__amd_rocclr_copyBuffer`); "
+           f"FETCH_SIZE is scaled by {factor['FETCH_SIZE']:.3f} and WRITE_SIZE by "
+           f"{factor['WRITE_SIZE']:.3f} so that the copy reads and writes its own size.", "",
+           "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled read GB | scaled write GB "
+           "| algorithmic GB | traffic / algorithmic |", "|---|---|---|---|---|---|---|"]
+    for key in ("up", "down"):
+        r = recs[key]
+        md.append(f"| {key} `{r['kernel']}` | {r['fetch_size_kib_per_dispatch']:.0f} | "
+                  f"{r['write_size_kib_per_dispatch']:.0f} | {r['read_bytes_per_launch']/1e9:.3f} | "
+                  f"{r['write_bytes_per_launch']/1e9:.3f} | {r['algorithmic_bytes_per_launch']/1e9:.3f} | "
+                  f"{r['bytes_per_launch']/r['algorithmic_bytes_per_launch']:.2f} |")
+    md += ["", "Algorithmic bytes: up = x_perm rows (A*d) + W1 and W3 of the 8 experts (2*N*d*f) + "
+           "activations written (A*f), bf16; down = activations (A*f) + W2 (N*f*d) bf16 + y_perm "
+           "(A*d) fp32.  Reads above the algorithmic bytes are re-fetches of x_perm row tiles and "
+           "weight column tiles that left the 4 MB per-XCD L2 between the tiles that use them.",
+           f"Kernel source hash at collection time: {src_hash()} (`{src}`)."]
+    out = os.path.join(ROOT, "profiles", "up_down_gemm_mixtral_T8192_hbm_traffic.md")
+    with open(out, "w") as fh:
+        fh.write("\n".join(md) + "\n")
+    print("\n".join(md))
+
+
+def summarize_rocprof(d, out, skip_first=0):
+    """Short text summary of rocprofv3 csv output in directory `d`.
+
+    With `skip_first` W, a second table gives each kernel's mean over its dispatches after the
+    first W (the warm-up forwards), the same dispatches bench.py's own events time.
+    """
     import csv
     lines = []
+    traces = sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True))
+    for p in traces if skip_first else []:
+        per = {}
+        for r in csv.DictReader(open(p)):
+            per.setdefault(r["Kernel_Name"], []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        lines.append(f"per-kernel mean after the first {skip_first} dispatches "
+                     f"({os.path.relpath(p, d)}):")
+        lines.append("| kernel | timed calls | mean us | min us | max us |")
+        lines.append("|---|---|---|---|---|")
+        for name, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+            t = v[skip_first:]
+            if t:
+                lines.append(f"| {name[:90]} | {len(t)} | {sum(t)/len(t):.1f} | {min(t):.1f} | "
+                             f"{max(t):.1f} |")
+        lines.append("")
     stats = sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True))
     for p in stats:
         rows = list(csv.DictReader(open(p)))
@@ -224,10 +328,20 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB")
     ap.add_argument("--summarize-rocprof", default=None, metavar="DIR")
     ap.add_argument("--summary-out", default=None)
+    ap.add_argument("--skip-first", type=int, default=0,
+                    help="with --summarize-rocprof: warm-up dispatches per kernel left out")
+    ap.add_argument("--write-traffic", nargs=2, default=None, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
 
+    if args.write_traffic:
+        cmds = [f"rocprofv3 --pmc {c} -d gpurun_out/pmc_{c} -o run --output-format csv -- python -u "
+                f"bench.py --steps 2 --warmup 1 --no-decode --no-cpu-baseline --copy-calibration "
+                f"{args.copy_calibration}" for c in ("FETCH_SIZE", "WRITE_SIZE")]
+        write_traffic(*args.write_traffic, args.copy_calibration, cmds)
+        return 0
+
     if args.summarize_rocprof:
-        summarize_rocprof(args.summarize_rocprof, args.summary_out)
+        summarize_rocprof(args.summarize_rocprof, args.summary_out, args.skip_first)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this layer's path runs on a single MI355X; "

@@ -10,10 +10,13 @@
 // up   : act[r, :] = silu(X[r] W1_e) * (X[r] W3_e)       (SwiGLU fused in the epilogue)
 // down : y_perm[r, :] = act[r] W2_e                        (fp32 out)
 //
-// bf16 path (MFMA): a block computes a 256-row x 256-column tile with 4 waves
-// (2 x 2, 128 x 128 per wave on 32x32x16 bf16 MFMAs, fp32 accumulators in
-// AGPRs).  For `up` the 256 columns are 128 columns of W1 and the same 128
-// columns of W3, so each lane holds both halves of its SwiGLU products.
+// bf16 path (MFMA): a block computes a 256-row x 256-column tile with 8 waves,
+// two per SIMD: the SIMDs split the tile 2 x 2 into 128 x 128 quadrants and
+// the two waves of a SIMD take 64 columns each (128 x 64 per wave on 32x32x16
+// bf16 MFMAs, fp32 accumulators), so one wave's MFMAs overlap the other's LDS
+// reads and load issue.  For `up` the 256 columns are 128 columns of W1 and
+// the same 128 columns of W3, and each wave holds 32 columns of each, so both
+// halves of its SwiGLU products are in the same lane.
 // k advances 64 at a time through two 64 KB LDS stages filled by direct
 // buffer -> LDS loads (no VGPRs in flight; every request is a whole 128-byte
 // line).  A (x_perm rows) is stored row-major and read with ds_read_b128; the
@@ -34,7 +37,7 @@
 
 namespace moe {
 
-constexpr int kBM = 256, kBN = 256, kGemmThreads = 256;
+constexpr int kBM = 256, kBN = 256, kGemmThreads = 512;
 constexpr int kGroupM = 8;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -143,23 +146,23 @@ __device__ __forceinline__ void gemm_issue(uint16_t* __restrict__ dst, __amdgpu_
   const uint32_t ka = (uint32_t)kstep * (kBK * 2);
   const uint32_t kb = (uint32_t)kstep * (uint32_t)(kBK * Nout * 2);
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, (lds_void*)(dst + (8 * w + i) * 512), 16,
+  for (int i = 0; i < 4; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, (lds_void*)(dst + (4 * w + i) * 512), 16,
                                              a_off[i] + ka, 0, 0, 0);
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rs, (lds_void*)(dst + 16384 + (8 * w + i) * 512), 16,
+  for (int i = 0; i < 4; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rs, (lds_void*)(dst + 16384 + (4 * w + i) * 512), 16,
                                              b_off[i] + kb, 0, 0, 0);
 }
 
 __device__ __forceinline__ void gemm_frags(const uint16_t* __restrict__ st, int s2,
-                                           const int (&a_rd)[4][4], const int (&b_rd)[4][4][2],
-                                           uint4 (&fa)[4], uint4 (&fb)[4]) {
+                                           const int (&a_rd)[4][4], const int (&b_rd)[4][2][2],
+                                           uint4 (&fa)[4], uint4 (&fb)[2]) {
   const uint16_t* bs_ = st + 16384;
 #pragma unroll
   for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const uint4*>(st + a_rd[s2][i]);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 2; ++j) {
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) i16x4*)(bs_ + b_rd[s2][j][0]));
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -169,12 +172,12 @@ __device__ __forceinline__ void gemm_frags(const uint16_t* __restrict__ st, int 
   }
 }
 
-__device__ __forceinline__ void gemm_mma(const uint4 (&fa)[4], const uint4 (&fb)[4],
-                                         f32x16 (&acc)[4][4]) {
+__device__ __forceinline__ void gemm_mma(const uint4 (&fa)[4], const uint4 (&fb)[2],
+                                         f32x16 (&acc)[4][2]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
+    for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
 }
 
 // Wait until this wave's LDS reads are done and all of its direct loads have
@@ -194,9 +197,9 @@ __device__ __forceinline__ void gemm_step(const uint16_t* __restrict__ cur, uint
                                           __amdgpu_buffer_rsrc_t a_rs, __amdgpu_buffer_rsrc_t b_rs,
                                           const uint32_t* a_off, const uint32_t* b_off, int w,
                                           int kstep, int Nout, const int (&a_rd)[4][4],
-                                          const int (&b_rd)[4][4][2], f32x16 (&acc)[4][4],
-                                          uint4 (&fa0)[4], uint4 (&fb0)[4]) {
-  uint4 fa1[4], fb1[4];
+                                          const int (&b_rd)[4][2][2], f32x16 (&acc)[4][2],
+                                          uint4 (&fa0)[4], uint4 (&fb0)[2]) {
+  uint4 fa1[4], fb1[2];
   gemm_frags(cur, 1, a_rd, b_rd, fa1, fb1);
   gemm_mma(fa0, fb0, acc);
   gemm_frags(cur, 2, a_rd, b_rd, fa0, fb0);
@@ -239,7 +242,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = w & 1, wn = w >> 1;
+  const int sm = w & 3, pw = w >> 2;        // SIMD quadrant, half of it
+  const int wm = sm & 1, wn = sm >> 1;
   const int l32 = lane & 31, h = lane >> 5;
   const int n0 = UP ? nt * (kBN / 2) : nt * kBN;
   const int tile_rows = min(rend - r0, kBM);
@@ -254,28 +258,28 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
       const_cast<uint16_t*>((UP ? Wb : Wa) + wexp), 0, wbytes, kRsrcWord3);
 
   // ---- direct global -> LDS loads: wave w issues A instructions 4w..4w+3
-  // (16 rows each) and B instructions 4w..4w+3 (4 k-rows of one sub-tile each).
-  uint32_t a_off[8], b_off[8];
+  // (8 rows each) and B instructions 4w..4w+3 (4 k-rows of one sub-tile each).
+  uint32_t a_off[4], b_off[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int a = 8 * w + i;                                  // A instruction: 8 rows
+  for (int i = 0; i < 4; ++i) {
+    const int a = 4 * w + i;                                  // A instruction: 8 rows
     int row = 8 * a + (lane >> 3);
     row = row < tile_rows ? row : tile_rows - 1;             // rows past the end repeat the last one
     const int c = (lane & 7) ^ ((row >> 1) & 7);
     a_off[i] = (uint32_t)((row * K + 8 * c) * 2);
-    const int b = 8 * w + i;                                  // B instruction: 4 k-rows of sub-tile b / 16
+    const int b = 4 * w + i;                                  // B instruction: 4 k-rows of sub-tile b / 16
     const int kr = 4 * (b & 15) + (lane >> 4);
     const int cb = (lane & 15) ^ (4 * (kr & 3));
     const int colbase = UP ? n0 : n0 + 128 * (b >> 4);
     b_off[i] = (uint32_t)((kr * Nout + colbase + 8 * cb) * 2);
   }
-  const __amdgpu_buffer_rsrc_t b_rs = (w >> 1) ? b_rs1 : b_rs0;   // wave-uniform
+  const __amdgpu_buffer_rsrc_t b_rs = (w >> 2) ? b_rs1 : b_rs0;   // wave-uniform
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
@@ -292,13 +296,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
   // B (transposing read): 16-lane group gq = lane / 16 covers columns
   // 16*(gq & 1) .. +15 of the 32-column fragment and k rows 8*(gq >> 1) + 4t .. +3;
   // lane i of the group points at row (i / 4), columns 4*(i % 4) .. +3.
-  int b_rd[4][4][2];
+  int b_rd[4][2][2];
   {
     const int gq = lane >> 4, i16 = lane & 15;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int q = UP ? (j >> 1) : wn;
-      const int cb = UP ? (wn * 64 + 32 * (j & 1)) : (32 * j);
+    for (int j = 0; j < 2; ++j) {
+      // UP: j = 0 -> W1 (sub-tile 0), j = 1 -> the same W3 columns (sub-tile 1)
+      const int q = UP ? j : wn;
+      const int cb = UP ? (wn * 64 + 32 * pw) : (64 * pw + 32 * j);
       const int col = cb + 16 * (gq & 1) + 4 * (i16 & 3);
 #pragma unroll
       for (int s2 = 0; s2 < 4; ++s2)
@@ -314,8 +319,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
   const int nk = K / kBK;
   gemm_issue(S0, a_rs, b_rs, a_off, b_off, w, 0, Nout);
   gemm_issue(S1, a_rs, b_rs, a_off, b_off, w, min(1, nk - 1), Nout);
-  asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // step 0 landed
-  uint4 fa0[4], fb0[4];
+  asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // step 0 landed
+  uint4 fa0[4], fb0[2];
   gemm_frags(S0, 0, a_rd, b_rd, fa0, fb0);
 #define MOE_STEP(C, N)                                                                      \
   gemm_step(C, C, N, a_rs, b_rs, a_off, b_off, w, min(kt + 2, nk - 1), Nout, a_rd, b_rd, acc, \
@@ -338,12 +343,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
       for (int r = 0; r < 16; ++r) {
         const int row = r0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
         if (row < rend) {
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const float h1 = acc[i][j][r], h3 = acc[i][j + 2][r];
-            const float gv = h1 * __builtin_amdgcn_rcpf(1.f + __expf(-h1)) * h3;
-            act[(size_t)row * Nout + n0 + wn * 64 + 32 * j + l32] = f32_to_bf16(gv);
-          }
+          const float h1 = acc[i][0][r], h3 = acc[i][1][r];
+          const float gv = h1 * __builtin_amdgcn_rcpf(1.f + __expf(-h1)) * h3;
+          act[(size_t)row * Nout + n0 + wn * 64 + 32 * pw + l32] = f32_to_bf16(gv);
         }
       }
   } else {
@@ -355,8 +357,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
         const int row = r0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
         if (row < rend) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            y[(size_t)row * Nout + n0 + wn * 128 + 32 * j + l32] = acc[i][j][r];
+          for (int j = 0; j < 2; ++j)
+            y[(size_t)row * Nout + n0 + wn * 128 + 64 * pw + 32 * j + l32] = acc[i][j][r];
         }
       }
   }

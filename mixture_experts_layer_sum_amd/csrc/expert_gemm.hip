@@ -19,13 +19,23 @@
 // halves of its SwiGLU products are in the same lane.
 // k advances 64 at a time through two 64 KB LDS stages filled by direct
 // buffer -> LDS loads (no VGPRs in flight; every request is a whole 128-byte
-// line).  A (x_perm rows) is stored row-major and read with ds_read_b128; the
+// line).  The texture unit accepts these loads at about 64 bytes per clock
+// per CU, so a 64 KB stage keeps it busy for about half of the stage's MFMA
+// time, and a wave waiting to issue a load cannot issue MFMAs.  Only one wave
+// of each SIMD loads (16 instructions per stage, two per MFMA of the slice
+// that follows the barrier); the other wave only computes and keeps the
+// matrix core busy meanwhile.
+// A (x_perm rows) is stored row-major and read with ds_read_b128; the
 // weights stay n-contiguous in LDS and the MFMA B operand (8 consecutive k per
 // lane) is assembled with the gfx950 transposing read ds_read_b64_tr_b16.
 // Both LDS layouts are XOR-swizzled per row so that the fragment reads are
 // bank-conflict free.  One barrier per k-step, placed after the last
 // fragment read of the current stage: the stage is refilled two steps ahead
 // while the last slice's MFMAs run.
+// A wave's four 32-row sub-tiles are tile rows 32 (2i + wm) (the two row
+// halves interleave), so in an expert's last, partial tile both halves have
+// about the same number of real rows; sub-tiles with no real row skip their
+// fragment reads and MFMAs (the loop is instantiated per count).
 // The row tiles of all experts are numbered consecutively; a block finds its
 // expert with a wave-wide prefix scan of the per-expert tile counts read from
 // `offsets` on the device, so the host never needs the routing result.
@@ -139,28 +149,31 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kBK = 64;
 
 // Direct global -> LDS loads of one 64-deep k-step into the stage at `dst`
-// (32768 elements): A at element 0, B sub-tile q at 16384 + 8192 q.
+// (32768 elements): A at element 0, B sub-tile q at 16384 + 8192 q.  Only the
+// four waves w = 0..3 load (8 A and 8 B instructions each).
 __device__ __forceinline__ void gemm_issue(uint16_t* __restrict__ dst, __amdgpu_buffer_rsrc_t a_rs,
                                            __amdgpu_buffer_rsrc_t b_rs, const uint32_t* a_off,
                                            const uint32_t* b_off, int w, int kstep, int Nout) {
   const uint32_t ka = (uint32_t)kstep * (kBK * 2);
   const uint32_t kb = (uint32_t)kstep * (uint32_t)(kBK * Nout * 2);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, (lds_void*)(dst + (4 * w + i) * 512), 16,
+  for (int i = 0; i < 8; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, (lds_void*)(dst + (8 * w + i) * 512), 16,
                                              a_off[i] + ka, 0, 0, 0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rs, (lds_void*)(dst + 16384 + (4 * w + i) * 512), 16,
+  for (int i = 0; i < 8; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rs, (lds_void*)(dst + 16384 + (8 * w + i) * 512), 16,
                                              b_off[i] + kb, 0, 0, 0);
 }
 
+template <int NV>
 __device__ __forceinline__ void gemm_frags(const uint16_t* __restrict__ st, int s2,
                                            const int (&a_rd)[4][4], const int (&b_rd)[4][2][2],
                                            uint4 (&fa)[4], uint4 (&fb)[2]) {
+  if (NV == 0) return;
   const uint16_t* bs_ = st + 16384;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const uint4*>(st + a_rd[s2][i]);
+  for (int i = 0; i < NV; ++i) fa[i] = *reinterpret_cast<const uint4*>(st + a_rd[s2][i]);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -172,10 +185,11 @@ __device__ __forceinline__ void gemm_frags(const uint16_t* __restrict__ st, int 
   }
 }
 
+template <int NV>
 __device__ __forceinline__ void gemm_mma(const uint4 (&fa)[4], const uint4 (&fb)[2],
                                          f32x16 (&acc)[4][2]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NV; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
 }
@@ -192,6 +206,7 @@ __device__ __forceinline__ void gemm_mma(const uint4 (&fa)[4], const uint4 (&fb)
 // slice's MFMAs run, and the next step's first slice is read from `nxt`.
 // `dst` is `cur`: a separate restrict parameter only so that the refill
 // carries its own alias scope and reading `nxt` does not wait for it.
+template <int NV, bool DMA>
 __device__ __forceinline__ void gemm_step(const uint16_t* __restrict__ cur, uint16_t* __restrict__ dst,
                                           const uint16_t* __restrict__ nxt,
                                           __amdgpu_buffer_rsrc_t a_rs, __amdgpu_buffer_rsrc_t b_rs,
@@ -200,17 +215,32 @@ __device__ __forceinline__ void gemm_step(const uint16_t* __restrict__ cur, uint
                                           const int (&b_rd)[4][2][2], f32x16 (&acc)[4][2],
                                           uint4 (&fa0)[4], uint4 (&fb0)[2]) {
   uint4 fa1[4], fb1[2];
-  gemm_frags(cur, 1, a_rd, b_rd, fa1, fb1);
-  gemm_mma(fa0, fb0, acc);
-  gemm_frags(cur, 2, a_rd, b_rd, fa0, fb0);
-  gemm_mma(fa1, fb1, acc);
-  gemm_frags(cur, 3, a_rd, b_rd, fa1, fb1);
-  gemm_mma(fa0, fb0, acc);
+  gemm_frags<NV>(cur, 1, a_rd, b_rd, fa1, fb1);
+  gemm_mma<NV>(fa0, fb0, acc);
+  gemm_frags<NV>(cur, 2, a_rd, b_rd, fa0, fb0);
+  gemm_mma<NV>(fa1, fb1, acc);
+  gemm_frags<NV>(cur, 3, a_rd, b_rd, fa1, fb1);
+  gemm_mma<NV>(fa0, fb0, acc);
   MOE_WAIT_BARRIER();
-  gemm_issue(dst, a_rs, b_rs, a_off, b_off, w, kstep, Nout);
-  __builtin_amdgcn_sched_barrier(0);     // keep the refill right after the barrier
-  gemm_frags(nxt, 0, a_rd, b_rd, fa0, fb0);
-  gemm_mma(fa1, fb1, acc);
+  if (DMA && NV == 4) {
+    // the refill is interleaved with the last slice's MFMAs, two loads per
+    // MFMA, so that this wave's MFMAs run while it waits to issue its loads
+    gemm_frags<NV>(nxt, 0, a_rd, b_rd, fa0, fb0);
+    gemm_issue(dst, a_rs, b_rs, a_off, b_off, w, kstep, Nout);
+    gemm_mma<NV>(fa1, fb1, acc);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    if (DMA) gemm_issue(dst, a_rs, b_rs, a_off, b_off, w, kstep, Nout);
+    __builtin_amdgcn_sched_barrier(0);     // keep the refill right after the barrier
+    gemm_frags<NV>(nxt, 0, a_rd, b_rd, fa0, fb0);
+    gemm_mma<NV>(fa1, fb1, acc);
+  }
 }
 
 // LDS layout of one stage (64 KB):
@@ -257,23 +287,26 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
   const __amdgpu_buffer_rsrc_t b_rs1 = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>((UP ? Wb : Wa) + wexp), 0, wbytes, kRsrcWord3);
 
-  // ---- direct global -> LDS loads: wave w issues A instructions 4w..4w+3
-  // (8 rows each) and B instructions 4w..4w+3 (4 k-rows of one sub-tile each).
-  uint32_t a_off[4], b_off[4];
+  // ---- direct global -> LDS loads: waves 0..3 issue A instructions 8w..8w+7
+  // (8 rows each) and B instructions 8w..8w+7 (4 k-rows of sub-tile (8w+i) / 16);
+  // waves 4..7 only compute, so on every SIMD one wave keeps issuing MFMAs while
+  // the other waits for the texture unit to accept its loads.
+  uint32_t a_off[8], b_off[8];
+  const int wl = w & 3;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int a = 4 * w + i;                                  // A instruction: 8 rows
+  for (int i = 0; i < 8; ++i) {
+    const int a = 8 * wl + i;                                 // A instruction: 8 rows
     int row = 8 * a + (lane >> 3);
     row = row < tile_rows ? row : tile_rows - 1;             // rows past the end repeat the last one
     const int c = (lane & 7) ^ ((row >> 1) & 7);
     a_off[i] = (uint32_t)((row * K + 8 * c) * 2);
-    const int b = 4 * w + i;                                  // B instruction: 4 k-rows of sub-tile b / 16
+    const int b = 8 * wl + i;                                 // B instruction: 4 k-rows of sub-tile b / 16
     const int kr = 4 * (b & 15) + (lane >> 4);
     const int cb = (lane & 15) ^ (4 * (kr & 3));
     const int colbase = UP ? n0 : n0 + 128 * (b >> 4);
     b_off[i] = (uint32_t)((kr * Nout + colbase + 8 * cb) * 2);
   }
-  const __amdgpu_buffer_rsrc_t b_rs = (w >> 2) ? b_rs1 : b_rs0;   // wave-uniform
+  const __amdgpu_buffer_rsrc_t b_rs = (wl >> 1) ? b_rs1 : b_rs0;   // wave-uniform
 
   f32x16 acc[4][2];
 #pragma unroll
@@ -290,7 +323,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
   for (int s2 = 0; s2 < 4; ++s2)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = wm * 128 + 32 * i + l32;
+      const int row = 32 * (2 * i + wm) + l32;
       a_rd[s2][i] = row * 64 + 8 * ((2 * s2 + h) ^ ((row >> 1) & 7));
     }
   // B (transposing read): 16-lane group gq = lane / 16 covers columns
@@ -317,22 +350,48 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
   }
 
   const int nk = K / kBK;
-  gemm_issue(S0, a_rs, b_rs, a_off, b_off, w, 0, Nout);
-  gemm_issue(S1, a_rs, b_rs, a_off, b_off, w, min(1, nk - 1), Nout);
-  asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // step 0 landed
-  uint4 fa0[4], fb0[2];
-  gemm_frags(S0, 0, a_rd, b_rd, fa0, fb0);
-#define MOE_STEP(C, N)                                                                      \
-  gemm_step(C, C, N, a_rs, b_rs, a_off, b_off, w, min(kt + 2, nk - 1), Nout, a_rd, b_rd, acc, \
-            fa0, fb0)
-  int kt = 0;
-  for (; kt + 2 <= nk; kt += 2) {
-    MOE_STEP(S0, S1); ++kt;
-    MOE_STEP(S1, S0); --kt;
+  // 32-row sub-tiles of this wave that hold rows of the expert (the rest are
+  // padding of the expert's last tile and are skipped)
+  const int nv = __builtin_amdgcn_readfirstlane(
+      min(4, max(0, (tile_rows - 32 * wm + 63) / 64)));
+#define MOE_KLOOP(NV, D0, D1)                                                                   \
+  do {                                                                                          \
+    uint4 fa0[4], fb0[2];                                                                       \
+    gemm_frags<NV>(S0, 0, a_rd, b_rd, fa0, fb0);                                                \
+    int kt = 0;                                                                                 \
+    for (; kt + 2 <= nk; kt += 2) {                                                             \
+      gemm_step<NV, D0>(S0, S0, S1, a_rs, b_rs, a_off, b_off, wl, min(kt + 2, nk - 1), Nout,    \
+                        a_rd, b_rd, acc, fa0, fb0);                                             \
+      gemm_step<NV, D1>(S1, S1, S0, a_rs, b_rs, a_off, b_off, wl, min(kt + 3, nk - 1), Nout,    \
+                        a_rd, b_rd, acc, fa0, fb0);                                             \
+    }                                                                                           \
+    if (kt < nk)                                                                                \
+      gemm_step<NV, D0>(S0, S0, S1, a_rs, b_rs, a_off, b_off, wl, min(kt + 2, nk - 1), Nout,    \
+                        a_rd, b_rd, acc, fa0, fb0);                                             \
+  } while (0)
+  if (pw == 0) {
+    gemm_issue(S0, a_rs, b_rs, a_off, b_off, wl, 0, Nout);
+    gemm_issue(S1, a_rs, b_rs, a_off, b_off, wl, min(1, nk - 1), Nout);
+    asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // step 0 landed
+    switch (nv) {
+      case 4: MOE_KLOOP(4, true, true); break;
+      case 3: MOE_KLOOP(3, true, true); break;
+      case 2: MOE_KLOOP(2, true, true); break;
+      case 1: MOE_KLOOP(1, true, true); break;
+      default: MOE_KLOOP(0, true, true); break;
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0): no LDS write in flight at exit
+  } else {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    switch (nv) {
+      case 4: MOE_KLOOP(4, false, false); break;
+      case 3: MOE_KLOOP(3, false, false); break;
+      case 2: MOE_KLOOP(2, false, false); break;
+      case 1: MOE_KLOOP(1, false, false); break;
+      default: MOE_KLOOP(0, false, false); break;
+    }
   }
-  if (kt < nk) MOE_STEP(S0, S1);
-#undef MOE_STEP
-  __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0): no LDS write in flight at exit
+#undef MOE_KLOOP
 
   // ---- epilogue
   if (UP) {
@@ -341,7 +400,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = r0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int row = r0 + 32 * (2 * i + wm) + 8 * (r >> 2) + 4 * h + (r & 3);
         if (row < rend) {
           const float h1 = acc[i][0][r], h3 = acc[i][1][r];
           const float gv = h1 * __builtin_amdgcn_rcpf(1.f + __expf(-h1)) * h3;
@@ -354,7 +413,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = r0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int row = r0 + 32 * (2 * i + wm) + 8 * (r >> 2) + 4 * h + (r & 3);
         if (row < rend) {
 #pragma unroll
           for (int j = 0; j < 2; ++j)

@@ -90,7 +90,7 @@ def time_layer(inp, dev, steps, warmup):
         moe.moe_expert_up(b.x_perm, b.offsets, dev["w1"], dev["w3"], b.act)
         if ev:
             ev[1].record(s)
-        moe.moe_expert_down(b.act, b.offsets, dev["w2"], b.y_perm)
+        moe.moe_expert_down(b.act, b.offsets, dev["w2"], b.y_perm, b.ws_down)
         if ev:
             ev[2].record(s)
         moe.moe_combine(b.y_perm, b.slot_row, b.topk_w, dev["hidden"].dtype, b.y)

@@ -58,15 +58,18 @@ typedef enum {
   MOE_OP_PERMUTE = 1,
   MOE_OP_EXPERT_FFN = 2,
   MOE_OP_COMBINE = 3,
-  MOE_OP_AUX_LOSS = 4
+  MOE_OP_AUX_LOSS = 4,
+  MOE_OP_EXPERT_DOWN = 5
 } moe_op;
 
 /* Human-readable name of a status code (static string). */
 const char* moe_status_string(moe_status s);
 
 /* Bytes of device workspace `op` needs for these sizes (0 if none).  Returns
- * 0 for an unknown op as well.  For MOE_OP_EXPERT_FFN, T*k is the row capacity
- * (max_rows) of x_perm / y_perm. */
+ * 0 for an unknown op as well.  For MOE_OP_EXPERT_FFN and MOE_OP_EXPERT_DOWN,
+ * T*k is the row capacity (max_rows) of x_perm / y_perm.  The two expert ops
+ * size their k-split buffers by the compute units of the CURRENT device
+ * (0 when no device is visible); query with that device current. */
 size_t moe_workspace_size(moe_op op, int T, int d, int N, int k, int f, moe_dtype dt);
 
 /*
@@ -133,7 +136,8 @@ moe_status moe_permute(const void* hidden, const int32_t* topk_idx, int T, int d
  *   w1, w3    [N, d, f] dtype dt;  w2 [N, f, d] dtype dt
  *   y_perm    [max_rows, d] fp32 out (rows >= offsets[N] not written)
  *   ws        moe_workspace_size(MOE_OP_EXPERT_FFN, T, d, N, k, f, dt) bytes
- *             with T*k = max_rows
+ *             with T*k = max_rows: the activations [max_rows, f] (padded to
+ *             256 bytes), then moe_expert_down's workspace
  */
 moe_status moe_expert_ffn(const void* x_perm, const int32_t* offsets, const void* w1,
                           const void* w3, const void* w2, int N, int d, int f, int max_rows,
@@ -145,9 +149,16 @@ moe_status moe_expert_up(const void* x_perm, const int32_t* offsets, const void*
                          const void* w3, int N, int d, int f, int max_rows, moe_dtype dt,
                          void* act, void* stream);
 
-/* Second grouped GEMM: y_perm[r] = act[r] W2_e, y_perm fp32. */
+/* Second grouped GEMM: y_perm[r] = act[r] W2_e, y_perm fp32.
+ *   ws  moe_workspace_size(MOE_OP_EXPERT_DOWN, T, d, N, k, f, dt) bytes with
+ *       T*k = max_rows (may be NULL when that size is 0).  When the tiles'
+ *       last round would leave most compute units idle, its tiles are split
+ *       over k and the partial tiles meet in `ws`; they are summed in a fixed
+ *       order, so results do not depend on scheduling.  Calls that share `ws`
+ *       must be ordered (same stream). */
 moe_status moe_expert_down(const void* act, const int32_t* offsets, const void* w2, int N, int d,
-                           int f, int max_rows, moe_dtype dt, float* y_perm, void* stream);
+                           int f, int max_rows, moe_dtype dt, float* y_perm, void* ws,
+                           size_t ws_bytes, void* stream);
 
 /*
  * moe_combine -- weighted combine back to token order (P1 §2.1: the output

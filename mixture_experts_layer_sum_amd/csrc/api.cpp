@@ -48,6 +48,12 @@ int capacity_of(int T, int k, int N, float cf) {
   return static_cast<int>(c);
 }
 
+// Activations held in the moe_expert_ffn workspace, padded to 256 bytes.
+size_t act_bytes(int rows, int f, moe_dtype dt) {
+  const size_t b = static_cast<size_t>(rows) * static_cast<size_t>(f) * elem_bytes(dt);
+  return (b + 255) & ~static_cast<size_t>(255);
+}
+
 }  // namespace
 
 extern "C" {
@@ -71,8 +77,12 @@ size_t moe_workspace_size(moe_op op, int T, int d, int N, int k, int f, moe_dtyp
       return dt == MOE_BF16 ? moe::route_ws_bytes(T, d, N) : 0;
     case MOE_OP_PERMUTE: return moe::permute_ws_bytes(T, N);
     case MOE_OP_EXPERT_FFN:
-      if (f < 1 || !dtype_ok(dt)) return 0;
-      return static_cast<size_t>(T) * k * static_cast<size_t>(f) * elem_bytes(dt);
+      if (d < 1 || f < 1 || !dtype_ok(dt)) return 0;
+      return act_bytes(T * k, f, dt) +
+             moe::expert_down_ws_bytes(N, d, f, T * k, dt == MOE_BF16);
+    case MOE_OP_EXPERT_DOWN:
+      if (d < 1 || f < 1 || !dtype_ok(dt)) return 0;
+      return moe::expert_down_ws_bytes(N, d, f, T * k, dt == MOE_BF16);
     case MOE_OP_AUX_LOSS: return moe::aux_ws_bytes(T, N);
     default: return 0;
   }
@@ -123,12 +133,16 @@ moe_status moe_expert_up(const void* x_perm, const int32_t* offsets, const void*
 }
 
 moe_status moe_expert_down(const void* act, const int32_t* offsets, const void* w2, int N, int d,
-                           int f, int max_rows, moe_dtype dt, float* y_perm, void* stream) {
+                           int f, int max_rows, moe_dtype dt, float* y_perm, void* ws,
+                           size_t ws_bytes, void* stream) {
   if (!act || !offsets || !w2 || !y_perm) return MOE_ERR_INVALID_ARG;
   moe_status s = check_expert_shape(N, d, f, max_rows, dt);
   if (s != MOE_OK) return s;
+  const size_t need = moe::expert_down_ws_bytes(N, d, f, max_rows, dt == MOE_BF16);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (need > 0 && !ws) return MOE_ERR_INVALID_ARG;
   return hip_status(moe::launch_expert_down(act, offsets, w2, N, d, f, max_rows, dt == MOE_BF16,
-                                            y_perm, as_stream(stream)));
+                                            y_perm, need > 0 ? ws : nullptr, as_stream(stream)));
 }
 
 moe_status moe_expert_ffn(const void* x_perm, const int32_t* offsets, const void* w1,
@@ -137,14 +151,16 @@ moe_status moe_expert_ffn(const void* x_perm, const int32_t* offsets, const void
   if (!x_perm || !offsets || !w1 || !w3 || !w2 || !y_perm) return MOE_ERR_INVALID_ARG;
   moe_status s = check_expert_shape(N, d, f, max_rows, dt);
   if (s != MOE_OK) return s;
-  const size_t need = static_cast<size_t>(max_rows) * static_cast<size_t>(f) * elem_bytes(dt);
-  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  const size_t need_act = act_bytes(max_rows, f, dt);
+  const size_t need_down = moe::expert_down_ws_bytes(N, d, f, max_rows, dt == MOE_BF16);
+  if (ws_bytes < need_act + need_down) return MOE_ERR_WORKSPACE;
   if (!ws) return MOE_ERR_INVALID_ARG;
   hipError_t e = moe::launch_expert_up(x_perm, offsets, w1, w3, N, d, f, max_rows, dt == MOE_BF16,
                                        ws, as_stream(stream));
   if (e != hipSuccess) return MOE_ERR_HIP;
+  void* down_ws = need_down > 0 ? static_cast<char*>(ws) + need_act : nullptr;
   return hip_status(moe::launch_expert_down(ws, offsets, w2, N, d, f, max_rows, dt == MOE_BF16,
-                                            y_perm, as_stream(stream)));
+                                            y_perm, down_ws, as_stream(stream)));
 }
 
 moe_status moe_combine(const float* y_perm, const int32_t* slot_row, const float* topk_w, int T,

@@ -113,19 +113,23 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
   return false;
 }
 
-// Block -> (row tile, column tile).  Blocks are dealt round-robin to the 8
+// Data-parallel block -> logical tile.  Blocks are dealt round-robin to the 8
 // XCDs, so block b runs on XCD b % 8: give XCD x the contiguous range
-// [x*per, (x+1)*per) of the real tiles (per = ceil(tiles / 8)), and inside a
-// range walk kGroupM row tiles for every column tile, so the blocks an XCD
-// runs at the same time share A rows and weight columns in its L2.
-__device__ __forceinline__ bool tile_of_block(int m_tiles, int n_tiles, int& mt, int& nt) {
-  const int total = m_tiles * n_tiles;
+// [x*per, (x+1)*per) of the `total` logical tiles (per = ceil(total / 8)).
+__device__ __forceinline__ bool dp_logical(int total, int& logical) {
   const int per = (total + 7) >> 3;
   const int b = blockIdx.x;
   const int local = b >> 3;
   if (local >= per) return false;
-  const int logical = (b & 7) * per + local;
-  if (logical >= total) return false;
+  logical = (b & 7) * per + local;
+  return logical < total;
+}
+
+// Logical tile -> (row tile, column tile): kGroupM row tiles are walked for
+// every column tile, so the blocks an XCD runs at the same time share A rows
+// and weight columns in its L2.
+__device__ __forceinline__ void tile_of_logical(int logical, int m_tiles, int n_tiles, int& mt,
+                                                int& nt) {
   const int span = kGroupM * n_tiles;
   const int grp = logical / span;
   const int first = grp * kGroupM;
@@ -133,7 +137,26 @@ __device__ __forceinline__ bool tile_of_block(int m_tiles, int n_tiles, int& mt,
   const int in = logical - grp * span;
   mt = first + in % gm;
   nt = in / gm;
-  return true;
+}
+
+// Split of the last, partial round of tiles over k.  With `total` tiles on
+// `num_cus` CUs (one block each) the last round holds r = total % num_cus
+// tiles; when that round would leave at least half of the CUs idle, each of
+// its r tiles is cut into `segs` k-ranges run by separate blocks (segs <= 4,
+// each range at least two k-steps).  Returns the number of tiles computed
+// whole (the first n_dp logical tiles).
+constexpr int kMaxSegs = 4;
+__device__ __forceinline__ int split_plan(int total, int nk, int num_cus, int& segs) {
+  segs = 1;
+  if (num_cus <= 0) return total;
+  const int r = total % num_cus;
+  if (r == 0 || 2 * r > num_cus) return total;
+  int s = num_cus / r;
+  s = s < kMaxSegs ? s : kMaxSegs;
+  s = s < nk / 2 ? s : nk / 2;
+  if (s < 2) return total;
+  segs = s;
+  return total - r;
 }
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -254,15 +277,38 @@ template <bool UP>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
     const uint16_t* __restrict__ X, const int32_t* __restrict__ offsets, int N,
     const uint16_t* __restrict__ Wa, const uint16_t* __restrict__ Wb, int K, int Nout,
-    int n_tiles, int max_rows, void* __restrict__ out) {
+    int n_tiles, int max_rows, void* __restrict__ out, float* __restrict__ part,
+    int32_t* __restrict__ tickets, int num_cus, int dp_grid) {
   // two 64 KB stages as separate LDS objects: the compiler tracks in-flight
   // direct loads per LDS object, so a read of one stage never waits on the
   // refill of the other
   __shared__ __align__(1024) uint16_t S0[32768], S1[32768];
+  __shared__ int s_last;
 
+  const int nk = K / kBK;
   const int m_tiles = count_tiles(offsets, N, kBM, max_rows);
+  const int total = m_tiles * n_tiles;
+  int segs;
+  const int n_dp = split_plan(total, nk, num_cus, segs);
+  // blocks [0, dp_grid) compute whole tiles; the rest compute k-ranges of the
+  // last n_sk tiles (block j: tile n_dp + j / segs, range j % segs)
+  int logical, kb = 0, kl = nk, slot = -1;
+  if ((int)blockIdx.x < dp_grid) {
+    if (!dp_logical(n_dp, logical)) return;
+  } else {
+    const int j = blockIdx.x - dp_grid;
+    if (j >= (total - n_dp) * segs) return;
+    logical = n_dp + j / segs;
+    const int seg = j % segs;
+    kb = seg * nk / segs;
+    kl = (seg + 1) * nk / segs - kb;
+    slot = j;
+  }
+  kb = __builtin_amdgcn_readfirstlane(kb);
+  kl = __builtin_amdgcn_readfirstlane(kl);
+  slot = __builtin_amdgcn_readfirstlane(slot);
   int mt, nt;
-  if (!tile_of_block(m_tiles, n_tiles, mt, nt)) return;
+  tile_of_logical(logical, m_tiles, n_tiles, mt, nt);
   int e, r0, rend;
   if (!find_tile(offsets, N, mt, kBM, max_rows, e, r0, rend)) return;
   e = __builtin_amdgcn_readfirstlane(e);
@@ -349,7 +395,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
     }
   }
 
-  const int nk = K / kBK;
   // 32-row sub-tiles of this wave that hold rows of the expert (the rest are
   // padding of the expert's last tile and are skipped)
   const int nv = __builtin_amdgcn_readfirstlane(
@@ -359,19 +404,19 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
     uint4 fa0[4], fb0[2];                                                                       \
     gemm_frags<NV>(S0, 0, a_rd, b_rd, fa0, fb0);                                                \
     int kt = 0;                                                                                 \
-    for (; kt + 2 <= nk; kt += 2) {                                                             \
-      gemm_step<NV, D0>(S0, S0, S1, a_rs, b_rs, a_off, b_off, wl, min(kt + 2, nk - 1), Nout,    \
-                        a_rd, b_rd, acc, fa0, fb0);                                             \
-      gemm_step<NV, D1>(S1, S1, S0, a_rs, b_rs, a_off, b_off, wl, min(kt + 3, nk - 1), Nout,    \
-                        a_rd, b_rd, acc, fa0, fb0);                                             \
+    for (; kt + 2 <= kl; kt += 2) {                                                             \
+      gemm_step<NV, D0>(S0, S0, S1, a_rs, b_rs, a_off, b_off, wl, kb + min(kt + 2, kl - 1),     \
+                        Nout, a_rd, b_rd, acc, fa0, fb0);                                       \
+      gemm_step<NV, D1>(S1, S1, S0, a_rs, b_rs, a_off, b_off, wl, kb + min(kt + 3, kl - 1),     \
+                        Nout, a_rd, b_rd, acc, fa0, fb0);                                       \
     }                                                                                           \
-    if (kt < nk)                                                                                \
-      gemm_step<NV, D0>(S0, S0, S1, a_rs, b_rs, a_off, b_off, wl, min(kt + 2, nk - 1), Nout,    \
-                        a_rd, b_rd, acc, fa0, fb0);                                             \
+    if (kt < kl)                                                                                \
+      gemm_step<NV, D0>(S0, S0, S1, a_rs, b_rs, a_off, b_off, wl, kb + min(kt + 2, kl - 1),     \
+                        Nout, a_rd, b_rd, acc, fa0, fb0);                                       \
   } while (0)
   if (pw == 0) {
-    gemm_issue(S0, a_rs, b_rs, a_off, b_off, wl, 0, Nout);
-    gemm_issue(S1, a_rs, b_rs, a_off, b_off, wl, min(1, nk - 1), Nout);
+    gemm_issue(S0, a_rs, b_rs, a_off, b_off, wl, kb, Nout);
+    gemm_issue(S1, a_rs, b_rs, a_off, b_off, wl, kb + min(1, kl - 1), Nout);
     asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // step 0 landed
     switch (nv) {
       case 4: MOE_KLOOP(4, true, true); break;
@@ -392,6 +437,45 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
     }
   }
 #undef MOE_KLOOP
+
+  // ---- k-range blocks: store the partial tile, and the last of a tile's
+  // blocks to arrive sums all of its partials in range order (the order, and
+  // so the result, does not depend on which block arrives last)
+  if (!UP && slot >= 0) {
+    float* mine = part + (size_t)slot * (kBM * kBN);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mine[((i * 2 + j) * 16 + r) * kGemmThreads + tid] = acc[i][j][r];
+    // every wave's stores are done before the barrier; one wave then makes the
+    // block's tile visible device-wide (a release per block, not per wave:
+    // each one writes back the XCD's L2)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const int tile_sk = slot / segs;
+    if (tid == 0) {
+      __threadfence();
+      const int last = atomicAdd(&tickets[tile_sk], 1) == segs - 1;
+      if (last) __threadfence();       // acquire the other blocks' partial tiles
+      s_last = last;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    const float* first = part + (size_t)tile_sk * segs * (kBM * kBN);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int el = ((i * 2 + j) * 16 + r) * kGemmThreads + tid;
+          float v = first[el];
+          for (int q = 1; q < segs; ++q) v += first[(size_t)q * (kBM * kBN) + el];
+          acc[i][j][r] = v;
+        }
+  }
 
   // ---- epilogue
   if (UP) {
@@ -659,6 +743,37 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
 
 static int round8(int x) { return (x + 7) & ~7; }
 
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
+__global__ void zero_tickets_kernel(int32_t* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+// Workspace of the down projection: one fp32 256 x 256 partial tile and one
+// ticket per CU for the k-split last round (MFMA path only).
+static size_t partial_bytes(int cus) { return (size_t)cus * kBM * kBN * sizeof(float); }
+
+size_t expert_down_ws_bytes(int N, int d, int f, int max_rows, bool bf16) {
+  (void)d;
+  (void)f;
+  if (!bf16 || rows_mt(max_rows, N) > 0) return 0;
+  const int cus = device_cus();
+  if (cus <= 0) return 0;
+  return partial_bytes(cus) + (((size_t)cus * sizeof(int32_t) + 255) & ~(size_t)255);
+}
+
 hipError_t launch_expert_up(const void* x_perm, const int32_t* offsets, const void* w1,
                             const void* w3, int N, int d, int f, int max_rows, bool bf16,
                             void* act, hipStream_t stream) {
@@ -671,7 +786,8 @@ hipError_t launch_expert_up(const void* x_perm, const int32_t* offsets, const vo
     hipLaunchKernelGGL(grouped_gemm_bf16_kernel<true>, dim3(grid), dim3(kGemmThreads), 0, stream,
                        static_cast<const uint16_t*>(x_perm), offsets, N,
                        static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w3), d, f,
-                       n_tiles, max_rows, act);
+                       n_tiles, max_rows, act, static_cast<float*>(nullptr),
+                       static_cast<int32_t*>(nullptr), 0, grid);
   } else {
     const int n_tiles = f / kFBN;
     const int mt_bound = (max_rows + kFBM - 1) / kFBM + N;
@@ -684,7 +800,7 @@ hipError_t launch_expert_up(const void* x_perm, const int32_t* offsets, const vo
 }
 
 hipError_t launch_expert_down(const void* act, const int32_t* offsets, const void* w2, int N,
-                              int d, int f, int max_rows, bool bf16, float* y_perm,
+                              int d, int f, int max_rows, bool bf16, float* y_perm, void* ws,
                               hipStream_t stream) {
   if (bf16 && rows_mt(max_rows, N) > 0) {
     launch_rows<false>(rows_mt(max_rows, N), act, offsets, N, w2, nullptr, f, d, max_rows,
@@ -692,11 +808,22 @@ hipError_t launch_expert_down(const void* act, const int32_t* offsets, const voi
   } else if (bf16) {
     const int n_tiles = d / kBN;
     const int mt_bound = (max_rows + kBM - 1) / kBM + N;
-    const int grid = round8(mt_bound * n_tiles);
+    const int dp_grid = round8(mt_bound * n_tiles);
+    const int cus = ws ? device_cus() : 0;
+    float* part = static_cast<float*>(ws);
+    int32_t* tickets = nullptr;
+    int grid = dp_grid;
+    if (cus > 0) {
+      tickets = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + partial_bytes(cus));
+      hipLaunchKernelGGL(zero_tickets_kernel, dim3((cus + 255) / 256), dim3(256), 0, stream,
+                         tickets, cus);
+      grid += round8(cus);
+    }
     hipLaunchKernelGGL(grouped_gemm_bf16_kernel<false>, dim3(grid), dim3(kGemmThreads), 0, stream,
                        static_cast<const uint16_t*>(act), offsets, N,
                        static_cast<const uint16_t*>(w2), static_cast<const uint16_t*>(nullptr), f,
-                       d, n_tiles, max_rows, static_cast<void*>(y_perm));
+                       d, n_tiles, max_rows, static_cast<void*>(y_perm), part, tickets, cus,
+                       dp_grid);
   } else {
     const int n_tiles = d / kFBN;
     const int mt_bound = (max_rows + kFBM - 1) / kFBM + N;

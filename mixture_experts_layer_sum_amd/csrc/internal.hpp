@@ -22,8 +22,9 @@ hipError_t launch_permute(const void* hidden, const int32_t* topk_idx, int T, in
 hipError_t launch_expert_up(const void* x_perm, const int32_t* offsets, const void* w1,
                             const void* w3, int N, int d, int f, int max_rows, bool bf16,
                             void* act, hipStream_t stream);
+size_t expert_down_ws_bytes(int N, int d, int f, int max_rows, bool bf16);   // current device
 hipError_t launch_expert_down(const void* act, const int32_t* offsets, const void* w2, int N,
-                              int d, int f, int max_rows, bool bf16, float* y_perm,
+                              int d, int f, int max_rows, bool bf16, float* y_perm, void* ws,
                               hipStream_t stream);
 
 hipError_t launch_combine(const float* y_perm, const int32_t* slot_row, const float* topk_w, int T,

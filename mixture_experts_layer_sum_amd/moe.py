@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
-MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_EXPERT_FFN, MOE_OP_COMBINE, MOE_OP_AUX_LOSS = range(5)
+(MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_EXPERT_FFN, MOE_OP_COMBINE, MOE_OP_AUX_LOSS,
+ MOE_OP_EXPERT_DOWN) = range(6)
 
 # Every symbol include/moe.h declares, with (restype, argtypes).
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -29,7 +30,7 @@ SIGNATURES = {
     "moe_permute": (_I, [_P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "moe_expert_ffn": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
     "moe_expert_up": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
-    "moe_expert_down": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
+    "moe_expert_down": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
     "moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "moe_aux_loss": (_I, [_P, _P, _I, _I, _I, _P, _P, _Z, _P]),
 }
@@ -136,12 +137,16 @@ def moe_expert_up(x_perm, offsets, w1, w3, act=None, stream=None):
     return act
 
 
-def moe_expert_down(act, offsets, w2, y_perm=None, stream=None):
+def moe_expert_down(act, offsets, w2, y_perm=None, ws=None, stream=None):
     max_rows, f = act.shape
     N, _, d = w2.shape
     y_perm = _empty((max_rows, d), torch.float32, act.device, y_perm)
+    if ws is None:
+        ws = torch.empty(max(1, workspace_size(MOE_OP_EXPERT_DOWN, max_rows, d, N, 1, f, act.dtype)),
+                         dtype=torch.uint8, device=act.device)
     _check(_lib.moe_expert_down(_ptr(act), _ptr(offsets), _ptr(w2), N, d, f, max_rows, _dt(act),
-                                _ptr(y_perm), _stream(stream)), "moe_expert_down")
+                                _ptr(y_perm), _ptr(ws), ws.numel(), _stream(stream)),
+           "moe_expert_down")
     return y_perm
 
 
@@ -151,7 +156,7 @@ def moe_expert_ffn(x_perm, offsets, w1, w3, w2, y_perm=None, ws=None, stream=Non
     dev = x_perm.device
     y_perm = _empty((max_rows, d), torch.float32, dev, y_perm)
     if ws is None:
-        ws = torch.empty(workspace_size(MOE_OP_EXPERT_FFN, max_rows, d, N, 1, f, x_perm.dtype),
+        ws = torch.empty(max(1, workspace_size(MOE_OP_EXPERT_FFN, max_rows, d, N, 1, f, x_perm.dtype)),
                          dtype=torch.uint8, device=dev)
     _check(_lib.moe_expert_ffn(_ptr(x_perm), _ptr(offsets), _ptr(w1), _ptr(w3), _ptr(w2), N, d, f,
                                max_rows, _dt(x_perm), _ptr(y_perm), _ptr(ws), ws.numel(),
@@ -203,6 +208,8 @@ class MoEBuffers:
         self.ws_route = e((max(1, workspace_size(MOE_OP_ROUTE, T, d, N, k, f, dtype)),), torch.uint8)
         self.ws_permute = e((max(1, workspace_size(MOE_OP_PERMUTE, T, d, N, k, f, dtype)),), torch.uint8)
         self.ws_aux = e((max(1, workspace_size(MOE_OP_AUX_LOSS, T, d, N, k, f, dtype)),), torch.uint8)
+        self.ws_down = e((max(1, workspace_size(MOE_OP_EXPERT_DOWN, T, d, N, k, f, dtype)),),
+                         torch.uint8)
 
 
 def moe_forward(hidden, w_router, w1, w3, w2, k, capacity_factor=0.0, bias=None,
@@ -221,7 +228,7 @@ def moe_forward(hidden, w_router, w1, w3, w2, k, capacity_factor=0.0, bias=None,
     moe_permute(hidden, b.topk_idx, N, capacity_factor, b.x_perm, b.perm_src, b.slot_row, b.kept,
                 b.offsets, b.ws_permute, stream)
     moe_expert_up(b.x_perm, b.offsets, w1, w3, b.act, stream)
-    moe_expert_down(b.act, b.offsets, w2, b.y_perm, stream)
+    moe_expert_down(b.act, b.offsets, w2, b.y_perm, b.ws_down, stream)
     moe_combine(b.y_perm, b.slot_row, b.topk_w, hidden.dtype, b.y, stream)
     moe_aux_loss(b.logits, b.counts, k, b.aux, b.ws_aux, stream)
     return b

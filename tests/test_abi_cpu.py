@@ -54,6 +54,10 @@ def test_workspace_sizes():
     assert lib.moe_workspace_size(moe.MOE_OP_PERMUTE, 257, 128, 8, 2, 256, F32) == 2 * 2 * 8 * 4
     assert lib.moe_workspace_size(moe.MOE_OP_EXPERT_FFN, 64, 128, 8, 2, 256, BF16) == 64 * 2 * 256 * 2
     assert lib.moe_workspace_size(moe.MOE_OP_EXPERT_FFN, 64, 128, 8, 2, 256, F32) == 64 * 2 * 256 * 4
+    # the k-split buffers of the down projection follow the current device (none here);
+    # the fp32 path never uses them
+    assert lib.moe_workspace_size(moe.MOE_OP_EXPERT_DOWN, 64, 128, 8, 2, 256, F32) == 0
+    assert lib.moe_workspace_size(moe.MOE_OP_EXPERT_DOWN, 64, 128, 8, 0, 256, BF16) == 0
     # one fp32 [N] partial per 64 tokens
     assert lib.moe_workspace_size(moe.MOE_OP_AUX_LOSS, 256, 128, 8, 2, 256, F32) == 4 * 8 * 4
     assert lib.moe_workspace_size(moe.MOE_OP_AUX_LOSS, 65, 128, 8, 2, 256, F32) == 2 * 8 * 4
@@ -122,8 +126,9 @@ def test_expert_ffn_rejects(kw, status):
 def test_expert_up_down_reject():
     assert lib.moe_expert_up(NUL, P, P, P, 8, 256, 256, 64, BF16, P, S) == INV
     assert lib.moe_expert_up(P, P, P, P, 8, 256, 200, 64, BF16, P, S) == UNS
-    assert lib.moe_expert_down(P, P, NUL, 8, 256, 256, 64, BF16, P, S) == INV
-    assert lib.moe_expert_down(P, P, P, 8, 128, 256, 64, BF16, P, S) == UNS
+    assert lib.moe_expert_down(P, P, NUL, 8, 256, 256, 64, BF16, P, P, 1 << 30, S) == INV
+    assert lib.moe_expert_down(P, P, P, 8, 128, 256, 64, BF16, P, P, 1 << 30, S) == UNS
+    assert lib.moe_expert_down(P, P, P, 8, 256, 256, 64, 3, P, P, 1 << 30, S) == UNS
 
 
 @pytest.mark.parametrize("args,status", [

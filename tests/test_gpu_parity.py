@@ -52,6 +52,9 @@ SMALL = [
     ("bf16_router_ksplit", 40, 1024, 64, 2, 128, "bf16", 0.0, None),
     ("bf16_router_ksplit_N200", 50, 1024, 200, 3, 128, "bf16", 0.0, None),
     ("bf16_rows_mt2", 300, 512, 32, 2, 256, "bf16", 0.0, None),
+    # ~130 row tiles x 2 column tiles: on a 256-CU device the down projection's
+    # last round (4 tiles) is split over k into 4 ranges each
+    ("bf16_down_ksplit4", 16500, 512, 2, 2, 512, "bf16", 0.0, None),
 ]
 
 
@@ -101,6 +104,26 @@ def test_deterministic_and_ffn_entry_matches_split(moe):
     torch.cuda.synchronize()
     A = g1["A"]
     assert torch.equal(y_ffn[:A], b.y_perm[:A])
+
+
+def test_down_workspace_is_checked(moe):
+    """The MFMA down projection needs its k-split workspace; a short one is refused."""
+    import ctypes
+    N, d, f, rows = 8, 256, 256, 4096
+    need = moe.workspace_size(moe.MOE_OP_EXPERT_DOWN, rows, d, N, 1, f, torch.bfloat16)
+    assert need > 0
+    act = torch.zeros(rows, f, dtype=torch.bfloat16, device="cuda")
+    w2 = torch.zeros(N, f, d, dtype=torch.bfloat16, device="cuda")
+    offs = (torch.arange(N + 1, dtype=torch.int32, device="cuda") * (rows // N)).contiguous()
+    y = torch.empty(rows, d, dtype=torch.float32, device="cuda")
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    st = moe._lib.moe_expert_down(act.data_ptr(), offs.data_ptr(), w2.data_ptr(), N, d, f, rows,
+                                  moe.MOE_BF16, y.data_ptr(), ws.data_ptr(), need - 1,
+                                  ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == moe.MOE_ERR_WORKSPACE
+    moe.moe_expert_down(act, offs, w2, y, ws)
+    torch.cuda.synchronize()
+    assert (y == 0).all()
 
 
 WORKLOADS = ["tiny_fp32", "n16_cf125", "mixtral", "skewed_zipf", "decode"]

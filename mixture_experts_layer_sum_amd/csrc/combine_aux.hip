@@ -62,38 +62,43 @@ hipError_t launch_combine(const float* y_perm, const int32_t* slot_row, const fl
   return hipGetLastError();
 }
 
-constexpr int kAuxTok = 64;    // tokens per block (16 per wave)
+constexpr int kAuxTok = 16;    // tokens per block (4 per wave)
 
-// part[b][e] = sum over the block's tokens of softmax(logits[t])_e, in token order.
+// part[b][e] = sum over the block's tokens of softmax(logits[t])_e, in token
+// order.  A wave loads its 4 tokens' logits before reducing any of them.
 __global__ __launch_bounds__(256) void aux_partial_kernel(const float* __restrict__ logits, int T,
                                                           int N, float* __restrict__ part) {
+  constexpr int TPW = kAuxTok / 4;
   __shared__ float red[4][256];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  const int tb = blockIdx.x * kAuxTok + w * (kAuxTok / 4);
-  for (int i = 0; i < kAuxTok / 4; ++i) {
+  const int tb = blockIdx.x * kAuxTok + w * TPW;
+  float v[TPW][4];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
     const int t = tb + i;
-    if (t >= T) break;
-    const float* L = logits + (size_t)t * N;
-    float v[4];
-    float m = -INFINITY;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int e = lane + 64 * c;
-      v[c] = (e < N) ? L[e] : -INFINITY;
-      m = fmaxf(m, v[c]);
+      v[i][c] = (t < T && e < N) ? logits[(size_t)t * N + e] : -INFINITY;
     }
+  }
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    if (tb + i >= T) break;
+    float m = fmaxf(fmaxf(v[i][0], v[i][1]), fmaxf(v[i][2], v[i][3]));
     m = wave_max(m);
     float s = 0.f;
+    float p[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      v[c] = (lane + 64 * c < N) ? __expf(v[c] - m) : 0.f;
-      s += v[c];
+      p[c] = (lane + 64 * c < N) ? __expf(v[i][c] - m) : 0.f;
+      s += p[c];
     }
     s = wave_sum(s);
     const float inv = 1.f / s;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[c] += v[c] * inv;
+    for (int c = 0; c < 4; ++c) acc[c] += p[c] * inv;
   }
 #pragma unroll
   for (int c = 0; c < 4; ++c) red[w][lane + 64 * c] = acc[c];
@@ -103,26 +108,53 @@ __global__ __launch_bounds__(256) void aux_partial_kernel(const float* __restric
 }
 
 // Single block: P_e = sum_b part[b][e] / T, then aux = N * sum_e f_e P_e.
+// The 256 threads split the blocks: expert e is summed by G = 256 / N' threads
+// (N' = N rounded up to a power of two), thread g taking blocks g, g + G, ...;
+// the G partial sums then meet in a fixed tree, so the order never changes.
 __global__ __launch_bounds__(256) void aux_final_kernel(const float* __restrict__ part, int nb,
                                                         const int32_t* __restrict__ counts, int T,
                                                         int N, int k, float* __restrict__ aux) {
-  __shared__ float red[256];
-  const int e = threadIdx.x;
-  float term = 0.f;
+  __shared__ double red[256];
+  __shared__ float term[256];
+  const int tid = threadIdx.x;
+  int np2 = 1;
+  while (np2 < N) np2 <<= 1;
+  const int G = 256 / np2;
+  const int e = tid % np2, g = tid / np2;
+  double s = 0.0;
   if (e < N) {
-    double s = 0.0;
-    for (int b = 0; b < nb; ++b) s += part[(size_t)b * N + e];
-    const double P = s / T;
-    const double fe = static_cast<double>(counts[e]) / (static_cast<double>(T) * k);
-    term = static_cast<float>(fe * P);
+    int b = g;
+    for (; b + 3 * G < nb; b += 4 * G) {
+      const float a0 = part[(size_t)b * N + e], a1 = part[(size_t)(b + G) * N + e];
+      const float a2 = part[(size_t)(b + 2 * G) * N + e], a3 = part[(size_t)(b + 3 * G) * N + e];
+      s += a0;
+      s += a1;
+      s += a2;
+      s += a3;
+    }
+    for (; b < nb; b += G) s += part[(size_t)b * N + e];
   }
-  red[e] = term;
+  red[tid] = s;
   __syncthreads();
-  for (int s = 128; s >= 1; s >>= 1) {
-    if (e < s) red[e] += red[e + s];
+  for (int h = G / 2; h >= 1; h >>= 1) {       // fold the G partial sums of each expert
+    if (g < h) red[tid] += red[tid + h * np2];
     __syncthreads();
   }
-  if (e == 0) aux[0] = red[0] * static_cast<float>(N);
+  if (tid < np2) {
+    float t = 0.f;
+    if (tid < N) {
+      const double P = red[tid] / T;
+      const double fe = static_cast<double>(counts[tid]) / (static_cast<double>(T) * k);
+      t = static_cast<float>(fe * P);
+    }
+    term[tid] = t;
+  }
+  __syncthreads();
+  for (int h = np2 / 2; h >= 1; h >>= 1) {
+    if (tid < h) term[tid] += term[tid + h];
+    __syncthreads();
+  }
+  if (tid == 0) aux[0] = term[0] * static_cast<float>(N);
 }
 
 size_t aux_ws_bytes(int T, int N) {

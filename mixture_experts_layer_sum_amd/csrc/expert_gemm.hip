@@ -509,19 +509,24 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
 
 // ---------------------------------------------------------------- few rows per expert
 // Decode-shaped batches give each expert only a handful of rows, so the work
-// is reading every active expert's weights once (HBM-bound).  One wave owns
-// one (expert, group of up to 16*MT rows, 64-column slice): it streams its
-// weight columns straight from global memory into registers -- every load is
-// a full 128-byte line -- and never touches LDS.
+// is reading every active expert's weights once (HBM-bound).  A wave owns one
+// (expert, group of rows, column slice): it streams its weight columns
+// straight from global memory into registers and never touches LDS.  How
+// many contiguous bytes of a weight row one load instruction covers decides
+// the DRAM efficiency on this part (a plain streaming read measured 5.9, 6.6
+// and 7.0 TB/s for 128-, 256- and 512-byte pieces per row), so the main
+// variant below reads 512 contiguous bytes per row per instruction.
 //
-// MFMA 16x16x32 with a column-permuted B operand: lane l = 16g + j loads the
-// 8 k-rows k0+8g .. k0+8g+7 of 8 adjacent weight columns (one 16-byte vector
-// per row) and transposes the 8x8 block in registers, giving 8 B operands
-// (8 consecutive k each).  MFMA number c then produces, in output column j,
-// weight column base(j) + c.  For `up`, lanes j < 8 read W1 columns
-// n0 + 8j .. n0 + 8j + 7 and lanes j >= 8 the same columns of W3, so a
-// shuffle across 8 lanes brings both halves of a SwiGLU product together.
-// For `down`, lane j reads W2 columns n0 + 8j .. n0 + 8j + 7 (128 columns).
+// Column-permuted B operand: a lane loads 8 k-rows of 8 adjacent weight
+// columns (one 16-byte vector per row) and transposes the 8x8 block in
+// registers, giving 8 MFMA B operands (8 consecutive k each); MFMA number c
+// then produces, in the lane's output column, weight column base + c.
+//
+// grouped_gemm_bf16_rows_kernel (up to 64 rows, 16x16x32 MFMAs): lane
+// l = 16g + j loads k-rows k0+8g .. +7; for `up` lanes j < 8 read W1 columns
+// n0 + 8j .. +7 and lanes j >= 8 the same columns of W3 (a shuffle across 8
+// lanes pairs the SwiGLU halves); for `down` lane j reads W2 columns
+// n0 + 8j .. +7 (128 columns).
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 // Streaming 16-byte load (weights are read once): non-temporal hint.
 __device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
@@ -648,33 +653,133 @@ __global__ __launch_bounds__(64) void grouped_gemm_bf16_rows_kernel(
   }
 }
 
-// Rows-per-expert threshold below which the streaming kernel is used.
+// Weight streaming with 32x32x16 MFMAs: a wave owns (expert, 32 rows, 256
+// weight columns of one k-row per instruction: 32 lanes x 16 bytes = 512
+// contiguous bytes).  Lane 32h + i loads k-rows k0 + 8h .. +7 of columns
+// 8i .. 8i+7 of its block and transposes them in registers; MFMA c then
+// yields, in output column i, weight column 8i + c.  UP: lanes i < 16 read W1
+// columns n0 + 8i .., lanes i >= 16 the same W3 columns (128 activation
+// columns per wave; a lane shuffle pairs the SwiGLU halves); DOWN: 256
+// columns of W2.
+template <bool UP>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void grouped_gemm_bf16_rows32_kernel(
+    const uint16_t* __restrict__ X, const int32_t* __restrict__ offsets, int N,
+    const uint16_t* __restrict__ Wa, const uint16_t* __restrict__ Wb, int K, int Nout,
+    int n_slices, int max_rows, void* __restrict__ out) {
+  const int mt = blockIdx.x / n_slices, ns = blockIdx.x - mt * n_slices;
+  int e, r0, rend;
+  if (!find_tile(offsets, N, mt, 32, max_rows, e, r0, rend)) return;
+  e = __builtin_amdgcn_readfirstlane(e);
+  r0 = __builtin_amdgcn_readfirstlane(r0);
+  rend = __builtin_amdgcn_readfirstlane(rend);
+
+  const int lane = threadIdx.x, i = lane & 31, h = lane >> 5;
+  const int n0 = ns * (UP ? 128 : 256);
+  const size_t wexp = (size_t)e * K * Nout;
+  const uint16_t* wsrc = UP ? ((i < 16 ? Wa : Wb) + wexp + n0 + 8 * (i & 15))
+                            : (Wa + wexp + n0 + 8 * i);
+  wsrc += (size_t)(8 * h) * Nout;
+  const uint16_t* asrc = X + (size_t)min(r0 + i, rend - 1) * K + 8 * h;
+
+  f32x16 acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[c][r] = 0.f;
+
+  const size_t rstride = (size_t)Nout;
+  uint4 wb[2][8], xa[2];
+#define MOE_R32_LOAD(S, k0)                                                           \
+  do {                                                                               \
+    _Pragma("unroll") for (int kk = 0; kk < 8; ++kk)                                 \
+        wb[S][kk] = load_stream(wsrc + (size_t)((k0) + kk) * rstride);               \
+    xa[S] = *reinterpret_cast<const uint4*>(asrc + (k0));                            \
+  } while (0)
+#define MOE_R32_MMA(S)                                                                \
+  do {                                                                               \
+    uint4 bf[8];                                                                     \
+    transpose8x8(wb[S], bf);                                                         \
+    _Pragma("unroll") for (int c = 0; c < 8; ++c) acc[c] = mfma32(xa[S], bf[c], acc[c]); \
+  } while (0)
+
+  const int nk = K / 16;                        // K is a multiple of 64: nk is even
+  MOE_R32_LOAD(0, 0);
+  for (int kt = 0; kt < nk; kt += 2) {
+    MOE_R32_LOAD(1, (kt + 1) * 16);
+    MOE_R32_MMA(0);
+    if (kt + 2 < nk) MOE_R32_LOAD(0, (kt + 2) * 16);
+    MOE_R32_MMA(1);
+  }
+#undef MOE_R32_LOAD
+#undef MOE_R32_MMA
+
+  // acc[c][r]: row r0 + 8 (r / 4) + 4h + r % 4, column (of lane i's block) 8i + c
+  if (UP) {
+    uint16_t* act = static_cast<uint16_t*>(out);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float v[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float mine = acc[c][r];
+        const float other = __shfl_xor(mine, 16, 64);    // W3 half for lanes i < 16
+        v[c] = mine * __builtin_amdgcn_rcpf(1.f + __expf(-mine)) * other;
+      }
+      const int row = r0 + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (i < 16 && row < rend) {
+        const uint4 pk = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                    pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+        *reinterpret_cast<uint4*>(act + (size_t)row * Nout + n0 + 8 * i) = pk;
+      }
+    }
+  } else {
+    float* y = static_cast<float*>(out);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = r0 + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (row < rend) {
+        float4* dst = reinterpret_cast<float4*>(y + (size_t)row * Nout + n0 + 8 * i);
+        dst[0] = make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]);
+        dst[1] = make_float4(acc[4][r], acc[5][r], acc[6][r], acc[7][r]);
+      }
+    }
+  }
+}
+
+template <bool UP>
+static void launch_rows32(const void* x, const int32_t* offsets, int N, const void* wa,
+                          const void* wb, int K, int Nout, int max_rows, void* out,
+                          hipStream_t stream) {
+  const int n_slices = Nout / (UP ? 128 : 256);
+  const int m_bound = (max_rows + 31) / 32 + N;
+  hipLaunchKernelGGL((grouped_gemm_bf16_rows32_kernel<UP>), dim3(m_bound * n_slices), dim3(64), 0,
+                     stream, static_cast<const uint16_t*>(x), offsets, N,
+                     static_cast<const uint16_t*>(wa), static_cast<const uint16_t*>(wb), K, Nout,
+                     n_slices, max_rows, out);
+}
+
+// Few rows per expert: 0 = the MFMA tile kernel; 1 = 32-row weight streaming
+// (average <= 32 rows per expert); 4 = 64-row weight streaming (<= 48).
 static int rows_mt(int max_rows, int N) {
   const int avg = (max_rows + N - 1) / N;
-  if (avg > 48) return 0;              // big tiles
-  return avg <= 16 ? 1 : (avg <= 32 ? 2 : 4);
+  if (avg > 48) return 0;
+  return avg <= 32 ? 1 : 4;
 }
 
 template <bool UP>
 static void launch_rows(int mt, const void* x, const int32_t* offsets, int N, const void* wa,
                         const void* wb, int K, int Nout, int max_rows, void* out,
                         hipStream_t stream) {
+  if (mt == 1) {
+    launch_rows32<UP>(x, offsets, N, wa, wb, K, Nout, max_rows, out, stream);
+    return;
+  }
   const int n_slices = Nout / (UP ? 64 : 128);
-  const int bm = 16 * mt;
-  const int m_bound = (max_rows + bm - 1) / bm + N;
-  const dim3 grid(m_bound * n_slices), block(64);
-  const auto* X = static_cast<const uint16_t*>(x);
-  const auto* A = static_cast<const uint16_t*>(wa);
-  const auto* B = static_cast<const uint16_t*>(wb);
-  if (mt == 1)
-    hipLaunchKernelGGL((grouped_gemm_bf16_rows_kernel<UP, 1>), grid, block, 0, stream, X, offsets,
-                       N, A, B, K, Nout, n_slices, max_rows, out);
-  else if (mt == 2)
-    hipLaunchKernelGGL((grouped_gemm_bf16_rows_kernel<UP, 2>), grid, block, 0, stream, X, offsets,
-                       N, A, B, K, Nout, n_slices, max_rows, out);
-  else
-    hipLaunchKernelGGL((grouped_gemm_bf16_rows_kernel<UP, 4>), grid, block, 0, stream, X, offsets,
-                       N, A, B, K, Nout, n_slices, max_rows, out);
+  const int m_bound = (max_rows + 63) / 64 + N;
+  hipLaunchKernelGGL((grouped_gemm_bf16_rows_kernel<UP, 4>), dim3(m_bound * n_slices), dim3(64), 0,
+                     stream, static_cast<const uint16_t*>(x), offsets, N,
+                     static_cast<const uint16_t*>(wa), static_cast<const uint16_t*>(wb), K, Nout,
+                     n_slices, max_rows, out);
 }
 
 // ---------------------------------------------------------------- fp32 (VALU)

@@ -109,6 +109,63 @@ __global__ __launch_bounds__(kChunk) void place_kernel(const int32_t* __restrict
     }
 }
 
+// All of the above in one block when every token fits in one chunk (T <= 256,
+// decode-sized batches): histogram, capacity, exclusive scan and places.
+__global__ __launch_bounds__(kChunk) void permute_one_chunk_kernel(
+    const int32_t* __restrict__ topk_idx, int T, int N, int k, int C, int32_t* __restrict__ kept,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ slot_row, int32_t* __restrict__ perm_src) {
+  __shared__ unsigned long long mask[256][4];
+  __shared__ int h[256];
+  __shared__ int sk[256];
+  __shared__ int off[256];
+  const int tid = threadIdx.x;
+  mask[tid][0] = mask[tid][1] = mask[tid][2] = mask[tid][3] = 0ull;
+  h[tid] = 0;
+  __syncthreads();
+  const int t = tid;
+  const int word = tid >> 6;
+  const unsigned long long bit = 1ull << (tid & 63);
+  if (t < T)
+    for (int j = 0; j < k; ++j) {
+      const int e = topk_idx[(size_t)t * k + j];
+      if (e >= 0 && e < N) {
+        atomicAdd(&h[e], 1);
+        atomicOr(&mask[e][word], bit);
+      }
+    }
+  __syncthreads();
+  const int e = tid;
+  const int kp = (e < N) ? (h[e] < C ? h[e] : C) : 0;
+  if (e < N) kept[e] = kp;
+  sk[e] = kp;
+  __syncthreads();
+  for (int s = 1; s < 256; s <<= 1) {     // inclusive Hillis-Steele scan
+    const int v = (e >= s) ? sk[e - s] : 0;
+    __syncthreads();
+    sk[e] += v;
+    __syncthreads();
+  }
+  off[e] = sk[e] - kp;
+  if (e < N) offsets[e] = sk[e] - kp;
+  if (e == N - 1) offsets[N] = sk[e];
+  __syncthreads();
+  if (t < T)
+    for (int j = 0; j < k; ++j) {
+      const int ex = topk_idx[(size_t)t * k + j];
+      int row = -1;
+      if (ex >= 0 && ex < N) {
+        int place = 0;
+        for (int q = 0; q < word; ++q) place += __popcll(mask[ex][q]);
+        place += __popcll(mask[ex][word] & (bit - 1ull));
+        if (place < C) {
+          row = off[ex] + place;
+          perm_src[row] = t;
+        }
+      }
+      slot_row[(size_t)t * k + j] = row;
+    }
+}
+
 // Copy hidden[t] into each of its kept rows of x_perm.  One block per token,
 // 16-byte vectors; a row is a whole number of vectors.
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restrict__ hidden,
@@ -139,13 +196,19 @@ hipError_t launch_permute(const void* hidden, const int32_t* topk_idx, int T, in
                           int32_t* slot_row, int32_t* kept, int32_t* offsets, void* ws,
                           hipStream_t stream) {
   const int nch = (T + kChunk - 1) / kChunk;
-  int32_t* hist = static_cast<int32_t*>(ws);
-  int32_t* base = hist + static_cast<size_t>(nch) * N;
-  hipLaunchKernelGGL(chunk_hist_kernel, dim3(nch), dim3(kChunk), 0, stream, topk_idx, T, N, k, hist);
-  hipLaunchKernelGGL(expert_scan_kernel, dim3(1), dim3(256), 0, stream, hist, nch, N, C, base, kept,
-                     offsets);
-  hipLaunchKernelGGL(place_kernel, dim3(nch), dim3(kChunk), 0, stream, topk_idx, T, N, k, C, base,
-                     offsets, slot_row, perm_src);
+  if (nch == 1) {
+    hipLaunchKernelGGL(permute_one_chunk_kernel, dim3(1), dim3(kChunk), 0, stream, topk_idx, T, N,
+                       k, C, kept, offsets, slot_row, perm_src);
+  } else {
+    int32_t* hist = static_cast<int32_t*>(ws);
+    int32_t* base = hist + static_cast<size_t>(nch) * N;
+    hipLaunchKernelGGL(chunk_hist_kernel, dim3(nch), dim3(kChunk), 0, stream, topk_idx, T, N, k,
+                       hist);
+    hipLaunchKernelGGL(expert_scan_kernel, dim3(1), dim3(256), 0, stream, hist, nch, N, C, base,
+                       kept, offsets);
+    hipLaunchKernelGGL(place_kernel, dim3(nch), dim3(kChunk), 0, stream, topk_idx, T, N, k, C,
+                       base, offsets, slot_row, perm_src);
+  }
   const int vpr = (d * elem_bytes) / 16;
   hipLaunchKernelGGL(gather_rows_kernel, dim3(T), dim3(256), 0, stream,
                      static_cast<const uint4*>(hidden), slot_row, k, vpr,

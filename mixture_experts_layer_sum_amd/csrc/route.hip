@@ -278,8 +278,17 @@ __global__ __launch_bounds__(256) void router_finish_kernel(const float* __restr
     if (t >= T) continue;
     const float* src = part + (size_t)t * N + e;
     const size_t slice = (size_t)T * N;
+    // slices summed in order; their loads are issued 8 at a time
     float v = 0.f;
-    for (int ks = 0; ks < KS; ++ks) v += src[ks * slice];
+    int ks = 0;
+    for (; ks + 8 <= KS; ks += 8) {
+      float a[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a[u] = src[(ks + u) * slice];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v += a[u];
+    }
+    for (; ks < KS; ++ks) v += src[ks * slice];
     v += (bias != nullptr) ? bias[e] : 0.f;
     lg[r * 257 + e] = v;
     logits[(size_t)t * N + e] = v;

@@ -59,8 +59,8 @@ def test_workspace_sizes():
     assert lib.moe_workspace_size(moe.MOE_OP_EXPERT_DOWN, 64, 128, 8, 2, 256, F32) == 0
     assert lib.moe_workspace_size(moe.MOE_OP_EXPERT_DOWN, 64, 128, 8, 0, 256, BF16) == 0
     # one fp32 [N] partial per 64 tokens
-    assert lib.moe_workspace_size(moe.MOE_OP_AUX_LOSS, 256, 128, 8, 2, 256, F32) == 4 * 8 * 4
-    assert lib.moe_workspace_size(moe.MOE_OP_AUX_LOSS, 65, 128, 8, 2, 256, F32) == 2 * 8 * 4
+    assert lib.moe_workspace_size(moe.MOE_OP_AUX_LOSS, 256, 128, 8, 2, 256, F32) == 16 * 8 * 4
+    assert lib.moe_workspace_size(moe.MOE_OP_AUX_LOSS, 65, 128, 8, 2, 256, F32) == 5 * 8 * 4
     assert lib.moe_workspace_size(17, 64, 128, 8, 2, 256, F32) == 0
     assert lib.moe_workspace_size(moe.MOE_OP_PERMUTE, 0, 128, 8, 2, 256, F32) == 0
 

@@ -51,7 +51,9 @@ SMALL = [
     ("bf16_big_expert_multi_tile", 1200, 256, 2, 2, 256, "bf16", 0.0, None),
     ("bf16_router_ksplit", 40, 1024, 64, 2, 128, "bf16", 0.0, None),
     ("bf16_router_ksplit_N200", 50, 1024, 200, 3, 128, "bf16", 0.0, None),
-    ("bf16_rows_mt2", 300, 512, 32, 2, 256, "bf16", 0.0, None),
+    # weight-streaming paths: 32-row tiles (some experts need two), 64-row tiles
+    ("bf16_rows32_two_tiles", 300, 512, 32, 2, 256, "bf16", 0.0, None),
+    ("bf16_rows64", 400, 512, 20, 2, 256, "bf16", 0.0, None),
     # ~130 row tiles x 2 column tiles: on a 256-CU device the down projection's
     # last round (4 tiles) is split over k into 4 ranges each
     ("bf16_down_ksplit4", 16500, 512, 2, 2, 512, "bf16", 0.0, None),

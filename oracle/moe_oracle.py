@@ -34,7 +34,19 @@ Readings of points the pages leave open (each also listed in the design notes):
   names SwiGLU; the formula is the standard GLU-variant one);
 * aux = N * sum_e f_e * P_e with f_e = counts_e / (T*k) from the router's
   pre-drop assignments and P_e the mean over tokens of the full-N softmax of
-  the logits (P1 §2.3, P2 §3.2); the 0.01-style coefficient is the caller's.
+  the logits (P1 §2.3, P2 §3.2); the 0.01-style coefficient is the caller's;
+* overflow re-routing (the alternative to dropping that P3 §2.3, P4 §2.2 and
+  P5 §2.2 mention, and P5 §4.2's capacity-aware routing code sketches as
+  "mask the original choice, take the next best"): one second dispatch round after the
+  capacity cut.  Each dropped assignment, in slot order within its token,
+  proposes the highest-logit expert that is not among the token's top-k picks,
+  not already proposed by an earlier dropped slot of the same token, and still
+  had room after the first round (kept_e < C); ties go to the lower index.
+  Proposals are admitted per expert in token order up to the room left
+  (C - kept_e); the rest are dropped.  A re-routed assignment keeps its gate
+  weight.  Inside an expert, first-round rows come before second-round rows,
+  each token-ascending.  Counts and the aux loss stay on the router's own
+  (pre-drop) assignments.
 """
 from __future__ import annotations
 
@@ -44,7 +56,8 @@ import numpy as np
 
 __all__ = [
     "router_logits", "select_topk", "gate_weights", "expert_counts", "capacity",
-    "dispatch", "silu", "swiglu_ffn", "aux_loss", "moe_forward", "moe_forward_per_token",
+    "dispatch", "dispatch_reroute", "silu", "swiglu_ffn", "aux_loss", "moe_forward",
+    "moe_forward_per_token",
 ]
 
 
@@ -132,6 +145,68 @@ def dispatch(idx, N: int, C: int) -> dict:
             "slot_row": slot_row, "perm_src": perm_src}
 
 
+def dispatch_reroute(idx, logits, N: int, C: int) -> dict:
+    """Capacity cut, then one re-routing round for the dropped assignments.
+
+    First round exactly as :func:`dispatch`.  Second round: every dropped
+    (t, j), in token order and slot order inside a token, proposes the best
+    expert by the float32 logits (larger first, lower index on ties) among
+    those that are not in token t's top-k, not proposed by an earlier dropped
+    slot of t, and had kept_e < C after the first round.  Each expert admits
+    proposals in token order while it has room left (C - kept_e).  P5 §4.2
+    (capacity-aware routing: mask the original pick, take the next best), P4
+    §2.2 and P5 §2.2 (over-capacity tokens are dropped or sent to the
+    next-best expert), P3 §2.3 (overflow is handed to other, idle experts).
+    """
+    idx = np.asarray(idx)
+    T, k = idx.shape
+    L32 = np.asarray(logits, np.float64).astype(np.float32)
+    first = dispatch(idx, N, C)
+    keep1, kept1 = first["keep"], first["kept"]
+    room = kept1 < C
+    prop = np.full((T, k), -1, np.int64)
+    for t in range(T):
+        taken = set(int(e) for e in idx[t])
+        for j in range(k):
+            if keep1[t, j]:
+                continue
+            best = -1
+            for e in range(N):
+                if e in taken or not room[e]:
+                    continue
+                if best < 0 or L32[t, e] > L32[t, best]:
+                    best = e
+            if best >= 0:
+                prop[t, j] = best
+                taken.add(best)
+    # admission, per expert in token order
+    place2 = np.full((T, k), -1, np.int64)
+    used = np.zeros(N, np.int64)
+    for t in range(T):
+        for j in range(k):
+            e = prop[t, j]
+            if e >= 0:
+                place2[t, j] = used[e]
+                used[e] += 1
+    keep2 = (prop >= 0) & (place2 < (C - kept1)[np.maximum(prop, 0)])
+    kept2 = np.array([min(int(used[e]), C - int(kept1[e])) for e in range(N)], np.int64)
+    kept = kept1 + kept2
+    offsets = np.zeros(N + 1, np.int64)
+    offsets[1:] = np.cumsum(kept)
+    expert = np.where(keep1, idx, np.where(keep2, prop, -1))
+    slot_row = np.full((T, k), -1, np.int64)
+    slot_row[keep1] = (offsets[idx] + first["place"])[keep1]
+    e2 = np.maximum(prop, 0)
+    slot_row[keep2] = (offsets[e2] + kept1[e2] + place2)[keep2]
+    perm_src = np.empty(int(offsets[-1]), np.int64)
+    for t in range(T):
+        for j in range(k):
+            if slot_row[t, j] >= 0:
+                perm_src[slot_row[t, j]] = t
+    return {"keep1": keep1, "proposal": prop, "keep2": keep2, "kept1": kept1, "kept": kept,
+            "offsets": offsets, "slot_row": slot_row, "perm_src": perm_src, "expert": expert}
+
+
 def silu(z):
     """silu(z) = z * sigmoid(z) = z / (1 + exp(-z))."""
     z = np.asarray(z, np.float64)
@@ -165,14 +240,15 @@ def aux_loss(logits, counts, k: int) -> float:
 
 
 def moe_forward(hidden, w_router, w1, w3, w2, k: int, capacity_factor: float = 0.0,
-                bias=None, tokens=None) -> dict:
+                bias=None, tokens=None, overflow: str = "drop") -> dict:
     """The layer forward, per expert (the page's gather -> FFN -> weighted add loop).
 
     ``w1[e]``, ``w3[e]``, ``w2[e]`` are indexed one expert at a time, so the
     caller may hand in lazy per-expert views.  If ``tokens`` is given, routing,
     counts, dispatch and aux cover every token but the expert FFN and the
     combine are evaluated only for those tokens (``y`` then has one row per
-    listed token).
+    listed token).  ``overflow`` is "drop" (the default) or "reroute"
+    (:func:`dispatch_reroute`).
 
     P1 §2.1 (route, top-k, softmax, weighted sum), P3 §4.1 (per-expert loop;
     its shortcut that weights every expert by the sum of both gate values is
@@ -186,7 +262,12 @@ def moe_forward(hidden, w_router, w1, w3, w2, k: int, capacity_factor: float = 0
     w = gate_weights(L, idx)
     counts = expert_counts(idx, N)
     C = capacity(T, k, N, capacity_factor)
-    disp = dispatch(idx, N, C)
+    if overflow == "drop":
+        disp = dispatch(idx, N, C)
+    elif overflow == "reroute":
+        disp = dispatch_reroute(idx, L, N, C)
+    else:
+        raise ValueError(f"unknown overflow policy {overflow!r}")
     slot_row, offsets, perm_src = disp["slot_row"], disp["offsets"], disp["perm_src"]
 
     tok = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
@@ -212,11 +293,15 @@ def moe_forward(hidden, w_router, w1, w3, w2, k: int, capacity_factor: float = 0
 
 
 def moe_forward_per_token(hidden, w_router, w1, w3, w2, k: int, capacity_factor: float = 0.0,
-                          bias=None) -> np.ndarray:
+                          bias=None, overflow: str = "drop") -> np.ndarray:
     """Brute force for tiny inputs: y_t = sum over kept slots j of w_tj * FFN_{i_tj}(x_t).
 
     One token and one slot at a time, with its own running per-expert counter
-    for the capacity cut; no permutation, no grouping.
+    for the capacity cut; no permutation, no grouping.  With
+    overflow="reroute" a second pass walks the dropped slots in token order,
+    each scanning the experts in logit order for one that is not the token's
+    and had room after the first pass, and keeps it while that expert's
+    second-pass count stays within its room.
     """
     hidden = np.asarray(hidden, np.float64)
     T, d = hidden.shape
@@ -227,10 +312,30 @@ def moe_forward_per_token(hidden, w_router, w1, w3, w2, k: int, capacity_factor:
     C = capacity(T, k, N, capacity_factor)
     seen = [0] * N
     y = np.zeros((T, d))
+    dropped = []
     for t in range(T):
         for j in range(k):
             e = int(idx[t, j])
             if seen[e] < C:
                 y[t] += w[t, j] * swiglu_ffn(hidden[t:t + 1], w1[e], w3[e], w2[e])[0]
+            else:
+                dropped.append((t, j))
             seen[e] += 1
+    if overflow == "reroute":
+        full = [min(c, C) for c in seen]            # rows each expert kept in the first pass
+        second = [0] * N
+        L32 = L.astype(np.float32)
+        chosen = {}
+        for t, j in dropped:
+            mine = set(int(e) for e in idx[t]) | chosen.setdefault(t, set())
+            order = sorted(range(N), key=lambda e: (-float(L32[t, e]), e))
+            cand = next((e for e in order if e not in mine and full[e] < C), None)
+            if cand is None:
+                continue
+            chosen[t].add(cand)
+            if second[cand] < C - full[cand]:
+                y[t] += w[t, j] * swiglu_ffn(hidden[t:t + 1], w1[cand], w3[cand], w2[cand])[0]
+            second[cand] += 1
+    elif overflow != "drop":
+        raise ValueError(f"unknown overflow policy {overflow!r}")
     return y

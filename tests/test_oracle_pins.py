@@ -303,6 +303,104 @@ def test_one_slot_dropped_keeps_unnormalised_weight():
     assert np.allclose(out["y"][1], ref, rtol=1e-13)
 
 
+# ---------------------------------------------------------------- overflow re-routing
+def test_reroute_hand_example_single_choice():
+    """Four tokens all pick expert 0 with room for one each (C = 1): the first
+    keeps it, the next two move to their best other expert, the fourth finds
+    its best other expert already taken and is dropped."""
+    idx = np.array([[0], [0], [0], [0]])
+    L = np.array([[3, 2, 1], [3, 1, 2], [3, 2, 1], [3, 1, 2]], np.float64)
+    r = O.dispatch_reroute(idx, L, 3, 1)
+    assert r["expert"].ravel().tolist() == [0, 2, 1, -1]
+    assert r["kept"].tolist() == [1, 1, 1]
+    assert r["offsets"].tolist() == [0, 1, 2, 3]
+    assert r["slot_row"].ravel().tolist() == [0, 2, 1, -1]
+    assert r["perm_src"].tolist() == [0, 2, 1]
+
+
+def test_reroute_hand_example_two_dropped_slots_take_distinct_experts():
+    """Both slots of a token dropped: they propose the two best other experts
+    (never the same one twice); a later token proposing the same experts finds
+    them full."""
+    idx = np.array([[0, 1], [0, 1], [0, 1]])
+    L = np.array([[4, 3, 2, 1]] * 3, np.float64)
+    r = O.dispatch_reroute(idx, L, 4, 1)
+    assert r["proposal"].tolist() == [[-1, -1], [2, 3], [2, 3]]
+    assert r["expert"].tolist() == [[0, 1], [2, 3], [-1, -1]]
+    assert r["slot_row"].tolist() == [[0, 1], [2, 3], [-1, -1]]
+
+
+def test_reroute_only_to_experts_with_room_after_the_first_round():
+    """An expert that is full after the first round is never proposed, even
+    when it has the best remaining logit."""
+    idx = np.array([[0], [1], [0]])
+    L = np.array([[5, 1, 0], [0, 5, 1], [5, 4, 1]], np.float64)
+    r = O.dispatch_reroute(idx, L, 3, 1)
+    # token 2 drops at expert 0; expert 1 (logit 4) is full, so it goes to 2
+    assert r["proposal"][2, 0] == 2
+    assert r["expert"].ravel().tolist() == [0, 1, 2]
+
+
+def test_reroute_without_overflow_is_the_drop_dispatch():
+    inp = _rand(T=40, N=8, k=2, seed=21)
+    a = _fwd(inp)
+    b = O.moe_forward(inp.hidden, inp.w_router, inp.w1, inp.w3, inp.w2, 2, 0.0, None,
+                      overflow="reroute")
+    for key in ("slot_row", "perm_src", "offsets", "kept"):
+        assert np.array_equal(a[key], b[key]), key
+    assert np.array_equal(a["y"], b["y"])
+
+
+@pytest.mark.parametrize("seed,cf", [(0, 0.5), (1, 1.0), (2, 0.25), (3, 1.5)])
+def test_reroute_invariants(seed, cf):
+    """Capacity holds, first-round places are untouched, re-routed slots land
+    on experts outside the token's picks (distinct within a token), and no
+    slot that the drop policy keeps is lost."""
+    bias = np.zeros(16, np.float32)
+    bias[:3] = [3.0, 2.0, 1.0]
+    inp = _rand(T=96, N=16, k=2, seed=seed, cf=cf, bias=bias)
+    L = O.router_logits(inp.hidden, inp.w_router, inp.bias)
+    idx = O.select_topk(L, 2)
+    C = O.capacity(96, 2, 16, cf)
+    d0 = O.dispatch(idx, 16, C)
+    r = O.dispatch_reroute(idx, L, 16, C)
+    assert (r["kept"] <= C).all()
+    assert np.array_equal(r["keep1"], d0["keep"])
+    moved = r["keep2"]
+    for t, j in zip(*np.nonzero(moved)):
+        assert r["expert"][t, j] not in idx[t]
+    for t in range(96):
+        ex = [e for e in r["expert"][t] if e >= 0]
+        assert len(ex) == len(set(ex))
+    # every row's expert is the one its slot names
+    for t in range(96):
+        for j in range(2):
+            row = r["slot_row"][t, j]
+            if row >= 0:
+                e = r["expert"][t, j]
+                assert r["offsets"][e] <= row < r["offsets"][e + 1]
+                assert r["perm_src"][row] == t
+    assert r["kept"].sum() >= d0["kept"].sum()
+    if (~d0["keep"]).any():
+        assert moved.any()
+
+
+@pytest.mark.parametrize("cf", [0.25, 0.75])
+def test_reroute_per_expert_path_equals_per_token_brute_force(cf):
+    bias = np.zeros(8, np.float32)
+    bias[:2] = [4.0, 3.0]                       # experts 0 and 1 overflow, the others have room
+    inp = _rand(T=40, N=8, k=2, seed=5, cf=cf, bias=bias)
+    a = O.moe_forward(inp.hidden, inp.w_router, inp.w1, inp.w3, inp.w2, 2, cf, inp.bias,
+                      overflow="reroute")
+    b = O.moe_forward_per_token(inp.hidden, inp.w_router, inp.w1, inp.w3, inp.w2, 2, cf,
+                                inp.bias, overflow="reroute")
+    assert np.allclose(a["y"], b, rtol=1e-12, atol=1e-12)
+    d = O.moe_forward(inp.hidden, inp.w_router, inp.w1, inp.w3, inp.w2, 2, cf, inp.bias)
+    moved = (a["slot_row"] >= 0) & (d["slot_row"] < 0)
+    assert moved.any()
+    assert not np.allclose(a["y"][moved.any(1)], d["y"][moved.any(1)])
+
+
 # ---------------------------------------------------------------- aux loss
 def test_aux_uniform_router_is_exactly_one():
     """W_router = 0 gives P_e = 1/N; with f summing to 1 the loss is exactly 1, also under drops."""
@@ -418,6 +516,15 @@ def test_pins_catch_planted_mistakes():
 
     # capacity without k: the workload capacities no longer come out
     assert capacity_without_k(4096, 2, 16, 1.25) != 640
+
+    # re-routing that ignores the first round's fill sends token 2 of the
+    # room example to the full expert 1
+    def reroute_ignoring_room(idx, L, N, C):
+        big = O.dispatch_reroute(idx, L, N, C + 10 ** 6)
+        return big
+    r = reroute_ignoring_room(np.array([[0], [1], [0]]),
+                              np.array([[5, 1, 0], [0, 5, 1], [5, 4, 1]], np.float64), 3, 1)
+    assert r["expert"].ravel().tolist() != [0, 1, 2]
 
     # keeping the last C tokens instead of the first: characterisation fails
     inp = _rand(T=64, N=8, k=2, seed=8)

@@ -15,6 +15,9 @@ Also reported in the same line:
                 against the bf16 dense MFMA peak; HBM traffic per launch from
                 rocprofv3 FETCH_SIZE/WRITE_SIZE when a committed counter
                 summary matches the current kernel source, else null;
+  skewed_overflow  the skewed 64-expert workload (T 16384, d 4096, top-2, f 2048,
+                CF 1.5, Zipf router bias): layer time with over-capacity
+                assignments dropped and with them re-routed once;
   decode        the decode-shaped workload (T 256, d 4096, 128 experts, top-2,
                 f 1536): layer time and the algorithmic bytes it must read
                 (the weights of every expert that got a token, router weights,
@@ -72,7 +75,7 @@ def upload(inp):
     return {k: t(getattr(inp, k)) for k in ("hidden", "w_router", "w1", "w3", "w2", "bias")}
 
 
-def time_layer(inp, dev, steps, warmup):
+def time_layer(inp, dev, steps, warmup, overflow="drop"):
     """Warm up, then time `steps` forwards; per-step HIP events bracket the GEMMs."""
     import torch
     from mixture_experts_layer_sum_amd import moe
@@ -83,8 +86,13 @@ def time_layer(inp, dev, steps, warmup):
     def step(ev=None):
         moe.moe_route(dev["hidden"], dev["w_router"], k, dev["bias"], b.logits, b.topk_idx, b.topk_w,
                       b.counts, b.ws_route)
-        moe.moe_permute(dev["hidden"], b.topk_idx, N, inp.capacity_factor, b.x_perm, b.perm_src,
-                        b.slot_row, b.kept, b.offsets, b.ws_permute)
+        if overflow == "drop":
+            moe.moe_permute(dev["hidden"], b.topk_idx, N, inp.capacity_factor, b.x_perm,
+                            b.perm_src, b.slot_row, b.kept, b.offsets, b.ws_permute)
+        else:
+            moe.moe_permute_reroute(dev["hidden"], b.topk_idx, b.logits, N, inp.capacity_factor,
+                                    b.x_perm, b.perm_src, b.slot_row, b.kept, b.offsets,
+                                    b.ws_permute)
         if ev:
             ev[0].record(s)
         moe.moe_expert_up(b.x_perm, b.offsets, dev["w1"], dev["w3"], b.act)
@@ -109,8 +117,10 @@ def time_layer(inp, dev, steps, warmup):
     down_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
     kept = b.kept.cpu().numpy()
     A = int(b.offsets[-1].item())
+    dropped = int((b.slot_row < 0).sum().item())
     return {"elapsed_s": elapsed, "ms_per_step": 1e3 * elapsed / steps, "up_ms": up_ms,
-            "down_ms": down_ms, "A": A, "kept": kept, "aux": float(b.aux.item())}
+            "down_ms": down_ms, "A": A, "kept": kept, "aux": float(b.aux.item()),
+            "dropped": dropped}
 
 
 def layer_flops(inp, A):
@@ -321,6 +331,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-skewed", action="store_true",
+                    help="skip the skewed 64-expert workload (drop vs re-route)")
     ap.add_argument("--no-main", action="store_true",
                     help="profiling aid: time only the decode-shaped layer (no JSON line)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -335,7 +347,7 @@ def main():
 
     if args.write_traffic:
         cmds = [f"rocprofv3 --pmc {c} -d gpurun_out/pmc_{c} -o run --output-format csv -- python -u "
-                f"bench.py --steps 2 --warmup 1 --no-decode --no-cpu-baseline --copy-calibration "
+                f"bench.py --steps 2 --warmup 1 --no-decode --no-skewed --no-cpu-baseline --copy-calibration "
                 f"{args.copy_calibration}" for c in ("FETCH_SIZE", "WRITE_SIZE")]
         write_traffic(*args.write_traffic, args.copy_calibration, cmds)
         return 0
@@ -408,6 +420,26 @@ def main():
                          "GB_per_s": gbs, "pct_hbm_peak": 100.0 * gbs / PEAK_HBM_GBS,
                          "up_ms": rd["up_ms"], "down_ms": rd["down_ms"]}
         del devd
+        torch.cuda.empty_cache()
+
+    if not args.no_skewed:
+        ks = "skewed_zipf"
+        wsk = synth.WORKLOADS[ks]
+        log(f"generating {wsk.name}")
+        inps = synth.make_workload_inputs(ks, seed=args.seed)
+        devs = upload(inps)
+        sk = {"workload": wsk.name}
+        for pol in ("drop", "reroute"):
+            rs = time_layer(inps, devs, max(args.steps, 20), args.warmup, overflow=pol)
+            fl = layer_flops(inps, rs["A"])
+            sk[pol] = {"ms_per_step": rs["ms_per_step"],
+                       "tokens_per_s": wsk.T / (rs["ms_per_step"] * 1e-3),
+                       "routed_rows": rs["A"], "dropped_assignments": rs["dropped"],
+                       "active_experts": int((rs["kept"] > 0).sum()),
+                       "layer_tflops": fl / (rs["ms_per_step"] * 1e-3) / 1e12,
+                       "up_ms": rs["up_ms"], "down_ms": rs["down_ms"]}
+        out["skewed_overflow"] = sk
+        del devs
         torch.cuda.empty_cache()
 
     if args.copy_calibration:

@@ -11,6 +11,7 @@
  *   logits  = hidden . W_router (+ bias)                          moe_route
  *   top-k per token, softmax over the k selected logits           moe_route
  *   per-expert counts, capacity cut, expert-contiguous permute    moe_permute
+ *   (or: over-capacity assignments re-routed once)                moe_permute_reroute
  *   per-expert SwiGLU FFN as one grouped GEMM pair                moe_expert_ffn
  *   weighted combine back to token order                          moe_combine
  *   load-balancing loss N * sum_e f_e * P_e                       moe_aux_loss
@@ -59,7 +60,8 @@ typedef enum {
   MOE_OP_EXPERT_FFN = 2,
   MOE_OP_COMBINE = 3,
   MOE_OP_AUX_LOSS = 4,
-  MOE_OP_EXPERT_DOWN = 5
+  MOE_OP_EXPERT_DOWN = 5,
+  MOE_OP_PERMUTE_REROUTE = 6
 } moe_op;
 
 /* Human-readable name of a status code (static string). */
@@ -121,6 +123,33 @@ moe_status moe_permute(const void* hidden, const int32_t* topk_idx, int T, int d
                        float capacity_factor, moe_dtype dt, void* x_perm, int32_t* perm_src,
                        int32_t* slot_row, int32_t* kept, int32_t* offsets, void* ws,
                        size_t ws_bytes, void* stream);
+
+/*
+ * moe_permute_reroute -- as moe_permute, but assignments over capacity get
+ * one second chance instead of being dropped.  P5 §4.2 (capacity-aware
+ * routing: mask the over-capacity pick, take the next-best expert), P4 §2.2
+ * and P5 §2.2 (over-capacity tokens are dropped or sent to the next-best
+ * expert), P3 §2.3 (overflow handed to idle experts).
+ *
+ *   First round exactly as moe_permute (kept1_e = min(count_e, C)).  Second
+ *   round: each dropped (t, j), in slot order within token t, proposes the
+ *   expert with the largest logits[t, e] (fp32; ties to the lower id) among
+ *   experts that are not in topk_idx[t, :], were not proposed by an earlier
+ *   dropped slot of t, and have kept1_e < C.  Each expert admits proposals in
+ *   token order while it has room (C - kept1_e); the rest stay dropped.
+ *   Inside an expert, first-round rows come first, then second-round rows,
+ *   each token-ascending.  A moved slot keeps its gate weight: moe_combine
+ *   needs no change.
+ *
+ *   logits  [T, N] fp32 (from moe_route)
+ *   other arguments, outputs and limits as moe_permute; kept[e] counts both
+ *   rounds (<= C)
+ *   ws      moe_workspace_size(MOE_OP_PERMUTE_REROUTE, T, d, N, k, f, dt) bytes
+ */
+moe_status moe_permute_reroute(const void* hidden, const int32_t* topk_idx, const float* logits,
+                               int T, int d, int N, int k, float capacity_factor, moe_dtype dt,
+                               void* x_perm, int32_t* perm_src, int32_t* slot_row, int32_t* kept,
+                               int32_t* offsets, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_expert_ffn -- every expert's SwiGLU FFN over its rows, as two grouped

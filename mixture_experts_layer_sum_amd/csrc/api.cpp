@@ -76,6 +76,9 @@ size_t moe_workspace_size(moe_op op, int T, int d, int N, int k, int f, moe_dtyp
       if (d < 1 || !dtype_ok(dt)) return 0;
       return dt == MOE_BF16 ? moe::route_ws_bytes(T, d, N) : 0;
     case MOE_OP_PERMUTE: return moe::permute_ws_bytes(T, N);
+    case MOE_OP_PERMUTE_REROUTE:
+      if (N > kMaxExperts || static_cast<int64_t>(T) * k >= (int64_t{1} << 31)) return 0;
+      return moe::permute_reroute_ws_bytes(T, N, k);
     case MOE_OP_EXPERT_FFN:
       if (d < 1 || f < 1 || !dtype_ok(dt)) return 0;
       return act_bytes(T * k, f, dt) +
@@ -120,6 +123,26 @@ moe_status moe_permute(const void* hidden, const int32_t* topk_idx, int T, int d
   const int C = capacity_of(T, k, N, capacity_factor);
   return hip_status(moe::launch_permute(hidden, topk_idx, T, d, N, k, C, elem_bytes(dt), x_perm,
                                         perm_src, slot_row, kept, offsets, ws, as_stream(stream)));
+}
+
+moe_status moe_permute_reroute(const void* hidden, const int32_t* topk_idx, const float* logits,
+                               int T, int d, int N, int k, float capacity_factor, moe_dtype dt,
+                               void* x_perm, int32_t* perm_src, int32_t* slot_row, int32_t* kept,
+                               int32_t* offsets, void* ws, size_t ws_bytes, void* stream) {
+  if (!hidden || !topk_idx || !logits || !x_perm || !perm_src || !slot_row || !kept || !offsets)
+    return MOE_ERR_INVALID_ARG;
+  if (std::isnan(capacity_factor)) return MOE_ERR_INVALID_ARG;
+  moe_status s = check_tnk(T, N, k);
+  if (s != MOE_OK) return s;
+  if ((s = check_d(d)) != MOE_OK) return s;
+  if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
+  const size_t need = moe::permute_reroute_ws_bytes(T, N, k);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (!ws) return MOE_ERR_INVALID_ARG;
+  const int C = capacity_of(T, k, N, capacity_factor);
+  return hip_status(moe::launch_permute_reroute(hidden, topk_idx, logits, T, d, N, k, C,
+                                                elem_bytes(dt), x_perm, perm_src, slot_row, kept,
+                                                offsets, ws, as_stream(stream)));
 }
 
 moe_status moe_expert_up(const void* x_perm, const int32_t* offsets, const void* w1,

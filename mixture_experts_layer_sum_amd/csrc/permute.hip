@@ -186,6 +186,210 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restric
   }
 }
 
+// ---------------------------------------------------------------- overflow re-routing
+// hotelren.com/news/3071227 §4.2 (capacity-aware routing: mask the original
+// pick of an over-capacity token and take its next-best expert),
+// 2kiu.com/news/2885792 §2.2 and hotelren.com/news/3071227 §2.2 (tokens over
+// capacity are dropped or sent to the next-best expert),
+// devpress.csdn.net/awstech/6a91abf4... §2.3 (overflow goes to idle experts).
+// One second dispatch round after the capacity cut: each dropped assignment,
+// in slot order within its token, proposes the highest-logit expert that is
+// not one of the token's picks, not proposed by an earlier dropped slot of
+// the token, and had room after the first round; experts admit proposals in
+// token order up to the room left.  Both rounds use the same order-free
+// machinery as the first (chunk histograms, per-expert scan, bitmask ranks).
+
+// rank[s] = place of slot s at expert ids[s] in token order (base[c][e] +
+// earlier slots of the chunk), or -1 where ids[s] is not an expert.
+__global__ __launch_bounds__(kChunk) void rank_kernel(const int32_t* __restrict__ ids, int T,
+                                                      int N, int k,
+                                                      const int32_t* __restrict__ base,
+                                                      int32_t* __restrict__ rank) {
+  __shared__ unsigned long long mask[256][4];
+  __shared__ int bs[256];
+  const int tid = threadIdx.x, c = blockIdx.x;
+  for (int e = tid; e < N; e += kChunk) {
+    mask[e][0] = mask[e][1] = mask[e][2] = mask[e][3] = 0ull;
+    bs[e] = base[(size_t)c * N + e];
+  }
+  __syncthreads();
+  const int t = c * kChunk + tid;
+  const int word = tid >> 6;
+  const unsigned long long bit = 1ull << (tid & 63);
+  if (t < T)
+    for (int j = 0; j < k; ++j) {
+      const int e = ids[(size_t)t * k + j];
+      if (e >= 0 && e < N) atomicOr(&mask[e][word], bit);
+    }
+  __syncthreads();
+  if (t < T)
+    for (int j = 0; j < k; ++j) {
+      const int e = ids[(size_t)t * k + j];
+      int r = -1;
+      if (e >= 0 && e < N) {
+        r = bs[e];
+        for (int q = 0; q < word; ++q) r += __popcll(mask[e][q]);
+        r += __popcll(mask[e][word] & (bit - 1ull));
+      }
+      rank[(size_t)t * k + j] = r;
+    }
+}
+
+// First-round totals: kept1[e] = min(count_e, C).
+__global__ __launch_bounds__(256) void first_round_scan_kernel(const int32_t* __restrict__ hist,
+                                                               int nchunks, int N, int C,
+                                                               int32_t* __restrict__ base,
+                                                               int32_t* __restrict__ kept1) {
+  const int e = threadIdx.x;
+  if (e >= N) return;
+  int run = 0;
+  for (int c = 0; c < nchunks; ++c) {
+    base[(size_t)c * N + e] = run;
+    run += hist[(size_t)c * N + e];
+  }
+  kept1[e] = run < C ? run : C;
+}
+
+// One thread per token: proposals of its dropped slots (logits in fp32, the
+// precision the router produced them in; ties to the lower expert id).
+__global__ __launch_bounds__(256) void propose_kernel(const int32_t* __restrict__ topk_idx,
+                                                      const float* __restrict__ logits,
+                                                      const int32_t* __restrict__ rank1,
+                                                      const int32_t* __restrict__ kept1, int T,
+                                                      int N, int k, int C,
+                                                      int32_t* __restrict__ prop) {
+  __shared__ int room[256];
+  for (int e = threadIdx.x; e < 256; e += blockDim.x) room[e] = (e < N) && kept1[e] < C;
+  __syncthreads();
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  unsigned long long taken[4] = {0ull, 0ull, 0ull, 0ull};
+  for (int j = 0; j < k; ++j) {
+    const int e = topk_idx[(size_t)t * k + j];
+    if (e >= 0 && e < N) taken[e >> 6] |= 1ull << (e & 63);
+  }
+  const float* L = logits + (size_t)t * N;
+  for (int j = 0; j < k; ++j) {
+    const size_t s = (size_t)t * k + j;
+    const int e0 = topk_idx[s];
+    int best = -1;
+    if (e0 >= 0 && e0 < N && rank1[s] >= C) {
+      float bv = 0.f;
+      for (int e = 0; e < N; ++e) {
+        if (!room[e] || ((taken[e >> 6] >> (e & 63)) & 1ull)) continue;
+        const float v = L[e];
+        if (best < 0 || v > bv) {
+          best = e;
+          bv = v;
+        }
+      }
+      if (best >= 0) taken[best >> 6] |= 1ull << (best & 63);
+    }
+    prop[s] = best;
+  }
+}
+
+// Second-round totals and the final layout: kept2[e] = min(proposals_e,
+// C - kept1[e]); kept = kept1 + kept2; offsets = exclusive scan of kept.
+__global__ __launch_bounds__(256) void second_round_scan_kernel(const int32_t* __restrict__ hist2,
+                                                                int nchunks, int N, int C,
+                                                                const int32_t* __restrict__ kept1,
+                                                                int32_t* __restrict__ base2,
+                                                                int32_t* __restrict__ kept,
+                                                                int32_t* __restrict__ offsets) {
+  __shared__ int sk[256];
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < N)
+    for (int c = 0; c < nchunks; ++c) {
+      base2[(size_t)c * N + e] = run;
+      run += hist2[(size_t)c * N + e];
+    }
+  int kp = 0;
+  if (e < N) {
+    const int k1 = kept1[e];
+    const int r2 = C - k1;
+    kp = k1 + (run < r2 ? run : r2);
+    kept[e] = kp;
+  }
+  sk[e] = kp;
+  __syncthreads();
+  for (int s = 1; s < 256; s <<= 1) {     // inclusive Hillis-Steele scan
+    const int v = (e >= s) ? sk[e - s] : 0;
+    __syncthreads();
+    sk[e] += v;
+    __syncthreads();
+  }
+  if (e < N) offsets[e] = sk[e] - kp;
+  if (e == N - 1) offsets[N] = sk[e];
+}
+
+// Rows of both rounds: first-round places first inside an expert, then the
+// admitted second-round places.
+__global__ __launch_bounds__(256) void reroute_place_kernel(
+    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ rank1,
+    const int32_t* __restrict__ prop, const int32_t* __restrict__ rank2,
+    const int32_t* __restrict__ kept1, const int32_t* __restrict__ offsets, int T, int N, int k,
+    int C, int32_t* __restrict__ slot_row, int32_t* __restrict__ perm_src) {
+  const size_t s = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= (size_t)T * k) return;
+  const int t = (int)(s / k);
+  const int e1 = topk_idx[s];
+  int row = -1;
+  if (e1 >= 0 && e1 < N && rank1[s] < C) {
+    row = offsets[e1] + rank1[s];
+  } else {
+    const int e2 = prop[s];
+    if (e2 >= 0 && rank2[s] < C - kept1[e2]) row = offsets[e2] + kept1[e2] + rank2[s];
+  }
+  slot_row[s] = row;
+  if (row >= 0) perm_src[row] = t;
+}
+
+size_t permute_reroute_ws_bytes(int T, int N, int k) {
+  const size_t nch = (static_cast<size_t>(T) + kChunk - 1) / kChunk;
+  const size_t ints = 4 * nch * N + N + 3 * static_cast<size_t>(T) * k;
+  return ints * sizeof(int32_t);
+}
+
+hipError_t launch_permute_reroute(const void* hidden, const int32_t* topk_idx,
+                                  const float* logits, int T, int d, int N, int k, int C,
+                                  int elem_bytes, void* x_perm, int32_t* perm_src,
+                                  int32_t* slot_row, int32_t* kept, int32_t* offsets, void* ws,
+                                  hipStream_t stream) {
+  const int nch = (T + kChunk - 1) / kChunk;
+  const size_t tk = static_cast<size_t>(T) * k;
+  int32_t* hist1 = static_cast<int32_t*>(ws);
+  int32_t* base1 = hist1 + static_cast<size_t>(nch) * N;
+  int32_t* hist2 = base1 + static_cast<size_t>(nch) * N;
+  int32_t* base2 = hist2 + static_cast<size_t>(nch) * N;
+  int32_t* kept1 = base2 + static_cast<size_t>(nch) * N;
+  int32_t* rank1 = kept1 + N;
+  int32_t* prop = rank1 + tk;
+  int32_t* rank2 = prop + tk;
+  hipLaunchKernelGGL(chunk_hist_kernel, dim3(nch), dim3(kChunk), 0, stream, topk_idx, T, N, k,
+                     hist1);
+  hipLaunchKernelGGL(first_round_scan_kernel, dim3(1), dim3(256), 0, stream, hist1, nch, N, C,
+                     base1, kept1);
+  hipLaunchKernelGGL(rank_kernel, dim3(nch), dim3(kChunk), 0, stream, topk_idx, T, N, k, base1,
+                     rank1);
+  hipLaunchKernelGGL(propose_kernel, dim3((T + 255) / 256), dim3(256), 0, stream, topk_idx,
+                     logits, rank1, kept1, T, N, k, C, prop);
+  hipLaunchKernelGGL(chunk_hist_kernel, dim3(nch), dim3(kChunk), 0, stream, prop, T, N, k, hist2);
+  hipLaunchKernelGGL(second_round_scan_kernel, dim3(1), dim3(256), 0, stream, hist2, nch, N, C,
+                     kept1, base2, kept, offsets);
+  hipLaunchKernelGGL(rank_kernel, dim3(nch), dim3(kChunk), 0, stream, prop, T, N, k, base2,
+                     rank2);
+  hipLaunchKernelGGL(reroute_place_kernel, dim3((unsigned)((tk + 255) / 256)), dim3(256), 0,
+                     stream, topk_idx, rank1, prop, rank2, kept1, offsets, T, N, k, C, slot_row,
+                     perm_src);
+  const int vpr = (d * elem_bytes) / 16;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(T), dim3(256), 0, stream,
+                     static_cast<const uint4*>(hidden), slot_row, k, vpr,
+                     static_cast<uint4*>(x_perm));
+  return hipGetLastError();
+}
+
 size_t permute_ws_bytes(int T, int N) {
   const size_t nch = (static_cast<size_t>(T) + kChunk - 1) / kChunk;
   return 2 * nch * static_cast<size_t>(N) * sizeof(int32_t);

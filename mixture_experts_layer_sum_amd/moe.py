@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
 (MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_EXPERT_FFN, MOE_OP_COMBINE, MOE_OP_AUX_LOSS,
- MOE_OP_EXPERT_DOWN) = range(6)
+ MOE_OP_EXPERT_DOWN, MOE_OP_PERMUTE_REROUTE) = range(7)
 
 # Every symbol include/moe.h declares, with (restype, argtypes).
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -28,6 +28,8 @@ SIGNATURES = {
     "moe_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
     "moe_route": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P]),
     "moe_permute": (_I, [_P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "moe_permute_reroute": (_I, [_P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _Z,
+                                 _P]),
     "moe_expert_ffn": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
     "moe_expert_up": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "moe_expert_down": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
@@ -128,6 +130,27 @@ def moe_permute(hidden, topk_idx, N, capacity_factor=0.0, x_perm=None, perm_src=
     return x_perm, perm_src, slot_row, kept, offsets
 
 
+def moe_permute_reroute(hidden, topk_idx, logits, N, capacity_factor=0.0, x_perm=None,
+                        perm_src=None, slot_row=None, kept=None, offsets=None, ws=None,
+                        stream=None):
+    T, d = hidden.shape
+    k = topk_idx.shape[1]
+    dev = hidden.device
+    x_perm = _empty((T * k, d), hidden.dtype, dev, x_perm)
+    perm_src = _empty((T * k,), torch.int32, dev, perm_src)
+    slot_row = _empty((T, k), torch.int32, dev, slot_row)
+    kept = _empty((N,), torch.int32, dev, kept)
+    offsets = _empty((N + 1,), torch.int32, dev, offsets)
+    if ws is None:
+        ws = torch.empty(max(1, workspace_size(MOE_OP_PERMUTE_REROUTE, T, d, N, k, 1, hidden.dtype)),
+                         dtype=torch.uint8, device=dev)
+    _check(_lib.moe_permute_reroute(_ptr(hidden), _ptr(topk_idx), _ptr(logits), T, d, N, k,
+                                    float(capacity_factor), _dt(hidden), _ptr(x_perm),
+                                    _ptr(perm_src), _ptr(slot_row), _ptr(kept), _ptr(offsets),
+                                    _ptr(ws), ws.numel(), _stream(stream)), "moe_permute_reroute")
+    return x_perm, perm_src, slot_row, kept, offsets
+
+
 def moe_expert_up(x_perm, offsets, w1, w3, act=None, stream=None):
     max_rows, d = x_perm.shape
     N, _, f = w1.shape
@@ -206,18 +229,23 @@ class MoEBuffers:
         self.y = e((T, d), dtype)
         self.aux = e((1,), torch.float32)
         self.ws_route = e((max(1, workspace_size(MOE_OP_ROUTE, T, d, N, k, f, dtype)),), torch.uint8)
-        self.ws_permute = e((max(1, workspace_size(MOE_OP_PERMUTE, T, d, N, k, f, dtype)),), torch.uint8)
+        self.ws_permute = e((max(1, workspace_size(MOE_OP_PERMUTE, T, d, N, k, f, dtype),
+                                 workspace_size(MOE_OP_PERMUTE_REROUTE, T, d, N, k, f, dtype)),),
+                            torch.uint8)
         self.ws_aux = e((max(1, workspace_size(MOE_OP_AUX_LOSS, T, d, N, k, f, dtype)),), torch.uint8)
         self.ws_down = e((max(1, workspace_size(MOE_OP_EXPERT_DOWN, T, d, N, k, f, dtype)),),
                          torch.uint8)
 
 
 def moe_forward(hidden, w_router, w1, w3, w2, k, capacity_factor=0.0, bias=None,
-                bufs: Optional[MoEBuffers] = None, stream=None):
+                bufs: Optional[MoEBuffers] = None, stream=None, overflow="drop"):
     """Run the five steps on the current stream.  Returns the MoEBuffers holding every result.
 
     ``y`` excludes the residual: the layer output with residual is hidden + y.
+    ``overflow`` is "drop" (moe_permute) or "reroute" (moe_permute_reroute).
     """
+    if overflow not in ("drop", "reroute"):
+        raise ValueError(f"unknown overflow policy {overflow!r}")
     T, d = hidden.shape
     N, _, f = w1.shape
     if bufs is None:
@@ -225,8 +253,12 @@ def moe_forward(hidden, w_router, w1, w3, w2, k, capacity_factor=0.0, bias=None,
     b = bufs
     moe_route(hidden, w_router, k, bias, b.logits, b.topk_idx, b.topk_w, b.counts, b.ws_route,
               stream)
-    moe_permute(hidden, b.topk_idx, N, capacity_factor, b.x_perm, b.perm_src, b.slot_row, b.kept,
-                b.offsets, b.ws_permute, stream)
+    if overflow == "drop":
+        moe_permute(hidden, b.topk_idx, N, capacity_factor, b.x_perm, b.perm_src, b.slot_row,
+                    b.kept, b.offsets, b.ws_permute, stream)
+    else:
+        moe_permute_reroute(hidden, b.topk_idx, b.logits, N, capacity_factor, b.x_perm, b.perm_src,
+                            b.slot_row, b.kept, b.offsets, b.ws_permute, stream)
     moe_expert_up(b.x_perm, b.offsets, w1, w3, b.act, stream)
     moe_expert_down(b.act, b.offsets, w2, b.y_perm, b.ws_down, stream)
     moe_combine(b.y_perm, b.slot_row, b.topk_w, hidden.dtype, b.y, stream)

@@ -52,6 +52,9 @@ def test_workspace_sizes():
     assert lib.moe_workspace_size(moe.MOE_OP_COMBINE, 64, 128, 8, 2, 256, F32) == 0
     # two int32 [chunks, N] tables, chunks of 256 tokens
     assert lib.moe_workspace_size(moe.MOE_OP_PERMUTE, 257, 128, 8, 2, 256, F32) == 2 * 2 * 8 * 4
+    # re-routing: four chunk tables, first-round kept, three per-slot arrays
+    assert lib.moe_workspace_size(moe.MOE_OP_PERMUTE_REROUTE, 257, 128, 8, 2, 256, F32) == \
+        (4 * 2 * 8 + 8 + 3 * 257 * 2) * 4
     assert lib.moe_workspace_size(moe.MOE_OP_EXPERT_FFN, 64, 128, 8, 2, 256, BF16) == 64 * 2 * 256 * 2
     assert lib.moe_workspace_size(moe.MOE_OP_EXPERT_FFN, 64, 128, 8, 2, 256, F32) == 64 * 2 * 256 * 4
     # the k-split buffers of the down projection follow the current device (none here);
@@ -121,6 +124,22 @@ def test_expert_ffn_rejects(kw, status):
         # fp32 accepts d = f = 64; a too-small workspace is then the only error
         kw = dict(kw, ws_bytes=128 * 64 * 4 - 1)
     assert ffn(**kw) == status
+
+
+def reroute(**kw):
+    a = dict(hidden=P, topk_idx=P, logits=P, T=64, d=128, N=8, k=2, cf=1.0, dt=BF16, x_perm=P,
+             perm_src=P, slot_row=P, kept=P, offsets=P, ws=P, ws_bytes=1 << 20, stream=S)
+    a.update(kw)
+    return lib.moe_permute_reroute(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(logits=NUL), INV), (dict(hidden=NUL), INV), (dict(ws=NUL), INV), (dict(cf=math.nan), INV),
+    (dict(k=9), INV), (dict(T=0), INV), (dict(N=300), UNS), (dict(d=100), UNS), (dict(dt=7), UNS),
+    (dict(ws_bytes=(4 * 1 * 8 + 8 + 3 * 64 * 2) * 4 - 1), WS),
+])
+def test_permute_reroute_rejects(kw, status):
+    assert reroute(**kw) == status
 
 
 def test_expert_up_down_reject():

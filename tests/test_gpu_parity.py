@@ -23,13 +23,14 @@ def moe():
     return m
 
 
-def _run(inp, label, sample=None, audit=True, bufs=None):
+def _run(inp, label, sample=None, audit=True, bufs=None, overflow="drop"):
     from tests import parity
     parity.log(f"{label}: T={inp.T} d={inp.d} N={inp.N} k={inp.k} f={inp.f} {inp.dtype} "
-               f"cf={inp.capacity_factor} bias={'yes' if inp.bias is not None else 'no'}")
+               f"cf={inp.capacity_factor} bias={'yes' if inp.bias is not None else 'no'} "
+               f"overflow={overflow}")
     dev = parity.to_device(inp)
-    g, b = parity.run_gpu(inp, dev, bufs)
-    rep = parity.check(inp, g, sample=sample, label=label, audit=audit)
+    g, b = parity.run_gpu(inp, dev, bufs, overflow=overflow)
+    rep = parity.check(inp, g, sample=sample, label=label, audit=audit, overflow=overflow)
     return rep, g, dev, b
 
 
@@ -126,6 +127,40 @@ def test_down_workspace_is_checked(moe):
     moe.moe_expert_down(act, offs, w2, y, ws)
     torch.cuda.synchronize()
     assert (y == 0).all()
+
+
+REROUTE = [
+    # label, T, d, N, k, f, dtype, cf, bias
+    ("f32_reroute", 300, 128, 8, 2, 192, "f32", 1.0, "skew"),
+    ("bf16_reroute_zipf", 513, 256, 64, 2, 256, "bf16", 1.5, "zipf"),
+    ("bf16_reroute_k1", 200, 256, 8, 1, 128, "bf16", 0.6, "skew"),
+    ("bf16_reroute_k4", 300, 256, 16, 4, 128, "bf16", 0.5, "skew"),
+    ("bf16_reroute_no_room", 64, 256, 8, 2, 128, "bf16", 0.01, "skew"),
+    ("bf16_reroute_many_chunks", 1500, 256, 16, 2, 128, "bf16", 0.75, "zipf"),
+]
+
+
+@pytest.mark.parametrize("case", REROUTE, ids=[c[0] for c in REROUTE])
+def test_reroute_small_shapes(moe, case):
+    label, T, d, N, k, f, dt, cf, bias = case
+    if bias == "zipf":
+        b = synth.zipf_bias(N)
+    else:
+        b = np.zeros(N, np.float32)
+        b[: min(3, N)] = [3.0, 2.0, 1.0][: min(3, N)]
+    for seed in (0, 1):
+        inp = synth.make_inputs(T, d, N, k, f, dt, cf, seed, bias=b)
+        rep, g, _, _ = _run(inp, f"{label}/seed{seed}", overflow="reroute")
+        assert (g["kept"] <= max(1, int(np.floor(T * k / N * cf)))).all()
+
+
+def test_reroute_workload_full_size(moe):
+    """The skewed 64-expert workload (heavy overflow) with re-routing, y on sampled tokens."""
+    inp = synth.make_workload_inputs("skewed_zipf", seed=0)
+    rng = np.random.default_rng(7)
+    sample = np.unique(np.concatenate([[0, inp.T - 1], rng.choice(inp.T, 48, replace=False)]))
+    rep, g, _, _ = _run(inp, "workload_skewed_zipf_reroute", sample=sample, overflow="reroute")
+    assert rep["tokens_on_other_experts"] <= inp.T // 100
 
 
 WORKLOADS = ["tiny_fp32", "n16_cf125", "mixtral", "skewed_zipf", "decode"]

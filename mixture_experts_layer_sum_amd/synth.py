@@ -12,6 +12,10 @@ drawn in parallel and any block can be regenerated on its own):
 * ``w1[e] [d, f]``       ~ N(0, 1) / sqrt(d)      stream ``[seed, 2, e]``
 * ``w3[e] [d, f]``       ~ N(0, 1) / sqrt(d)      stream ``[seed, 3, e]``
 * ``w2[e] [f, d]``       ~ N(0, 1) / sqrt(f)      stream ``[seed, 4, e]``
+* shared experts (optional, s = 0 .. Ns-1, hidden size fs):
+  ``w1s[s] [d, fs]``, ``w3s[s] [d, fs]`` ~ N(0, 1) / sqrt(d), streams
+  ``[seed, 5, s]``, ``[seed, 6, s]``; ``w2s[s] [fs, d]`` ~ N(0, 1) / sqrt(fs),
+  stream ``[seed, 7, s]``
 
 Normals are drawn as float32, scaled in float32, and for bf16 workloads
 rounded to bfloat16 with round-to-nearest-even (the bit patterns are kept as
@@ -99,6 +103,13 @@ class MoEInputs:
     w3: np.ndarray                # [N, d, f]
     w2: np.ndarray                # [N, f, d]
     bias: Optional[np.ndarray] = None   # [N] float32 or None
+    w1s: Optional[np.ndarray] = None    # [Ns, d, fs] shared experts, or None
+    w3s: Optional[np.ndarray] = None    # [Ns, d, fs]
+    w2s: Optional[np.ndarray] = None    # [Ns, fs, d]
+
+    @property
+    def n_shared(self) -> int:
+        return 0 if self.w1s is None else self.w1s.shape[0]
 
     def values(self, name: str) -> np.ndarray:
         """float32 values of a tensor (exact for bf16 storage)."""
@@ -127,7 +138,8 @@ def _threads():
 
 
 def make_inputs(T, d, N, k, f, dtype="bf16", capacity_factor=0.0, seed=0,
-                bias: Optional[np.ndarray] = None, zipf=False) -> MoEInputs:
+                bias: Optional[np.ndarray] = None, zipf=False, n_shared=0,
+                f_shared: Optional[int] = None) -> MoEInputs:
     """Draw one layer's inputs with the recipe in the module docstring."""
     assert dtype in ("f32", "bf16")
     st = np.uint16 if dtype == "bf16" else np.float32
@@ -153,8 +165,15 @@ def make_inputs(T, d, N, k, f, dtype="bf16", capacity_factor=0.0, seed=0,
         hidden, w_router = fh.result(), fr.result()
     if zipf and bias is None:
         bias = zipf_bias(N)
-    return MoEInputs(T, d, N, k, f, dtype, float(capacity_factor), hidden, w_router, w1, w3, w2,
-                     None if bias is None else np.asarray(bias, np.float32))
+    inp = MoEInputs(T, d, N, k, f, dtype, float(capacity_factor), hidden, w_router, w1, w3, w2,
+                    None if bias is None else np.asarray(bias, np.float32))
+    if n_shared > 0:
+        fs = f if f_shared is None else f_shared
+        ss = 1.0 / math.sqrt(fs)
+        inp.w1s = np.stack([_draw([seed, 5, q], (d, fs), sd, dtype) for q in range(n_shared)])
+        inp.w3s = np.stack([_draw([seed, 6, q], (d, fs), sd, dtype) for q in range(n_shared)])
+        inp.w2s = np.stack([_draw([seed, 7, q], (fs, d), ss, dtype) for q in range(n_shared)])
+    return inp
 
 
 def make_workload_inputs(key: str, seed: int = 0) -> MoEInputs:

@@ -46,7 +46,10 @@ Readings of points the pages leave open (each also listed in the design notes):
   (C - kept_e); the rest are dropped.  A re-routed assignment keeps its gate
   weight.  Inside an expert, first-round rows come before second-round rows,
   each token-ascending.  Counts and the aux loss stay on the router's own
-  (pre-drop) assignments.
+  (pre-drop) assignments;
+* shared experts (P2 §3.3: experts every token calls unconditionally, next to
+  the routed ones): each is a SwiGLU FFN of its own applied to every token,
+  dropped or not, and added to the routed sum with weight 1.
 """
 from __future__ import annotations
 
@@ -240,7 +243,7 @@ def aux_loss(logits, counts, k: int) -> float:
 
 
 def moe_forward(hidden, w_router, w1, w3, w2, k: int, capacity_factor: float = 0.0,
-                bias=None, tokens=None, overflow: str = "drop") -> dict:
+                bias=None, tokens=None, overflow: str = "drop", shared=None) -> dict:
     """The layer forward, per expert (the page's gather -> FFN -> weighted add loop).
 
     ``w1[e]``, ``w3[e]``, ``w2[e]`` are indexed one expert at a time, so the
@@ -248,7 +251,8 @@ def moe_forward(hidden, w_router, w1, w3, w2, k: int, capacity_factor: float = 0
     counts, dispatch and aux cover every token but the expert FFN and the
     combine are evaluated only for those tokens (``y`` then has one row per
     listed token).  ``overflow`` is "drop" (the default) or "reroute"
-    (:func:`dispatch_reroute`).
+    (:func:`dispatch_reroute`).  ``shared`` is None or ``(w1s, w3s, w2s)``
+    indexable by shared expert: y_t += sum_s FFN_s(x_t) (P2 §3.3).
 
     P1 §2.1 (route, top-k, softmax, weighted sum), P3 §4.1 (per-expert loop;
     its shortcut that weights every expert by the sum of both gate values is
@@ -287,13 +291,20 @@ def moe_forward(hidden, w_router, w1, w3, w2, k: int, capacity_factor: float = 0
             r = slot_row[t, j]
             if r >= 0:
                 y[n] += w[t, j] * y_perm[r]
-    return {"logits": L, "topk_idx": idx, "topk_w": w, "counts": counts, "capacity": C,
+    y_shared = None
+    if shared is not None:
+        w1s, w3s, w2s = shared
+        y_shared = np.zeros((tok.size, d))
+        for q in range(len(w1s)):
+            y_shared += swiglu_ffn(hidden[tok], w1s[q], w3s[q], w2s[q])
+        y = y + y_shared
+    return {"y_shared": y_shared, "logits": L, "topk_idx": idx, "topk_w": w, "counts": counts, "capacity": C,
             "kept": disp["kept"], "offsets": offsets, "slot_row": slot_row, "perm_src": perm_src,
             "y_perm": y_perm, "y": y, "tokens": tok, "aux": aux_loss(L, counts, k)}
 
 
 def moe_forward_per_token(hidden, w_router, w1, w3, w2, k: int, capacity_factor: float = 0.0,
-                          bias=None, overflow: str = "drop") -> np.ndarray:
+                          bias=None, overflow: str = "drop", shared=None) -> np.ndarray:
     """Brute force for tiny inputs: y_t = sum over kept slots j of w_tj * FFN_{i_tj}(x_t).
 
     One token and one slot at a time, with its own running per-expert counter
@@ -338,4 +349,9 @@ def moe_forward_per_token(hidden, w_router, w1, w3, w2, k: int, capacity_factor:
             second[cand] += 1
     elif overflow != "drop":
         raise ValueError(f"unknown overflow policy {overflow!r}")
+    if shared is not None:
+        w1s, w3s, w2s = shared
+        for t in range(T):
+            for q in range(len(w1s)):
+                y[t] += swiglu_ffn(hidden[t:t + 1], w1s[q], w3s[q], w2s[q])[0]
     return y

@@ -15,6 +15,8 @@ Also reported in the same line:
                 against the bf16 dense MFMA peak; HBM traffic per launch from
                 rocprofv3 FETCH_SIZE/WRITE_SIZE when a committed counter
                 summary matches the current kernel source, else null;
+  shared_expert the Mixtral-shaped layer plus one always-on shared expert of
+                the same size (f 14336), added with weight 1 in the combine;
   skewed_overflow  the skewed 64-expert workload (T 16384, d 4096, top-2, f 2048,
                 CF 1.5, Zipf router bias): layer time with over-capacity
                 assignments dropped and with them re-routed once;
@@ -75,12 +77,24 @@ def upload(inp):
     return {k: t(getattr(inp, k)) for k in ("hidden", "w_router", "w1", "w3", "w2", "bias")}
 
 
-def time_layer(inp, dev, steps, warmup, overflow="drop"):
+def upload_shared(inp):
+    import numpy as np
+    import torch
+
+    def t(a):
+        return torch.from_numpy(a.view(np.int16)).to("cuda").view(torch.bfloat16)
+
+    return (t(inp.w1s), t(inp.w3s), t(inp.w2s))
+
+
+def time_layer(inp, dev, steps, warmup, overflow="drop", shared=None):
     """Warm up, then time `steps` forwards; per-step HIP events bracket the GEMMs."""
     import torch
     from mixture_experts_layer_sum_amd import moe
     T, d, N, k, f = inp.T, inp.d, inp.N, inp.k, inp.f
-    b = moe.MoEBuffers(T, d, N, k, f, dev["hidden"].dtype)
+    ns = 0 if shared is None else shared[0].shape[0]
+    b = moe.MoEBuffers(T, d, N, k, f, dev["hidden"].dtype, n_shared=ns,
+                       f_shared=None if shared is None else shared[0].shape[2])
     s = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -101,7 +115,13 @@ def time_layer(inp, dev, steps, warmup, overflow="drop"):
         moe.moe_expert_down(b.act, b.offsets, dev["w2"], b.y_perm, b.ws_down)
         if ev:
             ev[2].record(s)
-        moe.moe_combine(b.y_perm, b.slot_row, b.topk_w, dev["hidden"].dtype, b.y)
+        if shared is not None:
+            for q in range(shared[0].shape[0]):
+                moe.moe_expert_ffn(dev["hidden"], b.shared_offsets, shared[0][q:q + 1],
+                                   shared[1][q:q + 1], shared[2][q:q + 1], b.y_shared[q],
+                                   b.ws_shared)
+        moe.moe_combine(b.y_perm, b.slot_row, b.topk_w, dev["hidden"].dtype, b.y,
+                        None if shared is None else b.y_shared)
         moe.moe_aux_loss(b.logits, b.counts, k, b.aux, b.ws_aux)
 
     for _ in range(warmup):
@@ -331,6 +351,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-shared", action="store_true",
+                    help="skip the Mixtral-shaped layer with one shared expert")
     ap.add_argument("--no-skewed", action="store_true",
                     help="skip the skewed 64-expert workload (drop vs re-route)")
     ap.add_argument("--no-main", action="store_true",
@@ -347,7 +369,7 @@ def main():
 
     if args.write_traffic:
         cmds = [f"rocprofv3 --pmc {c} -d gpurun_out/pmc_{c} -o run --output-format csv -- python -u "
-                f"bench.py --steps 2 --warmup 1 --no-decode --no-skewed --no-cpu-baseline --copy-calibration "
+                f"bench.py --steps 2 --warmup 1 --no-decode --no-skewed --no-shared --no-cpu-baseline --copy-calibration "
                 f"{args.copy_calibration}" for c in ("FETCH_SIZE", "WRITE_SIZE")]
         write_traffic(*args.write_traffic, args.copy_calibration, cmds)
         return 0
@@ -376,7 +398,7 @@ def main():
     key = "mixtral"
     w = synth.WORKLOADS[key]
     log(f"generating {w.name}")
-    inp = synth.make_workload_inputs(key, seed=args.seed)
+    inp = synth.make_workload_inputs(key, seed=args.seed, n_shared=0 if args.no_shared else 1)
     dev = upload(inp)
     log("timing")
     r = time_layer(inp, dev, args.steps, args.warmup)
@@ -402,6 +424,16 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": up_tflops / PEAK_BF16_TFLOPS,
                      "traffic": traffic, "work_per_launch": f"4*A*d*f = {up_flops:.4e} flop, A={A}"},
     }
+    if not args.no_shared:
+        log("timing with one shared expert")
+        sh = upload_shared(inp)
+        rs = time_layer(inp, dev, args.steps, args.warmup, shared=sh)
+        fl = layer_flops(inp, A) + 6.0 * inp.d * inp.w1s.shape[2] * inp.T
+        out["shared_expert"] = {"workload": w.name + "_plus1shared_f" + str(inp.w1s.shape[2]),
+                                "ms_per_step": rs["ms_per_step"],
+                                "tokens_per_s": inp.T / (rs["ms_per_step"] * 1e-3),
+                                "layer_tflops": fl / (rs["ms_per_step"] * 1e-3) / 1e12}
+        del sh
     del dev
     torch.cuda.empty_cache()
 

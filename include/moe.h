@@ -13,7 +13,7 @@
  *   per-expert counts, capacity cut, expert-contiguous permute    moe_permute
  *   (or: over-capacity assignments re-routed once)                moe_permute_reroute
  *   per-expert SwiGLU FFN as one grouped GEMM pair                moe_expert_ffn
- *   weighted combine back to token order                          moe_combine
+ *   weighted combine back to token order (+ shared experts)       moe_combine
  *   load-balancing loss N * sum_e f_e * P_e                       moe_aux_loss
  *
  * Conventions shared by every entry point:
@@ -191,15 +191,22 @@ moe_status moe_expert_down(const void* act, const int32_t* offsets, const void* 
 
 /*
  * moe_combine -- weighted combine back to token order (P1 §2.1: the output
- * is the gate-weighted sum of the selected experts' outputs; P3 §4.1 gather).
+ * is the gate-weighted sum of the selected experts' outputs; P3 §4.1 gather),
+ * plus the shared experts (P2 §3.3: experts every token calls, added with
+ * weight 1).
  *   y[t] = sum over j = 0..k-1 with slot_row[t, j] >= 0 of
  *          topk_w[t, j] * y_perm[slot_row[t, j]]
- *   summed in slot order in fp32, then stored in dtype dt.  Dropped slots
+ *        + sum over q = 0..n_shared-1 of y_shared[q][t]
+ *   summed in that order in fp32, then stored in dtype dt.  Dropped slots
  *   contribute nothing (weights are not renormalised); the residual is NOT
  *   added (the caller adds hidden + y).
+ *   y_shared  [n_shared, T, d] fp32, the shared experts' FFN outputs (each one
+ *             moe_expert_ffn over all T rows of hidden with offsets {0, T}),
+ *             or NULL with n_shared = 0
  */
-moe_status moe_combine(const float* y_perm, const int32_t* slot_row, const float* topk_w, int T,
-                       int d, int k, moe_dtype dt, void* y, void* stream);
+moe_status moe_combine(const float* y_perm, const int32_t* slot_row, const float* topk_w,
+                       const float* y_shared, int n_shared, int T, int d, int k, moe_dtype dt,
+                       void* y, void* stream);
 
 /*
  * moe_aux_loss -- load-balancing loss (P1 §2.3; P2 §3.2):

@@ -186,16 +186,17 @@ moe_status moe_expert_ffn(const void* x_perm, const int32_t* offsets, const void
                                             y_perm, down_ws, as_stream(stream)));
 }
 
-moe_status moe_combine(const float* y_perm, const int32_t* slot_row, const float* topk_w, int T,
-                       int d, int k, moe_dtype dt, void* y, void* stream) {
+moe_status moe_combine(const float* y_perm, const int32_t* slot_row, const float* topk_w,
+                       const float* y_shared, int n_shared, int T, int d, int k, moe_dtype dt,
+                       void* y, void* stream) {
   if (!y_perm || !slot_row || !topk_w || !y) return MOE_ERR_INVALID_ARG;
-  if (T < 1 || k < 1) return MOE_ERR_INVALID_ARG;
+  if (T < 1 || k < 1 || n_shared < 0 || (n_shared > 0 && !y_shared)) return MOE_ERR_INVALID_ARG;
   if (k > kMaxExperts) return MOE_ERR_UNSUPPORTED;
   moe_status s = check_d(d);
   if (s != MOE_OK) return s;
   if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
-  return hip_status(moe::launch_combine(y_perm, slot_row, topk_w, T, d, k, dt == MOE_BF16, y,
-                                        as_stream(stream)));
+  return hip_status(moe::launch_combine(y_perm, slot_row, topk_w, n_shared > 0 ? y_shared : nullptr,
+                                        n_shared, T, d, k, dt == MOE_BF16, y, as_stream(stream)));
 }
 
 moe_status moe_aux_loss(const float* logits, const int32_t* counts, int T, int N, int k,

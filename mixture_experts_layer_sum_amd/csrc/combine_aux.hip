@@ -4,6 +4,8 @@
 // sum of the selected experts' outputs; devpress.csdn.net/awstech/6a91abf4...
 // §4.1: gather the expert results back to token order.  Summed in slot order
 // in fp32; dropped slots add nothing and nothing is renormalised.
+// hotelren.com/news/5904824 §3.3: shared experts, called by every token, are
+// added with weight 1.
 //
 // Aux loss -- cf-1.com/news/5914943 §2.3 and hotelren.com/news/5904824 §3.2:
 // aux = N * sum_e f_e * P_e with f_e the share of router assignments at e
@@ -15,12 +17,16 @@
 
 namespace moe {
 
-// One block per token; each thread owns 4 consecutive columns.
+// One block per token; each thread owns 4 consecutive columns.  The shared
+// experts' outputs (y_shared [n_shared][T][d]) are added after the routed
+// slots, in shared-expert order.
 template <bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_perm,
                                                       const int32_t* __restrict__ slot_row,
-                                                      const float* __restrict__ topk_w, int d,
-                                                      int k, void* __restrict__ y) {
+                                                      const float* __restrict__ topk_w,
+                                                      const float* __restrict__ y_shared,
+                                                      int n_shared, int T, int d, int k,
+                                                      void* __restrict__ y) {
   __shared__ int srow[256];
   __shared__ float sw[256];
   const int t = blockIdx.x;
@@ -42,6 +48,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       acc.z = fmaf(wj, x.z, acc.z);
       acc.w = fmaf(wj, x.w, acc.w);
     }
+    for (int q = 0; q < n_shared; ++q) {
+      const float4 x = reinterpret_cast<const float4*>(y_shared + ((size_t)q * T + t) * d)[v];
+      acc.x += x.x;
+      acc.y += x.y;
+      acc.z += x.z;
+      acc.w += x.w;
+    }
     if (BF16) {
       reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + (size_t)t * d)[v] =
           make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
@@ -51,14 +64,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
-hipError_t launch_combine(const float* y_perm, const int32_t* slot_row, const float* topk_w, int T,
-                          int d, int k, bool bf16, void* y, hipStream_t stream) {
+hipError_t launch_combine(const float* y_perm, const int32_t* slot_row, const float* topk_w,
+                          const float* y_shared, int n_shared, int T, int d, int k, bool bf16,
+                          void* y, hipStream_t stream) {
   if (bf16)
     hipLaunchKernelGGL(combine_kernel<true>, dim3(T), dim3(256), 0, stream, y_perm, slot_row,
-                       topk_w, d, k, y);
+                       topk_w, y_shared, n_shared, T, d, k, y);
   else
     hipLaunchKernelGGL(combine_kernel<false>, dim3(T), dim3(256), 0, stream, y_perm, slot_row,
-                       topk_w, d, k, y);
+                       topk_w, y_shared, n_shared, T, d, k, y);
   return hipGetLastError();
 }
 

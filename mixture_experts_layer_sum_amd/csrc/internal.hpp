@@ -34,8 +34,9 @@ hipError_t launch_expert_down(const void* act, const int32_t* offsets, const voi
                               int d, int f, int max_rows, bool bf16, float* y_perm, void* ws,
                               hipStream_t stream);
 
-hipError_t launch_combine(const float* y_perm, const int32_t* slot_row, const float* topk_w, int T,
-                          int d, int k, bool bf16, void* y, hipStream_t stream);
+hipError_t launch_combine(const float* y_perm, const int32_t* slot_row, const float* topk_w,
+                          const float* y_shared, int n_shared, int T, int d, int k, bool bf16,
+                          void* y, hipStream_t stream);
 
 size_t aux_ws_bytes(int T, int N);
 hipError_t launch_aux(const float* logits, const int32_t* counts, int T, int N, int k, float* aux,

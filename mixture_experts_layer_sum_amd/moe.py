@@ -33,7 +33,7 @@ SIGNATURES = {
     "moe_expert_ffn": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
     "moe_expert_up": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "moe_expert_down": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
-    "moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P]),
+    "moe_combine": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "moe_aux_loss": (_I, [_P, _P, _I, _I, _I, _P, _P, _Z, _P]),
 }
 
@@ -187,12 +187,14 @@ def moe_expert_ffn(x_perm, offsets, w1, w3, w2, y_perm=None, ws=None, stream=Non
     return y_perm
 
 
-def moe_combine(y_perm, slot_row, topk_w, dtype, y=None, stream=None):
+def moe_combine(y_perm, slot_row, topk_w, dtype, y=None, y_shared=None, stream=None):
+    """y_shared: None or fp32 [n_shared, T, d] (the shared experts' outputs)."""
     T, k = slot_row.shape
     d = y_perm.shape[1]
     y = _empty((T, d), dtype, y_perm.device, y)
-    _check(_lib.moe_combine(_ptr(y_perm), _ptr(slot_row), _ptr(topk_w), T, d, k,
-                            MOE_BF16 if dtype == torch.bfloat16 else MOE_F32, _ptr(y),
+    n_shared = 0 if y_shared is None else y_shared.shape[0]
+    _check(_lib.moe_combine(_ptr(y_perm), _ptr(slot_row), _ptr(topk_w), _ptr(y_shared), n_shared,
+                            T, d, k, MOE_BF16 if dtype == torch.bfloat16 else MOE_F32, _ptr(y),
                             _stream(stream)), "moe_combine")
     return y
 
@@ -212,7 +214,7 @@ def moe_aux_loss(logits, counts, k, aux=None, ws=None, stream=None):
 class MoEBuffers:
     """Every output and workspace of one layer forward, allocated once."""
 
-    def __init__(self, T, d, N, k, f, dtype, device="cuda"):
+    def __init__(self, T, d, N, k, f, dtype, device="cuda", n_shared=0, f_shared=None):
         self.T, self.d, self.N, self.k, self.f, self.dtype = T, d, N, k, f, dtype
         e = lambda shape, dt: torch.empty(shape, dtype=dt, device=device)  # noqa: E731
         self.logits = e((T, N), torch.float32)
@@ -235,21 +237,32 @@ class MoEBuffers:
         self.ws_aux = e((max(1, workspace_size(MOE_OP_AUX_LOSS, T, d, N, k, f, dtype)),), torch.uint8)
         self.ws_down = e((max(1, workspace_size(MOE_OP_EXPERT_DOWN, T, d, N, k, f, dtype)),),
                          torch.uint8)
+        self.n_shared = n_shared
+        if n_shared:
+            fs = f if f_shared is None else f_shared
+            self.shared_offsets = torch.tensor([0, T], dtype=torch.int32, device=device)
+            self.y_shared = e((n_shared, T, d), torch.float32)
+            self.ws_shared = e((max(1, workspace_size(MOE_OP_EXPERT_FFN, T, d, 1, 1, fs, dtype)),),
+                               torch.uint8)
 
 
 def moe_forward(hidden, w_router, w1, w3, w2, k, capacity_factor=0.0, bias=None,
-                bufs: Optional[MoEBuffers] = None, stream=None, overflow="drop"):
+                bufs: Optional[MoEBuffers] = None, stream=None, overflow="drop", shared=None):
     """Run the five steps on the current stream.  Returns the MoEBuffers holding every result.
 
     ``y`` excludes the residual: the layer output with residual is hidden + y.
     ``overflow`` is "drop" (moe_permute) or "reroute" (moe_permute_reroute).
+    ``shared`` is None or (w1s [Ns, d, fs], w3s, w2s [Ns, fs, d]): shared experts every
+    token passes through, added with weight 1.
     """
     if overflow not in ("drop", "reroute"):
         raise ValueError(f"unknown overflow policy {overflow!r}")
     T, d = hidden.shape
     N, _, f = w1.shape
+    ns = 0 if shared is None else shared[0].shape[0]
     if bufs is None:
-        bufs = MoEBuffers(T, d, N, k, f, hidden.dtype, hidden.device)
+        bufs = MoEBuffers(T, d, N, k, f, hidden.dtype, hidden.device, ns,
+                          None if shared is None else shared[0].shape[2])
     b = bufs
     moe_route(hidden, w_router, k, bias, b.logits, b.topk_idx, b.topk_w, b.counts, b.ws_route,
               stream)
@@ -261,6 +274,12 @@ def moe_forward(hidden, w_router, w1, w3, w2, k, capacity_factor=0.0, bias=None,
                             b.slot_row, b.kept, b.offsets, b.ws_permute, stream)
     moe_expert_up(b.x_perm, b.offsets, w1, w3, b.act, stream)
     moe_expert_down(b.act, b.offsets, w2, b.y_perm, b.ws_down, stream)
-    moe_combine(b.y_perm, b.slot_row, b.topk_w, hidden.dtype, b.y, stream)
+    y_shared = None
+    if ns:
+        for q in range(ns):
+            moe_expert_ffn(hidden, b.shared_offsets, shared[0][q:q + 1], shared[1][q:q + 1],
+                           shared[2][q:q + 1], b.y_shared[q], b.ws_shared, stream)
+        y_shared = b.y_shared
+    moe_combine(b.y_perm, b.slot_row, b.topk_w, hidden.dtype, b.y, y_shared, stream)
     moe_aux_loss(b.logits, b.counts, k, b.aux, b.ws_aux, stream)
     return b

@@ -176,6 +176,8 @@ def make_inputs(T, d, N, k, f, dtype="bf16", capacity_factor=0.0, seed=0,
     return inp
 
 
-def make_workload_inputs(key: str, seed: int = 0) -> MoEInputs:
+def make_workload_inputs(key: str, seed: int = 0, n_shared: int = 0,
+                         f_shared: Optional[int] = None) -> MoEInputs:
     w = WORKLOADS[key]
-    return make_inputs(w.T, w.d, w.N, w.k, w.f, w.dtype, w.capacity_factor, seed, zipf=w.zipf_bias)
+    return make_inputs(w.T, w.d, w.N, w.k, w.f, w.dtype, w.capacity_factor, seed, zipf=w.zipf_bias,
+                       n_shared=n_shared, f_shared=f_shared)

@@ -47,7 +47,8 @@ def to_device(inp, device="cuda"):
         return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
     return {"hidden": t(inp.hidden), "w_router": t(inp.w_router), "w1": t(inp.w1),
-            "w3": t(inp.w3), "w2": t(inp.w2),
+            "w3": t(inp.w3), "w2": t(inp.w2), "w1s": t(inp.w1s), "w3s": t(inp.w3s),
+            "w2s": t(inp.w2s),
             "bias": None if inp.bias is None else t(inp.bias.astype(np.float32))}
 
 
@@ -55,8 +56,9 @@ def run_gpu(inp, dev, bufs=None, overflow="drop"):
     """One forward through the C ABI; returns (host results, buffers)."""
     import torch
     from mixture_experts_layer_sum_amd import moe
+    shared = None if inp.n_shared == 0 else (dev["w1s"], dev["w3s"], dev["w2s"])
     b = moe.moe_forward(dev["hidden"], dev["w_router"], dev["w1"], dev["w3"], dev["w2"], inp.k,
-                        inp.capacity_factor, dev["bias"], bufs, overflow=overflow)
+                        inp.capacity_factor, dev["bias"], bufs, overflow=overflow, shared=shared)
     torch.cuda.synchronize()
     return host_results(b), b
 
@@ -75,7 +77,8 @@ def host_results(b):
             "kept": h(b.kept).astype(np.int64), "offsets": h(b.offsets).astype(np.int64),
             "slot_row": h(b.slot_row).astype(np.int64), "perm_src": h(b.perm_src)[:A].astype(np.int64),
             "x_perm": h(b.x_perm[:A]), "y_perm": h(b.y_perm[:A]), "y": h(b.y),
-            "aux": float(b.aux.item()), "A": A}
+            "aux": float(b.aux.item()), "A": A,
+            "y_shared": h(b.y_shared) if getattr(b, "n_shared", 0) else None}
 
 
 def near_ties(logits32, k):
@@ -106,7 +109,9 @@ def check(inp, g, sample=None, label="", audit=True, y_tol=None, overflow="drop"
     t0 = time.time()
     ref = O.moe_forward(inp.values("hidden"), inp.values("w_router"), ExpertView(inp, "w1"),
                         ExpertView(inp, "w3"), ExpertView(inp, "w2"), k, inp.capacity_factor,
-                        inp.bias, tokens=sample, overflow=overflow)
+                        inp.bias, tokens=sample, overflow=overflow,
+                        shared=None if inp.n_shared == 0 else
+                        (inp.values("w1s"), inp.values("w3s"), inp.values("w2s")))
     log(f"{label}: oracle {time.time() - t0:.1f}s")
     L32 = ref["logits"].astype(np.float32)
     # logits: fp32 accumulation vs fp64 -- a loose sanity bar, the decision audit is below
@@ -162,9 +167,17 @@ def check(inp, g, sample=None, label="", audit=True, y_tol=None, overflow="drop"
     err = float(np.abs(ygpu[tok_ok] - yref[tok_ok]).max(initial=0.0))
     rel = err / den if den > 0 else err
     assert rel <= tol, f"{label}: y max rel err {rel:.3e} > {tol}"
-    # tokens with every slot dropped are exactly zero
+    # tokens with every slot dropped are exactly zero (without shared experts)
     dropped = (g["slot_row"] < 0).all(1)
-    assert (g["y"][dropped] == 0).all(), f"{label}: dropped tokens not zero"
+    if inp.n_shared == 0:
+        assert (g["y"][dropped] == 0).all(), f"{label}: dropped tokens not zero"
+    else:
+        # the shared experts' outputs on the evaluated tokens, summed over experts
+        ys = g["y_shared"].sum(0)[toks]
+        yr = ref["y_shared"]
+        den_s = float(np.abs(yr).max())
+        rel_s = float(np.abs(ys - yr).max()) / den_s if den_s > 0 else 0.0
+        assert rel_s <= tol, f"{label}: y_shared rel {rel_s:.3e}"
     # y_perm rows the oracle evaluated
     yp_rows = np.where(~np.isnan(ref["y_perm"][:, 0]))[0]
     if yp_rows.size and not excl.any() and same_experts.all():

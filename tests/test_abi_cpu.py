@@ -151,11 +151,13 @@ def test_expert_up_down_reject():
 
 
 @pytest.mark.parametrize("args,status", [
-    ((NUL, P, P, 64, 128, 2, BF16, P, S), INV), ((P, NUL, P, 64, 128, 2, BF16, P, S), INV),
-    ((P, P, NUL, 64, 128, 2, BF16, P, S), INV), ((P, P, P, 64, 128, 2, BF16, NUL, S), INV),
-    ((P, P, P, 0, 128, 2, BF16, P, S), INV), ((P, P, P, 64, 128, 0, BF16, P, S), INV),
-    ((P, P, P, 64, 130, 2, BF16, P, S), UNS), ((P, P, P, 64, 128, 2, 9, P, S), UNS),
-    ((P, P, P, 64, 128, 300, BF16, P, S), UNS),
+    ((NUL, P, P, NUL, 0, 64, 128, 2, BF16, P, S), INV), ((P, NUL, P, NUL, 0, 64, 128, 2, BF16, P, S), INV),
+    ((P, P, NUL, NUL, 0, 64, 128, 2, BF16, P, S), INV), ((P, P, P, NUL, 0, 64, 128, 2, BF16, NUL, S), INV),
+    ((P, P, P, NUL, 0, 0, 128, 2, BF16, P, S), INV), ((P, P, P, NUL, 0, 64, 128, 0, BF16, P, S), INV),
+    ((P, P, P, NUL, 0, 64, 130, 2, BF16, P, S), UNS), ((P, P, P, NUL, 0, 64, 128, 2, 9, P, S), UNS),
+    ((P, P, P, NUL, 0, 64, 128, 300, BF16, P, S), UNS),
+    # shared experts: a count without outputs, or a negative count
+    ((P, P, P, NUL, 1, 64, 128, 2, BF16, P, S), INV), ((P, P, P, P, -1, 64, 128, 2, BF16, P, S), INV),
 ])
 def test_combine_rejects(args, status):
     assert lib.moe_combine(*args) == status

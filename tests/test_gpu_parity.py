@@ -163,6 +163,34 @@ def test_reroute_workload_full_size(moe):
     assert rep["tokens_on_other_experts"] <= inp.T // 100
 
 
+SHARED = [
+    # label, T, d, N, k, f, dtype, cf, n_shared, f_shared, overflow
+    ("f32_shared1", 64, 128, 8, 2, 256, "f32", 0.0, 1, 128, "drop"),
+    ("bf16_shared1_drops", 300, 256, 8, 2, 256, "bf16", 1.0, 1, 384, "drop"),
+    ("bf16_shared2_all_dropped", 64, 256, 8, 2, 128, "bf16", 0.01, 2, 256, "drop"),
+    ("bf16_shared1_decode", 37, 256, 128, 2, 256, "bf16", 0.0, 1, 256, "drop"),
+    ("bf16_shared1_reroute", 300, 256, 16, 2, 128, "bf16", 0.75, 1, 128, "reroute"),
+]
+
+
+@pytest.mark.parametrize("case", SHARED, ids=[c[0] for c in SHARED])
+def test_shared_experts_small_shapes(moe, case):
+    label, T, d, N, k, f, dt, cf, ns, fs, overflow = case
+    b = np.zeros(N, np.float32)
+    b[: min(3, N)] = [3.0, 2.0, 1.0][: min(3, N)]
+    for seed in (0, 1):
+        inp = synth.make_inputs(T, d, N, k, f, dt, cf, seed, bias=b, n_shared=ns, f_shared=fs)
+        _run(inp, f"{label}/seed{seed}", overflow=overflow)
+
+
+def test_shared_expert_mixtral_full_size(moe):
+    """Mixtral-shaped layer plus one shared expert of the same size, y on sampled tokens."""
+    inp = synth.make_workload_inputs("mixtral", seed=0, n_shared=1)
+    rng = np.random.default_rng(11)
+    sample = np.unique(np.concatenate([[0, inp.T - 1], rng.choice(inp.T, 32, replace=False)]))
+    _run(inp, "workload_mixtral_shared1", sample=sample)
+
+
 WORKLOADS = ["tiny_fp32", "n16_cf125", "mixtral", "skewed_zipf", "decode"]
 
 

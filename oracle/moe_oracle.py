@@ -49,7 +49,13 @@ Readings of points the pages leave open (each also listed in the design notes):
   (pre-drop) assignments;
 * shared experts (P2 §3.3: experts every token calls unconditionally, next to
   the routed ones): each is a SwiGLU FFN of its own applied to every token,
-  dropped or not, and added to the routed sum with weight 1.
+  dropped or not, and added to the routed sum with weight 1;
+* FP8 expert weights (P1 §3.2: the experts are stored in FP8): each expert
+  matrix is quantised per output column to OCP FP8 E4M3 (1 sign, 4 exponent
+  bits with bias 7, 3 mantissa bits, subnormals, largest finite 448, no
+  infinity): scale = amax / 448 over the column (1 for an all-zero column),
+  code = round-to-nearest-even of w / scale, clamped to +-448, both divisions
+  in float32; the layer then runs on code * scale.
 """
 from __future__ import annotations
 
@@ -60,7 +66,8 @@ import numpy as np
 __all__ = [
     "router_logits", "select_topk", "gate_weights", "expert_counts", "capacity",
     "dispatch", "dispatch_reroute", "silu", "swiglu_ffn", "aux_loss", "moe_forward",
-    "moe_forward_per_token",
+    "moe_forward_per_token", "e4m3_decode", "e4m3_encode", "quantize_fp8_columns",
+    "dequantize_fp8_columns",
 ]
 
 
@@ -208,6 +215,66 @@ def dispatch_reroute(idx, logits, N: int, C: int) -> dict:
                 perm_src[slot_row[t, j]] = t
     return {"keep1": keep1, "proposal": prop, "keep2": keep2, "kept1": kept1, "kept": kept,
             "offsets": offsets, "slot_row": slot_row, "perm_src": perm_src, "expert": expert}
+
+
+def e4m3_decode(code):
+    """Value of OCP FP8 E4M3 codes (uint8 array): (-1)^s 2^(E-7) (1 + M/8), subnormal
+    2^-6 M/8 for E = 0, NaN for E = 15, M = 7."""
+    c = np.asarray(code, np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    E = (c >> 3) & 15
+    M = c & 7
+    v = np.where(E == 0, M / 8.0 * 2.0 ** -6, (1.0 + M / 8.0) * np.exp2(E - 7.0))
+    v = np.where((E == 15) & (M == 7), np.nan, v)
+    return s * v
+
+
+def e4m3_encode(x):
+    """Nearest OCP FP8 E4M3 code of float values with |x| <= 448 (ties to the even
+    mantissa).  Written from the format: the spacing of representable values is
+    2^(e-3) in binade [2^e, 2^(e+1)) for e >= -6, and 2^-9 below 2^-6."""
+    x = np.asarray(x, np.float64)
+    if np.any(np.abs(x) > 448) or np.any(np.isnan(x)):
+        raise ValueError("e4m3_encode expects finite values within +-448")
+    a = np.abs(x)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -6.0)
+    quantum = np.exp2(e - 3.0)
+    n = a / quantum                       # exact: a power-of-two rescale
+    r = np.floor(n)
+    frac = n - r
+    r = np.where((frac > 0.5) | ((frac == 0.5) & (r % 2 == 1)), r + 1, r)
+    q = r * quantum                       # the rounded magnitude (may step into the next binade)
+    # encode q: subnormal when q < 2^-6
+    code = np.zeros(x.shape, np.int64)
+    sub = q < 2.0 ** -6
+    code = np.where(sub, np.round(q / 2.0 ** -9).astype(np.int64), code)
+    with np.errstate(divide="ignore"):
+        eq = np.floor(np.log2(np.where(sub, 1.0, q)))
+    mant = np.where(sub, 0, np.round((q / np.exp2(eq) - 1.0) * 8.0)).astype(np.int64)
+    code = np.where(sub, code, ((eq + 7).astype(np.int64) << 3) | mant)
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_fp8_columns(w):
+    """Per-column FP8 quantisation of one expert matrix w [K, M] (float32 values).
+
+    scale[m] = amax_k |w[k, m]| / 448 in float32 (1 for an all-zero column);
+    code[k, m] = e4m3_encode(clamp(float32(w[k, m] / scale[m]), -448, 448)).
+    P1 §3.2 (expert weights stored in FP8 to save memory and bandwidth).
+    """
+    w = np.asarray(w, np.float32)
+    amax = np.abs(w).max(axis=0)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    r = (w / scale[None, :]).astype(np.float32)
+    r = np.clip(r, np.float32(-448.0), np.float32(448.0))
+    return e4m3_encode(r), scale
+
+
+def dequantize_fp8_columns(code, scale):
+    """The weights the FP8 layer computes with: code value * column scale (float64)."""
+    return e4m3_decode(code) * np.asarray(scale, np.float64)[None, :]
 
 
 def silu(z):

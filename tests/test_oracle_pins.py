@@ -443,6 +443,68 @@ def test_two_shared_experts_sum_and_match_brute_force():
     assert np.allclose(a["y"], b, rtol=1e-12, atol=1e-13)
 
 
+# ---------------------------------------------------------------- FP8 (OCP E4M3) weights
+def test_e4m3_code_values_from_the_format():
+    """Landmarks of OCP FP8 E4M3 (bias 7, 3 mantissa bits, no infinity)."""
+    dec = O.e4m3_decode(np.array([0x00, 0x80, 0x01, 0x07, 0x08, 0x38, 0x3F, 0x7E, 0xFE, 0x7F, 0xFF],
+                                 np.uint8))
+    assert dec[0] == 0.0 and dec[1] == 0.0 and np.signbit(dec[1])
+    assert dec[2] == 2.0 ** -9                    # smallest subnormal
+    assert dec[3] == 7 * 2.0 ** -9                # largest subnormal
+    assert dec[4] == 2.0 ** -6                    # smallest normal
+    assert dec[5] == 1.0
+    assert dec[6] == 1.875
+    assert dec[7] == 448.0 and dec[8] == -448.0   # largest finite
+    assert np.isnan(dec[9]) and np.isnan(dec[10])
+
+
+def test_e4m3_encode_is_the_nearest_code_by_brute_force():
+    """Against a table search over all finite codes: nearest value, ties to the
+    code with an even mantissa."""
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    vals = O.e4m3_decode(codes)
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.uniform(-448, 448, 3000), rng.uniform(-0.05, 0.05, 3000),
+                        vals, (vals[:-1] + vals[1:]) / 2])          # includes exact midpoints
+    x = x[np.abs(x) <= 448]
+    got = O.e4m3_encode(x)
+    for xi, gi in zip(x, got):
+        d = np.abs(vals - xi)
+        best = np.flatnonzero(d == d.min())
+        if best.size > 1:                       # tie: the even mantissa wins
+            best = [b for b in best if codes[b] & 1 == 0]
+        ref = codes[best[0]]
+        if vals[best[0]] == 0.0:                # +-0: the sign of x decides
+            assert O.e4m3_decode(np.array([gi], np.uint8))[0] == 0.0
+        else:
+            assert gi == ref, (xi, gi, ref)
+
+
+def test_e4m3_roundtrip_and_ties_to_even():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    assert np.array_equal(O.e4m3_encode(O.e4m3_decode(codes)), codes)
+    # halfway cases: 1.0625 between 1.0 (even) and 1.125; 1.1875 between 1.125 and
+    # 1.25 (even); 17 between 16 (even) and 18; 2^-10 between 0 (even) and 2^-9
+    assert O.e4m3_encode(np.array([1.0625, 1.1875, 17.0, 2.0 ** -10])).tolist() == \
+        [0x38, 0x3A, 0x58, 0x00]
+
+
+def test_fp8_column_quantisation():
+    rng = np.random.default_rng(4)
+    w = (rng.standard_normal((64, 5)) * [1e-3, 1.0, 30.0, 0.0, 5e2]).astype(np.float32)
+    q, scale = O.quantize_fp8_columns(w)
+    assert scale[3] == 1.0 and (q[:, 3] & 0x7F == 0).all()          # an all-zero column (+-0)
+    for m in (0, 1, 2, 4):
+        amax = np.abs(w[:, m]).max()
+        assert scale[m] == np.float32(amax) / np.float32(448.0)
+        k = int(np.abs(w[:, m]).argmax())
+        assert q[k, m] & 0x7F == 0x7E                               # the column's amax -> 448
+    wd = O.dequantize_fp8_columns(q, scale)
+    # relative error of a normal code is at most half a mantissa step: 2^-4
+    big = np.abs(w) >= 2.0 ** -6 * scale[None, :]
+    assert (np.abs(wd - w)[big] <= 2.0 ** -4 * np.abs(w)[big] + 1e-12).all()
+
+
 # ---------------------------------------------------------------- aux loss
 def test_aux_uniform_router_is_exactly_one():
     """W_router = 0 gives P_e = 1/N; with f summing to 1 the loss is exactly 1, also under drops."""

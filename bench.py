@@ -15,6 +15,9 @@ Also reported in the same line:
                 against the bf16 dense MFMA peak; HBM traffic per launch from
                 rocprofv3 FETCH_SIZE/WRITE_SIZE when a committed counter
                 summary matches the current kernel source, else null;
+  decode_fp8    the decode-shaped layer with FP8 (OCP E4M3, per-column fp32
+                scale) expert weights quantised on the GPU: bytes counted at one
+                byte per weight plus the scales;
   shared_expert the Mixtral-shaped layer plus one always-on shared expert of
                 the same size (f 14336), added with weight 1 in the combine;
   skewed_overflow  the skewed 64-expert workload (T 16384, d 4096, top-2, f 2048,
@@ -87,7 +90,7 @@ def upload_shared(inp):
     return (t(inp.w1s), t(inp.w3s), t(inp.w2s))
 
 
-def time_layer(inp, dev, steps, warmup, overflow="drop", shared=None):
+def time_layer(inp, dev, steps, warmup, overflow="drop", shared=None, fp8=None):
     """Warm up, then time `steps` forwards; per-step HIP events bracket the GEMMs."""
     import torch
     from mixture_experts_layer_sum_amd import moe
@@ -109,10 +112,16 @@ def time_layer(inp, dev, steps, warmup, overflow="drop", shared=None):
                                     b.ws_permute)
         if ev:
             ev[0].record(s)
-        moe.moe_expert_up(b.x_perm, b.offsets, dev["w1"], dev["w3"], b.act)
+        if fp8 is None:
+            moe.moe_expert_up(b.x_perm, b.offsets, dev["w1"], dev["w3"], b.act)
+        else:
+            moe.moe_expert_up_fp8(b.x_perm, b.offsets, fp8[0], fp8[1], fp8[3], fp8[4], b.act)
         if ev:
             ev[1].record(s)
-        moe.moe_expert_down(b.act, b.offsets, dev["w2"], b.y_perm, b.ws_down)
+        if fp8 is None:
+            moe.moe_expert_down(b.act, b.offsets, dev["w2"], b.y_perm, b.ws_down)
+        else:
+            moe.moe_expert_down_fp8(b.act, b.offsets, fp8[2], fp8[5], b.y_perm)
         if ev:
             ev[2].record(s)
         if shared is not None:
@@ -147,10 +156,11 @@ def layer_flops(inp, A):
     return 2.0 * inp.T * inp.d * inp.N + 6.0 * inp.d * inp.f * A
 
 
-def layer_bytes(inp, kept):
+def layer_bytes(inp, kept, weight_bytes=None):
     s = 2 if inp.dtype == "bf16" else 4
+    ws = s if weight_bytes is None else weight_bytes
     active = int((kept > 0).sum())
-    return active * 3.0 * inp.d * inp.f * s + inp.d * inp.N * s + 2.0 * inp.T * inp.d * s
+    return active * 3.0 * inp.d * inp.f * ws + inp.d * inp.N * s + 2.0 * inp.T * inp.d * s
 
 
 def blas_threads():
@@ -446,6 +456,21 @@ def main():
         rd = time_layer(inpd, devd, max(args.steps, 20), args.warmup)
         by = layer_bytes(inpd, rd["kept"])
         gbs = by / (rd["ms_per_step"] * 1e-3) / 1e9
+        # the same layer with FP8 (E4M3, per-column scale) expert weights
+        fq = [moe.moe_quantize_fp8(devd[n]) for n in ("w1", "w3", "w2")]
+        fp8 = (fq[0][0], fq[1][0], fq[2][0], fq[0][1], fq[1][1], fq[2][1])
+        torch.cuda.synchronize()
+        rf = time_layer(inpd, devd, max(args.steps, 20), args.warmup, fp8=fp8)
+        byf = layer_bytes(inpd, rf["kept"], weight_bytes=1) + \
+            4.0 * int((rf["kept"] > 0).sum()) * (2 * inpd.f + inpd.d)        # column scales
+        gbf = byf / (rf["ms_per_step"] * 1e-3) / 1e9
+        out["decode_fp8"] = {"workload": wd.name + "_fp8e4m3_weights",
+                             "ms_per_step": rf["ms_per_step"],
+                             "tokens_per_s": wd.T / (rf["ms_per_step"] * 1e-3),
+                             "algorithmic_bytes": byf, "GB_per_s": gbf,
+                             "pct_hbm_peak": 100.0 * gbf / PEAK_HBM_GBS,
+                             "up_ms": rf["up_ms"], "down_ms": rf["down_ms"]}
+        del fq, fp8
         out["decode"] = {"workload": wd.name, "ms_per_step": rd["ms_per_step"],
                          "tokens_per_s": wd.T / (rd["ms_per_step"] * 1e-3),
                          "active_experts": int((rd["kept"] > 0).sum()), "algorithmic_bytes": by,

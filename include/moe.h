@@ -190,6 +190,39 @@ moe_status moe_expert_down(const void* act, const int32_t* offsets, const void* 
                            size_t ws_bytes, void* stream);
 
 /*
+ * FP8 expert weights (P1 §3.1: experts stored in FP8) for decode-shaped
+ * batches, where the layer's time is reading the active experts' weights
+ * (P5 §2.2-2.3).  Format: OCP FP8 E4M3 (bias 7, 3 mantissa bits, subnormals,
+ * largest finite 448, no infinity), one fp32 scale per output column of each
+ * expert matrix.
+ *
+ * moe_quantize_fp8 -- per-column quantisation of N matrices w [N, K, M]
+ *   (dtype dt; K = the reduction dimension): for every (e, m)
+ *   scale[e, m] = max_k |w[e, k, m]| / 448 (1 if the column is all zero) and
+ *   q[e, k, m] = round-to-nearest-even(w[e, k, m] / scale[e, m]) clamped to
+ *   +-448, both divisions IEEE float32.  W1/W3 [N, d, f] give scales [N, f];
+ *   W2 [N, f, d] gives scales [N, d].
+ *   q [N, K, M] uint8 out, scale [N, M] fp32 out.
+ */
+moe_status moe_quantize_fp8(const void* w, moe_dtype dt, int N, int K, int M, uint8_t* q,
+                            float* scale, void* stream);
+
+/* moe_expert_up_fp8 / moe_expert_down_fp8 -- as moe_expert_up / moe_expert_down
+ * (bf16 activations) with W = code * column scale:
+ *   act[r] = silu((x_perm[r] Q1_e) * s1_e) * ((x_perm[r] Q3_e) * s3_e)
+ *   y_perm[r] = (act[r] Q2_e) * s2_e
+ * w1q, w3q [N, d, f] and w2q [N, f, d] uint8 codes, s1, s3 [N, f] and
+ * s2 [N, d] fp32 (from moe_quantize_fp8).  They run on the weight-streaming
+ * kernels only: the bf16 shape limits and ceil(max_rows / N) <= 32, else
+ * MOE_ERR_UNSUPPORTED. */
+moe_status moe_expert_up_fp8(const void* x_perm, const int32_t* offsets, const uint8_t* w1q,
+                             const uint8_t* w3q, const float* s1, const float* s3, int N, int d,
+                             int f, int max_rows, void* act, void* stream);
+moe_status moe_expert_down_fp8(const void* act, const int32_t* offsets, const uint8_t* w2q,
+                               const float* s2, int N, int d, int f, int max_rows, float* y_perm,
+                               void* stream);
+
+/*
  * moe_combine -- weighted combine back to token order (P1 §2.1: the output
  * is the gate-weighted sum of the selected experts' outputs; P3 §4.1 gather),
  * plus the shared experts (P2 §3.3: experts every token calls, added with

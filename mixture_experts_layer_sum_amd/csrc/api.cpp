@@ -186,6 +186,45 @@ moe_status moe_expert_ffn(const void* x_perm, const int32_t* offsets, const void
                                             y_perm, down_ws, as_stream(stream)));
 }
 
+moe_status moe_quantize_fp8(const void* w, moe_dtype dt, int N, int K, int M, uint8_t* q,
+                            float* scale, void* stream) {
+  if (!w || !q || !scale) return MOE_ERR_INVALID_ARG;
+  if (N < 1 || K < 1 || M < 1) return MOE_ERR_INVALID_ARG;
+  if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
+  if (N > 65535) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_quantize_fp8(w, dt == MOE_BF16, N, K, M, q, scale,
+                                             as_stream(stream)));
+}
+
+// FP8 weights run on the weight-streaming kernels only: bf16 activations,
+// the bf16 shape limits, and at most 32 rows per expert on average.
+static moe_status check_fp8_shape(int N, int d, int f, int max_rows) {
+  moe_status s = check_expert_shape(N, d, f, max_rows, MOE_BF16);
+  if (s != MOE_OK) return s;
+  if (!moe::fp8_rows_supported(max_rows, N)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status moe_expert_up_fp8(const void* x_perm, const int32_t* offsets, const uint8_t* w1q,
+                             const uint8_t* w3q, const float* s1, const float* s3, int N, int d,
+                             int f, int max_rows, void* act, void* stream) {
+  if (!x_perm || !offsets || !w1q || !w3q || !s1 || !s3 || !act) return MOE_ERR_INVALID_ARG;
+  moe_status s = check_fp8_shape(N, d, f, max_rows);
+  if (s != MOE_OK) return s;
+  return hip_status(moe::launch_expert_up_fp8(x_perm, offsets, w1q, w3q, s1, s3, N, d, f,
+                                              max_rows, act, as_stream(stream)));
+}
+
+moe_status moe_expert_down_fp8(const void* act, const int32_t* offsets, const uint8_t* w2q,
+                               const float* s2, int N, int d, int f, int max_rows, float* y_perm,
+                               void* stream) {
+  if (!act || !offsets || !w2q || !s2 || !y_perm) return MOE_ERR_INVALID_ARG;
+  moe_status s = check_fp8_shape(N, d, f, max_rows);
+  if (s != MOE_OK) return s;
+  return hip_status(moe::launch_expert_down_fp8(act, offsets, w2q, s2, N, d, f, max_rows, y_perm,
+                                                as_stream(stream)));
+}
+
 moe_status moe_combine(const float* y_perm, const int32_t* slot_row, const float* topk_w,
                        const float* y_shared, int n_shared, int T, int d, int k, moe_dtype dt,
                        void* y, void* stream) {

@@ -34,6 +34,16 @@ hipError_t launch_expert_down(const void* act, const int32_t* offsets, const voi
                               int d, int f, int max_rows, bool bf16, float* y_perm, void* ws,
                               hipStream_t stream);
 
+hipError_t launch_quantize_fp8(const void* w, bool bf16, int N, int K, int M, uint8_t* q,
+                               float* scale, hipStream_t stream);
+bool fp8_rows_supported(int max_rows, int N);
+hipError_t launch_expert_up_fp8(const void* x_perm, const int32_t* offsets, const uint8_t* w1q,
+                                const uint8_t* w3q, const float* s1, const float* s3, int N,
+                                int d, int f, int max_rows, void* act, hipStream_t stream);
+hipError_t launch_expert_down_fp8(const void* act, const int32_t* offsets, const uint8_t* w2q,
+                                  const float* s2, int N, int d, int f, int max_rows,
+                                  float* y_perm, hipStream_t stream);
+
 hipError_t launch_combine(const float* y_perm, const int32_t* slot_row, const float* topk_w,
                           const float* y_shared, int n_shared, int T, int d, int k, bool bf16,
                           void* y, hipStream_t stream);

@@ -33,6 +33,9 @@ SIGNATURES = {
     "moe_expert_ffn": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
     "moe_expert_up": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "moe_expert_down": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
+    "moe_quantize_fp8": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
+    "moe_expert_up_fp8": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
+    "moe_expert_down_fp8": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "moe_combine": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "moe_aux_loss": (_I, [_P, _P, _I, _I, _I, _P, _P, _Z, _P]),
 }
@@ -187,6 +190,35 @@ def moe_expert_ffn(x_perm, offsets, w1, w3, w2, y_perm=None, ws=None, stream=Non
     return y_perm
 
 
+def moe_quantize_fp8(w, q=None, scale=None, stream=None):
+    """Per-column OCP FP8 E4M3 codes and fp32 scales of w [N, K, M] (bf16 or fp32)."""
+    N, K, M = w.shape
+    q = _empty((N, K, M), torch.uint8, w.device, q)
+    scale = _empty((N, M), torch.float32, w.device, scale)
+    _check(_lib.moe_quantize_fp8(_ptr(w), _dt(w), N, K, M, _ptr(q), _ptr(scale), _stream(stream)),
+           "moe_quantize_fp8")
+    return q, scale
+
+
+def moe_expert_up_fp8(x_perm, offsets, w1q, w3q, s1, s3, act=None, stream=None):
+    max_rows, d = x_perm.shape
+    N, _, f = w1q.shape
+    act = _empty((max_rows, f), torch.bfloat16, x_perm.device, act)
+    _check(_lib.moe_expert_up_fp8(_ptr(x_perm), _ptr(offsets), _ptr(w1q), _ptr(w3q), _ptr(s1),
+                                  _ptr(s3), N, d, f, max_rows, _ptr(act), _stream(stream)),
+           "moe_expert_up_fp8")
+    return act
+
+
+def moe_expert_down_fp8(act, offsets, w2q, s2, y_perm=None, stream=None):
+    max_rows, f = act.shape
+    N, _, d = w2q.shape
+    y_perm = _empty((max_rows, d), torch.float32, act.device, y_perm)
+    _check(_lib.moe_expert_down_fp8(_ptr(act), _ptr(offsets), _ptr(w2q), _ptr(s2), N, d, f,
+                                    max_rows, _ptr(y_perm), _stream(stream)), "moe_expert_down_fp8")
+    return y_perm
+
+
 def moe_combine(y_perm, slot_row, topk_w, dtype, y=None, y_shared=None, stream=None):
     """y_shared: None or fp32 [n_shared, T, d] (the shared experts' outputs)."""
     T, k = slot_row.shape
@@ -247,13 +279,16 @@ class MoEBuffers:
 
 
 def moe_forward(hidden, w_router, w1, w3, w2, k, capacity_factor=0.0, bias=None,
-                bufs: Optional[MoEBuffers] = None, stream=None, overflow="drop", shared=None):
+                bufs: Optional[MoEBuffers] = None, stream=None, overflow="drop", shared=None,
+                fp8=None):
     """Run the five steps on the current stream.  Returns the MoEBuffers holding every result.
 
     ``y`` excludes the residual: the layer output with residual is hidden + y.
     ``overflow`` is "drop" (moe_permute) or "reroute" (moe_permute_reroute).
     ``shared`` is None or (w1s [Ns, d, fs], w3s, w2s [Ns, fs, d]): shared experts every
     token passes through, added with weight 1.
+    ``fp8`` is None or (w1q, w3q, w2q, s1, s3, s2) from moe_quantize_fp8: the expert GEMMs
+    then read the FP8 codes (w1, w3, w2 are only used for their shapes).
     """
     if overflow not in ("drop", "reroute"):
         raise ValueError(f"unknown overflow policy {overflow!r}")
@@ -272,8 +307,13 @@ def moe_forward(hidden, w_router, w1, w3, w2, k, capacity_factor=0.0, bias=None,
     else:
         moe_permute_reroute(hidden, b.topk_idx, b.logits, N, capacity_factor, b.x_perm, b.perm_src,
                             b.slot_row, b.kept, b.offsets, b.ws_permute, stream)
-    moe_expert_up(b.x_perm, b.offsets, w1, w3, b.act, stream)
-    moe_expert_down(b.act, b.offsets, w2, b.y_perm, b.ws_down, stream)
+    if fp8 is None:
+        moe_expert_up(b.x_perm, b.offsets, w1, w3, b.act, stream)
+        moe_expert_down(b.act, b.offsets, w2, b.y_perm, b.ws_down, stream)
+    else:
+        w1q, w3q, w2q, s1, s3, s2 = fp8
+        moe_expert_up_fp8(b.x_perm, b.offsets, w1q, w3q, s1, s3, b.act, stream)
+        moe_expert_down_fp8(b.act, b.offsets, w2q, s2, b.y_perm, stream)
     y_shared = None
     if ns:
         for q in range(ns):

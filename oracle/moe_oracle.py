@@ -50,7 +50,7 @@ Readings of points the pages leave open (each also listed in the design notes):
 * shared experts (P2 §3.3: experts every token calls unconditionally, next to
   the routed ones): each is a SwiGLU FFN of its own applied to every token,
   dropped or not, and added to the routed sum with weight 1;
-* FP8 expert weights (P1 §3.2: the experts are stored in FP8): each expert
+* FP8 expert weights (P1 §3.1: the experts are stored in FP8): each expert
   matrix is quantised per output column to OCP FP8 E4M3 (1 sign, 4 exponent
   bits with bias 7, 3 mantissa bits, subnormals, largest finite 448, no
   infinity): scale = amax / 448 over the column (1 for an all-zero column),
@@ -262,7 +262,7 @@ def quantize_fp8_columns(w):
 
     scale[m] = amax_k |w[k, m]| / 448 in float32 (1 for an all-zero column);
     code[k, m] = e4m3_encode(clamp(float32(w[k, m] / scale[m]), -448, 448)).
-    P1 §3.2 (expert weights stored in FP8 to save memory and bandwidth).
+    P1 §3.1 (expert weights stored in FP8 to save memory and bandwidth).
     """
     w = np.asarray(w, np.float32)
     amax = np.abs(w).max(axis=0)

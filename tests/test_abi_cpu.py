@@ -27,7 +27,7 @@ S = ctypes.c_void_p(0)
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_symbols_are_exported():
@@ -140,6 +140,20 @@ def reroute(**kw):
 ])
 def test_permute_reroute_rejects(kw, status):
     assert reroute(**kw) == status
+
+
+def test_fp8_entry_points_reject():
+    assert lib.moe_quantize_fp8(NUL, BF16, 2, 64, 64, P, P, S) == INV
+    assert lib.moe_quantize_fp8(P, BF16, 0, 64, 64, P, P, S) == INV
+    assert lib.moe_quantize_fp8(P, BF16, 2, 64, 64, NUL, P, S) == INV
+    assert lib.moe_quantize_fp8(P, 5, 2, 64, 64, P, P, S) == UNS
+    # up: null scale; too many rows per expert for the streaming kernel; d not a multiple of 256
+    assert lib.moe_expert_up_fp8(P, P, P, P, NUL, P, 8, 256, 256, 64, P, S) == INV
+    assert lib.moe_expert_up_fp8(P, P, P, P, P, P, 8, 256, 256, 8 * 33, P, S) == UNS
+    assert lib.moe_expert_up_fp8(P, P, P, P, P, P, 8, 128, 256, 64, P, S) == UNS
+    assert lib.moe_expert_down_fp8(P, P, P, NUL, 8, 256, 256, 64, P, S) == INV
+    assert lib.moe_expert_down_fp8(P, P, P, P, 8, 256, 256, 8 * 33, P, S) == UNS
+    assert lib.moe_expert_down_fp8(P, P, P, P, 8, 256, 192, 64, P, S) == UNS
 
 
 def test_expert_up_down_reject():

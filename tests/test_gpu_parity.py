@@ -191,6 +191,83 @@ def test_shared_expert_mixtral_full_size(moe):
     _run(inp, "workload_mixtral_shared1", sample=sample)
 
 
+# ---------------------------------------------------------------- FP8 expert weights
+def _dev_bf16(a):
+    return torch.from_numpy(a.view(np.int16)).to("cuda").view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_fp8_quantiser_is_bit_exact(moe, dt):
+    """Codes and scales equal the oracle's own E4M3 quantisation, byte for byte."""
+    import oracle.moe_oracle as O
+    rng = np.random.default_rng(9)
+    w = rng.standard_normal((3, 256, 384)).astype(np.float32)
+    w[0, :, 5] = 0.0                                   # an all-zero column
+    w[1, :, 7] *= 1e-6                                 # tiny values: subnormal codes
+    w[2, :, 9] *= 300.0                                # large values
+    w[2, 17, 11] = -w[2, :, 11].__abs__().max() * 2    # a lone negative peak
+    if dt == "bf16":
+        bits = synth.f32_to_bf16_bits(w)
+        wv, wdev = synth.bf16_bits_to_f32(bits), _dev_bf16(bits)
+    else:
+        wv, wdev = w, torch.from_numpy(w).cuda()
+    q, sc = moe.moe_quantize_fp8(wdev)
+    torch.cuda.synchronize()
+    q, sc = q.cpu().numpy(), sc.cpu().numpy()
+    for e in range(3):
+        rq, rs = O.quantize_fp8_columns(wv[e])
+        assert np.array_equal(sc[e], rs), e
+        assert np.array_equal(q[e], rq), e
+
+
+def _fp8_layer(moe, inp, label, sample=None):
+    """The layer with FP8 expert weights quantised on the GPU, against the oracle's layer on
+    the oracle's own dequantised weights (same codes: the quantiser is bit-exact)."""
+    import oracle.moe_oracle as O
+    from tests import parity
+    dev = parity.to_device(inp)
+    q1, s1 = moe.moe_quantize_fp8(dev["w1"])
+    q3, s3 = moe.moe_quantize_fp8(dev["w3"])
+    q2, s2 = moe.moe_quantize_fp8(dev["w2"])
+    b = moe.moe_forward(dev["hidden"], dev["w_router"], dev["w1"], dev["w3"], dev["w2"], inp.k,
+                        inp.capacity_factor, dev["bias"], fp8=(q1, q3, q2, s1, s3, s2))
+    torch.cuda.synchronize()
+    g = parity.host_results(b)
+
+    class Deq:
+        def __init__(self, name):
+            self.name = name
+
+        def __getitem__(self, e):
+            qq, ss = O.quantize_fp8_columns(inp.expert_values(self.name, e))
+            return O.dequantize_fp8_columns(qq, ss)
+
+    ref = O.moe_forward(inp.values("hidden"), inp.values("w_router"), Deq("w1"), Deq("w3"),
+                        Deq("w2"), inp.k, inp.capacity_factor, inp.bias, tokens=sample)
+    same = (g["topk_idx"] == ref["topk_idx"]).all(1)
+    assert np.array_equal(g["slot_row"][same], ref["slot_row"][same]), label
+    toks = ref["tokens"]
+    ok = same[toks]
+    yr, yg = ref["y"][ok], g["y"][toks][ok]
+    rel = float(np.abs(yg - yr).max()) / float(np.abs(yr).max())
+    parity.log(f"{label}: fp8 layer y rel {rel:.3e} on {ok.sum()} tokens")
+    assert rel <= parity.Y_TOL["bf16"], f"{label}: y rel {rel:.3e}"
+    return rel
+
+
+@pytest.mark.parametrize("shape", [(37, 256, 16, 2, 256), (200, 512, 32, 2, 384), (1, 256, 8, 2, 128)])
+def test_fp8_layer_small(moe, shape):
+    T, d, N, k, f = shape
+    for seed in (0, 1):
+        inp = synth.make_inputs(T, d, N, k, f, "bf16", 0.0, seed)
+        _fp8_layer(moe, inp, f"fp8_T{T}_d{d}_N{N}_f{f}/seed{seed}")
+
+
+def test_fp8_decode_workload_full_size(moe):
+    inp = synth.make_workload_inputs("decode", seed=0)
+    _fp8_layer(moe, inp, "fp8_decode_T256", sample=np.array([0, 97, 180, 255]))
+
+
 WORKLOADS = ["tiny_fp32", "n16_cf125", "mixtral", "skewed_zipf", "decode"]
 
 

@@ -55,7 +55,13 @@ Readings of points the pages leave open (each also listed in the design notes):
   bits with bias 7, 3 mantissa bits, subnormals, largest finite 448, no
   infinity): scale = amax / 448 over the column (1 for an all-zero column),
   code = round-to-nearest-even of w / scale, clamped to +-448, both divisions
-  in float32; the layer then runs on code * scale.
+  in float32; the layer then runs on code * scale;
+* backward pass (the training step the pages' aux loss exists for: P1 §2.3,
+  P2 §3.2): gradients of L = <dy, y> + aux_coef * aux with respect to hidden,
+  W_router, bias, W1, W3, W2.  The top-k choice, the capacity cut and the
+  counts f_e are piecewise constant (no gradient); gradients reach the router
+  through the softmax over the k selected logits and through P_e in the aux
+  loss.
 """
 from __future__ import annotations
 
@@ -67,7 +73,7 @@ __all__ = [
     "router_logits", "select_topk", "gate_weights", "expert_counts", "capacity",
     "dispatch", "dispatch_reroute", "silu", "swiglu_ffn", "aux_loss", "moe_forward",
     "moe_forward_per_token", "e4m3_decode", "e4m3_encode", "quantize_fp8_columns",
-    "dequantize_fp8_columns",
+    "dequantize_fp8_columns", "moe_backward",
 ]
 
 
@@ -422,3 +428,84 @@ def moe_forward_per_token(hidden, w_router, w1, w3, w2, k: int, capacity_factor:
             for q in range(len(w1s)):
                 y[t] += swiglu_ffn(hidden[t:t + 1], w1s[q], w3s[q], w2s[q])[0]
     return y
+
+
+def moe_backward(hidden, w_router, w1, w3, w2, k: int, dy, capacity_factor: float = 0.0,
+                 bias=None, aux_coef: float = 0.0, overflow: str = "drop") -> dict:
+    """Gradients of L = sum(dy * y) + aux_coef * aux (float64, from the definitions).
+
+    Per kept slot (t, j) at expert e with gate weight w and row x = hidden[t]:
+      g = w * dy[t] is the gradient reaching the expert's output;
+      h1 = x W1_e, h3 = x W3_e, a = silu(h1) * h3;
+      dW2_e += a^T g;  da = g W2_e^T;
+      dh3 = da * silu(h1);  dh1 = da * h3 * silu'(h1),
+      silu'(z) = s + z s (1 - s) with s = sigmoid(z);
+      dW1_e += x^T dh1;  dW3_e += x^T dh3;  dhidden[t] += dh1 W1_e^T + dh3 W3_e^T;
+      dgate[t, j] = <dy[t], FFN_e(x)>.
+    Softmax over the selected logits: dlogit[t, i_j] = w_j (dgate_j - sum_m w_m dgate_m).
+    Aux loss: d aux / d logits[t, e] = (N / T) p_te (f_e - sum_m p_tm f_m), p = full softmax.
+    Router: dW_router = hidden^T dlogits, dbias = sum_t dlogits, dhidden += dlogits W_router^T.
+    """
+    hidden = np.asarray(hidden, np.float64)
+    T, d = hidden.shape
+    dy = np.asarray(dy, np.float64)
+    Wr = np.asarray(w_router, np.float64)
+    L = router_logits(hidden, w_router, bias)
+    N = L.shape[1]
+    idx = select_topk(L, k)
+    w = gate_weights(L, idx)
+    counts = expert_counts(idx, N)
+    C = capacity(T, k, N, capacity_factor)
+    disp = dispatch(idx, N, C) if overflow == "drop" else dispatch_reroute(idx, L, N, C)
+    slot_row, offsets, perm_src = disp["slot_row"], disp["offsets"], disp["perm_src"]
+    row_slot = {}
+    for t in range(T):
+        for j in range(k):
+            if slot_row[t, j] >= 0:
+                row_slot[int(slot_row[t, j])] = (t, j)
+    f = np.asarray(w1[0]).shape[1]
+    dW1 = np.zeros((N, d, f))
+    dW3 = np.zeros((N, d, f))
+    dW2 = np.zeros((N, f, d))
+    dhidden = np.zeros((T, d))
+    dgate = np.zeros((T, k))
+    for e in range(N):
+        rows = np.arange(offsets[e], offsets[e + 1])
+        if rows.size == 0:
+            continue
+        W1 = np.asarray(w1[e], np.float64)
+        W3 = np.asarray(w3[e], np.float64)
+        W2 = np.asarray(w2[e], np.float64)
+        tj = [row_slot[int(r)] for r in rows]
+        tok = np.array([t for t, _ in tj])
+        slot = np.array([j for _, j in tj])
+        X = hidden[tok]
+        h1, h3 = X @ W1, X @ W3
+        s = 1.0 / (1.0 + np.exp(-h1))
+        a = h1 * s * h3
+        Y = a @ W2
+        gw = w[tok, slot][:, None]
+        G = gw * dy[tok]
+        dgate[tok, slot] = np.sum(dy[tok] * Y, axis=1)
+        dW2[e] = a.T @ G
+        da = G @ W2.T
+        dh3 = da * (h1 * s)
+        dh1 = da * h3 * (s + h1 * s * (1.0 - s))
+        dW1[e] = X.T @ dh1
+        dW3[e] = X.T @ dh3
+        np.add.at(dhidden, tok, dh1 @ W1.T + dh3 @ W3.T)
+    dlog = np.zeros((T, N))
+    wsel = np.take_along_axis(w, np.arange(k)[None, :].repeat(T, 0), 1)
+    inner = np.sum(wsel * dgate, axis=1, keepdims=True)
+    np.put_along_axis(dlog, idx, wsel * (dgate - inner), axis=1)
+    if aux_coef != 0.0:
+        m = L.max(axis=1, keepdims=True)
+        p = np.exp(L - m)
+        p /= p.sum(axis=1, keepdims=True)
+        fe = counts.astype(np.float64) / float(T * k)
+        dlog += aux_coef * (N / T) * p * (fe[None, :] - np.sum(p * fe[None, :], axis=1, keepdims=True))
+    dW_router = hidden.T @ dlog
+    dbias = dlog.sum(axis=0)
+    dhidden += dlog @ Wr.T
+    return {"dhidden": dhidden, "dw_router": dW_router, "dbias": dbias, "dw1": dW1, "dw3": dW3,
+            "dw2": dW2, "dgate": dgate, "dlogits": dlog, "topk_idx": idx, "slot_row": slot_row}

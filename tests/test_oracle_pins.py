@@ -642,3 +642,127 @@ def test_pins_catch_planted_mistakes():
     m = _Mutant(gate_weights=full_softmax_weights)
     out = m.moe_forward(inp.hidden, inp.w_router, inp.w1, inp.w3, inp.w2, 2)
     assert not np.allclose(out["topk_w"].sum(1), 1.0)
+
+
+# ---------------------------------------------------------------- backward pass
+def _loss_and_fd(inp, k, cf, dy, coef, overflow, eps=1e-6):
+    """Central differences of L = <dy, y> + coef * aux through the forward oracle.
+
+    Entries whose perturbation changes the top-k choice are NaN (the choice is
+    piecewise constant, so the derivative there is one-sided)."""
+    P = {"hidden": inp.hidden, "w_router": inp.w_router, "w1": inp.w1, "w3": inp.w3,
+         "w2": inp.w2, "bias": inp.bias}
+    P = {n: np.asarray(v, np.float64) for n, v in P.items()}
+
+    def loss(Q):
+        out = O.moe_forward(Q["hidden"], Q["w_router"], Q["w1"], Q["w3"], Q["w2"], k, cf,
+                            Q["bias"], overflow=overflow)
+        return float(np.sum(dy * out["y"])) + coef * float(out["aux"]), out
+
+    _, base = loss(P)
+    grads = {}
+    for name, arr in P.items():
+        G = np.full(arr.shape, np.nan)
+        for i in np.ndindex(arr.shape):
+            vals = []
+            for sgn in (1.0, -1.0):
+                Q = dict(P)
+                Q[name] = arr.copy()
+                Q[name][i] += sgn * eps
+                l, out = loss(Q)
+                if not np.array_equal(out["topk_idx"], base["topk_idx"]):
+                    break
+                vals.append(l)
+            if len(vals) == 2:
+                G[i] = (vals[0] - vals[1]) / (2 * eps)
+        grads[name] = G
+    return grads, base
+
+
+_GRAD_KEYS = {"hidden": "dhidden", "w_router": "dw_router", "w1": "dw1", "w3": "dw3",
+              "w2": "dw2", "bias": "dbias"}
+
+
+def _backward(inp, k, cf, dy, coef, overflow, mod=O):
+    return mod.moe_backward(inp.hidden, inp.w_router, inp.w1, inp.w3, inp.w2, k, dy, cf,
+                            inp.bias, aux_coef=coef, overflow=overflow)
+
+
+def _fd_agrees(inp, k, cf, dy, coef, overflow, g):
+    fd, _ = _loss_and_fd(inp, k, cf, dy, coef, overflow)
+    worst = 0.0
+    for name, key in _GRAD_KEYS.items():
+        ok = ~np.isnan(fd[name])
+        assert ok.mean() > 0.9
+        scale = max(1.0, float(np.abs(fd[name][ok]).max()))
+        worst = max(worst, float(np.abs(fd[name][ok] - g[key][ok]).max()) / scale)
+    return worst
+
+
+@pytest.mark.parametrize("cf,coef,overflow,seed", [
+    (0.0, 0.0, "drop", 0),        # no capacity limit, no aux loss
+    (0.8, 0.37, "drop", 1),       # dropped slots and the aux-loss term
+    (0.8, 0.05, "reroute", 2),    # re-routed slots keep their gate weight
+])
+def test_backward_matches_finite_differences_of_the_forward(cf, coef, overflow, seed):
+    """Every gradient equals the central difference of the pinned forward (fp64, eps 1e-6)."""
+    inp = synth.make_inputs(10, 6, 4, 2, 5, "f32", cf, seed,
+                            bias=np.array([0.5, 0.0, -0.3, 0.2], np.float32))
+    dy = np.random.default_rng(100 + seed).standard_normal((10, 6))
+    g = _backward(inp, 2, cf, dy, coef, overflow)
+    if cf > 0:
+        assert (g["slot_row"] < 0).any()          # the case really drops slots
+    assert _fd_agrees(inp, 2, cf, dy, coef, overflow, g) < 1e-6
+
+
+def test_backward_softmax_shift_invariance():
+    """Adding one constant to a token's logits changes neither the top-k set, the
+    weights nor P: each token's logit gradient sums to zero, so dbias sums to zero
+    and every row of dW_router does too."""
+    inp = _rand(T=32, d=8, N=8, k=2, f=16, seed=3, cf=1.0)
+    dy = np.random.default_rng(4).standard_normal((32, 8))
+    g = _backward(inp, 2, 1.0, dy, 0.1, "drop")
+    assert np.abs(g["dlogits"].sum(1)).max() < 1e-12
+    assert abs(g["dbias"].sum()) < 1e-12
+    assert np.abs(g["dw_router"].sum(1)).max() < 1e-12
+
+
+def test_backward_fully_dropped_token_has_no_gradient_without_aux():
+    """A token whose every slot is dropped skips the layer (y = 0 there), so with
+    no aux term nothing flows back to it or from it."""
+    inp = _rand(T=16, d=8, N=4, k=1, f=8, seed=5, cf=0.25)
+    inp.bias = np.array([6.0, 0.0, 0.0, 0.0], np.float32)    # everyone wants expert 0
+    dy = np.random.default_rng(6).standard_normal((16, 8))
+    g = _backward(inp, 1, 0.25, dy, 0.0, "drop")
+    gone = (g["slot_row"] < 0).all(1)
+    assert gone.any()
+    assert np.abs(g["dhidden"][gone]).max() == 0.0
+    assert np.abs(g["dlogits"][gone]).max() == 0.0
+    # with k = 1 the single weight is exactly 1: the router gets nothing either
+    assert np.abs(g["dlogits"]).max() == 0.0
+
+
+def test_backward_pins_catch_planted_mistakes():
+    """Plant a plausible mistake in a copy of the oracle's backward; the
+    finite-difference pin must reject each."""
+    import inspect
+    src = inspect.getsource(O.moe_backward)
+    mistakes = [
+        ("s + h1 * s * (1.0 - s)", "s"),                       # silu' without its second term
+        ("wsel * (dgate - inner)", "wsel * dgate"),            # softmax Jacobian without the mean
+        ("(fe[None, :] - np.sum", "(fe[None, :] + np.sum"),    # aux gradient sign
+        ("dW2[e] = a.T @ G", "dW2[e] = a.T @ dy[tok]"),        # gate weight left out of dW2
+        ("dhidden += dlog @ Wr.T", "pass"),                    # router path into dhidden dropped
+    ]
+    inp = synth.make_inputs(10, 6, 4, 2, 5, "f32", 0.8, 1,
+                            bias=np.array([0.5, 0.0, -0.3, 0.2], np.float32))
+    dy = np.random.default_rng(101).standard_normal((10, 6))
+    for old, new in mistakes:
+        assert old in src, old
+        ns = dict(vars(O))
+        exec(compile(src.replace(old, new), "<mutant>", "exec"), ns)
+
+        class M:
+            moe_backward = staticmethod(ns["moe_backward"])
+        g = _backward(inp, 2, 0.8, dy, 0.37, "drop", mod=M)
+        assert _fd_agrees(inp, 2, 0.8, dy, 0.37, "drop", g) > 1e-3, old

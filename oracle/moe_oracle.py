@@ -56,8 +56,9 @@ Readings of points the pages leave open (each also listed in the design notes):
   infinity): scale = amax / 448 over the column (1 for an all-zero column),
   code = round-to-nearest-even of w / scale, clamped to +-448, both divisions
   in float32; the layer then runs on code * scale;
-* backward pass (the training step the pages' aux loss exists for: P1 §2.3,
-  P2 §3.2): gradients of L = <dy, y> + aux_coef * aux with respect to hidden,
+* backward pass (the training step the aux loss exists for: P1 §2.3, P2 §3.2;
+  every expert keeps gradients of its own: P4 §2.2; only the selected experts
+  receive any: P4 §5.1): gradients of L = <dy, y> + aux_coef * aux with respect to hidden,
   W_router, bias, W1, W3, W2.  The top-k choice, the capacity cut and the
   counts f_e are piecewise constant (no gradient); gradients reach the router
   through the softmax over the k selected logits and through P_e in the aux

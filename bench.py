@@ -15,6 +15,11 @@ Also reported in the same line:
                 against the bf16 dense MFMA peak; HBM traffic per launch from
                 rocprofv3 FETCH_SIZE/WRITE_SIZE when a committed counter
                 summary matches the current kernel source, else null;
+  backward      the backward pass of the Mixtral-shaped layer (gradients of
+                <dy, y> + 0.01 * aux into hidden, the router and every expert's
+                W1/W3/W2, fp32 gradients): its time, the expert GEMMs' rate
+                (16*A*d*f flop: recompute of h1/h3, da, dx, dW1/dW3, dW2)
+                against the bf16 MFMA peak, and forward + backward per step;
   decode_fp8    the decode-shaped layer with FP8 (OCP E4M3, per-column fp32
                 scale) expert weights quantised on the GPU: bytes counted at one
                 byte per weight plus the scales;
@@ -150,6 +155,53 @@ def time_layer(inp, dev, steps, warmup, overflow="drop", shared=None, fp8=None):
     return {"elapsed_s": elapsed, "ms_per_step": 1e3 * elapsed / steps, "up_ms": up_ms,
             "down_ms": down_ms, "A": A, "kept": kept, "aux": float(b.aux.item()),
             "dropped": dropped}
+
+
+def time_backward(inp, dev, steps, warmup, coef=0.01):
+    """One forward (untimed), then `steps` backward passes; HIP events on the launch
+    stream bracket the three backward entry points of each pass."""
+    import torch
+    from mixture_experts_layer_sum_amd import moe, synth
+    T, d, N, k, f = inp.T, inp.d, inp.N, inp.k, inp.f
+    b = moe.moe_forward(dev["hidden"], dev["w_router"], dev["w1"], dev["w3"], dev["w2"], k,
+                        inp.capacity_factor, dev["bias"])
+    gb = moe.MoEGradBuffers(T, d, N, k, f, dev["hidden"].dtype)
+    dyh = synth.make_dy(T, d, inp.dtype, seed=11)
+    dy = (torch.from_numpy(dyh.view("int16")).cuda().view(torch.bfloat16) if inp.dtype == "bf16"
+          else torch.from_numpy(dyh).cuda())
+    s = torch.cuda.current_stream()
+    want_db = dev["bias"] is not None
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(s)
+        moe.moe_combine_backward(dy, b.y_perm, b.slot_row, b.topk_w, gb.g_perm, gb.dgate)
+        if ev:
+            ev[1].record(s)
+        moe.moe_expert_backward(b.x_perm, gb.g_perm, b.offsets, dev["w1"], dev["w3"], dev["w2"],
+                                gb.dx_perm, gb.dw1, gb.dw3, gb.dw2, gb.ws_expert)
+        if ev:
+            ev[2].record(s)
+        moe.moe_router_backward(dev["hidden"], dev["w_router"], b.logits, b.topk_idx, b.topk_w,
+                                b.counts, gb.dgate, gb.dx_perm, b.slot_row, coef, gb.dhidden,
+                                gb.dw_router, gb.dbias, want_db, gb.ws_router)
+        if ev:
+            ev[3].record(s)
+
+    for _ in range(warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    part = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j in range(3)]
+    A = int(b.offsets[-1].item())
+    del gb, b
+    return {"ms_per_step": 1e3 * elapsed / steps, "combine_ms": part[0], "expert_ms": part[1],
+            "router_ms": part[2], "A": A}
 
 
 def layer_flops(inp, A):
@@ -368,6 +420,8 @@ def main():
     ap.add_argument("--no-main", action="store_true",
                     help="profiling aid: time only the decode-shaped layer (no JSON line)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward-pass object")
     ap.add_argument("--cpu-tokens", type=int, default=8192)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB")
     ap.add_argument("--summarize-rocprof", default=None, metavar="DIR")
@@ -444,6 +498,22 @@ def main():
                                 "tokens_per_s": inp.T / (rs["ms_per_step"] * 1e-3),
                                 "layer_tflops": fl / (rs["ms_per_step"] * 1e-3) / 1e12}
         del sh
+    if not args.no_backward:
+        log("timing the backward pass")
+        rb = time_backward(inp, dev, args.steps, args.warmup)
+        bfl = 16.0 * rb["A"] * inp.d * inp.f
+        gt = bfl / (rb["expert_ms"] * 1e-3) / 1e12
+        out["backward"] = {"workload": w.name + "_backward_auxcoef0.01",
+                           "ms_per_step": rb["ms_per_step"],
+                           "tokens_per_s": inp.T / (rb["ms_per_step"] * 1e-3),
+                           "kernel_ms": {"combine_backward": rb["combine_ms"],
+                                         "expert_backward": rb["expert_ms"],
+                                         "router_backward": rb["router_ms"]},
+                           "expert_gemm_tflops": gt, "expert_gemm_frac_mfma_peak": gt / PEAK_BF16_TFLOPS,
+                           "work_per_launch": f"16*A*d*f = {bfl:.4e} flop over 5 GEMM launches, A={rb['A']}",
+                           "forward_plus_backward_ms": ms + rb["ms_per_step"],
+                           "training_tokens_per_s": inp.T / ((ms + rb["ms_per_step"]) * 1e-3)}
+        torch.cuda.empty_cache()
     del dev
     torch.cuda.empty_cache()
 

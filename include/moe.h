@@ -16,6 +16,12 @@
  *   weighted combine back to token order (+ shared experts)       moe_combine
  *   load-balancing loss N * sum_e f_e * P_e                       moe_aux_loss
  *
+ * Its backward (gradients of <dy, y> + aux_coef * aux; P1 §2.3, P4 §2.2,
+ * P4 §5.1):
+ *   through the combine                                           moe_combine_backward
+ *   through both grouped GEMMs (dx, dW1, dW3, dW2)               moe_expert_backward
+ *   through the softmax, the aux loss and the router linear       moe_router_backward
+ *
  * Conventions shared by every entry point:
  *   - Every pointer argument is a DEVICE pointer owned by the caller, to a
  *     contiguous row-major array; the library never allocates, frees, keeps
@@ -61,7 +67,9 @@ typedef enum {
   MOE_OP_COMBINE = 3,
   MOE_OP_AUX_LOSS = 4,
   MOE_OP_EXPERT_DOWN = 5,
-  MOE_OP_PERMUTE_REROUTE = 6
+  MOE_OP_PERMUTE_REROUTE = 6,
+  MOE_OP_EXPERT_BACKWARD = 7,
+  MOE_OP_ROUTER_BACKWARD = 8
 } moe_op;
 
 /* Human-readable name of a status code (static string). */
@@ -71,7 +79,9 @@ const char* moe_status_string(moe_status s);
  * 0 for an unknown op as well.  For MOE_OP_EXPERT_FFN and MOE_OP_EXPERT_DOWN,
  * T*k is the row capacity (max_rows) of x_perm / y_perm.  The two expert ops
  * size their k-split buffers by the compute units of the CURRENT device
- * (0 when no device is visible); query with that device current. */
+ * (0 when no device is visible); query with that device current.
+ * MOE_OP_EXPERT_BACKWARD: T*k is max_rows.  MOE_OP_ROUTER_BACKWARD: d and N
+ * of the router, T tokens. */
 size_t moe_workspace_size(moe_op op, int T, int d, int N, int k, int f, moe_dtype dt);
 
 /*
@@ -251,6 +261,70 @@ moe_status moe_combine(const float* y_perm, const int32_t* slot_row, const float
  */
 moe_status moe_aux_loss(const float* logits, const int32_t* counts, int T, int N, int k,
                         float* aux, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward pass.  The top-k choice, the capacity cut and the counts are
+ * piecewise constant and pass no gradient; gradients reach the router through
+ * the softmax over the k selected logits and through P_e of the aux loss
+ * (P4 §5.1: only the selected experts get a gradient).  Every gradient output
+ * is fp32.  Inputs are the forward's outputs for the same batch (moe_route,
+ * moe_permute or moe_permute_reroute, moe_expert_ffn).
+ *
+ * moe_combine_backward -- for every kept slot (t, j), r = slot_row[t, j]:
+ *   g_perm[r]   = topk_w[t, j] * dy[t]            (dtype dt)
+ *   dgate[t, j] = <dy[t], y_perm[r]>              (fp32; 0 for dropped slots)
+ *   dy [T, d] dtype dt; y_perm [max_rows, d] fp32 (moe_expert_ffn);
+ *   g_perm [max_rows, d] dtype dt out (rows >= offsets[N] not written);
+ *   dgate [T, k] fp32 out.
+ */
+moe_status moe_combine_backward(const void* dy, const float* y_perm, const int32_t* slot_row,
+                                const float* topk_w, int T, int d, int k, moe_dtype dt,
+                                void* g_perm, float* dgate, void* stream);
+
+/*
+ * moe_expert_backward -- backward of every expert's SwiGLU FFN (P4 §2.2: each
+ * expert has gradients of its own), for rows r of expert e (h1 = x_perm[r] W1_e,
+ * h3 = x_perm[r] W3_e recomputed, s = sigmoid(h1), a = h1 s h3,
+ * da = g_perm[r] W2_e^T, dh1 = da h3 (s + h1 s (1 - s)), dh3 = da h1 s):
+ *   dx_perm[r] = dh1 W1_e^T + dh3 W3_e^T           [max_rows, d] fp32 out
+ *   dw1[e] = sum_r x_perm[r]^T dh1,  dw3[e] = sum_r x_perm[r]^T dh3     [N, d, f] fp32 out
+ *   dw2[e] = sum_r a^T g_perm[r]                                        [N, f, d] fp32 out
+ * An expert with no rows gets zero weight gradients.  Rows >= offsets[N] of
+ * dx_perm are not written.
+ *   x_perm, g_perm [max_rows, d] dtype dt; offsets [N+1]; w1, w3 [N, d, f],
+ *   w2 [N, f, d] dtype dt.
+ *   ws  moe_workspace_size(MOE_OP_EXPERT_BACKWARD, T, d, N, k, f, dt) bytes,
+ *       T*k = max_rows: da [max_rows, f] fp32, [dh1 | dh3] [max_rows, 2f] and
+ *       a [max_rows, f] in dtype dt, each padded to 256 bytes.
+ *   Limits: those of moe_expert_ffn; for bf16 f a multiple of 256 and
+ *   max_rows * f < 2^29.
+ */
+moe_status moe_expert_backward(const void* x_perm, const void* g_perm, const int32_t* offsets,
+                               const void* w1, const void* w3, const void* w2, int N, int d,
+                               int f, int max_rows, moe_dtype dt, float* dx_perm, float* dw1,
+                               float* dw3, float* dw2, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_router_backward -- through the softmax over the k selected logits, the
+ * aux loss (coefficient aux_coef, P1 §2.3) and the router linear:
+ *   dlogit[t, e] = aux_coef (N / T) p[t, e] (f_e - sum_m p[t, m] f_m)
+ *                  (p = softmax over all N, f_e = counts[e] / (T k))
+ *                + sum_j [topk_idx[t, j] = e] topk_w[t, j] (dgate[t, j] - sum_m topk_w[t, m] dgate[t, m])
+ *   dhidden[t]   = sum_j dx_perm[slot_row[t, j]] (kept slots) + dlogit[t] W_router^T
+ *   dw_router    = hidden^T dlogit  [d, N] fp32 out
+ *   dbias        = sum_t dlogit[t]  [N] fp32 out, or NULL to skip
+ *   hidden [T, d], w_router [d, N] dtype dt; logits [T, N], topk_w, dgate [T, k]
+ *   fp32; topk_idx, slot_row [T, k], counts [N] int32; dx_perm [max_rows, d]
+ *   fp32; dhidden [T, d] fp32 out.  Sums over tokens are taken in a fixed
+ *   order (results do not depend on scheduling).
+ *   ws  moe_workspace_size(MOE_OP_ROUTER_BACKWARD, T, d, N, k, f, dt) bytes.
+ */
+moe_status moe_router_backward(const void* hidden, const void* w_router, const float* logits,
+                               const int32_t* topk_idx, const float* topk_w,
+                               const int32_t* counts, const float* dgate, const float* dx_perm,
+                               const int32_t* slot_row, float aux_coef, int T, int d, int N,
+                               int k, moe_dtype dt, float* dhidden, float* dw_router, float* dbias,
+                               void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -20,7 +20,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libmoe_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["route.hip", "permute.hip", "expert_gemm.hip", "fp8.hip", "combine_aux.hip", "api.cpp"]
+SOURCES = ["route.hip", "permute.hip", "expert_gemm.hip", "fp8.hip", "combine_aux.hip", "backward.hip",
+           "api.cpp"]
 
 
 def _hipcc() -> str:

@@ -87,6 +87,12 @@ size_t moe_workspace_size(moe_op op, int T, int d, int N, int k, int f, moe_dtyp
       if (d < 1 || f < 1 || !dtype_ok(dt)) return 0;
       return moe::expert_down_ws_bytes(N, d, f, T * k, dt == MOE_BF16);
     case MOE_OP_AUX_LOSS: return moe::aux_ws_bytes(T, N);
+    case MOE_OP_EXPERT_BACKWARD:
+      if (d < 1 || f < 1 || !dtype_ok(dt)) return 0;
+      return moe::expert_backward_ws_bytes(d, f, T * k, dt == MOE_BF16);
+    case MOE_OP_ROUTER_BACKWARD:
+      if (d < 1 || N > kMaxExperts) return 0;
+      return moe::router_backward_ws_bytes(T, d, N);
     default: return 0;
   }
 }
@@ -246,6 +252,62 @@ moe_status moe_aux_loss(const float* logits, const int32_t* counts, int T, int N
   if (ws_bytes < moe::aux_ws_bytes(T, N)) return MOE_ERR_WORKSPACE;
   if (!ws) return MOE_ERR_INVALID_ARG;
   return hip_status(moe::launch_aux(logits, counts, T, N, k, aux, ws, as_stream(stream)));
+}
+
+moe_status moe_combine_backward(const void* dy, const float* y_perm, const int32_t* slot_row,
+                                const float* topk_w, int T, int d, int k, moe_dtype dt,
+                                void* g_perm, float* dgate, void* stream) {
+  if (!dy || !y_perm || !slot_row || !topk_w || !g_perm || !dgate) return MOE_ERR_INVALID_ARG;
+  if (T < 1 || k < 1) return MOE_ERR_INVALID_ARG;
+  if (k > kMaxExperts || static_cast<int64_t>(T) * k >= (int64_t{1} << 31)) return MOE_ERR_UNSUPPORTED;
+  moe_status s = check_d(d);
+  if (s != MOE_OK) return s;
+  if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_combine_backward(dy, y_perm, slot_row, topk_w, T, d, k,
+                                                 dt == MOE_BF16, g_perm, dgate, as_stream(stream)));
+}
+
+moe_status moe_expert_backward(const void* x_perm, const void* g_perm, const int32_t* offsets,
+                               const void* w1, const void* w3, const void* w2, int N, int d,
+                               int f, int max_rows, moe_dtype dt, float* dx_perm, float* dw1,
+                               float* dw3, float* dw2, void* ws, size_t ws_bytes, void* stream) {
+  if (!x_perm || !g_perm || !offsets || !w1 || !w3 || !w2 || !dx_perm || !dw1 || !dw3 || !dw2)
+    return MOE_ERR_INVALID_ARG;
+  moe_status s = check_expert_shape(N, d, f, max_rows, dt);
+  if (s != MOE_OK) return s;
+  // bf16: 256-column tiles over f, and 32-bit buffer offsets into [rows, 2f]
+  if (dt == MOE_BF16 && (f % 256 != 0 ||
+                         static_cast<int64_t>(max_rows) * f >= (int64_t{1} << 29)))
+    return MOE_ERR_UNSUPPORTED;
+  const size_t need = moe::expert_backward_ws_bytes(d, f, max_rows, dt == MOE_BF16);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (!ws) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_expert_backward(x_perm, g_perm, offsets, w1, w3, w2, N, d, f,
+                                                max_rows, dt == MOE_BF16, dx_perm, dw1, dw3, dw2,
+                                                ws, as_stream(stream)));
+}
+
+moe_status moe_router_backward(const void* hidden, const void* w_router, const float* logits,
+                               const int32_t* topk_idx, const float* topk_w,
+                               const int32_t* counts, const float* dgate, const float* dx_perm,
+                               const int32_t* slot_row, float aux_coef, int T, int d, int N,
+                               int k, moe_dtype dt, float* dhidden, float* dw_router, float* dbias,
+                               void* ws, size_t ws_bytes, void* stream) {
+  if (!hidden || !w_router || !logits || !topk_idx || !topk_w || !counts || !dgate || !dx_perm ||
+      !slot_row || !dhidden || !dw_router)
+    return MOE_ERR_INVALID_ARG;
+  if (std::isnan(aux_coef)) return MOE_ERR_INVALID_ARG;
+  moe_status s = check_tnk(T, N, k);
+  if (s != MOE_OK) return s;
+  if ((s = check_d(d)) != MOE_OK) return s;
+  if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
+  const size_t need = moe::router_backward_ws_bytes(T, d, N);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (!ws) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_router_backward(hidden, w_router, logits, topk_idx, topk_w,
+                                                counts, dgate, dx_perm, slot_row, aux_coef, T, d,
+                                                N, k, dt == MOE_BF16, dhidden, dw_router, dbias,
+                                                ws, as_stream(stream)));
 }
 
 }  // extern "C"

@@ -1,0 +1,882 @@
+// Backward pass of the layer: gradients of L = <dy, y> + aux_coef * aux.
+//
+// The aux loss exists for training (cf-1.com/news/5914943 §2.3,
+// hotelren.com/news/5904824 §3.2); every expert keeps gradients of its own
+// (2kiu.com/news/2885792 §2.2) and only the selected experts receive any
+// (2kiu.com/news/2885792 §5.1).  The weight gradients keep the weights'
+// layout, one tensor per matrix sliced by expert (2kiu.com/news/2885792 §5.4):
+// [N, d, f] for W1 and W3, [N, f, d] for W2, in fp32.
+// The top-k choice, the capacity cut and the counts are piecewise constant:
+// gradients reach the router through the softmax over the k selected logits
+// and through the mean router probability in the aux loss.
+//
+// Steps (r = row of slot (t, j) in the expert-contiguous order, w = its gate
+// weight, x = hidden[t], h1 = x W1_e, h3 = x W3_e, a = silu(h1) * h3):
+//   combine  : g[r] = w * dy[t];  dgate[t, j] = <dy[t], y_perm[r]>
+//   da       : da[r] = g[r] W2_e^T                              (grouped, NT)
+//   swiglu   : recompute h1, h3; dh1 = da * h3 * silu'(h1), dh3 = da * silu(h1),
+//              a = silu(h1) * h3                                 (grouped, NN)
+//   dx       : dx[r] = dh1[r] W1_e^T + dh3[r] W3_e^T              (grouped, NT, K = 2f)
+//   weights  : dW2_e = a_e^T g_e;  [dW1_e | dW3_e] = x_e^T [dh1_e | dh3_e]
+//                                                   (per expert, k = the expert's rows)
+//   router   : dlogit = softmax-over-k Jacobian of dgate + aux_coef * d aux / d logits;
+//              dhidden[t] = sum_j dx[slot (t, j)] + dlogit[t] W_router^T;
+//              dW_router = hidden^T dlogit;  dbias = sum_t dlogit[t]
+//
+// bf16 GEMMs run on one MFMA tile kernel with the forward's structure (256 x
+// 256 tiles, 8 waves, two 64 KB LDS stages filled by direct buffer -> LDS
+// loads issued by one wave per SIMD) and a template per step that sets how
+// each operand is laid out in memory: k-contiguous operands (x, g, dh rows;
+// W2 and W1/W3 read as their transposes) are staged row-major and read with
+// ds_read_b128; m- or n-contiguous operands (W1/W3 in the recompute, every
+// operand of the weight gradients, whose depth is the expert's token rows)
+// are staged k-row-major and read with the transposing ds_read_b64_tr_b16.
+// The weight gradients' depth ends at the expert's last row: the buffer
+// resource stops there, so the loads past it return zeros.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace moe {
+namespace bwd {
+
+enum Mode { kDA = 0, kDX = 1, kSwiGLU = 2, kWGrad = 3 };
+
+constexpr int kBM = 256, kBN = 256, kBK = 64, kThreads = 512, kGroupM = 8;
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One GEMM launch.  Row indices r are rows of the expert-contiguous order.
+struct Args {
+  const void* a;            // A operand base
+  int lda;                  // its row stride (elements)
+  const void* b0;           // B operand (DX: W1 for k < ksplit steps; SwiGLU: W1)
+  const void* b1;           // DX: W3; SwiGLU: W3
+  int ldb;
+  long long b_estride;      // elements between experts' weight matrices (grouped-row steps)
+  const int32_t* offsets;
+  int n_exp, max_rows;
+  int K;                    // depth of the grouped-row steps
+  int M;                    // WGrad: rows of each expert's output
+  int Nn;                   // output columns (SwiGLU: f)
+  int n_tiles;              // output column tiles (set by the launcher)
+  int ksplit;               // DX: 64-deep k-steps read from b0 before b1
+  float* out0;              // fp32 output (DA: da, DX: dx, WGrad: columns < nsplit)
+  float* out1;              // WGrad: columns >= nsplit
+  int ldo, nsplit;
+  long long o_estride;      // WGrad: elements between experts' outputs
+  const float* da;          // SwiGLU: da [rows, f] (input)
+  void* dh;                 // SwiGLU: [dh1 | dh3] [rows, 2f] (output)
+  void* act;                // SwiGLU: a [rows, f] (output)
+  int f;
+};
+
+__device__ __forceinline__ bool dp_logical(int total, int& logical) {
+  const int per = (total + 7) >> 3;
+  const int b = blockIdx.x;
+  const int local = b >> 3;
+  if (local >= per) return false;
+  logical = (b & 7) * per + local;
+  return logical < total;
+}
+
+__device__ __forceinline__ void tile_of_logical(int logical, int m_tiles, int n_tiles, int& mt,
+                                                int& nt) {
+  const int span = kGroupM * n_tiles;
+  const int grp = logical / span;
+  const int first = grp * kGroupM;
+  const int gm = (m_tiles - first) < kGroupM ? (m_tiles - first) : kGroupM;
+  const int in = logical - grp * span;
+  mt = first + in % gm;
+  nt = in / gm;
+}
+
+__device__ __forceinline__ uint4 frag_tr(const uint16_t* p) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p + 512));
+  const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+  return make_uint4(l2.x, l2.y, h2.x, h2.y);
+}
+
+// Fragment reads of 16-deep slice s2 of a stage: A sub-tiles i < NV, B sub-tiles j < 2.
+// Row-major operands: element offset base + 4096 i (A) / 2048 j (B), base per s2.
+// Transposed operands: base per sub-tile + 2048 s2.
+template <int NV, bool AT, bool BT>
+__device__ __forceinline__ void frags(const uint16_t* __restrict__ st, int s2,
+                                      const int (&a_rd)[4], const int (&b_rd)[4], uint4 (&fa)[4],
+                                      uint4 (&fb)[2]) {
+  if (NV == 0) return;
+  const uint16_t* bs = st + 16384;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    if (AT)
+      fa[i] = frag_tr(st + a_rd[i] + 2048 * s2);
+    else
+      fa[i] = *reinterpret_cast<const uint4*>(st + a_rd[s2] + 4096 * i);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (BT)
+      fb[j] = frag_tr(bs + b_rd[j] + 2048 * s2);
+    else
+      fb[j] = *reinterpret_cast<const uint4*>(bs + b_rd[s2] + 2048 * j);
+  }
+}
+
+template <int NV>
+__device__ __forceinline__ void mma(const uint4 (&fa)[4], const uint4 (&fb)[2],
+                                    f32x16 (&acc)[4][2]) {
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
+}
+
+// Per-lane state of the direct loads issued by one loading wave.
+struct Loader {
+  __amdgpu_buffer_rsrc_t a_rs, b_rs0, b_rs1;
+  uint32_t a_off[8], b_off[8];
+  uint32_t a_kstride, b_kstride;
+  int ksplit;
+  int w;                      // loading wave 0..3
+};
+
+__device__ __forceinline__ void issue(uint16_t* __restrict__ dst, const Loader& L, int kstep) {
+  const uint32_t ka = (uint32_t)kstep * L.a_kstride;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(L.a_rs, (lds_void*)(dst + (8 * L.w + i) * 512), 16,
+                                             L.a_off[i] + ka, 0, 0, 0);
+  const bool hi = kstep >= L.ksplit;
+  const __amdgpu_buffer_rsrc_t b_rs = hi ? L.b_rs1 : L.b_rs0;
+  const uint32_t kb = (uint32_t)(hi ? kstep - L.ksplit : kstep) * L.b_kstride;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rs, (lds_void*)(dst + 16384 + (8 * L.w + i) * 512),
+                                             16, L.b_off[i] + kb, 0, 0, 0);
+}
+
+#define MOE_BWD_WAIT_BARRIER() asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory")
+
+// One 64-deep k-step (the forward GEMM's schedule): fa0/fb0 hold slice 0 of
+// `cur` on entry; after the barrier that follows the last read of `cur`, the
+// loading waves refill `cur` two steps ahead, interleaved with the last
+// slice's MFMAs, and slice 0 of `nxt` is read.
+template <int NV, bool DMA, bool AT, bool BT>
+__device__ __forceinline__ void kstep_body(const uint16_t* __restrict__ cur,
+                                           uint16_t* __restrict__ dst,
+                                           const uint16_t* __restrict__ nxt, const Loader& L,
+                                           int kstep, const int (&a_rd)[4], const int (&b_rd)[4],
+                                           f32x16 (&acc)[4][2], uint4 (&fa0)[4], uint4 (&fb0)[2]) {
+  uint4 fa1[4], fb1[2];
+  frags<NV, AT, BT>(cur, 1, a_rd, b_rd, fa1, fb1);
+  mma<NV>(fa0, fb0, acc);
+  frags<NV, AT, BT>(cur, 2, a_rd, b_rd, fa0, fb0);
+  mma<NV>(fa1, fb1, acc);
+  frags<NV, AT, BT>(cur, 3, a_rd, b_rd, fa1, fb1);
+  mma<NV>(fa0, fb0, acc);
+  MOE_BWD_WAIT_BARRIER();
+  if (DMA && NV == 4) {
+    frags<NV, AT, BT>(nxt, 0, a_rd, b_rd, fa0, fb0);
+    issue(dst, L, kstep);
+    mma<NV>(fa1, fb1, acc);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    if (DMA) issue(dst, L, kstep);
+    __builtin_amdgcn_sched_barrier(0);
+    frags<NV, AT, BT>(nxt, 0, a_rd, b_rd, fa0, fb0);
+    mma<NV>(fa1, fb1, acc);
+  }
+}
+
+__device__ __forceinline__ int clamp_off(const int32_t* offsets, int e, int max_rows, int lo) {
+  return min(max(offsets[e], lo), max_rows);
+}
+
+// LDS layout of one stage (64 KB): A at element 0, B at 16384.
+//   row-major operand  [256 rows][64 k]: chunk c of row r at position c ^ ((r >> 1) & 7)
+//   transposed operand 2 x [64 k][128 cols]: chunk c of k-row kr at c ^ (4 (kr & 3))
+template <int MODE>
+__global__ __launch_bounds__(kThreads, 1) void bwd_gemm_bf16_kernel(Args p) {
+  constexpr bool AT = MODE == kWGrad;                       // A m-contiguous
+  constexpr bool BT = MODE == kSwiGLU || MODE == kWGrad;    // B n-contiguous
+  constexpr bool GK = MODE == kWGrad;                       // depth = the expert's rows
+  __shared__ __align__(1024) uint16_t S0[32768], S1[32768];
+
+  int e, r0, rend, mt, nt, m0 = 0, kl;
+  if (GK) {
+    const int m_tiles = p.M / kBM;
+    const int tpe = m_tiles * p.n_tiles;
+    int logical;
+    if (!dp_logical(tpe * p.n_exp, logical)) return;
+    e = logical / tpe;
+    tile_of_logical(logical - e * tpe, m_tiles, p.n_tiles, mt, nt);
+    r0 = clamp_off(p.offsets, e, p.max_rows, 0);
+    rend = min(max(p.offsets[e + 1], r0), p.max_rows);
+    m0 = mt * kBM;
+    kl = (rend - r0 + kBK - 1) / kBK;
+  } else {
+    const int m_tiles = count_tiles(p.offsets, p.n_exp, kBM, p.max_rows);
+    int logical;
+    if (!dp_logical(m_tiles * p.n_tiles, logical)) return;
+    tile_of_logical(logical, m_tiles, p.n_tiles, mt, nt);
+    if (!find_tile(p.offsets, p.n_exp, mt, kBM, p.max_rows, e, r0, rend)) return;
+    kl = p.K / kBK;
+  }
+  e = __builtin_amdgcn_readfirstlane(e);
+  r0 = __builtin_amdgcn_readfirstlane(r0);
+  rend = __builtin_amdgcn_readfirstlane(rend);
+  nt = __builtin_amdgcn_readfirstlane(nt);
+  m0 = __builtin_amdgcn_readfirstlane(m0);
+  kl = __builtin_amdgcn_readfirstlane(kl);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int sm = w & 3, pw = w >> 2;
+  const int wm = sm & 1, wn = sm >> 1;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int n0 = MODE == kSwiGLU ? nt * (kBN / 2) : nt * kBN;
+  const int rows = rend - r0;
+  const int tile_rows = min(rows, kBM);
+
+  // ---- load set-up (only waves 0..3 issue loads)
+  Loader L;
+  L.w = w & 3;
+  L.ksplit = MODE == kDX ? p.ksplit : 0x7FFFFFFF;
+  const uint16_t* A = static_cast<const uint16_t*>(p.a) + (size_t)r0 * p.lda;
+  L.a_rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(A), 0,
+                                             (GK ? rows : tile_rows) * p.lda * 2, kRsrcWord3);
+  if (GK) {
+    const uint16_t* B = static_cast<const uint16_t*>(p.b0) + (size_t)r0 * p.ldb;
+    L.b_rs0 = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(B), 0, rows * p.ldb * 2,
+                                                kRsrcWord3);
+    L.b_rs1 = L.b_rs0;
+  } else {
+    const size_t wexp = (size_t)e * p.b_estride;
+    const int wbytes = (int)(p.b_estride * 2);
+    L.b_rs0 = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(static_cast<const uint16_t*>(p.b0) + wexp), 0, wbytes, kRsrcWord3);
+    L.b_rs1 = MODE == kSwiGLU || MODE == kDX
+                  ? __builtin_amdgcn_make_buffer_rsrc(
+                        const_cast<uint16_t*>(static_cast<const uint16_t*>(p.b1) + wexp), 0,
+                        wbytes, kRsrcWord3)
+                  : L.b_rs0;
+  }
+  L.a_kstride = AT ? (uint32_t)(kBK * p.lda * 2) : (uint32_t)(kBK * 2);
+  L.b_kstride = BT ? (uint32_t)(kBK * p.ldb * 2) : (uint32_t)(kBK * 2);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int ins = 8 * L.w + i;
+    if (AT) {
+      const int q = ins >> 4, kr = 4 * (ins & 15) + (lane >> 4);
+      const int cb = (lane & 15) ^ (4 * (kr & 3));
+      L.a_off[i] = (uint32_t)((kr * p.lda + m0 + 128 * q + 8 * cb) * 2);
+    } else {
+      int row = 8 * ins + (lane >> 3);
+      const int c = (lane & 7) ^ ((row >> 1) & 7);
+      row = row < tile_rows ? row : tile_rows - 1;         // rows past the end repeat the last one
+      L.a_off[i] = (uint32_t)((row * p.lda + 8 * c) * 2);
+    }
+    if (BT) {
+      const int q = ins >> 4, kr = 4 * (ins & 15) + (lane >> 4);
+      const int cb = (lane & 15) ^ (4 * (kr & 3));
+      const int col = (MODE == kSwiGLU ? n0 : n0 + 128 * q) + 8 * cb;
+      L.b_off[i] = (uint32_t)((kr * p.ldb + col) * 2);
+    } else {
+      const int nrow = 8 * ins + (lane >> 3);
+      const int c = (lane & 7) ^ ((nrow >> 1) & 7);
+      L.b_off[i] = (uint32_t)(((n0 + nrow) * p.ldb + 8 * c) * 2);
+    }
+  }
+  if (MODE == kSwiGLU && (L.w >> 1)) L.b_rs0 = L.b_rs1;     // sub-tile 1 holds the W3 columns
+
+  // ---- fragment addresses (element offsets inside a stage)
+  int a_rd[4], b_rd[4];
+  {
+    const int gq = lane >> 4, i16 = lane & 15;
+    const int sw = (l32 >> 1) & 7;
+    if (AT) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rb = 32 * (2 * i + wm);
+        const int q = rb >> 7, cl = rb & 127;
+        const int col = cl + 16 * (gq & 1) + 4 * (i16 & 3);
+        const int kr = 8 * (gq >> 1) + (i16 >> 2);
+        a_rd[i] = q * 8192 + kr * 128 + 8 * ((col >> 3) ^ (4 * (kr & 3))) + (col & 7);
+      }
+    } else {
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) a_rd[s2] = (32 * wm + l32) * 64 + 8 * ((2 * s2 + h) ^ sw);
+    }
+    if (BT) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int q = MODE == kSwiGLU ? j : wn;
+        const int cb = MODE == kSwiGLU ? (wn * 64 + 32 * pw) : (64 * pw + 32 * j);
+        const int col = cb + 16 * (gq & 1) + 4 * (i16 & 3);
+        const int kr = 8 * (gq >> 1) + (i16 >> 2);
+        b_rd[j] = q * 8192 + kr * 128 + 8 * ((col >> 3) ^ (4 * (kr & 3))) + (col & 7);
+      }
+      b_rd[2] = b_rd[3] = 0;
+    } else {
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2)
+        b_rd[s2] = (wn * 128 + 64 * pw + l32) * 64 + 8 * ((2 * s2 + h) ^ sw);
+    }
+  }
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nv = GK ? 4 : __builtin_amdgcn_readfirstlane(min(4, max(0, (tile_rows - 32 * wm + 63) / 64)));
+#define MOE_BWD_KLOOP(NV, D)                                                               \
+  do {                                                                                     \
+    uint4 fa0[4], fb0[2];                                                                  \
+    frags<NV, AT, BT>(S0, 0, a_rd, b_rd, fa0, fb0);                                        \
+    int kt = 0;                                                                            \
+    for (; kt + 2 <= kl; kt += 2) {                                                        \
+      kstep_body<NV, D, AT, BT>(S0, S0, S1, L, min(kt + 2, kl - 1), a_rd, b_rd, acc, fa0,  \
+                                fb0);                                                      \
+      kstep_body<NV, D, AT, BT>(S1, S1, S0, L, min(kt + 3, kl - 1), a_rd, b_rd, acc, fa0,  \
+                                fb0);                                                      \
+    }                                                                                      \
+    if (kt < kl)                                                                           \
+      kstep_body<NV, D, AT, BT>(S0, S0, S1, L, min(kt + 2, kl - 1), a_rd, b_rd, acc, fa0,  \
+                                fb0);                                                      \
+  } while (0)
+  if (kl > 0) {
+    if (pw == 0) {
+      issue(S0, L, 0);
+      issue(S1, L, min(1, kl - 1));
+      asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      switch (nv) {
+        case 4: MOE_BWD_KLOOP(4, true); break;
+        case 3: MOE_BWD_KLOOP(3, true); break;
+        case 2: MOE_BWD_KLOOP(2, true); break;
+        case 1: MOE_BWD_KLOOP(1, true); break;
+        default: MOE_BWD_KLOOP(0, true); break;
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0): no LDS write in flight at exit
+    } else {
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      switch (nv) {
+        case 4: MOE_BWD_KLOOP(4, false); break;
+        case 3: MOE_BWD_KLOOP(3, false); break;
+        case 2: MOE_BWD_KLOOP(2, false); break;
+        case 1: MOE_BWD_KLOOP(1, false); break;
+        default: MOE_BWD_KLOOP(0, false); break;
+      }
+    }
+  }
+#undef MOE_BWD_KLOOP
+
+  // ---- epilogues.  acc[i][j][r]: tile row 32 (2i + wm) + 8 (r / 4) + 4h + r % 4.
+  if (MODE == kSwiGLU) {
+    uint16_t* dh = static_cast<uint16_t*>(p.dh);
+    uint16_t* act = static_cast<uint16_t*>(p.act);
+    const int col = n0 + wn * 64 + 32 * pw + l32;
+    const int f = p.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = r0 + 32 * (2 * i + wm) + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (row < rend) {
+          const float h1 = acc[i][0][r], h3 = acc[i][1][r];
+          const float g = p.da[(size_t)row * f + col];
+          const float s = __builtin_amdgcn_rcpf(1.f + __expf(-h1));
+          const float sl = h1 * s;
+          dh[(size_t)row * 2 * f + col] = f32_to_bf16(g * h3 * (s + sl * (1.f - s)));
+          dh[(size_t)row * 2 * f + f + col] = f32_to_bf16(g * sl);
+          act[(size_t)row * f + col] = f32_to_bf16(sl * h3);
+        }
+      }
+  } else if (MODE == kWGrad) {
+    const bool low = n0 < p.nsplit;
+    float* o = (low ? p.out0 : p.out1) + (size_t)e * p.o_estride;
+    const int cbase = (low ? n0 : n0 - p.nsplit) + wn * 128 + 64 * pw + l32;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + 32 * (2 * i + wm) + 8 * (r >> 2) + 4 * h + (r & 3);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) o[(size_t)row * p.ldo + cbase + 32 * j] = acc[i][j][r];
+      }
+  } else {
+    const int cbase = n0 + wn * 128 + 64 * pw + l32;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = r0 + 32 * (2 * i + wm) + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (row < rend) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) p.out0[(size_t)row * p.ldo + cbase + 32 * j] = acc[i][j][r];
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------- fp32 (VALU)
+// The same four steps on 64 x 64 tiles, one k element at a time from LDS.
+constexpr int kFB = 64, kFK = 16;
+
+template <int MODE>
+__global__ __launch_bounds__(256) void bwd_gemm_f32_kernel(Args p) {
+  constexpr bool GK = MODE == kWGrad;
+  __shared__ float As[kFK][kFB + 1];
+  __shared__ float B0[kFK][kFB + 1];
+  __shared__ float B1[kFK][kFB + 1];
+  const float* a = static_cast<const float*>(p.a);
+  const float* b0 = static_cast<const float*>(p.b0);
+  const float* b1 = static_cast<const float*>(p.b1);
+  int e, r0, rend, m0 = 0, depth;
+  const int nt = blockIdx.y;
+  if (GK) {
+    e = blockIdx.z;
+    m0 = blockIdx.x * kFB;
+    r0 = clamp_off(p.offsets, e, p.max_rows, 0);
+    rend = min(max(p.offsets[e + 1], r0), p.max_rows);
+    depth = (rend - r0 + kFK - 1) / kFK * kFK;
+  } else {
+    if (!find_tile(p.offsets, p.n_exp, blockIdx.x, kFB, p.max_rows, e, r0, rend)) return;
+    depth = p.K;
+  }
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int n0 = nt * kFB;
+  const size_t wexp = (size_t)e * p.b_estride;
+  float c0[4][4] = {}, c1[4][4] = {};
+  for (int k0 = 0; k0 < depth; k0 += kFK) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int item = tid + 256 * q;          // 64 x 16 items
+      const int mm = item >> 4, kk = item & 15;      // A: row mm, depth kk
+      const int kr = item >> 6, nn = item & 63;      // B: depth kr, column nn
+      const int kA = k0 + kk, kB = k0 + kr;
+      float av, bv0, bv1 = 0.f;
+      if (GK) {
+        av = r0 + kA < rend ? a[(size_t)(r0 + kA) * p.lda + m0 + mm] : 0.f;
+        bv0 = r0 + kB < rend ? b0[(size_t)(r0 + kB) * p.ldb + n0 + nn] : 0.f;
+      } else {
+        av = r0 + mm < rend ? a[(size_t)(r0 + mm) * p.lda + kA] : 0.f;
+        if (MODE == kSwiGLU) {
+          bv0 = b0[wexp + (size_t)kB * p.ldb + n0 + nn];
+          bv1 = b1[wexp + (size_t)kB * p.ldb + n0 + nn];
+        } else if (MODE == kDX) {
+          const int kf = p.ksplit * kBK;             // = f
+          bv0 = kB < kf ? b0[wexp + (size_t)(n0 + nn) * p.ldb + kB]
+                        : b1[wexp + (size_t)(n0 + nn) * p.ldb + kB - kf];
+        } else {
+          bv0 = b0[wexp + (size_t)(n0 + nn) * p.ldb + kB];
+        }
+      }
+      As[kk][mm] = av;
+      B0[kr][nn] = bv0;
+      B1[kr][nn] = bv1;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kFK; ++kk) {
+      float av[4], bv[4], bw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bv[j] = B0[kk][tx * 4 + j];
+        bw[j] = B1[kk][tx * 4 + j];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          c0[i][j] = fmaf(av[i], bv[j], c0[i][j]);
+          if (MODE == kSwiGLU) c1[i][j] = fmaf(av[i], bw[j], c1[i][j]);
+        }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int mloc = ty * 4 + i;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + tx * 4 + j;
+      if (GK) {
+        const bool low = n0 < p.nsplit;
+        float* o = (low ? p.out0 : p.out1) + (size_t)e * p.o_estride;
+        o[(size_t)(m0 + mloc) * p.ldo + (low ? col : col - p.nsplit)] = c0[i][j];
+        continue;
+      }
+      const int row = r0 + mloc;
+      if (row >= rend) continue;
+      if (MODE == kSwiGLU) {
+        const int f = p.f;
+        const float h1 = c0[i][j], h3 = c1[i][j];
+        const float g = p.da[(size_t)row * f + col];
+        const float s = 1.f / (1.f + expf(-h1));
+        const float sl = h1 * s;
+        float* dh = static_cast<float*>(p.dh);
+        dh[(size_t)row * 2 * f + col] = g * h3 * (s + sl * (1.f - s));
+        dh[(size_t)row * 2 * f + f + col] = g * sl;
+        static_cast<float*>(p.act)[(size_t)row * f + col] = sl * h3;
+      } else {
+        p.out0[(size_t)row * p.ldo + col] = c0[i][j];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- combine backward
+// One wave per token: g[r] = w * dy[t] and dgate[t, j] = <dy[t], y_perm[r]>
+// (a fixed butterfly sum), 0 for dropped slots.
+template <bool BF16>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(const void* __restrict__ dy,
+                                                          const float* __restrict__ y_perm,
+                                                          const int32_t* __restrict__ slot_row,
+                                                          const float* __restrict__ topk_w, int T,
+                                                          int d, int k, void* __restrict__ g,
+                                                          float* __restrict__ dgate) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T) return;
+  for (int j = 0; j < k; ++j) {
+    const int r = slot_row[(size_t)t * k + j];
+    if (r < 0) {
+      if (lane == 0) dgate[(size_t)t * k + j] = 0.f;
+      continue;
+    }
+    const float w = topk_w[(size_t)t * k + j];
+    float dot = 0.f;
+    for (int c = 8 * lane; c < d; c += 512) {
+      float v[8];
+      if (BF16) {
+        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(dy) + (size_t)t * d + c);
+        v[0] = bf16lo(u.x); v[1] = bf16hi(u.x); v[2] = bf16lo(u.y); v[3] = bf16hi(u.y);
+        v[4] = bf16lo(u.z); v[5] = bf16hi(u.z); v[6] = bf16lo(u.w); v[7] = bf16hi(u.w);
+      } else {
+        const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(dy) + (size_t)t * d + c);
+        const float4 x0 = src[0], x1 = src[1];
+        v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+        v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+      }
+      const float4* yp = reinterpret_cast<const float4*>(y_perm + (size_t)r * d + c);
+      const float4 y0 = yp[0], y1 = yp[1];
+      dot = fmaf(v[0], y0.x, dot); dot = fmaf(v[1], y0.y, dot);
+      dot = fmaf(v[2], y0.z, dot); dot = fmaf(v[3], y0.w, dot);
+      dot = fmaf(v[4], y1.x, dot); dot = fmaf(v[5], y1.y, dot);
+      dot = fmaf(v[6], y1.z, dot); dot = fmaf(v[7], y1.w, dot);
+      if (BF16) {
+        const uint4 pk = make_uint4(pack_bf16x2(w * v[0], w * v[1]), pack_bf16x2(w * v[2], w * v[3]),
+                                    pack_bf16x2(w * v[4], w * v[5]), pack_bf16x2(w * v[6], w * v[7]));
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(g) + (size_t)r * d + c) = pk;
+      } else {
+        float4* dst = reinterpret_cast<float4*>(static_cast<float*>(g) + (size_t)r * d + c);
+        dst[0] = make_float4(w * v[0], w * v[1], w * v[2], w * v[3]);
+        dst[1] = make_float4(w * v[4], w * v[5], w * v[6], w * v[7]);
+      }
+    }
+    dot = wave_sum(dot);
+    if (lane == 0) dgate[(size_t)t * k + j] = dot;
+  }
+}
+
+// ---------------------------------------------------------------- router backward
+// One thread per token: dlogit[t, :] =
+//   aux_coef * (N / T) * p[t, e] * (f_e - sum_m p[t, m] f_m)        (p = softmax of all N)
+//   + at each selected id i_j: w_j * (dgate_j - sum_m w_m dgate_m)   (softmax over k)
+__global__ __launch_bounds__(256) void router_dlogit_kernel(
+    const float* __restrict__ logits, const int32_t* __restrict__ topk_idx,
+    const float* __restrict__ topk_w, const int32_t* __restrict__ counts,
+    const float* __restrict__ dgate, float aux_coef, int T, int N, int k, float* __restrict__ dlog) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  const float* L = logits + (size_t)t * N;
+  float* D = dlog + (size_t)t * N;
+  if (aux_coef != 0.f) {
+    float m = L[0];
+    for (int e = 1; e < N; ++e) m = fmaxf(m, L[e]);
+    float z = 0.f, pf = 0.f;
+    const float inv_tk = 1.f / ((float)T * (float)k);
+    for (int e = 0; e < N; ++e) {
+      const float x = expf(L[e] - m);
+      z += x;
+      pf += x * ((float)counts[e] * inv_tk);
+    }
+    const float rz = 1.f / z;
+    pf *= rz;
+    const float scale = aux_coef * (float)N / (float)T;
+    for (int e = 0; e < N; ++e) {
+      const float pe = expf(L[e] - m) * rz;
+      D[e] = scale * pe * ((float)counts[e] * inv_tk - pf);
+    }
+  } else {
+    for (int e = 0; e < N; ++e) D[e] = 0.f;
+  }
+  float inner = 0.f;
+  for (int j = 0; j < k; ++j) inner = fmaf(topk_w[(size_t)t * k + j], dgate[(size_t)t * k + j], inner);
+  for (int j = 0; j < k; ++j) {
+    const int e = topk_idx[(size_t)t * k + j];
+    const float wj = topk_w[(size_t)t * k + j];
+    D[e] += wj * (dgate[(size_t)t * k + j] - inner);
+  }
+}
+
+// dhidden for 32 tokens x 256 columns per block: the router term
+// dlogit[t] W_router^T (W_router is [d, N]) plus the token's slot rows of dx.
+constexpr int kDxTok = 32;
+template <bool BF16>
+__global__ __launch_bounds__(256) void router_dx_kernel(
+    const void* __restrict__ w_router, const float* __restrict__ dlog,
+    const float* __restrict__ dx_perm, const int32_t* __restrict__ slot_row, int T, int d, int N,
+    int k, float* __restrict__ dhidden) {
+  extern __shared__ float sh[];          // [kDxTok][N] dlogit, then [kDxTok][k] slot rows
+  float* dl = sh;
+  int* sr = reinterpret_cast<int*>(sh + kDxTok * N);
+  const int t0 = blockIdx.y * kDxTok;
+  const int nt = min(kDxTok, T - t0);
+  for (int i = threadIdx.x; i < kDxTok * N; i += 256)
+    dl[i] = i < nt * N ? dlog[(size_t)t0 * N + i] : 0.f;
+  for (int i = threadIdx.x; i < kDxTok * k; i += 256)
+    sr[i] = i < nt * k ? slot_row[(size_t)t0 * k + i] : -1;
+  __syncthreads();
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= d) return;
+  float acc[kDxTok];
+#pragma unroll
+  for (int t = 0; t < kDxTok; ++t) acc[t] = 0.f;
+  for (int e = 0; e < N; ++e) {
+    const float wv = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(w_router)[(size_t)c * N + e])
+                          : static_cast<const float*>(w_router)[(size_t)c * N + e];
+#pragma unroll
+    for (int t = 0; t < kDxTok; ++t) acc[t] = fmaf(dl[t * N + e], wv, acc[t]);
+  }
+#pragma unroll
+  for (int t = 0; t < kDxTok; ++t) {
+    if (t < nt) {
+      float v = acc[t];
+      for (int j = 0; j < k; ++j) {
+        const int r = sr[t * k + j];
+        if (r >= 0) v += dx_perm[(size_t)r * d + c];
+      }
+      dhidden[(size_t)(t0 + t) * d + c] = v;
+    }
+  }
+}
+
+// Partial dW_router = hidden^T dlogit over one chunk of 64 tokens, for 256
+// columns and a group of up to 16 experts per block; the first column block
+// also writes the chunk's partial dbias.
+constexpr int kDwTok = 64, kDwE = 16;
+template <bool BF16>
+__global__ __launch_bounds__(256) void router_dw_kernel(const void* __restrict__ hidden,
+                                                        const float* __restrict__ dlog, int T,
+                                                        int d, int N, float* __restrict__ part_w,
+                                                        float* __restrict__ part_b) {
+  __shared__ float dl[kDwTok][kDwE];
+  const int chunk = blockIdx.y, eg = blockIdx.z * kDwE;
+  const int t0 = chunk * kDwTok, nt = min(kDwTok, T - t0);
+  const int ne = min(kDwE, N - eg);
+  for (int i = threadIdx.x; i < kDwTok * kDwE; i += 256) {
+    const int t = i / kDwE, e = i % kDwE;
+    dl[t][e] = (t < nt && e < ne) ? dlog[(size_t)(t0 + t) * N + eg + e] : 0.f;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0 && threadIdx.x < ne) {
+    float s = 0.f;
+    for (int t = 0; t < nt; ++t) s += dl[t][threadIdx.x];
+    part_b[(size_t)chunk * N + eg + threadIdx.x] = s;
+  }
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= d) return;
+  float acc[kDwE];
+#pragma unroll
+  for (int e = 0; e < kDwE; ++e) acc[e] = 0.f;
+  for (int t = 0; t < nt; ++t) {
+    const float hv = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(hidden)[(size_t)(t0 + t) * d + c])
+                          : static_cast<const float*>(hidden)[(size_t)(t0 + t) * d + c];
+#pragma unroll
+    for (int e = 0; e < kDwE; ++e) acc[e] = fmaf(hv, dl[t][e], acc[e]);
+  }
+  float* o = part_w + ((size_t)chunk * d + c) * N + eg;
+  for (int e = 0; e < ne; ++e) o[e] = acc[e];
+}
+
+// Sum of the chunk partials in chunk order (deterministic).
+__global__ __launch_bounds__(256) void router_dw_reduce_kernel(const float* __restrict__ part_w,
+                                                               const float* __restrict__ part_b,
+                                                               int n_chunks, int d, int N,
+                                                               float* __restrict__ dw,
+                                                               float* __restrict__ dbias) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t dn = (size_t)d * N;
+  if (i < dn) {
+    float s = 0.f;
+    for (int q = 0; q < n_chunks; ++q) s += part_w[(size_t)q * dn + i];
+    dw[i] = s;
+  }
+  if (dbias && i < (size_t)N) {
+    float s = 0.f;
+    for (int q = 0; q < n_chunks; ++q) s += part_b[(size_t)q * N + i];
+    dbias[i] = s;
+  }
+}
+
+static int round8(int x) { return (x + 7) & ~7; }
+static size_t pad256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+template <int MODE>
+static void gemm(const Args& a, bool bf16, hipStream_t stream) {
+  if (bf16) {
+    Args b = a;
+    b.n_tiles = a.Nn / (MODE == kSwiGLU ? kBN / 2 : kBN);
+    int grid;
+    if (MODE == kWGrad) {
+      grid = round8((a.M / kBM) * b.n_tiles * a.n_exp);
+    } else {
+      const int mt_bound = (a.max_rows + kBM - 1) / kBM + a.n_exp;
+      grid = round8(mt_bound * b.n_tiles);
+    }
+    hipLaunchKernelGGL(bwd_gemm_bf16_kernel<MODE>, dim3(grid), dim3(kThreads), 0, stream, b);
+  } else {
+    Args b = a;
+    b.n_tiles = a.Nn / kFB;
+    dim3 grid;
+    if (MODE == kWGrad) grid = dim3(a.M / kFB, b.n_tiles, a.n_exp);
+    else grid = dim3((a.max_rows + kFB - 1) / kFB + a.n_exp, b.n_tiles, 1);
+    hipLaunchKernelGGL(bwd_gemm_f32_kernel<MODE>, grid, dim3(256), 0, stream, b);
+  }
+}
+
+}  // namespace bwd
+
+size_t expert_backward_ws_bytes(int d, int f, int max_rows, bool bf16) {
+  (void)d;
+  const size_t rows = (size_t)max_rows, eb = bf16 ? 2 : 4;
+  return bwd::pad256(rows * f * 4) + bwd::pad256(rows * 2 * f * eb) + bwd::pad256(rows * f * eb);
+}
+
+hipError_t launch_combine_backward(const void* dy, const float* y_perm, const int32_t* slot_row,
+                                   const float* topk_w, int T, int d, int k, bool bf16,
+                                   void* g_perm, float* dgate, hipStream_t stream) {
+  const dim3 grid((T + 3) / 4);
+  if (bf16)
+    hipLaunchKernelGGL(bwd::combine_bwd_kernel<true>, grid, dim3(256), 0, stream, dy, y_perm,
+                       slot_row, topk_w, T, d, k, g_perm, dgate);
+  else
+    hipLaunchKernelGGL(bwd::combine_bwd_kernel<false>, grid, dim3(256), 0, stream, dy, y_perm,
+                       slot_row, topk_w, T, d, k, g_perm, dgate);
+  return hipGetLastError();
+}
+
+hipError_t launch_expert_backward(const void* x_perm, const void* g_perm, const int32_t* offsets,
+                                  const void* w1, const void* w3, const void* w2, int N, int d,
+                                  int f, int max_rows, bool bf16, float* dx_perm, float* dw1,
+                                  float* dw3, float* dw2, void* ws, hipStream_t stream) {
+  using namespace bwd;
+  const size_t rows = (size_t)max_rows, eb = bf16 ? 2 : 4;
+  char* base = static_cast<char*>(ws);
+  float* da = reinterpret_cast<float*>(base);
+  void* dh = base + pad256(rows * f * 4);
+  void* act = static_cast<char*>(dh) + pad256(rows * 2 * f * eb);
+  Args a{};
+  a.offsets = offsets;
+  a.n_exp = N;
+  a.max_rows = max_rows;
+
+  // da = g W2_e^T  ([rows, d] x [f, d]^T)
+  Args s = a;
+  s.a = g_perm; s.lda = d;
+  s.b0 = w2; s.b1 = w2; s.ldb = d; s.b_estride = (long long)f * d;
+  s.K = d; s.Nn = f; s.out0 = da; s.ldo = f;
+  gemm<kDA>(s, bf16, stream);
+
+  // recompute h1, h3 and form dh1, dh3, a
+  s = a;
+  s.a = x_perm; s.lda = d;
+  s.b0 = w1; s.b1 = w3; s.ldb = f; s.b_estride = (long long)d * f;
+  s.K = d; s.Nn = f; s.da = da; s.dh = dh; s.act = act; s.f = f;
+  gemm<kSwiGLU>(s, bf16, stream);
+
+  // dx = [dh1 | dh3] [W1_e | W3_e]^T  ([rows, 2f] x [d, 2f]^T)
+  s = a;
+  s.a = dh; s.lda = 2 * f;
+  s.b0 = w1; s.b1 = w3; s.ldb = f; s.b_estride = (long long)d * f;
+  s.K = 2 * f; s.ksplit = f / kBK; s.Nn = d; s.out0 = dx_perm; s.ldo = d;
+  gemm<kDX>(s, bf16, stream);
+
+  // dW2_e = a_e^T g_e  ([f, rows] x [rows, d])
+  s = a;
+  s.a = act; s.lda = f;
+  s.b0 = g_perm; s.b1 = g_perm; s.ldb = d;
+  s.M = f; s.Nn = d; s.out0 = dw2; s.out1 = dw2; s.ldo = d; s.nsplit = d;
+  s.o_estride = (long long)f * d;
+  gemm<kWGrad>(s, bf16, stream);
+
+  // [dW1_e | dW3_e] = x_e^T [dh1_e | dh3_e]  ([d, rows] x [rows, 2f])
+  s = a;
+  s.a = x_perm; s.lda = d;
+  s.b0 = dh; s.b1 = dh; s.ldb = 2 * f;
+  s.M = d; s.Nn = 2 * f; s.out0 = dw1; s.out1 = dw3; s.ldo = f; s.nsplit = f;
+  s.o_estride = (long long)d * f;
+  gemm<kWGrad>(s, bf16, stream);
+  return hipGetLastError();
+}
+
+size_t router_backward_ws_bytes(int T, int d, int N) {
+  const size_t chunks = (size_t)(T + bwd::kDwTok - 1) / bwd::kDwTok;
+  return bwd::pad256((size_t)T * N * 4) + bwd::pad256(chunks * d * N * 4) +
+         bwd::pad256(chunks * N * 4);
+}
+
+hipError_t launch_router_backward(const void* hidden, const void* w_router, const float* logits,
+                                  const int32_t* topk_idx, const float* topk_w,
+                                  const int32_t* counts, const float* dgate, const float* dx_perm,
+                                  const int32_t* slot_row, float aux_coef, int T, int d, int N,
+                                  int k, bool bf16, float* dhidden, float* dw_router, float* dbias,
+                                  void* ws, hipStream_t stream) {
+  using namespace bwd;
+  const int chunks = (T + kDwTok - 1) / kDwTok;
+  char* base = static_cast<char*>(ws);
+  float* dlog = reinterpret_cast<float*>(base);
+  float* part_w = reinterpret_cast<float*>(base + pad256((size_t)T * N * 4));
+  float* part_b = reinterpret_cast<float*>(reinterpret_cast<char*>(part_w) +
+                                           pad256((size_t)chunks * d * N * 4));
+  hipLaunchKernelGGL(router_dlogit_kernel, dim3((T + 255) / 256), dim3(256), 0, stream, logits,
+                     topk_idx, topk_w, counts, dgate, aux_coef, T, N, k, dlog);
+  const dim3 gx((d + 255) / 256, (T + kDxTok - 1) / kDxTok);
+  const size_t shx = (size_t)kDxTok * (N + k) * 4;
+  if (bf16)
+    hipLaunchKernelGGL(router_dx_kernel<true>, gx, dim3(256), shx, stream, w_router, dlog, dx_perm,
+                       slot_row, T, d, N, k, dhidden);
+  else
+    hipLaunchKernelGGL(router_dx_kernel<false>, gx, dim3(256), shx, stream, w_router, dlog,
+                       dx_perm, slot_row, T, d, N, k, dhidden);
+  const dim3 gw((d + 255) / 256, chunks, (N + kDwE - 1) / kDwE);
+  if (bf16)
+    hipLaunchKernelGGL(router_dw_kernel<true>, gw, dim3(256), 0, stream, hidden, dlog, T, d, N,
+                       part_w, part_b);
+  else
+    hipLaunchKernelGGL(router_dw_kernel<false>, gw, dim3(256), 0, stream, hidden, dlog, T, d, N,
+                       part_w, part_b);
+  const size_t dn = (size_t)d * N;
+  hipLaunchKernelGGL(router_dw_reduce_kernel, dim3((unsigned)((dn + 255) / 256)), dim3(256), 0,
+                     stream, part_w, part_b, chunks, d, N, dw_router, dbias);
+  return hipGetLastError();
+}
+
+}  // namespace moe

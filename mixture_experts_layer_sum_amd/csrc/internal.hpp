@@ -52,4 +52,20 @@ size_t aux_ws_bytes(int T, int N);
 hipError_t launch_aux(const float* logits, const int32_t* counts, int T, int N, int k, float* aux,
                       void* ws, hipStream_t stream);
 
+hipError_t launch_combine_backward(const void* dy, const float* y_perm, const int32_t* slot_row,
+                                   const float* topk_w, int T, int d, int k, bool bf16,
+                                   void* g_perm, float* dgate, hipStream_t stream);
+size_t expert_backward_ws_bytes(int d, int f, int max_rows, bool bf16);
+hipError_t launch_expert_backward(const void* x_perm, const void* g_perm, const int32_t* offsets,
+                                  const void* w1, const void* w3, const void* w2, int N, int d,
+                                  int f, int max_rows, bool bf16, float* dx_perm, float* dw1,
+                                  float* dw3, float* dw2, void* ws, hipStream_t stream);
+size_t router_backward_ws_bytes(int T, int d, int N);
+hipError_t launch_router_backward(const void* hidden, const void* w_router, const float* logits,
+                                  const int32_t* topk_idx, const float* topk_w,
+                                  const int32_t* counts, const float* dgate, const float* dx_perm,
+                                  const int32_t* slot_row, float aux_coef, int T, int d, int N,
+                                  int k, bool bf16, float* dhidden, float* dw_router, float* dbias,
+                                  void* ws, hipStream_t stream);
+
 }  // namespace moe

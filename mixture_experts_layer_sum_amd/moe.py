@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
 (MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_EXPERT_FFN, MOE_OP_COMBINE, MOE_OP_AUX_LOSS,
- MOE_OP_EXPERT_DOWN, MOE_OP_PERMUTE_REROUTE) = range(7)
+ MOE_OP_EXPERT_DOWN, MOE_OP_PERMUTE_REROUTE, MOE_OP_EXPERT_BACKWARD,
+ MOE_OP_ROUTER_BACKWARD) = range(9)
 
 # Every symbol include/moe.h declares, with (restype, argtypes).
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -38,6 +39,11 @@ SIGNATURES = {
     "moe_expert_down_fp8": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "moe_combine": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "moe_aux_loss": (_I, [_P, _P, _I, _I, _I, _P, _P, _Z, _P]),
+    "moe_combine_backward": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
+    "moe_expert_backward": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P,
+                                 _Z, _P]),
+    "moe_router_backward": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _F, _I, _I, _I, _I, _I, _P,
+                                 _P, _P, _P, _Z, _P]),
 }
 
 
@@ -323,3 +329,97 @@ def moe_forward(hidden, w_router, w1, w3, w2, k, capacity_factor=0.0, bias=None,
     moe_combine(b.y_perm, b.slot_row, b.topk_w, hidden.dtype, b.y, y_shared, stream)
     moe_aux_loss(b.logits, b.counts, k, b.aux, b.ws_aux, stream)
     return b
+
+
+# ---------------------------------------------------------------- backward
+def moe_combine_backward(dy, y_perm, slot_row, topk_w, g_perm=None, dgate=None, stream=None):
+    T, d = dy.shape
+    k = slot_row.shape[1]
+    g_perm = _empty((y_perm.shape[0], d), dy.dtype, dy.device, g_perm)
+    dgate = _empty((T, k), torch.float32, dy.device, dgate)
+    _check(_lib.moe_combine_backward(_ptr(dy), _ptr(y_perm), _ptr(slot_row), _ptr(topk_w), T, d, k,
+                                     _dt(dy), _ptr(g_perm), _ptr(dgate), _stream(stream)),
+           "moe_combine_backward")
+    return g_perm, dgate
+
+
+def moe_expert_backward(x_perm, g_perm, offsets, w1, w3, w2, dx_perm=None, dw1=None, dw3=None,
+                        dw2=None, ws=None, stream=None):
+    max_rows, d = x_perm.shape
+    N, _, f = w1.shape
+    dev = x_perm.device
+    dx_perm = _empty((max_rows, d), torch.float32, dev, dx_perm)
+    dw1 = _empty((N, d, f), torch.float32, dev, dw1)
+    dw3 = _empty((N, d, f), torch.float32, dev, dw3)
+    dw2 = _empty((N, f, d), torch.float32, dev, dw2)
+    if ws is None:
+        ws = torch.empty(max(1, workspace_size(MOE_OP_EXPERT_BACKWARD, max_rows, d, N, 1, f,
+                                               x_perm.dtype)), dtype=torch.uint8, device=dev)
+    _check(_lib.moe_expert_backward(_ptr(x_perm), _ptr(g_perm), _ptr(offsets), _ptr(w1), _ptr(w3),
+                                    _ptr(w2), N, d, f, max_rows, _dt(x_perm), _ptr(dx_perm),
+                                    _ptr(dw1), _ptr(dw3), _ptr(dw2), _ptr(ws), ws.numel(),
+                                    _stream(stream)), "moe_expert_backward")
+    return dx_perm, dw1, dw3, dw2
+
+
+def moe_router_backward(hidden, w_router, logits, topk_idx, topk_w, counts, dgate, dx_perm,
+                        slot_row, aux_coef=0.0, dhidden=None, dw_router=None, dbias=None,
+                        want_dbias=True, ws=None, stream=None):
+    T, d = hidden.shape
+    N = w_router.shape[1]
+    k = topk_idx.shape[1]
+    dev = hidden.device
+    dhidden = _empty((T, d), torch.float32, dev, dhidden)
+    dw_router = _empty((d, N), torch.float32, dev, dw_router)
+    if want_dbias:
+        dbias = _empty((N,), torch.float32, dev, dbias)
+    if ws is None:
+        ws = torch.empty(max(1, workspace_size(MOE_OP_ROUTER_BACKWARD, T, d, N, k, 1,
+                                               hidden.dtype)), dtype=torch.uint8, device=dev)
+    _check(_lib.moe_router_backward(_ptr(hidden), _ptr(w_router), _ptr(logits), _ptr(topk_idx),
+                                    _ptr(topk_w), _ptr(counts), _ptr(dgate), _ptr(dx_perm),
+                                    _ptr(slot_row), float(aux_coef), T, d, N, k, _dt(hidden),
+                                    _ptr(dhidden), _ptr(dw_router),
+                                    _ptr(dbias) if want_dbias else None, _ptr(ws), ws.numel(),
+                                    _stream(stream)), "moe_router_backward")
+    return dhidden, dw_router, (dbias if want_dbias else None)
+
+
+class MoEGradBuffers:
+    """Every gradient and workspace of one layer backward, allocated once (fp32 gradients)."""
+
+    def __init__(self, T, d, N, k, f, dtype, device="cuda"):
+        e = lambda shape, dt: torch.empty(shape, dtype=dt, device=device)  # noqa: E731
+        self.g_perm = e((T * k, d), dtype)
+        self.dgate = e((T, k), torch.float32)
+        self.dx_perm = e((T * k, d), torch.float32)
+        self.dw1 = e((N, d, f), torch.float32)
+        self.dw3 = e((N, d, f), torch.float32)
+        self.dw2 = e((N, f, d), torch.float32)
+        self.dhidden = e((T, d), torch.float32)
+        self.dw_router = e((d, N), torch.float32)
+        self.dbias = e((N,), torch.float32)
+        self.ws_expert = e((max(1, workspace_size(MOE_OP_EXPERT_BACKWARD, T, d, N, k, f, dtype)),),
+                           torch.uint8)
+        self.ws_router = e((max(1, workspace_size(MOE_OP_ROUTER_BACKWARD, T, d, N, k, f, dtype)),),
+                           torch.uint8)
+
+
+def moe_backward(hidden, w_router, w1, w3, w2, dy, fwd: MoEBuffers, aux_coef=0.0,
+                 grads: Optional[MoEGradBuffers] = None, want_dbias=True, stream=None):
+    """Gradients of <dy, y> + aux_coef * aux for the batch `fwd` holds (moe_forward's
+    buffers of the same call).  Returns the MoEGradBuffers (dhidden, dw_router, dbias,
+    dw1, dw3, dw2 in fp32)."""
+    T, d = hidden.shape
+    N, _, f = w1.shape
+    k = fwd.topk_idx.shape[1]
+    if grads is None:
+        grads = MoEGradBuffers(T, d, N, k, f, hidden.dtype, hidden.device)
+    g = grads
+    moe_combine_backward(dy, fwd.y_perm, fwd.slot_row, fwd.topk_w, g.g_perm, g.dgate, stream)
+    moe_expert_backward(fwd.x_perm, g.g_perm, fwd.offsets, w1, w3, w2, g.dx_perm, g.dw1, g.dw3,
+                        g.dw2, g.ws_expert, stream)
+    moe_router_backward(hidden, w_router, fwd.logits, fwd.topk_idx, fwd.topk_w, fwd.counts,
+                        g.dgate, g.dx_perm, fwd.slot_row, aux_coef, g.dhidden, g.dw_router,
+                        g.dbias, want_dbias, g.ws_router, stream)
+    return g

@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the MoE layer forward.
+"""Seeded synthetic inputs for the MoE layer forward and backward.
 
 This module only draws random numbers and rounds them to the storage dtype;
 it holds none of the layer's arithmetic.  Both the HIP path (through the
@@ -16,6 +16,7 @@ drawn in parallel and any block can be regenerated on its own):
   ``w1s[s] [d, fs]``, ``w3s[s] [d, fs]`` ~ N(0, 1) / sqrt(d), streams
   ``[seed, 5, s]``, ``[seed, 6, s]``; ``w2s[s] [fs, d]`` ~ N(0, 1) / sqrt(fs),
   stream ``[seed, 7, s]``
+* backward: the output gradient ``dy [T, d]`` ~ N(0, 1), stream ``[seed, 8]``
 
 Normals are drawn as float32, scaled in float32, and for bf16 workloads
 rounded to bfloat16 with round-to-nearest-even (the bit patterns are kept as
@@ -40,7 +41,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "MoEInputs", "make_inputs", "make_workload_inputs",
-    "bf16_bits_to_f32", "f32_to_bf16_bits", "zipf_bias",
+    "bf16_bits_to_f32", "f32_to_bf16_bits", "zipf_bias", "make_dy",
 ]
 
 
@@ -174,6 +175,12 @@ def make_inputs(T, d, N, k, f, dtype="bf16", capacity_factor=0.0, seed=0,
         inp.w3s = np.stack([_draw([seed, 6, q], (d, fs), sd, dtype) for q in range(n_shared)])
         inp.w2s = np.stack([_draw([seed, 7, q], (fs, d), ss, dtype) for q in range(n_shared)])
     return inp
+
+
+def make_dy(T: int, d: int, dtype: str = "bf16", seed: int = 0) -> np.ndarray:
+    """The output gradient of a backward pass (recipe in the module docstring);
+    bf16 bit patterns as uint16 for bf16, else float32."""
+    return _draw([seed, 8], (T, d), 1.0, dtype)
 
 
 def make_workload_inputs(key: str, seed: int = 0, n_shared: int = 0,

@@ -74,7 +74,7 @@ __all__ = [
     "router_logits", "select_topk", "gate_weights", "expert_counts", "capacity",
     "dispatch", "dispatch_reroute", "silu", "swiglu_ffn", "aux_loss", "moe_forward",
     "moe_forward_per_token", "e4m3_decode", "e4m3_encode", "quantize_fp8_columns",
-    "dequantize_fp8_columns", "moe_backward",
+    "dequantize_fp8_columns", "swiglu_backward", "moe_backward", "moe_backward_sampled",
 ]
 
 
@@ -431,39 +431,94 @@ def moe_forward_per_token(hidden, w_router, w1, w3, w2, k: int, capacity_factor:
     return y
 
 
+def swiglu_backward(X, G, W1, W3, W2, cols=None) -> dict:
+    """One expert's SwiGLU FFN backward for rows X [n, d] whose output gradient is G [n, d].
+
+    h1 = X W1, h3 = X W3, s = sigmoid(h1), a = h1 s h3 (= silu(h1) * h3), y = a W2;
+    da = G W2^T;  dh3 = da * h1 s;  dh1 = da * h3 * (s + h1 s (1 - s))  (silu'(z) = s + z s (1 - s));
+    dW1 = X^T dh1, dW3 = X^T dh3, dW2 = a^T G, dX = dh1 W1^T + dh3 W3^T.
+    With ``cols`` (indices into f) only dW1[:, cols], dW3[:, cols] and dW2[cols, :] are
+    formed: every step above is local to a column of f, so they equal the same entries of
+    the full result.  Without ``cols`` dX and y are returned as well.
+    """
+    X = np.asarray(X, np.float64)
+    G = np.asarray(G, np.float64)
+    c = slice(None) if cols is None else np.asarray(cols)
+    W1c = np.asarray(np.asarray(W1)[:, c], np.float64)
+    W3c = np.asarray(np.asarray(W3)[:, c], np.float64)
+    W2c = np.asarray(np.asarray(W2)[c, :], np.float64)
+    h1, h3 = X @ W1c, X @ W3c
+    s = 1.0 / (1.0 + np.exp(-h1))
+    a = h1 * s * h3
+    da = G @ W2c.T
+    dh3 = da * (h1 * s)
+    dh1 = da * h3 * (s + h1 * s * (1.0 - s))
+    out = {"dw1": X.T @ dh1, "dw3": X.T @ dh3, "dw2": a.T @ G}
+    if cols is None:
+        out["dx"] = dh1 @ W1c.T + dh3 @ W3c.T
+        out["y"] = a @ W2c
+    return out
+
+
+def _routing(hidden, w_router, k, capacity_factor, bias, overflow):
+    L = router_logits(hidden, w_router, bias)
+    T, N = L.shape
+    idx = select_topk(L, k)
+    w = gate_weights(L, idx)
+    counts = expert_counts(idx, N)
+    C = capacity(T, k, N, capacity_factor)
+    if overflow == "drop":
+        disp = dispatch(idx, N, C)
+    elif overflow == "reroute":
+        disp = dispatch_reroute(idx, L, N, C)
+    else:
+        raise ValueError(f"unknown overflow policy {overflow!r}")
+    slot_row, offsets = disp["slot_row"], disp["offsets"]
+    A = int(offsets[-1])
+    row_tok = np.empty(A, np.int64)
+    row_j = np.empty(A, np.int64)
+    for t in range(T):
+        for j in range(k):
+            r = slot_row[t, j]
+            if r >= 0:
+                row_tok[r], row_j[r] = t, j
+    return {"L": L, "idx": idx, "w": w, "counts": counts, "slot_row": slot_row,
+            "offsets": offsets, "row_tok": row_tok, "row_j": row_j, "N": N, "T": T}
+
+
+def _dlogits(L, idx, w, dgate, counts, T, k, aux_coef):
+    """Logit gradient of the rows given: softmax over the k selected logits, plus
+    aux_coef times d aux / d logits = (N / T) p (f - sum_m p_m f_m), p = softmax of all N."""
+    n, N = L.shape
+    dlog = np.zeros((n, N))
+    inner = np.sum(w * dgate, axis=1, keepdims=True)
+    np.put_along_axis(dlog, idx, w * (dgate - inner), axis=1)
+    if aux_coef != 0.0:
+        p = np.exp(L - L.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        fe = counts.astype(np.float64) / float(T * k)
+        dlog += aux_coef * (N / T) * p * (fe[None, :] - np.sum(p * fe[None, :], axis=1, keepdims=True))
+    return dlog
+
+
 def moe_backward(hidden, w_router, w1, w3, w2, k: int, dy, capacity_factor: float = 0.0,
                  bias=None, aux_coef: float = 0.0, overflow: str = "drop") -> dict:
     """Gradients of L = sum(dy * y) + aux_coef * aux (float64, from the definitions).
 
-    Per kept slot (t, j) at expert e with gate weight w and row x = hidden[t]:
-      g = w * dy[t] is the gradient reaching the expert's output;
-      h1 = x W1_e, h3 = x W3_e, a = silu(h1) * h3;
-      dW2_e += a^T g;  da = g W2_e^T;
-      dh3 = da * silu(h1);  dh1 = da * h3 * silu'(h1),
-      silu'(z) = s + z s (1 - s) with s = sigmoid(z);
-      dW1_e += x^T dh1;  dW3_e += x^T dh3;  dhidden[t] += dh1 W1_e^T + dh3 W3_e^T;
-      dgate[t, j] = <dy[t], FFN_e(x)>.
+    Per kept slot (t, j) at expert e with gate weight w: g = w * dy[t] is the gradient
+    reaching the expert's output (:func:`swiglu_backward` for the expert's rows gives
+    dW1_e, dW3_e, dW2_e and each row's dX), and dgate[t, j] = <dy[t], FFN_e(x_t)>.
     Softmax over the selected logits: dlogit[t, i_j] = w_j (dgate_j - sum_m w_m dgate_m).
     Aux loss: d aux / d logits[t, e] = (N / T) p_te (f_e - sum_m p_tm f_m), p = full softmax.
-    Router: dW_router = hidden^T dlogits, dbias = sum_t dlogits, dhidden += dlogits W_router^T.
+    Router: dW_router = hidden^T dlogits, dbias = sum_t dlogits,
+    dhidden[t] = sum of its slots' dX rows + dlogits[t] W_router^T.
     """
     hidden = np.asarray(hidden, np.float64)
     T, d = hidden.shape
     dy = np.asarray(dy, np.float64)
     Wr = np.asarray(w_router, np.float64)
-    L = router_logits(hidden, w_router, bias)
-    N = L.shape[1]
-    idx = select_topk(L, k)
-    w = gate_weights(L, idx)
-    counts = expert_counts(idx, N)
-    C = capacity(T, k, N, capacity_factor)
-    disp = dispatch(idx, N, C) if overflow == "drop" else dispatch_reroute(idx, L, N, C)
-    slot_row, offsets, perm_src = disp["slot_row"], disp["offsets"], disp["perm_src"]
-    row_slot = {}
-    for t in range(T):
-        for j in range(k):
-            if slot_row[t, j] >= 0:
-                row_slot[int(slot_row[t, j])] = (t, j)
+    R = _routing(hidden, w_router, k, capacity_factor, bias, overflow)
+    N, offsets = R["N"], R["offsets"]
     f = np.asarray(w1[0]).shape[1]
     dW1 = np.zeros((N, d, f))
     dW3 = np.zeros((N, d, f))
@@ -474,39 +529,62 @@ def moe_backward(hidden, w_router, w1, w3, w2, k: int, dy, capacity_factor: floa
         rows = np.arange(offsets[e], offsets[e + 1])
         if rows.size == 0:
             continue
-        W1 = np.asarray(w1[e], np.float64)
-        W3 = np.asarray(w3[e], np.float64)
-        W2 = np.asarray(w2[e], np.float64)
-        tj = [row_slot[int(r)] for r in rows]
-        tok = np.array([t for t, _ in tj])
-        slot = np.array([j for _, j in tj])
-        X = hidden[tok]
-        h1, h3 = X @ W1, X @ W3
-        s = 1.0 / (1.0 + np.exp(-h1))
-        a = h1 * s * h3
-        Y = a @ W2
-        gw = w[tok, slot][:, None]
-        G = gw * dy[tok]
-        dgate[tok, slot] = np.sum(dy[tok] * Y, axis=1)
-        dW2[e] = a.T @ G
-        da = G @ W2.T
-        dh3 = da * (h1 * s)
-        dh1 = da * h3 * (s + h1 * s * (1.0 - s))
-        dW1[e] = X.T @ dh1
-        dW3[e] = X.T @ dh3
-        np.add.at(dhidden, tok, dh1 @ W1.T + dh3 @ W3.T)
-    dlog = np.zeros((T, N))
-    wsel = np.take_along_axis(w, np.arange(k)[None, :].repeat(T, 0), 1)
-    inner = np.sum(wsel * dgate, axis=1, keepdims=True)
-    np.put_along_axis(dlog, idx, wsel * (dgate - inner), axis=1)
-    if aux_coef != 0.0:
-        m = L.max(axis=1, keepdims=True)
-        p = np.exp(L - m)
-        p /= p.sum(axis=1, keepdims=True)
-        fe = counts.astype(np.float64) / float(T * k)
-        dlog += aux_coef * (N / T) * p * (fe[None, :] - np.sum(p * fe[None, :], axis=1, keepdims=True))
+        tok, slot = R["row_tok"][rows], R["row_j"][rows]
+        G = R["w"][tok, slot][:, None] * dy[tok]
+        out = swiglu_backward(hidden[tok], G, w1[e], w3[e], w2[e])
+        dgate[tok, slot] = np.sum(dy[tok] * out["y"], axis=1)
+        dW1[e], dW3[e], dW2[e] = out["dw1"], out["dw3"], out["dw2"]
+        np.add.at(dhidden, tok, out["dx"])
+    dlog = _dlogits(R["L"], R["idx"], R["w"], dgate, R["counts"], T, k, aux_coef)
     dW_router = hidden.T @ dlog
     dbias = dlog.sum(axis=0)
     dhidden += dlog @ Wr.T
     return {"dhidden": dhidden, "dw_router": dW_router, "dbias": dbias, "dw1": dW1, "dw3": dW3,
-            "dw2": dW2, "dgate": dgate, "dlogits": dlog, "topk_idx": idx, "slot_row": slot_row}
+            "dw2": dW2, "dgate": dgate, "dlogits": dlog, "topk_idx": R["idx"],
+            "slot_row": R["slot_row"], "offsets": offsets}
+
+
+def moe_backward_sampled(hidden, w_router, w1, w3, w2, k: int, dy, capacity_factor: float = 0.0,
+                         bias=None, aux_coef: float = 0.0, overflow: str = "drop", tokens=(),
+                         expert_cols=()) -> dict:
+    """Entries of :func:`moe_backward` at sizes where the whole is too slow on a CPU.
+
+    Routing, counts and dispatch cover every token (they are cheap); then
+    * ``dhidden[t]`` for each t in ``tokens``: only the token's own slots are run
+      (dX and dgate are local to a row), plus its logit gradient;
+    * for each ``(e, cols)`` in ``expert_cols``: dW1_e[:, cols], dW3_e[:, cols] and
+      dW2_e[cols, :] over all of expert e's rows (local to a column of f).
+    Returns {"dhidden": {t: [d]}, "dw": {(e, tuple(cols)): (dW1 cols, dW3 cols, dW2 rows)},
+    "topk_idx", "slot_row", "offsets"}.
+    """
+    hidden = np.asarray(hidden)
+    T, d = hidden.shape
+    dy = np.asarray(dy)
+    R = _routing(hidden, w_router, k, capacity_factor, bias, overflow)
+    offsets = R["offsets"]
+    Wr = np.asarray(w_router, np.float64)
+    res = {"dhidden": {}, "dw": {}, "topk_idx": R["idx"], "slot_row": R["slot_row"],
+           "offsets": offsets}
+    for t in tokens:
+        x = np.asarray(hidden[t], np.float64)[None]
+        g_dy = np.asarray(dy[t], np.float64)
+        acc = np.zeros(d)
+        dg = np.zeros((1, k))
+        for j in range(k):
+            r = R["slot_row"][t, j]
+            if r < 0:
+                continue
+            e = int(np.searchsorted(offsets, r, side="right") - 1)
+            out = swiglu_backward(x, R["w"][t, j] * g_dy[None], w1[e], w3[e], w2[e])
+            acc += out["dx"][0]
+            dg[0, j] = float(g_dy @ out["y"][0])
+        dl = _dlogits(R["L"][t:t + 1], R["idx"][t:t + 1], R["w"][t:t + 1], dg, R["counts"], T, k,
+                      aux_coef)
+        res["dhidden"][int(t)] = acc + (dl @ Wr.T)[0]
+    for e, cols in expert_cols:
+        rows = np.arange(offsets[e], offsets[e + 1])
+        tok, slot = R["row_tok"][rows], R["row_j"][rows]
+        G = R["w"][tok, slot][:, None] * np.asarray(dy[tok], np.float64)
+        out = swiglu_backward(np.asarray(hidden[tok], np.float64), G, w1[e], w3[e], w2[e], cols)
+        res["dw"][(int(e), tuple(int(c) for c in cols))] = (out["dw1"], out["dw3"], out["dw2"])
+    return res

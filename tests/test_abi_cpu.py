@@ -65,6 +65,16 @@ def test_workspace_sizes():
     assert lib.moe_workspace_size(moe.MOE_OP_AUX_LOSS, 256, 128, 8, 2, 256, F32) == 16 * 8 * 4
     assert lib.moe_workspace_size(moe.MOE_OP_AUX_LOSS, 65, 128, 8, 2, 256, F32) == 5 * 8 * 4
     assert lib.moe_workspace_size(17, 64, 128, 8, 2, 256, F32) == 0
+    # backward: da fp32 [rows, f], [dh1 | dh3] [rows, 2f] and a [rows, f] in the layer dtype
+    rows, f = 64 * 2, 256
+    assert lib.moe_workspace_size(moe.MOE_OP_EXPERT_BACKWARD, 64, 128, 8, 2, f, BF16) == \
+        rows * f * 4 + rows * 2 * f * 2 + rows * f * 2
+    assert lib.moe_workspace_size(moe.MOE_OP_EXPERT_BACKWARD, 64, 128, 8, 2, f, F32) == \
+        rows * f * 4 + rows * 2 * f * 4 + rows * f * 4
+    # router: dlogit [T, N], partial dW [ceil(T/64), d, N], partial dbias [ceil(T/64), N]
+    assert lib.moe_workspace_size(moe.MOE_OP_ROUTER_BACKWARD, 128, 256, 8, 2, 0, BF16) == \
+        128 * 8 * 4 + 2 * 256 * 8 * 4 + 256
+    assert lib.moe_workspace_size(moe.MOE_OP_ROUTER_BACKWARD, 128, 256, 300, 2, 0, BF16) == 0
     assert lib.moe_workspace_size(moe.MOE_OP_PERMUTE, 0, 128, 8, 2, 256, F32) == 0
 
 
@@ -190,3 +200,40 @@ def test_aux_rejects(args, status):
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(ImportError):
         moe.load_library(str(tmp_path / "nope.so"))
+
+
+def test_backward_entry_points_reject():
+    # combine backward: null output, k = 0, d not a multiple of 64, unknown dtype
+    assert lib.moe_combine_backward(P, P, P, P, 64, 128, 2, BF16, NUL, P, S) == INV
+    assert lib.moe_combine_backward(P, P, P, P, 64, 128, 0, BF16, P, P, S) == INV
+    assert lib.moe_combine_backward(P, P, P, P, 64, 100, 2, BF16, P, P, S) == UNS
+    assert lib.moe_combine_backward(P, P, P, P, 64, 128, 2, 7, P, P, S) == UNS
+    big = 1 << 40
+    # expert backward: null gradient output; bf16 f not a multiple of 256; too many rows x f;
+    # workspace too small; null workspace
+    assert lib.moe_expert_backward(P, P, P, P, P, P, 8, 256, 256, 64, BF16, P, NUL, P, P, P, big,
+                                   S) == INV
+    assert lib.moe_expert_backward(P, P, P, P, P, P, 8, 256, 384, 64, BF16, P, P, P, P, P, big,
+                                   S) == UNS
+    assert lib.moe_expert_backward(P, P, P, P, P, P, 8, 256, 16384, 1 << 15, BF16, P, P, P, P, P,
+                                   big, S) == UNS
+    assert lib.moe_expert_backward(P, P, P, P, P, P, 8, 256, 256, 64, BF16, P, P, P, P, P, 1000,
+                                   S) == WS
+    assert lib.moe_expert_backward(P, P, P, P, P, P, 8, 256, 256, 64, BF16, P, P, P, P, NUL, big,
+                                   S) == INV
+    # fp32 allows f a multiple of 64
+    ws = lib.moe_workspace_size(moe.MOE_OP_EXPERT_BACKWARD, 64, 128, 8, 1, 192, F32)
+    assert lib.moe_expert_backward(P, P, P, P, P, P, 8, 128, 192, 64, F32, P, P, P, P, P, ws - 1,
+                                   S) == WS
+    # router backward: null dgate; NaN coefficient; k > N; workspace too small; dbias may be NULL
+    args = [P, P, P, P, P, P, P, P, P, 0.01, 64, 128, 8, 2, BF16, P, P, NUL, P, big, S]
+    a = list(args); a[6] = NUL
+    assert lib.moe_router_backward(*a) == INV
+    a = list(args); a[9] = math.nan
+    assert lib.moe_router_backward(*a) == INV
+    a = list(args); a[13] = 9
+    assert lib.moe_router_backward(*a) == INV
+    a = list(args); a[19] = 100
+    assert lib.moe_router_backward(*a) == WS
+    a = list(args); a[18] = NUL
+    assert lib.moe_router_backward(*a) == INV

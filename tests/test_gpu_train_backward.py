@@ -1,0 +1,172 @@
+"""GPU parity of the backward pass: the HIP path through the C ABI against the
+oracle's gradients (oracle.moe_backward, fp64).
+
+Bar: for every gradient tensor, max |gpu - oracle| / max |oracle| <= 2e-2 for
+bf16 layers (the HIP path rounds g = w dy, dh1, dh3 and a to bf16 before the
+GEMMs that consume them, as the forward rounds its activations) and <= 1e-4 for
+fp32 layers; experts that receive no rows get weight gradients that are exactly
+zero; the routing the gradients are taken at is compared exactly first.
+"""
+import numpy as np
+import pytest
+
+from mixture_experts_layer_sum_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+GRAD_TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+@pytest.fixture(scope="module")
+def moe():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    from mixture_experts_layer_sum_amd import moe as m   # raises if the library is missing
+    return m
+
+
+def _dev(a, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _rel(gpu, ref):
+    den = float(np.abs(ref).max(initial=0.0))
+    err = float(np.abs(gpu - ref).max(initial=0.0))
+    return err / den if den > 0 else err
+
+
+def run_backward(moe, inp, coef, overflow="drop", label=""):
+    import oracle.moe_oracle as O
+    from tests import parity
+    parity.log(f"{label}: T={inp.T} d={inp.d} N={inp.N} k={inp.k} f={inp.f} {inp.dtype} "
+               f"cf={inp.capacity_factor} aux_coef={coef} overflow={overflow}")
+    dev = parity.to_device(inp)
+    g, b = parity.run_gpu(inp, dev, overflow=overflow)
+    dy = synth.make_dy(inp.T, inp.d, inp.dtype, seed=11)
+    gr = moe.moe_backward(dev["hidden"], dev["w_router"], dev["w1"], dev["w3"], dev["w2"],
+                          _dev(dy, inp.dtype), b, coef, want_dbias=inp.bias is not None)
+    torch.cuda.synchronize()
+    dyv = synth.bf16_bits_to_f32(dy) if inp.dtype == "bf16" else dy
+    ref = O.moe_backward(inp.values("hidden"), inp.values("w_router"),
+                         parity.ExpertView(inp, "w1"), parity.ExpertView(inp, "w3"),
+                         parity.ExpertView(inp, "w2"), inp.k, dyv, inp.capacity_factor, inp.bias,
+                         aux_coef=coef, overflow=overflow)
+    # the gradients are taken at one routing: it must be the oracle's
+    assert np.array_equal(g["topk_idx"], ref["topk_idx"]), f"{label}: routing differs"
+    assert np.array_equal(g["slot_row"], ref["slot_row"]), f"{label}: dispatch differs"
+    tol = GRAD_TOL[inp.dtype]
+    host = {"dhidden": gr.dhidden, "dw_router": gr.dw_router, "dw1": gr.dw1, "dw3": gr.dw3,
+            "dw2": gr.dw2, "dgate": gr.dgate}
+    if inp.bias is not None:
+        host["dbias"] = gr.dbias
+    rep = {}
+    for name, t in host.items():
+        got = t.cpu().numpy().astype(np.float64)
+        rel = _rel(got, ref[name])
+        rep[name] = rel
+        assert rel <= tol, f"{label}: {name} max rel err {rel:.3e} > {tol}"
+    # experts with no rows: weight gradients exactly zero
+    empty = np.where(np.diff(g["offsets"]) == 0)[0]
+    for e in empty:
+        for name in ("dw1", "dw3", "dw2"):
+            assert (host[name][e] == 0).all().item(), f"{label}: {name}[{e}] of an empty expert"
+    parity.log(f"{label}: rel errors {rep}; empty experts {empty.tolist()}")
+    return rep
+
+
+SMALL = [
+    # label, T, d, N, k, f, dtype, cf, bias, aux_coef, overflow
+    ("f32_tiny", 64, 128, 8, 2, 192, "f32", 0.0, None, 0.0, "drop"),
+    ("f32_drop_aux", 300, 128, 8, 2, 128, "f32", 1.0, "skew", 0.01, "drop"),
+    ("f32_k1", 77, 64, 4, 1, 64, "f32", 0.0, None, 0.5, "drop"),
+    ("bf16_ragged", 300, 256, 4, 2, 512, "bf16", 0.0, None, 0.0, "drop"),
+    ("bf16_drop_aux_bias", 1000, 512, 8, 2, 256, "bf16", 1.0, "skew", 0.01, "drop"),
+    ("bf16_empty_experts", 200, 256, 16, 2, 256, "bf16", 0.0, "hot", 0.1, "drop"),
+    ("bf16_reroute", 600, 256, 8, 2, 256, "bf16", 0.8, "skew", 0.01, "reroute"),
+    ("bf16_multi_tile_rows", 1500, 256, 2, 2, 256, "bf16", 0.0, None, 0.0, "drop"),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_backward_small(moe, case):
+    label, T, d, N, k, f, dt, cf, bias, coef, overflow = case
+    b = None
+    if bias == "skew":
+        b = np.zeros(N, np.float32)
+        b[:3] = [1.5, 1.0, 0.5]
+    elif bias == "hot":
+        b = np.full(N, -4.0, np.float32)
+        b[:4] = 2.0                        # experts 4.. get (almost) nothing
+    inp = synth.make_inputs(T, d, N, k, f, dt, cf, 0, bias=b)
+    run_backward(moe, inp, coef, overflow, label)
+
+
+def test_backward_is_deterministic(moe):
+    inp = synth.make_inputs(500, 256, 8, 2, 256, "bf16", 1.0, 3)
+    from tests import parity
+    dev = parity.to_device(inp)
+    outs = []
+    for _ in range(2):
+        _, b = parity.run_gpu(inp, dev)
+        dy = _dev(synth.make_dy(inp.T, inp.d, "bf16", 5), "bf16")
+        gr = moe.moe_backward(dev["hidden"], dev["w_router"], dev["w1"], dev["w3"], dev["w2"], dy,
+                              b, 0.01)
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (gr.dhidden, gr.dw_router, gr.dw1, gr.dw3, gr.dw2)])
+    for a, c in zip(*outs):
+        assert torch.equal(a, c)
+
+
+@pytest.mark.parametrize("key", ["mixtral", "skewed_zipf"])
+def test_backward_workload_full_size(moe, key):
+    """Full-size workload in the launch configuration the benchmark times: routing
+    exact for every token; dhidden on sampled tokens and dW1/dW3 columns and dW2 rows
+    of sampled experts from the oracle entry by entry; dW_router and dbias checked by
+    the softmax shift invariance (each token's logit gradient sums to zero)."""
+    import oracle.moe_oracle as O
+    from tests import parity
+    inp = synth.make_workload_inputs(key, seed=0)
+    coef = 0.01
+    parity.log(f"backward_{key}: forward + backward on the GPU")
+    dev = parity.to_device(inp)
+    g, b = parity.run_gpu(inp, dev)
+    dy = synth.make_dy(inp.T, inp.d, inp.dtype, seed=11)
+    gr = moe.moe_backward(dev["hidden"], dev["w_router"], dev["w1"], dev["w3"], dev["w2"],
+                          _dev(dy, inp.dtype), b, coef, want_dbias=inp.bias is not None)
+    torch.cuda.synchronize()
+    T, N, f = inp.T, inp.N, inp.f
+    toks = [0, 1, T // 2 + 1, T - 1]
+    rows = np.diff(g["offsets"])
+    busiest, idlest = int(rows.argmax()), int(rows.argmin())
+    ec = [(busiest, [0, 1, f // 2 + 3, f - 1]), (idlest, [5, f - 2])]
+    parity.log(f"backward_{key}: oracle on tokens {toks}, experts/columns {ec}, "
+               f"rows per expert {rows.min()}..{rows.max()}")
+    smp = O.moe_backward_sampled(inp.values("hidden"), inp.values("w_router"),
+                                 parity.ExpertView(inp, "w1"), parity.ExpertView(inp, "w3"),
+                                 parity.ExpertView(inp, "w2"), inp.k,
+                                 synth.bf16_bits_to_f32(dy), inp.capacity_factor, inp.bias,
+                                 aux_coef=coef, tokens=toks, expert_cols=ec)
+    assert np.array_equal(g["topk_idx"], smp["topk_idx"]), "routing differs"
+    assert np.array_equal(g["slot_row"], smp["slot_row"]), "dispatch differs"
+    tol = GRAD_TOL[inp.dtype]
+    dh = gr.dhidden[toks].cpu().numpy()
+    ref = np.stack([smp["dhidden"][t] for t in toks])
+    rep = {"dhidden": _rel(dh, ref)}
+    for e, cols in ec:
+        r1, r3, r2 = smp["dw"][(e, tuple(cols))]
+        rep[f"dw1[{e}]"] = _rel(gr.dw1[e][:, cols].cpu().numpy(), r1)
+        rep[f"dw3[{e}]"] = _rel(gr.dw3[e][:, cols].cpu().numpy(), r3)
+        rep[f"dw2[{e}]"] = _rel(gr.dw2[e][cols, :].cpu().numpy(), r2)
+    for name, rel in rep.items():
+        assert rel <= tol, f"backward_{key}: {name} max rel err {rel:.3e} > {tol}"
+    wr = gr.dw_router.cpu().numpy().astype(np.float64)
+    assert np.abs(wr).max() > 0
+    assert np.abs(wr.sum(1)).max() <= 1e-4 * np.abs(wr).max(), "dW_router rows do not sum to 0"
+    if inp.bias is not None:
+        db = gr.dbias.cpu().numpy().astype(np.float64)
+        assert abs(db.sum()) <= 1e-4 * np.abs(db).max()
+    parity.log(f"backward_{key}: rel errors {rep}")

@@ -746,23 +746,49 @@ def test_backward_pins_catch_planted_mistakes():
     """Plant a plausible mistake in a copy of the oracle's backward; the
     finite-difference pin must reject each."""
     import inspect
-    src = inspect.getsource(O.moe_backward)
+    fns = [O.swiglu_backward, O._dlogits, O.moe_backward]
+    srcs = {fn.__name__: inspect.getsource(fn) for fn in fns}
     mistakes = [
         ("s + h1 * s * (1.0 - s)", "s"),                       # silu' without its second term
-        ("wsel * (dgate - inner)", "wsel * dgate"),            # softmax Jacobian without the mean
+        ("w * (dgate - inner)", "w * dgate"),                  # softmax Jacobian without the mean
         ("(fe[None, :] - np.sum", "(fe[None, :] + np.sum"),    # aux gradient sign
-        ("dW2[e] = a.T @ G", "dW2[e] = a.T @ dy[tok]"),        # gate weight left out of dW2
+        ('"dw2": a.T @ G', '"dw2": (h1 * h3).T @ G'),          # dW2 from h1 h3 instead of silu(h1) h3
         ("dhidden += dlog @ Wr.T", "pass"),                    # router path into dhidden dropped
+        ("dh3 = da * (h1 * s)", "dh3 = da * h1"),              # dh3 without the sigmoid
     ]
     inp = synth.make_inputs(10, 6, 4, 2, 5, "f32", 0.8, 1,
                             bias=np.array([0.5, 0.0, -0.3, 0.2], np.float32))
     dy = np.random.default_rng(101).standard_normal((10, 6))
     for old, new in mistakes:
-        assert old in src, old
+        hits = [n for n, src in srcs.items() if old in src]
+        assert len(hits) == 1, old
         ns = dict(vars(O))
-        exec(compile(src.replace(old, new), "<mutant>", "exec"), ns)
+        for n, src in srcs.items():
+            exec(compile(src.replace(old, new) if n == hits[0] else src, "<mutant>", "exec"), ns)
 
         class M:
             moe_backward = staticmethod(ns["moe_backward"])
         g = _backward(inp, 2, 0.8, dy, 0.37, "drop", mod=M)
         assert _fd_agrees(inp, 2, 0.8, dy, 0.37, "drop", g) > 1e-3, old
+
+
+@pytest.mark.parametrize("overflow,cf,coef", [("drop", 1.0, 0.2), ("reroute", 0.8, 0.05)])
+def test_backward_sampled_entries_equal_the_full_backward(overflow, cf, coef):
+    """The row- and column-local entries the full-size tests use are the same
+    numbers as the (finite-difference pinned) full backward."""
+    inp = _rand(T=40, d=8, N=4, k=2, f=12, seed=9, cf=cf,
+                bias=np.array([0.8, 0.2, 0.0, -0.5], np.float32))
+    dy = np.random.default_rng(12).standard_normal((40, 8))
+    full = _backward(inp, 2, cf, dy, coef, overflow)
+    toks = [0, 7, 39]
+    ec = [(0, [0, 5, 11]), (3, [2])]
+    smp = O.moe_backward_sampled(inp.hidden, inp.w_router, inp.w1, inp.w3, inp.w2, 2, dy, cf,
+                                 inp.bias, aux_coef=coef, overflow=overflow, tokens=toks,
+                                 expert_cols=ec)
+    for t in toks:
+        assert np.allclose(smp["dhidden"][t], full["dhidden"][t], rtol=1e-12, atol=1e-12)
+    for e, cols in ec:
+        d1, d3, d2 = smp["dw"][(e, tuple(cols))]
+        assert np.allclose(d1, full["dw1"][e][:, cols], rtol=1e-12, atol=1e-12)
+        assert np.allclose(d3, full["dw3"][e][:, cols], rtol=1e-12, atol=1e-12)
+        assert np.allclose(d2, full["dw2"][e][cols, :], rtol=1e-12, atol=1e-12)

@@ -433,7 +433,7 @@ def main():
 
     if args.write_traffic:
         cmds = [f"rocprofv3 --pmc {c} -d gpurun_out/pmc_{c} -o run --output-format csv -- python -u "
-                f"bench.py --steps 2 --warmup 1 --no-decode --no-skewed --no-shared --no-cpu-baseline --copy-calibration "
+                f"bench.py --steps 2 --warmup 1 --no-decode --no-skewed --no-shared --no-backward --no-cpu-baseline --copy-calibration "
                 f"{args.copy_calibration}" for c in ("FETCH_SIZE", "WRITE_SIZE")]
         write_traffic(*args.write_traffic, args.copy_calibration, cmds)
         return 0

@@ -502,7 +502,7 @@ def _dlogits(L, idx, w, dgate, counts, T, k, aux_coef):
 
 
 def moe_backward(hidden, w_router, w1, w3, w2, k: int, dy, capacity_factor: float = 0.0,
-                 bias=None, aux_coef: float = 0.0, overflow: str = "drop") -> dict:
+                 bias=None, aux_coef: float = 0.0, overflow: str = "drop", shared=None) -> dict:
     """Gradients of L = sum(dy * y) + aux_coef * aux (float64, from the definitions).
 
     Per kept slot (t, j) at expert e with gate weight w: g = w * dy[t] is the gradient
@@ -512,6 +512,9 @@ def moe_backward(hidden, w_router, w1, w3, w2, k: int, dy, capacity_factor: floa
     Aux loss: d aux / d logits[t, e] = (N / T) p_te (f_e - sum_m p_tm f_m), p = full softmax.
     Router: dW_router = hidden^T dlogits, dbias = sum_t dlogits,
     dhidden[t] = sum of its slots' dX rows + dlogits[t] W_router^T.
+    Shared experts (``shared`` = (w1s, w3s, w2s), P2 §3.3, weight 1 on every token):
+    :func:`swiglu_backward` over all T rows with g = dy gives dw1s/dw3s/dw2s, and
+    their dX rows are added to dhidden.
     """
     hidden = np.asarray(hidden, np.float64)
     T, d = hidden.shape
@@ -539,9 +542,18 @@ def moe_backward(hidden, w_router, w1, w3, w2, k: int, dy, capacity_factor: floa
     dW_router = hidden.T @ dlog
     dbias = dlog.sum(axis=0)
     dhidden += dlog @ Wr.T
-    return {"dhidden": dhidden, "dw_router": dW_router, "dbias": dbias, "dw1": dW1, "dw3": dW3,
-            "dw2": dW2, "dgate": dgate, "dlogits": dlog, "topk_idx": R["idx"],
-            "slot_row": R["slot_row"], "offsets": offsets}
+    res = {"dhidden": dhidden, "dw_router": dW_router, "dbias": dbias, "dw1": dW1, "dw3": dW3,
+           "dw2": dW2, "dgate": dgate, "dlogits": dlog, "topk_idx": R["idx"],
+           "slot_row": R["slot_row"], "offsets": offsets}
+    if shared is not None:
+        w1s, w3s, w2s = shared
+        outs = [swiglu_backward(hidden, dy, w1s[q], w3s[q], w2s[q]) for q in range(len(w1s))]
+        for o in outs:
+            dhidden += o["dx"]
+        res["dw1s"] = np.stack([o["dw1"] for o in outs])
+        res["dw3s"] = np.stack([o["dw3"] for o in outs])
+        res["dw2s"] = np.stack([o["dw2"] for o in outs])
+    return res
 
 
 def moe_backward_sampled(hidden, w_router, w1, w3, w2, k: int, dy, capacity_factor: float = 0.0,

@@ -652,11 +652,14 @@ def _loss_and_fd(inp, k, cf, dy, coef, overflow, eps=1e-6):
     piecewise constant, so the derivative there is one-sided)."""
     P = {"hidden": inp.hidden, "w_router": inp.w_router, "w1": inp.w1, "w3": inp.w3,
          "w2": inp.w2, "bias": inp.bias}
+    if inp.n_shared:
+        P.update({"w1s": inp.w1s, "w3s": inp.w3s, "w2s": inp.w2s})
     P = {n: np.asarray(v, np.float64) for n, v in P.items()}
 
     def loss(Q):
+        sh = (Q["w1s"], Q["w3s"], Q["w2s"]) if inp.n_shared else None
         out = O.moe_forward(Q["hidden"], Q["w_router"], Q["w1"], Q["w3"], Q["w2"], k, cf,
-                            Q["bias"], overflow=overflow)
+                            Q["bias"], overflow=overflow, shared=sh)
         return float(np.sum(dy * out["y"])) + coef * float(out["aux"]), out
 
     _, base = loss(P)
@@ -680,18 +683,21 @@ def _loss_and_fd(inp, k, cf, dy, coef, overflow, eps=1e-6):
 
 
 _GRAD_KEYS = {"hidden": "dhidden", "w_router": "dw_router", "w1": "dw1", "w3": "dw3",
-              "w2": "dw2", "bias": "dbias"}
+              "w2": "dw2", "bias": "dbias", "w1s": "dw1s", "w3s": "dw3s", "w2s": "dw2s"}
 
 
 def _backward(inp, k, cf, dy, coef, overflow, mod=O):
+    sh = (inp.w1s, inp.w3s, inp.w2s) if inp.n_shared else None
     return mod.moe_backward(inp.hidden, inp.w_router, inp.w1, inp.w3, inp.w2, k, dy, cf,
-                            inp.bias, aux_coef=coef, overflow=overflow)
+                            inp.bias, aux_coef=coef, overflow=overflow, shared=sh)
 
 
 def _fd_agrees(inp, k, cf, dy, coef, overflow, g):
     fd, _ = _loss_and_fd(inp, k, cf, dy, coef, overflow)
     worst = 0.0
     for name, key in _GRAD_KEYS.items():
+        if name not in fd:
+            continue
         ok = ~np.isnan(fd[name])
         assert ok.mean() > 0.9
         scale = max(1.0, float(np.abs(fd[name][ok]).max()))
@@ -699,15 +705,17 @@ def _fd_agrees(inp, k, cf, dy, coef, overflow, g):
     return worst
 
 
-@pytest.mark.parametrize("cf,coef,overflow,seed", [
-    (0.0, 0.0, "drop", 0),        # no capacity limit, no aux loss
-    (0.8, 0.37, "drop", 1),       # dropped slots and the aux-loss term
-    (0.8, 0.05, "reroute", 2),    # re-routed slots keep their gate weight
+@pytest.mark.parametrize("cf,coef,overflow,seed,ns", [
+    (0.0, 0.0, "drop", 0, 0),        # no capacity limit, no aux loss
+    (0.8, 0.37, "drop", 1, 0),       # dropped slots and the aux-loss term
+    (0.8, 0.05, "reroute", 2, 0),    # re-routed slots keep their gate weight
+    (0.8, 0.1, "drop", 3, 2),        # two shared experts (weight 1 on every token)
 ])
-def test_backward_matches_finite_differences_of_the_forward(cf, coef, overflow, seed):
+def test_backward_matches_finite_differences_of_the_forward(cf, coef, overflow, seed, ns):
     """Every gradient equals the central difference of the pinned forward (fp64, eps 1e-6)."""
     inp = synth.make_inputs(10, 6, 4, 2, 5, "f32", cf, seed,
-                            bias=np.array([0.5, 0.0, -0.3, 0.2], np.float32))
+                            bias=np.array([0.5, 0.0, -0.3, 0.2], np.float32), n_shared=ns,
+                            f_shared=3 if ns else None)
     dy = np.random.default_rng(100 + seed).standard_normal((10, 6))
     g = _backward(inp, 2, cf, dy, coef, overflow)
     if cf > 0:
@@ -792,3 +800,23 @@ def test_backward_sampled_entries_equal_the_full_backward(overflow, cf, coef):
         assert np.allclose(d1, full["dw1"][e][:, cols], rtol=1e-12, atol=1e-12)
         assert np.allclose(d3, full["dw3"][e][:, cols], rtol=1e-12, atol=1e-12)
         assert np.allclose(d2, full["dw2"][e][cols, :], rtol=1e-12, atol=1e-12)
+
+
+def test_backward_shared_pin_catches_a_dropped_shared_path():
+    """A copy of the oracle that forgets the shared experts' dX in dhidden fails
+    the finite-difference pin."""
+    import inspect
+    src = inspect.getsource(O.moe_backward)
+    old = 'dhidden += o["dx"]'
+    assert old in src
+    ns = dict(vars(O))
+    exec(compile(src.replace(old, "pass"), "<mutant>", "exec"), ns)
+
+    class M:
+        moe_backward = staticmethod(ns["moe_backward"])
+    inp = synth.make_inputs(10, 6, 4, 2, 5, "f32", 0.8, 3,
+                            bias=np.array([0.5, 0.0, -0.3, 0.2], np.float32), n_shared=2,
+                            f_shared=3)
+    dy = np.random.default_rng(103).standard_normal((10, 6))
+    g = _backward(inp, 2, 0.8, dy, 0.1, "drop", mod=M)
+    assert _fd_agrees(inp, 2, 0.8, dy, 0.1, "drop", g) > 1e-3

@@ -311,20 +311,25 @@ moe_status moe_expert_backward(const void* x_perm, const void* g_perm, const int
  *                  (p = softmax over all N, f_e = counts[e] / (T k))
  *                + sum_j [topk_idx[t, j] = e] topk_w[t, j] (dgate[t, j] - sum_m topk_w[t, m] dgate[t, m])
  *   dhidden[t]   = sum_j dx_perm[slot_row[t, j]] (kept slots) + dlogit[t] W_router^T
+ *                  + sum_q dx_shared[q][t]
  *   dw_router    = hidden^T dlogit  [d, N] fp32 out
  *   dbias        = sum_t dlogit[t]  [N] fp32 out, or NULL to skip
  *   hidden [T, d], w_router [d, N] dtype dt; logits [T, N], topk_w, dgate [T, k]
  *   fp32; topk_idx, slot_row [T, k], counts [N] int32; dx_perm [max_rows, d]
- *   fp32; dhidden [T, d] fp32 out.  Sums over tokens are taken in a fixed
+ *   fp32; dhidden [T, d] fp32 out.  dx_shared [n_shared, T, d] fp32: the shared
+ *   experts' input gradients (each one moe_expert_backward over all T rows of
+ *   hidden with g_perm = dy and offsets {0, T}; P2 §3.3), or NULL with
+ *   n_shared = 0.  Sums over tokens are taken in a fixed
  *   order (results do not depend on scheduling).
  *   ws  moe_workspace_size(MOE_OP_ROUTER_BACKWARD, T, d, N, k, f, dt) bytes.
  */
 moe_status moe_router_backward(const void* hidden, const void* w_router, const float* logits,
                                const int32_t* topk_idx, const float* topk_w,
                                const int32_t* counts, const float* dgate, const float* dx_perm,
-                               const int32_t* slot_row, float aux_coef, int T, int d, int N,
-                               int k, moe_dtype dt, float* dhidden, float* dw_router, float* dbias,
-                               void* ws, size_t ws_bytes, void* stream);
+                               const int32_t* slot_row, const float* dx_shared, int n_shared,
+                               float aux_coef, int T, int d, int N, int k, moe_dtype dt,
+                               float* dhidden, float* dw_router, float* dbias, void* ws,
+                               size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

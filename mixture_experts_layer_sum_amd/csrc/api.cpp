@@ -290,12 +290,14 @@ moe_status moe_expert_backward(const void* x_perm, const void* g_perm, const int
 moe_status moe_router_backward(const void* hidden, const void* w_router, const float* logits,
                                const int32_t* topk_idx, const float* topk_w,
                                const int32_t* counts, const float* dgate, const float* dx_perm,
-                               const int32_t* slot_row, float aux_coef, int T, int d, int N,
-                               int k, moe_dtype dt, float* dhidden, float* dw_router, float* dbias,
-                               void* ws, size_t ws_bytes, void* stream) {
+                               const int32_t* slot_row, const float* dx_shared, int n_shared,
+                               float aux_coef, int T, int d, int N, int k, moe_dtype dt,
+                               float* dhidden, float* dw_router, float* dbias, void* ws,
+                               size_t ws_bytes, void* stream) {
   if (!hidden || !w_router || !logits || !topk_idx || !topk_w || !counts || !dgate || !dx_perm ||
       !slot_row || !dhidden || !dw_router)
     return MOE_ERR_INVALID_ARG;
+  if (n_shared < 0 || (n_shared > 0 && !dx_shared)) return MOE_ERR_INVALID_ARG;
   if (std::isnan(aux_coef)) return MOE_ERR_INVALID_ARG;
   moe_status s = check_tnk(T, N, k);
   if (s != MOE_OK) return s;
@@ -305,9 +307,10 @@ moe_status moe_router_backward(const void* hidden, const void* w_router, const f
   if (ws_bytes < need) return MOE_ERR_WORKSPACE;
   if (!ws) return MOE_ERR_INVALID_ARG;
   return hip_status(moe::launch_router_backward(hidden, w_router, logits, topk_idx, topk_w,
-                                                counts, dgate, dx_perm, slot_row, aux_coef, T, d,
-                                                N, k, dt == MOE_BF16, dhidden, dw_router, dbias,
-                                                ws, as_stream(stream)));
+                                                counts, dgate, dx_perm, slot_row,
+                                                n_shared > 0 ? dx_shared : nullptr, n_shared,
+                                                aux_coef, T, d, N, k, dt == MOE_BF16, dhidden,
+                                                dw_router, dbias, ws, as_stream(stream)));
 }
 
 }  // extern "C"

@@ -637,13 +637,15 @@ __global__ __launch_bounds__(256) void router_dlogit_kernel(
 }
 
 // dhidden for 32 tokens x 256 columns per block: the router term
-// dlogit[t] W_router^T (W_router is [d, N]) plus the token's slot rows of dx.
+// dlogit[t] W_router^T (W_router is [d, N]), plus the token's slot rows of dx
+// in slot order, plus the shared experts' dx rows in shared-expert order.
 constexpr int kDxTok = 32;
 template <bool BF16>
 __global__ __launch_bounds__(256) void router_dx_kernel(
     const void* __restrict__ w_router, const float* __restrict__ dlog,
-    const float* __restrict__ dx_perm, const int32_t* __restrict__ slot_row, int T, int d, int N,
-    int k, float* __restrict__ dhidden) {
+    const float* __restrict__ dx_perm, const int32_t* __restrict__ slot_row,
+    const float* __restrict__ dx_shared, int n_shared, int T, int d, int N, int k,
+    float* __restrict__ dhidden) {
   extern __shared__ float sh[];          // [kDxTok][N] dlogit, then [kDxTok][k] slot rows
   float* dl = sh;
   int* sr = reinterpret_cast<int*>(sh + kDxTok * N);
@@ -673,6 +675,7 @@ __global__ __launch_bounds__(256) void router_dx_kernel(
         const int r = sr[t * k + j];
         if (r >= 0) v += dx_perm[(size_t)r * d + c];
       }
+      for (int q = 0; q < n_shared; ++q) v += dx_shared[((size_t)q * T + t0 + t) * d + c];
       dhidden[(size_t)(t0 + t) * d + c] = v;
     }
   }
@@ -846,9 +849,10 @@ size_t router_backward_ws_bytes(int T, int d, int N) {
 hipError_t launch_router_backward(const void* hidden, const void* w_router, const float* logits,
                                   const int32_t* topk_idx, const float* topk_w,
                                   const int32_t* counts, const float* dgate, const float* dx_perm,
-                                  const int32_t* slot_row, float aux_coef, int T, int d, int N,
-                                  int k, bool bf16, float* dhidden, float* dw_router, float* dbias,
-                                  void* ws, hipStream_t stream) {
+                                  const int32_t* slot_row, const float* dx_shared, int n_shared,
+                                  float aux_coef, int T, int d, int N, int k, bool bf16,
+                                  float* dhidden, float* dw_router, float* dbias, void* ws,
+                                  hipStream_t stream) {
   using namespace bwd;
   const int chunks = (T + kDwTok - 1) / kDwTok;
   char* base = static_cast<char*>(ws);
@@ -862,10 +866,10 @@ hipError_t launch_router_backward(const void* hidden, const void* w_router, cons
   const size_t shx = (size_t)kDxTok * (N + k) * 4;
   if (bf16)
     hipLaunchKernelGGL(router_dx_kernel<true>, gx, dim3(256), shx, stream, w_router, dlog, dx_perm,
-                       slot_row, T, d, N, k, dhidden);
+                       slot_row, dx_shared, n_shared, T, d, N, k, dhidden);
   else
     hipLaunchKernelGGL(router_dx_kernel<false>, gx, dim3(256), shx, stream, w_router, dlog,
-                       dx_perm, slot_row, T, d, N, k, dhidden);
+                       dx_perm, slot_row, dx_shared, n_shared, T, d, N, k, dhidden);
   const dim3 gw((d + 255) / 256, chunks, (N + kDwE - 1) / kDwE);
   if (bf16)
     hipLaunchKernelGGL(router_dw_kernel<true>, gw, dim3(256), 0, stream, hidden, dlog, T, d, N,

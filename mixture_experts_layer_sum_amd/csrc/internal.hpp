@@ -64,8 +64,9 @@ size_t router_backward_ws_bytes(int T, int d, int N);
 hipError_t launch_router_backward(const void* hidden, const void* w_router, const float* logits,
                                   const int32_t* topk_idx, const float* topk_w,
                                   const int32_t* counts, const float* dgate, const float* dx_perm,
-                                  const int32_t* slot_row, float aux_coef, int T, int d, int N,
-                                  int k, bool bf16, float* dhidden, float* dw_router, float* dbias,
-                                  void* ws, hipStream_t stream);
+                                  const int32_t* slot_row, const float* dx_shared, int n_shared,
+                                  float aux_coef, int T, int d, int N, int k, bool bf16,
+                                  float* dhidden, float* dw_router, float* dbias, void* ws,
+                                  hipStream_t stream);
 
 }  // namespace moe

@@ -42,8 +42,8 @@ SIGNATURES = {
     "moe_combine_backward": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
     "moe_expert_backward": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P,
                                  _Z, _P]),
-    "moe_router_backward": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _F, _I, _I, _I, _I, _I, _P,
-                                 _P, _P, _P, _Z, _P]),
+    "moe_router_backward": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _F, _I, _I, _I, _I,
+                                 _I, _P, _P, _P, _P, _Z, _P]),
 }
 
 
@@ -364,7 +364,7 @@ def moe_expert_backward(x_perm, g_perm, offsets, w1, w3, w2, dx_perm=None, dw1=N
 
 def moe_router_backward(hidden, w_router, logits, topk_idx, topk_w, counts, dgate, dx_perm,
                         slot_row, aux_coef=0.0, dhidden=None, dw_router=None, dbias=None,
-                        want_dbias=True, ws=None, stream=None):
+                        want_dbias=True, ws=None, stream=None, dx_shared=None):
     T, d = hidden.shape
     N = w_router.shape[1]
     k = topk_idx.shape[1]
@@ -376,9 +376,11 @@ def moe_router_backward(hidden, w_router, logits, topk_idx, topk_w, counts, dgat
     if ws is None:
         ws = torch.empty(max(1, workspace_size(MOE_OP_ROUTER_BACKWARD, T, d, N, k, 1,
                                                hidden.dtype)), dtype=torch.uint8, device=dev)
+    ns = 0 if dx_shared is None else dx_shared.shape[0]
     _check(_lib.moe_router_backward(_ptr(hidden), _ptr(w_router), _ptr(logits), _ptr(topk_idx),
                                     _ptr(topk_w), _ptr(counts), _ptr(dgate), _ptr(dx_perm),
-                                    _ptr(slot_row), float(aux_coef), T, d, N, k, _dt(hidden),
+                                    _ptr(slot_row), _ptr(dx_shared), ns, float(aux_coef), T, d, N,
+                                    k, _dt(hidden),
                                     _ptr(dhidden), _ptr(dw_router),
                                     _ptr(dbias) if want_dbias else None, _ptr(ws), ws.numel(),
                                     _stream(stream)), "moe_router_backward")
@@ -388,7 +390,7 @@ def moe_router_backward(hidden, w_router, logits, topk_idx, topk_w, counts, dgat
 class MoEGradBuffers:
     """Every gradient and workspace of one layer backward, allocated once (fp32 gradients)."""
 
-    def __init__(self, T, d, N, k, f, dtype, device="cuda"):
+    def __init__(self, T, d, N, k, f, dtype, device="cuda", n_shared=0, f_shared=None):
         e = lambda shape, dt: torch.empty(shape, dtype=dt, device=device)  # noqa: E731
         self.g_perm = e((T * k, d), dtype)
         self.dgate = e((T, k), torch.float32)
@@ -403,23 +405,44 @@ class MoEGradBuffers:
                            torch.uint8)
         self.ws_router = e((max(1, workspace_size(MOE_OP_ROUTER_BACKWARD, T, d, N, k, f, dtype)),),
                            torch.uint8)
+        self.n_shared = n_shared
+        if n_shared:
+            fs = f if f_shared is None else f_shared
+            self.dx_shared = e((n_shared, T, d), torch.float32)
+            self.dw1s = e((n_shared, d, fs), torch.float32)
+            self.dw3s = e((n_shared, d, fs), torch.float32)
+            self.dw2s = e((n_shared, fs, d), torch.float32)
+            self.ws_shared = e((max(1, workspace_size(MOE_OP_EXPERT_BACKWARD, T, d, 1, 1, fs,
+                                                      dtype)),), torch.uint8)
 
 
 def moe_backward(hidden, w_router, w1, w3, w2, dy, fwd: MoEBuffers, aux_coef=0.0,
-                 grads: Optional[MoEGradBuffers] = None, want_dbias=True, stream=None):
+                 grads: Optional[MoEGradBuffers] = None, want_dbias=True, stream=None,
+                 shared=None):
     """Gradients of <dy, y> + aux_coef * aux for the batch `fwd` holds (moe_forward's
     buffers of the same call).  Returns the MoEGradBuffers (dhidden, dw_router, dbias,
-    dw1, dw3, dw2 in fp32)."""
+    dw1, dw3, dw2 in fp32; with ``shared`` = (w1s, w3s, w2s) also dw1s, dw3s, dw2s)."""
     T, d = hidden.shape
     N, _, f = w1.shape
     k = fwd.topk_idx.shape[1]
+    ns = 0 if shared is None else shared[0].shape[0]
     if grads is None:
-        grads = MoEGradBuffers(T, d, N, k, f, hidden.dtype, hidden.device)
+        grads = MoEGradBuffers(T, d, N, k, f, hidden.dtype, hidden.device, ns,
+                               None if shared is None else shared[0].shape[2])
     g = grads
+    dx_shared = None
+    if ns:
+        # each shared expert: the expert backward over all T rows with weight 1 (g = dy)
+        for q in range(ns):
+            moe_expert_backward(hidden, dy, fwd.shared_offsets, shared[0][q:q + 1],
+                                shared[1][q:q + 1], shared[2][q:q + 1], g.dx_shared[q],
+                                g.dw1s[q:q + 1], g.dw3s[q:q + 1], g.dw2s[q:q + 1], g.ws_shared,
+                                stream)
+        dx_shared = g.dx_shared
     moe_combine_backward(dy, fwd.y_perm, fwd.slot_row, fwd.topk_w, g.g_perm, g.dgate, stream)
     moe_expert_backward(fwd.x_perm, g.g_perm, fwd.offsets, w1, w3, w2, g.dx_perm, g.dw1, g.dw3,
                         g.dw2, g.ws_expert, stream)
     moe_router_backward(hidden, w_router, fwd.logits, fwd.topk_idx, fwd.topk_w, fwd.counts,
                         g.dgate, g.dx_perm, fwd.slot_row, aux_coef, g.dhidden, g.dw_router,
-                        g.dbias, want_dbias, g.ws_router, stream)
+                        g.dbias, want_dbias, g.ws_router, stream, dx_shared)
     return g

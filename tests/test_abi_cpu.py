@@ -225,15 +225,20 @@ def test_backward_entry_points_reject():
     ws = lib.moe_workspace_size(moe.MOE_OP_EXPERT_BACKWARD, 64, 128, 8, 1, 192, F32)
     assert lib.moe_expert_backward(P, P, P, P, P, P, 8, 128, 192, 64, F32, P, P, P, P, P, ws - 1,
                                    S) == WS
-    # router backward: null dgate; NaN coefficient; k > N; workspace too small; dbias may be NULL
-    args = [P, P, P, P, P, P, P, P, P, 0.01, 64, 128, 8, 2, BF16, P, P, NUL, P, big, S]
+    # router backward: null dgate; NaN coefficient; k > N; workspace too small; null
+    # workspace; shared count without their gradients; negative shared count
+    args = [P, P, P, P, P, P, P, P, P, NUL, 0, 0.01, 64, 128, 8, 2, BF16, P, P, NUL, P, big, S]
     a = list(args); a[6] = NUL
     assert lib.moe_router_backward(*a) == INV
-    a = list(args); a[9] = math.nan
+    a = list(args); a[11] = math.nan
     assert lib.moe_router_backward(*a) == INV
-    a = list(args); a[13] = 9
+    a = list(args); a[15] = 9
     assert lib.moe_router_backward(*a) == INV
-    a = list(args); a[19] = 100
+    a = list(args); a[21] = 100
     assert lib.moe_router_backward(*a) == WS
-    a = list(args); a[18] = NUL
+    a = list(args); a[20] = NUL
+    assert lib.moe_router_backward(*a) == INV
+    a = list(args); a[10] = 1
+    assert lib.moe_router_backward(*a) == INV
+    a = list(args); a[10] = -1; a[9] = P
     assert lib.moe_router_backward(*a) == INV

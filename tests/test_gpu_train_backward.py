@@ -47,14 +47,18 @@ def run_backward(moe, inp, coef, overflow="drop", label=""):
     dev = parity.to_device(inp)
     g, b = parity.run_gpu(inp, dev, overflow=overflow)
     dy = synth.make_dy(inp.T, inp.d, inp.dtype, seed=11)
+    sh = (dev["w1s"], dev["w3s"], dev["w2s"]) if inp.n_shared else None
     gr = moe.moe_backward(dev["hidden"], dev["w_router"], dev["w1"], dev["w3"], dev["w2"],
-                          _dev(dy, inp.dtype), b, coef, want_dbias=inp.bias is not None)
+                          _dev(dy, inp.dtype), b, coef, want_dbias=inp.bias is not None,
+                          shared=sh)
     torch.cuda.synchronize()
     dyv = synth.bf16_bits_to_f32(dy) if inp.dtype == "bf16" else dy
     ref = O.moe_backward(inp.values("hidden"), inp.values("w_router"),
                          parity.ExpertView(inp, "w1"), parity.ExpertView(inp, "w3"),
                          parity.ExpertView(inp, "w2"), inp.k, dyv, inp.capacity_factor, inp.bias,
-                         aux_coef=coef, overflow=overflow)
+                         aux_coef=coef, overflow=overflow,
+                         shared=(inp.values("w1s"), inp.values("w3s"), inp.values("w2s"))
+                         if inp.n_shared else None)
     # the gradients are taken at one routing: it must be the oracle's
     assert np.array_equal(g["topk_idx"], ref["topk_idx"]), f"{label}: routing differs"
     assert np.array_equal(g["slot_row"], ref["slot_row"]), f"{label}: dispatch differs"
@@ -63,6 +67,8 @@ def run_backward(moe, inp, coef, overflow="drop", label=""):
             "dw2": gr.dw2, "dgate": gr.dgate}
     if inp.bias is not None:
         host["dbias"] = gr.dbias
+    if inp.n_shared:
+        host.update({"dw1s": gr.dw1s, "dw3s": gr.dw3s, "dw2s": gr.dw2s})
     rep = {}
     for name, t in host.items():
         got = t.cpu().numpy().astype(np.float64)
@@ -88,12 +94,17 @@ SMALL = [
     ("bf16_empty_experts", 200, 256, 16, 2, 256, "bf16", 0.0, "hot", 0.1, "drop"),
     ("bf16_reroute", 600, 256, 8, 2, 256, "bf16", 0.8, "skew", 0.01, "reroute"),
     ("bf16_multi_tile_rows", 1500, 256, 2, 2, 256, "bf16", 0.0, None, 0.0, "drop"),
+    # shared experts: every token, weight 1; two of them, and one with all routed slots dropped
+    ("f32_two_shared", 100, 128, 8, 2, 128, "f32", 1.0, None, 0.01, "drop", 2, 64),
+    ("bf16_shared", 400, 256, 8, 2, 256, "bf16", 1.0, "skew", 0.01, "drop", 1, 512),
+    ("bf16_shared_all_dropped", 64, 256, 8, 2, 256, "bf16", 0.01, "skew", 0.0, "drop", 1, 256),
 ]
 
 
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
 def test_backward_small(moe, case):
-    label, T, d, N, k, f, dt, cf, bias, coef, overflow = case
+    label, T, d, N, k, f, dt, cf, bias, coef, overflow = case[:11]
+    ns, fs = case[11:] if len(case) > 11 else (0, None)
     b = None
     if bias == "skew":
         b = np.zeros(N, np.float32)
@@ -101,7 +112,7 @@ def test_backward_small(moe, case):
     elif bias == "hot":
         b = np.full(N, -4.0, np.float32)
         b[:4] = 2.0                        # experts 4.. get (almost) nothing
-    inp = synth.make_inputs(T, d, N, k, f, dt, cf, 0, bias=b)
+    inp = synth.make_inputs(T, d, N, k, f, dt, cf, 0, bias=b, n_shared=ns, f_shared=fs)
     run_backward(moe, inp, coef, overflow, label)
 
 

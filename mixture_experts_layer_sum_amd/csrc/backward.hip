@@ -386,18 +386,39 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_bf16_kernel(Args p) {
 
   // ---- epilogues.  acc[i][j][r]: tile row 32 (2i + wm) + 8 (r / 4) + 4h + r % 4.
   if (MODE == kSwiGLU) {
+    // Stage the tile's da block (256 rows x 128 fp32 columns, 128 KB) in the
+    // two LDS stages with direct loads from every wave, so that the epilogue
+    // does not wait on 64 dependent global loads per lane: after every
+    // fragment read and every refill is done, wave w loads rows 32 w .. 32 w + 31
+    // (two 512-byte rows per 1 KB instruction; rows past the tile read zeros).
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    {
+      const __amdgpu_buffer_rsrc_t da_rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(p.da + (size_t)r0 * p.f + n0), 0, tile_rows * p.f * 4, kRsrcWord3);
+      const uint32_t vo = (uint32_t)(((32 * w + (lane >> 5)) * p.f + 4 * (lane & 31)) * 4);
+      uint16_t* dst = (w < 4 ? S0 : S1) + (w & 3) * 8192;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(da_rs, (lds_void*)(dst + i * 512), 16, vo,
+                                                 (uint32_t)(2 * i * p.f * 4), 0, 0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    const float* da0 = reinterpret_cast<const float*>(S0);
+    const float* da1 = reinterpret_cast<const float*>(S1);
     uint16_t* dh = static_cast<uint16_t*>(p.dh);
     uint16_t* act = static_cast<uint16_t*>(p.act);
-    const int col = n0 + wn * 64 + 32 * pw + l32;
+    const int cl = wn * 64 + 32 * pw + l32;
+    const int col = n0 + cl;
     const int f = p.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = r0 + 32 * (2 * i + wm) + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int tr = 32 * (2 * i + wm) + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int row = r0 + tr;
         if (row < rend) {
           const float h1 = acc[i][0][r], h3 = acc[i][1][r];
-          const float g = p.da[(size_t)row * f + col];
+          const float g = i < 2 ? da0[tr * 128 + cl] : da1[(tr - 128) * 128 + cl];
           const float s = __builtin_amdgcn_rcpf(1.f + __expf(-h1));
           const float sl = h1 * s;
           dh[(size_t)row * 2 * f + col] = f32_to_bf16(g * h3 * (s + sl * (1.f - s)));

@@ -94,6 +94,15 @@ SMALL = [
     ("bf16_empty_experts", 200, 256, 16, 2, 256, "bf16", 0.0, "hot", 0.1, "drop"),
     ("bf16_reroute", 600, 256, 8, 2, 256, "bf16", 0.8, "skew", 0.01, "reroute"),
     ("bf16_multi_tile_rows", 1500, 256, 2, 2, 256, "bf16", 0.0, None, 0.0, "drop"),
+    # edge shapes: k = 4, N not a multiple of 8 with k = 3, one token, N = 64 and 256 (most
+    # experts empty), k = N (dense softmax), f = 3 * 256
+    ("bf16_k4_N16", 200, 256, 16, 4, 256, "bf16", 0.0, None, 0.05, "drop"),
+    ("bf16_N12_k3_cap", 130, 256, 12, 3, 256, "bf16", 0.8, None, 0.01, "drop"),
+    ("bf16_single_token", 1, 256, 8, 2, 256, "bf16", 0.0, None, 0.01, "drop"),
+    ("bf16_N64_sparse", 100, 256, 64, 2, 256, "bf16", 0.0, None, 0.01, "drop"),
+    ("bf16_N256", 70, 256, 256, 2, 256, "bf16", 0.0, None, 0.01, "drop"),
+    ("f32_k_eq_N", 40, 64, 4, 4, 64, "f32", 0.0, None, 0.1, "drop"),
+    ("bf16_d512_f768", 300, 512, 8, 2, 768, "bf16", 1.25, None, 0.01, "drop"),
     # shared experts: every token, weight 1; two of them, and one with all routed slots dropped
     ("f32_two_shared", 100, 128, 8, 2, 128, "f32", 1.0, None, 0.01, "drop", 2, 64),
     ("bf16_shared", 400, 256, 8, 2, 256, "bf16", 1.0, "skew", 0.01, "drop", 1, 512),

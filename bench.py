@@ -432,9 +432,11 @@ def main():
     args = ap.parse_args()
 
     if args.write_traffic:
-        cmds = [f"rocprofv3 --pmc {c} -d gpurun_out/pmc_{c} -o run --output-format csv -- python -u "
-                f"bench.py --steps 2 --warmup 1 --no-decode --no-skewed --no-shared --no-backward --no-cpu-baseline --copy-calibration "
-                f"{args.copy_calibration}" for c in ("FETCH_SIZE", "WRITE_SIZE")]
+        # the counter runs these two commands, with -d the directories given here
+        cmds = [f"rocprofv3 --pmc {c} -d {dr} -o run --output-format csv -- python -u "
+                f"bench.py --steps 2 --warmup 1 --no-decode --no-skewed --no-shared --no-backward "
+                f"--no-cpu-baseline --copy-calibration {args.copy_calibration}"
+                for c, dr in zip(("FETCH_SIZE", "WRITE_SIZE"), args.write_traffic)]
         write_traffic(*args.write_traffic, args.copy_calibration, cmds)
         return 0
 

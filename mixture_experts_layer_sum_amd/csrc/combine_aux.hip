@@ -122,29 +122,30 @@ __global__ __launch_bounds__(256) void aux_partial_kernel(const float* __restric
 }
 
 // Single block: P_e = sum_b part[b][e] / T, then aux = N * sum_e f_e P_e.
-// The 256 threads split the blocks: expert e is summed by G = 256 / N' threads
+// The 1024 threads split the blocks: expert e is summed by G = 1024 / N' threads
 // (N' = N rounded up to a power of two), thread g taking blocks g, g + G, ...;
 // the G partial sums then meet in a fixed tree, so the order never changes.
-__global__ __launch_bounds__(256) void aux_final_kernel(const float* __restrict__ part, int nb,
+constexpr int kAuxFinal = 1024;
+__global__ __launch_bounds__(kAuxFinal) void aux_final_kernel(const float* __restrict__ part, int nb,
                                                         const int32_t* __restrict__ counts, int T,
                                                         int N, int k, float* __restrict__ aux) {
-  __shared__ double red[256];
+  __shared__ double red[kAuxFinal];
   __shared__ float term[256];
   const int tid = threadIdx.x;
   int np2 = 1;
   while (np2 < N) np2 <<= 1;
-  const int G = 256 / np2;
+  const int G = kAuxFinal / np2;
   const int e = tid % np2, g = tid / np2;
   double s = 0.0;
   if (e < N) {
+    // 16 loads in flight, summed in block order
     int b = g;
-    for (; b + 3 * G < nb; b += 4 * G) {
-      const float a0 = part[(size_t)b * N + e], a1 = part[(size_t)(b + G) * N + e];
-      const float a2 = part[(size_t)(b + 2 * G) * N + e], a3 = part[(size_t)(b + 3 * G) * N + e];
-      s += a0;
-      s += a1;
-      s += a2;
-      s += a3;
+    for (; b + 15 * G < nb; b += 16 * G) {
+      float a[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) a[u] = part[(size_t)(b + u * G) * N + e];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) s += a[u];
     }
     for (; b < nb; b += G) s += part[(size_t)b * N + e];
   }
@@ -181,7 +182,8 @@ hipError_t launch_aux(const float* logits, const int32_t* counts, int T, int N, 
   const int nb = (T + kAuxTok - 1) / kAuxTok;
   float* part = static_cast<float*>(ws);
   hipLaunchKernelGGL(aux_partial_kernel, dim3(nb), dim3(256), 0, stream, logits, T, N, part);
-  hipLaunchKernelGGL(aux_final_kernel, dim3(1), dim3(256), 0, stream, part, nb, counts, T, N, k, aux);
+  hipLaunchKernelGGL(aux_final_kernel, dim3(1), dim3(kAuxFinal), 0, stream, part, nb, counts, T, N,
+                     k, aux);
   return hipGetLastError();
 }
 

@@ -36,6 +36,30 @@ __global__ __launch_bounds__(kChunk) void chunk_hist_kernel(const int32_t* __res
   for (int e = tid; e < N; e += kChunk) hist[(size_t)c * N + e] = h[e];
 }
 
+// Exclusive scan of expert e's counts over the chunks, in chunk order:
+// base[c][e] = sum of hist[c'][e] for c' < c; returns the total.  The loads
+// are issued 16 at a time (they do not depend on each other), so a thread
+// waits on memory about nchunks / 16 times instead of nchunks times.
+__device__ __forceinline__ int scan_chunks(const int32_t* __restrict__ hist, int nchunks, int N,
+                                           int e, int32_t* __restrict__ base) {
+  int run = 0, c = 0;
+  for (; c + 16 <= nchunks; c += 16) {
+    int v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = hist[(size_t)(c + u) * N + e];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      base[(size_t)(c + u) * N + e] = run;
+      run += v[u];
+    }
+  }
+  for (; c < nchunks; ++c) {
+    base[(size_t)c * N + e] = run;
+    run += hist[(size_t)c * N + e];
+  }
+  return run;
+}
+
 // One block of 256 threads; thread e scans expert e over the chunks.
 __global__ __launch_bounds__(256) void expert_scan_kernel(const int32_t* __restrict__ hist,
                                                           int nchunks, int N, int C,
@@ -44,12 +68,7 @@ __global__ __launch_bounds__(256) void expert_scan_kernel(const int32_t* __restr
                                                           int32_t* __restrict__ offsets) {
   __shared__ int sk[256];
   const int e = threadIdx.x;
-  int run = 0;
-  if (e < N)
-    for (int c = 0; c < nchunks; ++c) {
-      base[(size_t)c * N + e] = run;
-      run += hist[(size_t)c * N + e];
-    }
+  const int run = (e < N) ? scan_chunks(hist, nchunks, N, e, base) : 0;
   const int kp = (e < N) ? (run < C ? run : C) : 0;
   if (e < N) kept[e] = kp;
   sk[e] = kp;
@@ -242,11 +261,7 @@ __global__ __launch_bounds__(256) void first_round_scan_kernel(const int32_t* __
                                                                int32_t* __restrict__ kept1) {
   const int e = threadIdx.x;
   if (e >= N) return;
-  int run = 0;
-  for (int c = 0; c < nchunks; ++c) {
-    base[(size_t)c * N + e] = run;
-    run += hist[(size_t)c * N + e];
-  }
+  const int run = scan_chunks(hist, nchunks, N, e, base);
   kept1[e] = run < C ? run : C;
 }
 
@@ -299,12 +314,7 @@ __global__ __launch_bounds__(256) void second_round_scan_kernel(const int32_t* _
                                                                 int32_t* __restrict__ offsets) {
   __shared__ int sk[256];
   const int e = threadIdx.x;
-  int run = 0;
-  if (e < N)
-    for (int c = 0; c < nchunks; ++c) {
-      base2[(size_t)c * N + e] = run;
-      run += hist2[(size_t)c * N + e];
-    }
+  const int run = (e < N) ? scan_chunks(hist2, nchunks, N, e, base2) : 0;
   int kp = 0;
   if (e < N) {
     const int k1 = kept1[e];

@@ -35,31 +35,55 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     sw[j] = topk_w[(size_t)t * k + j];
   }
   __syncthreads();
+  // four column groups per pass, so that each slot's four loads are in flight together
   const int nv = d >> 2;
-  for (int v = threadIdx.x; v < nv; v += blockDim.x) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int v0 = threadIdx.x; v0 < nv; v0 += 4 * blockDim.x) {
+    float4 acc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < k; ++j) {
       const int r = srow[j];
       if (r < 0) continue;
       const float wj = sw[j];
-      const float4 x = reinterpret_cast<const float4*>(y_perm + (size_t)r * d)[v];
-      acc.x = fmaf(wj, x.x, acc.x);
-      acc.y = fmaf(wj, x.y, acc.y);
-      acc.z = fmaf(wj, x.z, acc.z);
-      acc.w = fmaf(wj, x.w, acc.w);
+      const float4* src = reinterpret_cast<const float4*>(y_perm + (size_t)r * d);
+      float4 x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int v = v0 + u * blockDim.x;
+        x[u] = v < nv ? src[v] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        acc[u].x = fmaf(wj, x[u].x, acc[u].x);
+        acc[u].y = fmaf(wj, x[u].y, acc[u].y);
+        acc[u].z = fmaf(wj, x[u].z, acc[u].z);
+        acc[u].w = fmaf(wj, x[u].w, acc[u].w);
+      }
     }
     for (int q = 0; q < n_shared; ++q) {
-      const float4 x = reinterpret_cast<const float4*>(y_shared + ((size_t)q * T + t) * d)[v];
-      acc.x += x.x;
-      acc.y += x.y;
-      acc.z += x.z;
-      acc.w += x.w;
+      const float4* src = reinterpret_cast<const float4*>(y_shared + ((size_t)q * T + t) * d);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int v = v0 + u * blockDim.x;
+        if (v < nv) {
+          const float4 x = src[v];
+          acc[u].x += x.x;
+          acc[u].y += x.y;
+          acc[u].z += x.z;
+          acc[u].w += x.w;
+        }
+      }
     }
-    if (BF16) {
-      reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + (size_t)t * d)[v] =
-          make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
-    } else {
-      reinterpret_cast<float4*>(static_cast<float*>(y) + (size_t)t * d)[v] = acc;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int v = v0 + u * blockDim.x;
+      if (v >= nv) continue;
+      if (BF16) {
+        reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + (size_t)t * d)[v] =
+            make_uint2(pack_bf16x2(acc[u].x, acc[u].y), pack_bf16x2(acc[u].z, acc[u].w));
+      } else {
+        reinterpret_cast<float4*>(static_cast<float*>(y) + (size_t)t * d)[v] = acc[u];
+      }
     }
   }
 }

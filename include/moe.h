@@ -100,8 +100,9 @@ size_t moe_workspace_size(moe_op op, int T, int d, int N, int k, int f, moe_dtyp
  *   counts    [N] int32 out: number of tokens that chose each expert (before
  *             any capacity drop); sum(counts) = T*k
  *   ws        device workspace of moe_workspace_size(MOE_OP_ROUTE, ...) bytes
- *             (partial logits when the hidden dimension is split across
- *             blocks; may be NULL when that size is 0)
+ *             (bf16: w_router transposed when T >= 2048, else partial logits
+ *             when the hidden dimension is split across blocks; may be NULL
+ *             when that size is 0)
  */
 moe_status moe_route(const void* hidden, const void* w_router, const float* bias, int T, int d,
                      int N, int k, moe_dtype dt, float* logits, int32_t* topk_idx, float* topk_w,

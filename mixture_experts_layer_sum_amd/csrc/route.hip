@@ -84,6 +84,53 @@ __device__ __forceinline__ void topk_row(const float* lg, int t, int N, int k,
   }
 }
 
+// Top-k + softmax + histogram of one token by one thread (k <= kTopkThread):
+// k passes over the token's N logits in LDS, pass p taking the best
+// (larger logit, then lower expert id) among those ranked after pass p - 1's
+// pick.  Many tokens run side by side, one per thread, instead of one token
+// per wave through a chain of dependent shuffles.
+constexpr int kTopkThread = 16;
+__device__ __forceinline__ void topk_thread(const float* lg, int t, int N, int k,
+                                            int32_t* __restrict__ topk_idx,
+                                            float* __restrict__ topk_w, int* hist) {
+  float pv = INFINITY, vmax = 0.f, s = 0.f;
+  int pe = -1;
+  float sv[kTopkThread];
+  int si[kTopkThread];
+#pragma unroll
+  for (int p = 0; p < kTopkThread; ++p) {
+    if (p >= k) break;
+    float bv = -INFINITY;
+    int be = -1;
+    for (int e = 0; e < N; ++e) {
+      const float v = lg[e];
+      // ranked after the previous pick: smaller logit, or equal logit and larger id
+      const bool after = v < pv || (v == pv && e > pe);
+      if (after && (be < 0 || v > bv)) {
+        bv = v;
+        be = e;
+      }
+    }
+    sv[p] = bv;
+    si[p] = be;
+    pv = bv;
+    pe = be;
+  }
+  vmax = sv[0];
+#pragma unroll
+  for (int p = 0; p < kTopkThread; ++p)
+    if (p < k) s += __expf(sv[p] - vmax);
+  const float inv = 1.f / s;
+#pragma unroll
+  for (int p = 0; p < kTopkThread; ++p) {
+    if (p < k) {
+      topk_idx[(size_t)t * k + p] = si[p];
+      topk_w[(size_t)t * k + p] = __expf(sv[p] - vmax) * inv;
+      atomicAdd(&hist[si[p]], 1);
+    }
+  }
+}
+
 // Top-k for the 16 rows of one wave (fp32 router): rows 16w .. 16w+15 of lg.
 __device__ __forceinline__ void topk_rows(const float* lg, int ldl, int t0, int T, int N, int k,
                                           int32_t* __restrict__ topk_idx,
@@ -258,6 +305,141 @@ __global__ __launch_bounds__(64 * WAVES) void router_bf16_kernel(
     if (hist[e]) atomicAdd(&counts[e], hist[e]);
 }
 
+// ---------------------------------------------------------------- large batches
+// For batches of at least kRtBigT tokens the router reads W_router transposed,
+// WT [N16][d] (expert rows contiguous in d, rows N .. N16-1 zero), which
+// router_prep_kernel writes into the workspace in the same launch that clears
+// the counts.  Both MFMA operands are then plain 16-byte loads and a wave keeps
+// several 32-deep steps of hidden in flight:
+//   16x16x32 MFMAs, A = 16 experts of WT (lane 16g + j: expert 16et + j,
+//   k 8g .. 8g+7), B = 16 tokens of hidden (lane 16g + j: token j, the same k).
+// A block owns 16 tokens; its waves split d into contiguous ranges, and their
+// partial logits are summed in wave order through LDS (fixed order).
+constexpr int kRtBigT = 2048;
+constexpr int kRtBigWaves = 8;
+
+__global__ __launch_bounds__(256) void router_prep_kernel(const uint16_t* __restrict__ wr, int d,
+                                                          int N, int N16, uint16_t* __restrict__ wt,
+                                                          int32_t* __restrict__ counts) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < N) counts[i] = 0;
+  if (i < N16 * d) {
+    const int e = i / d, kk = i - e * d;
+    wt[i] = e < N ? wr[(size_t)kk * N + e] : (uint16_t)0;
+  }
+}
+
+template <int MT, int NT>
+__global__ __launch_bounds__(64 * kRtBigWaves) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void router_wt_kernel(
+    const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ wt,
+    const float* __restrict__ bias, int T, int d, int N, int k, float* __restrict__ logits,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int32_t* __restrict__ counts) {
+  constexpr int ROWS = 16 * MT;
+  constexpr int LD = 16 * NT + 1;
+  // k-steps per batch of loads; two batches are in flight (double buffer of
+  // about 96 registers): the next batch is issued before the current one's MFMAs
+  constexpr int KB = (48 / (4 * (MT + NT))) < 1 ? 1 : (48 / (4 * (MT + NT)));
+  __shared__ float red[ROWS][LD];
+  __shared__ int hist[256];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 15, g = lane >> 4;
+  const int t0 = blockIdx.x * ROWS;
+  for (int i = tid; i < 256; i += 64 * kRtBigWaves) hist[i] = 0;
+
+  const int nks = d / 32;
+  const int ks0 = w * nks / kRtBigWaves, ks1 = (w + 1) * nks / kRtBigWaves;
+  const uint16_t* brow[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) brow[m] = hidden + (size_t)min(t0 + 16 * m + j, T - 1) * d + 8 * g;
+  const uint16_t* arow = wt + (size_t)j * d + 8 * g;
+  const size_t tile = (size_t)16 * d;                 // next 16 experts of WT
+
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int et = 0; et < NT; ++et) acc[m][et] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // whole batches of KB steps, double-buffered; the remaining steps one at a time
+  uint4 bv[2][KB][MT], av[2][KB][NT];
+#define MOE_RT_LOAD(B, NB, K0)                                                              \
+  do {                                                                                      \
+    _Pragma("unroll") for (int u = 0; u < NB; ++u) {                                        \
+      const int k0 = 32 * ((K0) + u);                                                       \
+      _Pragma("unroll") for (int m = 0; m < MT; ++m)                                        \
+          bv[B][u][m] = *reinterpret_cast<const uint4*>(brow[m] + k0);                      \
+      _Pragma("unroll") for (int et = 0; et < NT; ++et)                                     \
+          av[B][u][et] = *reinterpret_cast<const uint4*>(arow + et * tile + k0);            \
+    }                                                                                       \
+  } while (0)
+#define MOE_RT_MMA(B, NB)                                                                   \
+  do {                                                                                      \
+    __builtin_amdgcn_sched_barrier(0); /* loads issued above stay above the MFMAs */        \
+    _Pragma("unroll") for (int u = 0; u < NB; ++u)                                          \
+        _Pragma("unroll") for (int m = 0; m < MT; ++m)                                      \
+            _Pragma("unroll") for (int et = 0; et < NT; ++et)                               \
+                acc[m][et] = mfma16(av[B][u][et], bv[B][u][m], acc[m][et]);                 \
+  } while (0)
+  const int nb = (ks1 - ks0) / KB;
+  if (nb > 0) MOE_RT_LOAD(0, KB, ks0);
+  int i = 0;
+  for (; i + 2 <= nb; i += 2) {
+    MOE_RT_LOAD(1, KB, ks0 + (i + 1) * KB);
+    MOE_RT_MMA(0, KB);
+    if (i + 2 < nb) MOE_RT_LOAD(0, KB, ks0 + (i + 2) * KB);
+    MOE_RT_MMA(1, KB);
+  }
+  if (i < nb) MOE_RT_MMA(0, KB);
+  for (int ks = ks0 + nb * KB; ks < ks1; ++ks) {
+    MOE_RT_LOAD(0, 1, ks);
+    MOE_RT_MMA(0, 1);
+  }
+#undef MOE_RT_LOAD
+#undef MOE_RT_MMA
+  // acc[m][et][r]: expert 16 et + 4g + r, token 16 m + j.  The waves add their
+  // partial logits into one LDS tile in wave order (fixed order).
+  for (int ww = 0; ww < kRtBigWaves; ++ww) {
+    if (w == ww) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int et = 0; et < NT; ++et)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float& dst = red[16 * m + j][16 * et + 4 * g + r];
+            dst = ww == 0 ? acc[m][et][r] : dst + acc[m][et][r];
+          }
+    }
+    __syncthreads();
+  }
+  const int nt = min(ROWS, T - t0);
+  for (int i = tid; i < ROWS * N; i += 64 * kRtBigWaves) {
+    const int r = i / N, e = i - r * N;
+    const float v = red[r][e] + ((bias != nullptr) ? bias[e] : 0.f);
+    red[r][e] = v;
+    if (r < nt) logits[(size_t)(t0 + r) * N + e] = v;
+  }
+  __syncthreads();
+  if (k <= kTopkThread) {
+    if (tid < nt) topk_thread(&red[tid][0], t0 + tid, N, k, topk_idx, topk_w, hist);
+  } else {
+    for (int r = w; r < nt; r += kRtBigWaves)
+      topk_row(&red[r][0], t0 + r, N, k, topk_idx, topk_w, hist);
+  }
+  __syncthreads();
+  for (int e = tid; e < N; e += 64 * kRtBigWaves)
+    if (hist[e]) atomicAdd(&counts[e], hist[e]);
+}
+
+// Rows of WT: 16 per expert tile, the tile count rounded up to the kernel's
+// power of two (the padding rows are zero).
+static int router_n16(int N) {
+  int nt = 1;
+  while (16 * nt < N) nt <<= 1;
+  return 16 * nt;
+}
+
 // Completes the tokens of a k-split router: sums the KS partial tiles in
 // slice order, adds the bias, writes the logits and runs the top-k epilogue.
 // One block = 4 tokens, 4 waves (one token each).
@@ -313,6 +495,7 @@ static int router_kslices(int T, int d, int N) {
 }
 
 size_t route_ws_bytes(int T, int d, int N) {
+  if (T >= kRtBigT) return static_cast<size_t>(router_n16(N)) * d * sizeof(uint16_t);
   const int ks = router_kslices(T, d, N);
   return ks > 1 ? static_cast<size_t>(ks) * T * N * sizeof(float) : 0;
 }
@@ -350,6 +533,35 @@ __global__ __launch_bounds__(kRtThreads) void router_f32_kernel(
 hipError_t launch_route(const void* hidden, const void* w_router, const float* bias, int T, int d,
                         int N, int k, bool bf16, float* logits, int32_t* topk_idx, float* topk_w,
                         int32_t* counts, void* ws, hipStream_t stream) {
+  if (bf16 && T >= kRtBigT) {
+    const int N16 = router_n16(N);
+    uint16_t* wt = static_cast<uint16_t*>(ws);
+    const auto* h = static_cast<const uint16_t*>(hidden);
+    hipLaunchKernelGGL(router_prep_kernel, dim3((N16 * d + 255) / 256), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(w_router), d, N, N16, wt, counts);
+    // about one block per CU: 16 MT tokens per block (MT <= 4, and 1 beyond 128 experts)
+    const int mt = T >= 4 * 16 * 256 ? 4 : (T >= 2 * 16 * 256 ? 2 : 1);
+    const dim3 block(64 * kRtBigWaves);
+#define MOE_ROUTER_WT(MT, NT)                                                                  \
+  hipLaunchKernelGGL((router_wt_kernel<MT, NT>), dim3((T + 16 * MT - 1) / (16 * MT)), block, 0,  \
+                     stream, h, wt, bias, T, d, N, k, logits, topk_idx, topk_w, counts)
+#define MOE_ROUTER_WT_MT(NT)                                                                   \
+  do {                                                                                         \
+    if (mt == 4) MOE_ROUTER_WT(4, NT);                                                         \
+    else if (mt == 2) MOE_ROUTER_WT(2, NT);                                                    \
+    else MOE_ROUTER_WT(1, NT);                                                                 \
+  } while (0)
+    switch (N16 / 16) {
+      case 1: MOE_ROUTER_WT_MT(1); break;
+      case 2: MOE_ROUTER_WT_MT(2); break;
+      case 4: MOE_ROUTER_WT_MT(4); break;
+      case 8: MOE_ROUTER_WT_MT(8); break;
+      default: MOE_ROUTER_WT(1, 16); break;       // N <= 256
+    }
+#undef MOE_ROUTER_WT_MT
+#undef MOE_ROUTER_WT
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(zero_i32_kernel, dim3((N + 255) / 256), dim3(256), 0, stream, counts, N);
   const dim3 grid((T + kRtTok - 1) / kRtTok), block(kRtThreads);
   if (!bf16) {

@@ -47,7 +47,11 @@ def test_status_strings():
 def test_workspace_sizes():
     assert lib.moe_workspace_size(moe.MOE_OP_ROUTE, 64, 128, 8, 2, 256, F32) == 0
     # bf16 router: partial logits when few token tiles split the hidden dim
-    assert lib.moe_workspace_size(moe.MOE_OP_ROUTE, 8192, 4096, 8, 2, 256, BF16) == 0
+    # bf16 batches of >= 2048 tokens: W_router transposed, 16 rows per expert tile
+    # (tile count rounded up to a power of two)
+    assert lib.moe_workspace_size(moe.MOE_OP_ROUTE, 8192, 4096, 8, 2, 256, BF16) == 16 * 4096 * 2
+    assert lib.moe_workspace_size(moe.MOE_OP_ROUTE, 2048, 1024, 40, 2, 256, BF16) == 64 * 1024 * 2
+    assert lib.moe_workspace_size(moe.MOE_OP_ROUTE, 4096, 2048, 256, 2, 256, BF16) == 256 * 2048 * 2
     assert lib.moe_workspace_size(moe.MOE_OP_ROUTE, 256, 4096, 128, 2, 256, BF16) == 16 * 256 * 128 * 4
     assert lib.moe_workspace_size(moe.MOE_OP_COMBINE, 64, 128, 8, 2, 256, F32) == 0
     # two int32 [chunks, N] tables, chunks of 256 tokens

@@ -86,6 +86,19 @@ def test_uniform_router_exact_ties(moe):
         assert g["aux"] == 1.0
 
 
+@pytest.mark.parametrize("T,N,k", [(2048, 8, 2), (4096, 64, 3), (2048, 40, 16), (2048, 24, 20)])
+def test_uniform_router_exact_ties_large_batch(moe, T, N, k):
+    """The large-batch router (transposed W_router, one thread per token for k <= 16,
+    one wave per token above): with W_router = 0 every logit ties and experts
+    0..k-1 win with weight 1/k."""
+    inp = synth.make_inputs(T, 256, N, k, 128, "bf16", 0.0, 3)
+    inp.w_router[:] = 0
+    rep, g, _, _ = _run(inp, f"uniform_router_T{T}_N{N}_k{k}", audit=False)
+    assert (g["topk_idx"] == np.arange(k)).all()
+    assert np.all(np.abs(g["topk_w"] - 1.0 / k) <= 1e-7)
+    assert abs(g["aux"] - 1.0) <= 1e-6
+
+
 def test_zero_hidden_gives_zero(moe):
     inp = synth.make_inputs(64, 256, 8, 2, 128, "bf16", 0.0, 4)
     inp.hidden[:] = 0

@@ -58,6 +58,11 @@ SMALL = [
     # ~130 row tiles x 2 column tiles: on a 256-CU device the down projection's
     # last round (4 tiles) is split over k into 4 ranges each
     ("bf16_down_ksplit4", 16500, 512, 2, 2, 512, "bf16", 0.0, None),
+    # the large-batch router (>= 2048 tokens): 256 experts (16 expert tiles), 40 experts
+    # (tiles padded to 4) with k = 3 and a capacity cut, and one token below the threshold
+    ("bf16_router_wt_N256", 2048, 256, 256, 2, 128, "bf16", 0.0, None),
+    ("bf16_router_wt_N40_k3", 2048, 256, 40, 3, 128, "bf16", 1.0, None),
+    ("bf16_router_below_threshold", 2047, 256, 40, 3, 128, "bf16", 1.0, None),
 ]
 
 

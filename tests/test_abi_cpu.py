@@ -170,6 +170,13 @@ def test_fp8_entry_points_reject():
     assert lib.moe_expert_down_fp8(P, P, P, P, 8, 256, 192, 64, P, S) == UNS
 
 
+def test_expert_matrix_size_limit():
+    # d * f * 2 bytes >= 2^31: one bf16 expert matrix is past the 31-bit resource range
+    assert lib.moe_expert_up(P, P, P, P, 8, 32768, 32768, 64, BF16, P, S) == UNS
+    assert lib.moe_expert_down(P, P, P, 8, 32768, 32768, 64, BF16, P, P, 1 << 40, S) == UNS
+    assert lib.moe_expert_ffn(P, P, P, P, P, 8, 32768, 32768, 64, BF16, P, P, 1 << 40, S) == UNS
+
+
 def test_expert_up_down_reject():
     assert lib.moe_expert_up(NUL, P, P, P, 8, 256, 256, 64, BF16, P, S) == INV
     assert lib.moe_expert_up(P, P, P, P, 8, 256, 200, 64, BF16, P, S) == UNS

@@ -298,8 +298,8 @@ moe_status moe_combine_backward(const void* dy, const float* y_perm, const int32
  *   ws  moe_workspace_size(MOE_OP_EXPERT_BACKWARD, T, d, N, k, f, dt) bytes,
  *       T*k = max_rows: da [max_rows, f] fp32, [dh1 | dh3] [max_rows, 2f] and
  *       a [max_rows, f] in dtype dt, each padded to 256 bytes.
- *   Limits: those of moe_expert_ffn; for bf16 f a multiple of 256 and
- *   max_rows * f < 2^29.
+ *   Limits: those of moe_expert_ffn; for bf16 f a multiple of 256,
+ *   max_rows * f < 2^29 and max_rows * d < 2^30.
  */
 moe_status moe_expert_backward(const void* x_perm, const void* g_perm, const int32_t* offsets,
                                const void* w1, const void* w3, const void* w2, int N, int d,

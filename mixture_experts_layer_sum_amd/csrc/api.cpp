@@ -277,9 +277,11 @@ moe_status moe_expert_backward(const void* x_perm, const void* g_perm, const int
     return MOE_ERR_INVALID_ARG;
   moe_status s = check_expert_shape(N, d, f, max_rows, dt);
   if (s != MOE_OK) return s;
-  // bf16: 256-column tiles over f, and 32-bit buffer offsets into [rows, 2f]
+  // bf16: 256-column tiles over f, and 31-bit buffer ranges over an expert's rows of
+  // [dh1 | dh3] ([rows, 2f]) and of x_perm / g_perm ([rows, d])
   if (dt == MOE_BF16 && (f % 256 != 0 ||
-                         static_cast<int64_t>(max_rows) * f >= (int64_t{1} << 29)))
+                         static_cast<int64_t>(max_rows) * f >= (int64_t{1} << 29) ||
+                         static_cast<int64_t>(max_rows) * d >= (int64_t{1} << 30)))
     return MOE_ERR_UNSUPPORTED;
   const size_t need = moe::expert_backward_ws_bytes(d, f, max_rows, dt == MOE_BF16);
   if (ws_bytes < need) return MOE_ERR_WORKSPACE;

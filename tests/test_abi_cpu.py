@@ -228,6 +228,8 @@ def test_backward_entry_points_reject():
                                    S) == UNS
     assert lib.moe_expert_backward(P, P, P, P, P, P, 8, 256, 16384, 1 << 15, BF16, P, P, P, P, P,
                                    big, S) == UNS
+    assert lib.moe_expert_backward(P, P, P, P, P, P, 8, 65536, 256, 1 << 14, BF16, P, P, P, P, P,
+                                   big, S) == UNS
     assert lib.moe_expert_backward(P, P, P, P, P, P, 8, 256, 256, 64, BF16, P, P, P, P, P, 1000,
                                    S) == WS
     assert lib.moe_expert_backward(P, P, P, P, P, P, 8, 256, 256, 64, BF16, P, P, P, P, NUL, big,

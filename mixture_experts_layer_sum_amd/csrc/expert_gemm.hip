@@ -12,30 +12,36 @@
 //
 // bf16 path (MFMA): a block computes a 256-row x 256-column tile with 8 waves,
 // two per SIMD: the SIMDs split the tile 2 x 2 into 128 x 128 quadrants and
-// the two waves of a SIMD take 64 columns each (128 x 64 per wave on 32x32x16
-// bf16 MFMAs, fp32 accumulators), so one wave's MFMAs overlap the other's LDS
-// reads and load issue.  For `up` the 256 columns are 128 columns of W1 and
-// the same 128 columns of W3, and each wave holds 32 columns of each, so both
-// halves of its SwiGLU products are in the same lane.
-// k advances 64 at a time through two 64 KB LDS stages filled by direct
-// buffer -> LDS loads (no VGPRs in flight; every request is a whole 128-byte
-// line).  The texture unit accepts these loads at about 64 bytes per clock
-// per CU, so a 64 KB stage keeps it busy for about half of the stage's MFMA
-// time, and a wave waiting to issue a load cannot issue MFMAs.  Only one wave
-// of each SIMD loads (16 instructions per stage, two per MFMA of the slice
-// that follows the barrier); the other wave only computes and keeps the
-// matrix core busy meanwhile.
+// the two waves of a SIMD take 64 columns each (128 x 64 per wave: 8 x 4
+// blocks of the 16x16x32 bf16 MFMA, fp32 accumulators), so one wave's MFMAs
+// overlap the other's LDS reads and load issue.  Under the chip's power limit
+// the 16x16x32 MFMA sustains a higher clock than the 32x32x16 one for the same
+// work (an MFMA-only loop on random data measured 1.90 vs 1.75 PFLOP/s); the
+// LDS bytes per flop depend on the 128 x 64 wave tile only, not on the MFMA
+// shape.  For `up` the 256 columns are 128 columns of W1 and the same 128
+// columns of W3, and each wave holds 32 columns of each, so both halves of its
+// SwiGLU products are in the same lane.
+// k advances 64 at a time (two 32-deep MFMA slices) through two 64 KB LDS
+// stages filled by direct buffer -> LDS loads (no VGPRs in flight; every
+// request is a whole 128-byte line).  The texture unit accepts these loads at
+// about 64 bytes per clock per CU, so a 64 KB stage keeps it busy for about
+// half of the stage's MFMA time, and a wave waiting to issue a load cannot
+// issue MFMAs.  Only one wave of each SIMD loads (16 instructions per stage,
+// one per two MFMAs of the slice that follows the barrier); the other wave
+// only computes and keeps the matrix core busy meanwhile.
 // A (x_perm rows) is stored row-major and read with ds_read_b128; the
 // weights stay n-contiguous in LDS and the MFMA B operand (8 consecutive k per
 // lane) is assembled with the gfx950 transposing read ds_read_b64_tr_b16.
 // Both LDS layouts are XOR-swizzled per row so that the fragment reads are
 // bank-conflict free.  One barrier per k-step, placed after the last
 // fragment read of the current stage: the stage is refilled two steps ahead
-// while the last slice's MFMAs run.
+// while the second slice's MFMAs run.
 // A wave's four 32-row sub-tiles are tile rows 32 (2i + wm) (the two row
 // halves interleave), so in an expert's last, partial tile both halves have
 // about the same number of real rows; sub-tiles with no real row skip their
-// fragment reads and MFMAs (the loop is instantiated per count).
+// fragment reads and MFMAs (the loop is instantiated per count).  Rows past
+// the tile's end lie past the range of the A buffer resource and load as
+// zeros.
 // The row tiles of all experts are numbered consecutively; a block finds its
 // expert with a wave-wide prefix scan of the per-expert tile counts read from
 // `offsets` on the device, so the host never needs the routing result.
@@ -112,47 +118,68 @@ constexpr int kBK = 64;
 // Direct global -> LDS loads of one 64-deep k-step into the stage at `dst`
 // (32768 elements): A at element 0, B sub-tile q at 16384 + 8192 q.  Only the
 // four waves w = 0..3 load (8 A and 8 B instructions each).
+struct LoadState {
+  uint32_t a_v0, a_v1, b_v;     // per-lane parts of the A (row parity 0 / 1) and B offsets
+  uint32_t a_u, b_u;            // wave-uniform parts
+  uint32_t a_step, b_step;      // bytes between this wave's consecutive A / B instructions
+};
 __device__ __forceinline__ void gemm_issue(uint16_t* __restrict__ dst, __amdgpu_buffer_rsrc_t a_rs,
-                                           __amdgpu_buffer_rsrc_t b_rs, const uint32_t* a_off,
-                                           const uint32_t* b_off, int w, int kstep, int Nout) {
+                                           __amdgpu_buffer_rsrc_t b_rs, const LoadState& L, int w,
+                                           int kstep, int Nout) {
   const uint32_t ka = (uint32_t)kstep * (kBK * 2);
   const uint32_t kb = (uint32_t)kstep * (uint32_t)(kBK * Nout * 2);
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, (lds_void*)(dst + (8 * w + i) * 512), 16,
-                                             a_off[i] + ka, 0, 0, 0);
+                                             ((i & 1) ? L.a_v1 : L.a_v0) + (L.a_u + i * L.a_step + ka), 0, 0, 0);
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rs, (lds_void*)(dst + 16384 + (8 * w + i) * 512), 16,
-                                             b_off[i] + kb, 0, 0, 0);
+                                             L.b_v + (L.b_u + i * L.b_step + kb), 0, 0, 0);
 }
 
-template <int NV>
-__device__ __forceinline__ void gemm_frags(const uint16_t* __restrict__ st, int s2,
-                                           const int (&a_rd)[4][4], const int (&b_rd)[4][2][2],
-                                           uint4 (&fa)[4], uint4 (&fb)[2]) {
-  if (NV == 0) return;
-  const uint16_t* bs_ = st + 16384;
+
+// Fragments of the 16x16x32 MFMA (lane l: row / column l % 16, k values
+// 8 (l / 16) .. +7 of a 32-deep slice).  A row block ib of slice s is one
+// ds_read_b128 at a_base[s] + 4096 (ib / 2) + 1024 (ib % 2); B column block
+// jb = 2 j + jj is two transposing reads at b_base[j] + 16 jj + 4096 s (k rows
+// +0..3 and +4..7 of the lane group).
+__device__ __forceinline__ uint4 rd_b(const uint16_t* __restrict__ st, int b_addr) {
+  const uint16_t* p = st + 16384 + b_addr;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p + 512));
+  const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+  return make_uint4(l2.x, l2.y, h2.x, h2.y);
+}
+
+__device__ __forceinline__ uint4 rd_a(const uint16_t* __restrict__ st, int a_addr, int ib) {
+  return *reinterpret_cast<const uint4*>(st + a_addr + 4096 * (ib >> 1) + 1024 * (ib & 1));
+}
+
+__device__ __forceinline__ void rd_bs(const uint16_t* __restrict__ st, const int (&b_base)[2], int s,
+                                      uint4 (&fb)[4]) {
 #pragma unroll
-  for (int i = 0; i < NV; ++i) fa[i] = *reinterpret_cast<const uint4*>(st + a_rd[s2][i]);
+  for (int jb = 0; jb < 4; ++jb) fb[jb] = rd_b(st, b_base[jb >> 1] + 16 * (jb & 1) + 4096 * s);
+}
+
+// The 32 MFMAs of one slice for the NB row blocks that hold rows (A in fa, B
+// in fb).  Each A register is refilled with the next slice's fragment (slice
+// ns of stage nst) right after its last use; with ROLLB the B registers are
+// refilled the same way during the last row block (fewer registers live),
+// otherwise the caller reads the next B into registers of its own first.
+template <int NB, bool ROLLB>
+__device__ __forceinline__ void slice_mma(uint4 (&fb)[4], uint4 (&fa)[8], f32x4 (&acc)[8][4],
+                                          const uint16_t* __restrict__ nst, const int (&a_base)[2],
+                                          const int (&b_base)[2], int ns) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)(bs_ + b_rd[s2][j][0]));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)(bs_ + b_rd[s2][j][1]));
-    const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-    fb[j] = make_uint4(l2.x, l2.y, h2.x, h2.y);
+  for (int ib = 0; ib < NB; ++ib) {
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+      acc[ib][jb] = mfma16(fa[ib], fb[jb], acc[ib][jb]);
+      if (ROLLB && ib == NB - 1) fb[jb] = rd_b(nst, b_base[jb >> 1] + 16 * (jb & 1) + 4096 * ns);
+    }
+    fa[ib] = rd_a(nst, a_base[ns], ib);
   }
-}
-
-template <int NV>
-__device__ __forceinline__ void gemm_mma(const uint4 (&fa)[4], const uint4 (&fb)[2],
-                                         f32x16 (&acc)[4][2]) {
-#pragma unroll
-  for (int i = 0; i < NV; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
 }
 
 // Wait until this wave's LDS reads are done and all of its direct loads have
@@ -160,47 +187,72 @@ __device__ __forceinline__ void gemm_mma(const uint4 (&fa)[4], const uint4 (&fb)
 // (no load in it), so that no LDS access moves across it.
 #define MOE_WAIT_BARRIER() asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
-// One 64-deep k-step.  On entry fa0/fb0 hold the first 16-deep slice of the
-// step (stage `cur`).  The barrier after the last fragment read of `cur`
-// certifies that every wave is done with it and that the next step has
-// landed in `nxt`; `cur` is then refilled two steps ahead while the last
-// slice's MFMAs run, and the next step's first slice is read from `nxt`.
-// `dst` is `cur`: a separate restrict parameter only so that the refill
-// carries its own alias scope and reading `nxt` does not wait for it.
-template <int NV, bool DMA>
+// One 64-deep k-step (two 32-deep slices).  On entry fa/fb hold slice 0 of
+// stage `cur`.  The barrier after the last fragment read of `cur` certifies
+// that every wave is done with it and that the next step has landed in `nxt`;
+// `cur` is then refilled two steps ahead while slice 1's MFMAs run, and the
+// next step's slice 0 is read from `nxt`.  `dst` is `cur`: a separate restrict
+// parameter only so that the refill carries its own alias scope and reading
+// `nxt` does not wait for it.
+template <int NB, bool DMA, bool ROLLB>
 __device__ __forceinline__ void gemm_step(const uint16_t* __restrict__ cur, uint16_t* __restrict__ dst,
                                           const uint16_t* __restrict__ nxt,
                                           __amdgpu_buffer_rsrc_t a_rs, __amdgpu_buffer_rsrc_t b_rs,
-                                          const uint32_t* a_off, const uint32_t* b_off, int w,
-                                          int kstep, int Nout, const int (&a_rd)[4][4],
-                                          const int (&b_rd)[4][2][2], f32x16 (&acc)[4][2],
-                                          uint4 (&fa0)[4], uint4 (&fb0)[2]) {
-  uint4 fa1[4], fb1[2];
-  gemm_frags<NV>(cur, 1, a_rd, b_rd, fa1, fb1);
-  gemm_mma<NV>(fa0, fb0, acc);
-  gemm_frags<NV>(cur, 2, a_rd, b_rd, fa0, fb0);
-  gemm_mma<NV>(fa1, fb1, acc);
-  gemm_frags<NV>(cur, 3, a_rd, b_rd, fa1, fb1);
-  gemm_mma<NV>(fa0, fb0, acc);
+                                          const LoadState& Ld, int w, int kstep, int Nout,
+                                          const int (&a_base)[2], const int (&b_base)[2],
+                                          f32x4 (&acc)[8][4], uint4 (&fa)[8], uint4 (&fb)[4]) {
+  uint4 fb1[4];
+  if (NB > 0) {
+    if (ROLLB) {
+      slice_mma<NB, true>(fb, fa, acc, cur, a_base, b_base, 1);
+    } else {
+      rd_bs(cur, b_base, 1, fb1);
+      slice_mma<NB, false>(fb, fa, acc, cur, a_base, b_base, 1);
+    }
+  }
   MOE_WAIT_BARRIER();
-  if (DMA && NV == 4) {
-    // the refill is interleaved with the last slice's MFMAs, two loads per
-    // MFMA, so that this wave's MFMAs run while it waits to issue its loads
-    gemm_frags<NV>(nxt, 0, a_rd, b_rd, fa0, fb0);
-    gemm_issue(dst, a_rs, b_rs, a_off, b_off, w, kstep, Nout);
-    gemm_mma<NV>(fa1, fb1, acc);
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+  if (DMA && NB == 8) {
+    // the refill is interleaved with slice 1's MFMAs, one load per two MFMAs,
+    // so that this wave's MFMAs run while it waits to issue its loads
+    if (ROLLB) {
+      gemm_issue(dst, a_rs, b_rs, Ld, w, kstep, Nout);
+      slice_mma<NB, true>(fb, fa, acc, nxt, a_base, b_base, 0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < 7; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 9, 0);
+    } else {
+      rd_bs(nxt, b_base, 0, fb);
+      gemm_issue(dst, a_rs, b_rs, Ld, w, kstep, Nout);
+      slice_mma<NB, false>(fb1, fa, acc, nxt, a_base, b_base, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   } else {
-    if (DMA) gemm_issue(dst, a_rs, b_rs, a_off, b_off, w, kstep, Nout);
+    if (DMA) gemm_issue(dst, a_rs, b_rs, Ld, w, kstep, Nout);
     __builtin_amdgcn_sched_barrier(0);     // keep the refill right after the barrier
-    gemm_frags<NV>(nxt, 0, a_rd, b_rd, fa0, fb0);
-    gemm_mma<NV>(fa1, fb1, acc);
+    if (NB > 0) {
+      if (ROLLB) {
+        slice_mma<NB, true>(fb, fa, acc, nxt, a_base, b_base, 0);
+      } else {
+        rd_bs(nxt, b_base, 0, fb);
+        slice_mma<NB, false>(fb1, fa, acc, nxt, a_base, b_base, 0);
+      }
+    }
   }
 }
 
@@ -258,7 +310,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int sm = w & 3, pw = w >> 2;        // SIMD quadrant, half of it
   const int wm = sm & 1, wn = sm >> 1;
-  const int l32 = lane & 31, h = lane >> 5;
   const int n0 = UP ? nt * (kBN / 2) : nt * kBN;
   const int tile_rows = min(rend - r0, kBM);
 
@@ -275,61 +326,52 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
   // (8 rows each) and B instructions 8w..8w+7 (4 k-rows of sub-tile (8w+i) / 16);
   // waves 4..7 only compute, so on every SIMD one wave keeps issuing MFMAs while
   // the other waits for the texture unit to accept its loads.
-  uint32_t a_off[8], b_off[8];
+  // Rows past the tile's end lie past the A resource's range and load as zeros.
   const int wl = w & 3;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int a = 8 * wl + i;                                 // A instruction: 8 rows
-    int row = 8 * a + (lane >> 3);
-    row = row < tile_rows ? row : tile_rows - 1;             // rows past the end repeat the last one
-    const int c = (lane & 7) ^ ((row >> 1) & 7);
-    a_off[i] = (uint32_t)((row * K + 8 * c) * 2);
-    const int b = 8 * wl + i;                                 // B instruction: 4 k-rows of sub-tile b / 16
-    const int kr = 4 * (b & 15) + (lane >> 4);
-    const int cb = (lane & 15) ^ (4 * (kr & 3));
-    const int colbase = UP ? n0 : n0 + 128 * (b >> 4);
-    b_off[i] = (uint32_t)((kr * Nout + colbase + 8 * cb) * 2);
+  LoadState Ld;
+  {
+    const int rl = lane >> 3;                               // row within an 8-row instruction
+    Ld.a_v0 = (uint32_t)((rl * K + 8 * ((lane & 7) ^ (lane >> 4))) * 2);
+    Ld.a_v1 = (uint32_t)((rl * K + 8 * ((lane & 7) ^ (4 + (lane >> 4)))) * 2);
+    Ld.a_u = (uint32_t)(16 * K * 8 * wl);
+    Ld.a_step = (uint32_t)(16 * K);
+    const int cb = (lane & 15) ^ (4 * (lane >> 4));
+    Ld.b_v = (uint32_t)(((lane >> 4) * Nout + 8 * cb) * 2);
+    const int colbase = UP ? n0 : n0 + 128 * (wl >> 1);
+    Ld.b_u = (uint32_t)((32 * (wl & 1) * Nout + colbase) * 2);
+    Ld.b_step = (uint32_t)(8 * Nout);
   }
   const __amdgpu_buffer_rsrc_t b_rs = (wl >> 1) ? b_rs1 : b_rs0;   // wave-uniform
 
-  f32x16 acc[4][2];
+  f32x4 acc[8][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
 
-  // fragment addresses (element offsets inside a stage)
-  // A: row wm*128 + 32i + l32, chunk 2s + h  (s = 16-deep sub-step)
-  int a_rd[4][4];
+  // A: row block ib = rows 64 (ib >> 1) + 32 wm + 16 (ib & 1) + (lane & 15),
+  // chunk 4 s + (lane >> 4); the swizzle depends on the lane only
+  int a_base[2];
+  {
+    const int row = 32 * wm + (lane & 15);
 #pragma unroll
-  for (int s2 = 0; s2 < 4; ++s2)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 32 * (2 * i + wm) + l32;
-      a_rd[s2][i] = row * 64 + 8 * ((2 * s2 + h) ^ ((row >> 1) & 7));
-    }
-  // B (transposing read): 16-lane group gq = lane / 16 covers columns
-  // 16*(gq & 1) .. +15 of the 32-column fragment and k rows 8*(gq >> 1) + 4t .. +3;
-  // lane i of the group points at row (i / 4), columns 4*(i % 4) .. +3.
-  int b_rd[4][2][2];
+    for (int s2 = 0; s2 < 2; ++s2) a_base[s2] = row * 64 + 8 * ((4 * s2 + (lane >> 4)) ^ ((row >> 1) & 7));
+  }
+  // B (transposing read): group gq = lane / 16 covers k rows 8 gq + 4 t .. +3 of the
+  // slice; lane i of the group points at row i / 4, columns 4 (i % 4) .. +3
+  int b_base[2];
   {
     const int gq = lane >> 4, i16 = lane & 15;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      // UP: j = 0 -> W1 (sub-tile 0), j = 1 -> the same W3 columns (sub-tile 1)
       const int q = UP ? j : wn;
       const int cb = UP ? (wn * 64 + 32 * pw) : (64 * pw + 32 * j);
-      const int col = cb + 16 * (gq & 1) + 4 * (i16 & 3);
-#pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int kr = 16 * s2 + 8 * (gq >> 1) + 4 * t + (i16 >> 2);
-          const int c = (col >> 3) ^ (4 * (kr & 3));
-          b_rd[s2][j][t] = q * (64 * 128) + kr * 128 + 8 * c + (col & 7);
-        }
+      const int col = cb + 4 * (i16 & 3);
+      const int kr = 8 * gq + (i16 >> 2);
+      const int c = (col >> 3) ^ (4 * (kr & 3));
+      b_base[j] = q * (64 * 128) + kr * 128 + 8 * c + (col & 7);
     }
   }
 
@@ -339,22 +381,25 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
       min(4, max(0, (tile_rows - 32 * wm + 63) / 64)));
 #define MOE_KLOOP(NV, D0, D1)                                                                   \
   do {                                                                                          \
-    uint4 fa0[4], fb0[2];                                                                       \
-    gemm_frags<NV>(S0, 0, a_rd, b_rd, fa0, fb0);                                                \
+    uint4 fa[8], fb[4];                                                                         \
+    if (2 * NV > 0) {                                                                           \
+      rd_bs(S0, b_base, 0, fb);                                                                 \
+      _Pragma("unroll") for (int ib = 0; ib < 2 * NV; ++ib) fa[ib] = rd_a(S0, a_base[0], ib);    \
+    }                                                                                           \
     int kt = 0;                                                                                 \
     for (; kt + 2 <= kl; kt += 2) {                                                             \
-      gemm_step<NV, D0>(S0, S0, S1, a_rs, b_rs, a_off, b_off, wl, kb + min(kt + 2, kl - 1),     \
-                        Nout, a_rd, b_rd, acc, fa0, fb0);                                       \
-      gemm_step<NV, D1>(S1, S1, S0, a_rs, b_rs, a_off, b_off, wl, kb + min(kt + 3, kl - 1),     \
-                        Nout, a_rd, b_rd, acc, fa0, fb0);                                       \
+      gemm_step<2 * NV, D0, !UP>(S0, S0, S1, a_rs, b_rs, Ld, wl, kb + min(kt + 2, kl - 1),      \
+                                 Nout, a_base, b_base, acc, fa, fb);                            \
+      gemm_step<2 * NV, D1, !UP>(S1, S1, S0, a_rs, b_rs, Ld, wl, kb + min(kt + 3, kl - 1),      \
+                                 Nout, a_base, b_base, acc, fa, fb);                            \
     }                                                                                           \
     if (kt < kl)                                                                                \
-      gemm_step<NV, D0>(S0, S0, S1, a_rs, b_rs, a_off, b_off, wl, kb + min(kt + 2, kl - 1),     \
-                        Nout, a_rd, b_rd, acc, fa0, fb0);                                       \
+      gemm_step<2 * NV, D0, !UP>(S0, S0, S1, a_rs, b_rs, Ld, wl, kb + min(kt + 2, kl - 1),      \
+                                 Nout, a_base, b_base, acc, fa, fb);                            \
   } while (0)
   if (pw == 0) {
-    gemm_issue(S0, a_rs, b_rs, a_off, b_off, wl, kb, Nout);
-    gemm_issue(S1, a_rs, b_rs, a_off, b_off, wl, kb + min(1, kl - 1), Nout);
+    gemm_issue(S0, a_rs, b_rs, Ld, wl, kb, Nout);
+    gemm_issue(S1, a_rs, b_rs, Ld, wl, kb + min(1, kl - 1), Nout);
     asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // step 0 landed
     switch (nv) {
       case 4: MOE_KLOOP(4, true, true); break;
@@ -380,13 +425,22 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
   // blocks to arrive sums all of its partials in range order (the order, and
   // so the result, does not depend on which block arrives last)
   if (!UP && slot >= 0) {
-    float* mine = part + (size_t)slot * (kBM * kBN);
+    // partial tiles through buffer instructions: the element offset goes in
+    // the scalar offset, so no per-element address register is needed.  (Each
+    // vector element is copied to a float before the bit cast: a bit cast of
+    // the element expression itself compiled to element 0.)
+    const __amdgpu_buffer_rsrc_t mine = __builtin_amdgcn_make_buffer_rsrc(
+        part + (size_t)slot * (kBM * kBN), 0, kBM * kBN * 4, kRsrcWord3);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mine[((i * 2 + j) * 16 + r) * kGemmThreads + tid] = acc[i][j][r];
+        for (int r = 0; r < 4; ++r) {
+          const float v = acc[i][j][r];
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), mine, tid * 4,
+                                                ((i * 4 + j) * 4 + r) * kGemmThreads * 4, 0);
+        }
     // every wave's stores are done before the barrier; one wave then makes the
     // block's tile visible device-wide (a release per block, not per wave:
     // each one writes back the XCD's L2)
@@ -401,45 +455,59 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
     }
     __syncthreads();
     if (!s_last) return;
-    const float* first = part + (size_t)tile_sk * segs * (kBM * kBN);
+    const __amdgpu_buffer_rsrc_t all = __builtin_amdgcn_make_buffer_rsrc(
+        part + (size_t)tile_sk * segs * (kBM * kBN), 0, segs * kBM * kBN * 4, kRsrcWord3);
+    for (int q = 0; q < segs; ++q) {
+      const int qo = q * kBM * kBN * 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int el = ((i * 2 + j) * 16 + r) * kGemmThreads + tid;
-          float v = first[el];
-          for (int q = 1; q < segs; ++q) v += first[(size_t)q * (kBM * kBN) + el];
-          acc[i][j][r] = v;
-        }
+          for (int r = 0; r < 4; ++r) {
+            const float v = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(all, tid * 4,
+                                                            qo + ((i * 4 + j) * 4 + r) * kGemmThreads * 4, 0));
+            acc[i][j][r] = q == 0 ? v : acc[i][j][r] + v;
+          }
+    }
   }
 
-  // ---- epilogue
+  // ---- epilogue: block (ib, jb), lane l, element r is row
+  // 64 (ib >> 1) + 32 wm + 16 (ib & 1) + 4 (l >> 4) + r, column 16 (jb & 1) + (l & 15)
+  // of the wave's column group jb >> 1
   if (UP) {
     uint16_t* act = static_cast<uint16_t*>(out);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int ib = 0; ib < 8; ++ib)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = r0 + 32 * (2 * i + wm) + 8 * (r >> 2) + 4 * h + (r & 3);
+      for (int r = 0; r < 4; ++r) {
+        const int row = r0 + 64 * (ib >> 1) + 32 * wm + 16 * (ib & 1) + 4 * (lane >> 4) + r;
         if (row < rend) {
-          const float h1 = acc[i][0][r], h3 = acc[i][1][r];
-          const float gv = h1 * __builtin_amdgcn_rcpf(1.f + __expf(-h1)) * h3;
-          act[(size_t)row * Nout + n0 + wn * 64 + 32 * pw + l32] = f32_to_bf16(gv);
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const float h1 = acc[ib][jj][r], h3 = acc[ib][2 + jj][r];
+            const float gv = h1 * __builtin_amdgcn_rcpf(1.f + __expf(-h1)) * h3;
+            act[(size_t)row * Nout + n0 + wn * 64 + 32 * pw + 16 * jj + (lane & 15)] = f32_to_bf16(gv);
+          }
         }
       }
   } else {
-    float* y = static_cast<float*>(out);
+    // buffer stores over the tile's rows: rows past the tile's end fall outside
+    // the resource's range and are dropped
+    const __amdgpu_buffer_rsrc_t y_rs = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<float*>(out) + (size_t)r0 * Nout, 0, tile_rows * Nout * 4, kRsrcWord3);
+    const int vbase = ((32 * wm + 4 * (lane >> 4)) * Nout + n0 + wn * 128 + 64 * pw + (lane & 15)) * 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int ib = 0; ib < 8; ++ib)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = r0 + 32 * (2 * i + wm) + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (row < rend) {
+      for (int r = 0; r < 4; ++r) {
+        const int vo = vbase + (64 * (ib >> 1) + 16 * (ib & 1) + r) * Nout * 4;
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-            y[(size_t)row * Nout + n0 + wn * 128 + 64 * pw + 32 * j + l32] = acc[i][j][r];
+        for (int jb = 0; jb < 4; ++jb) {
+          const float v = acc[ib][jb][r];
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), y_rs,
+                                                vo + (32 * (jb >> 1) + 16 * (jb & 1)) * 4, 0, 0);
         }
       }
   }

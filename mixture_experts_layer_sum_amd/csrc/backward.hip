@@ -24,8 +24,9 @@
 //              dW_router = hidden^T dlogit;  dbias = sum_t dlogit[t]
 //
 // bf16 GEMMs run on one MFMA tile kernel with the forward's structure (256 x
-// 256 tiles, 8 waves, two 64 KB LDS stages filled by direct buffer -> LDS
-// loads issued by one wave per SIMD) and a template per step that sets how
+// 256 tiles, 8 waves of 128 x 64 on 16x16x32 bf16 MFMAs, two 64 KB LDS stages
+// filled by direct buffer -> LDS loads issued by one wave per SIMD) and a
+// template per step that sets how
 // each operand is laid out in memory: k-contiguous operands (x, g, dh rows;
 // W2 and W1/W3 read as their transposes) are staged row-major and read with
 // ds_read_b128; m- or n-contiguous operands (W1/W3 in the recompute, every
@@ -101,44 +102,51 @@ __device__ __forceinline__ uint4 frag_tr(const uint16_t* p) {
   return make_uint4(l2.x, l2.y, h2.x, h2.y);
 }
 
-// Fragment reads of 16-deep slice s2 of a stage: A sub-tiles i < NV, B sub-tiles j < 2.
-// Row-major operands: element offset base + 4096 i (A) / 2048 j (B), base per s2.
-// Transposed operands: base per sub-tile + 2048 s2.
-template <int NV, bool AT, bool BT>
-__device__ __forceinline__ void frags(const uint16_t* __restrict__ st, int s2,
-                                      const int (&a_rd)[4], const int (&b_rd)[4], uint4 (&fa)[4],
-                                      uint4 (&fb)[2]) {
-  if (NV == 0) return;
+// Fragments of the 16x16x32 MFMA (lane l: row / column l % 16, k values
+// 8 (l / 16) .. +7 of a 32-deep slice s).  A row blocks ib (16 rows each) and
+// B column blocks jb (16 columns each); two base addresses per operand:
+//   row-major A:  ab[s] + 4096 (ib / 2) + 1024 (ib % 2)
+//   transposed A: ab[(ib / 2) % 2] + 8192 (ib / 4) + 16 (ib % 2) + 4096 s
+//   row-major B:  bb[s] + 1024 jb
+//   transposed B: bb[jb / 2] + 16 (jb % 2) + 4096 s
+template <bool AT>
+__device__ __forceinline__ uint4 rd_a(const uint16_t* __restrict__ st, const int (&ab)[2], int s, int ib) {
+  if (AT) return frag_tr(st + ab[(ib >> 1) & 1] + 8192 * (ib >> 2) + 16 * (ib & 1) + 4096 * s);
+  return *reinterpret_cast<const uint4*>(st + ab[s] + 4096 * (ib >> 1) + 1024 * (ib & 1));
+}
+template <bool BT>
+__device__ __forceinline__ uint4 rd_b(const uint16_t* __restrict__ st, const int (&bb)[2], int s, int jb) {
   const uint16_t* bs = st + 16384;
+  if (BT) return frag_tr(bs + bb[jb >> 1] + 16 * (jb & 1) + 4096 * s);
+  return *reinterpret_cast<const uint4*>(bs + bb[s] + 1024 * jb);
+}
+
+// The MFMAs of one slice for the NB row blocks that hold rows, each fragment
+// register refilled with slice ns of stage nst right after its last use (A
+// row block by row block, B during the last row block).
+template <int NB, bool AT, bool BT>
+__device__ __forceinline__ void slice_mma(uint4 (&fa)[8], uint4 (&fb)[4], f32x4 (&acc)[8][4],
+                                          const uint16_t* __restrict__ nst, const int (&ab)[2],
+                                          const int (&bb)[2], int ns) {
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    if (AT)
-      fa[i] = frag_tr(st + a_rd[i] + 2048 * s2);
-    else
-      fa[i] = *reinterpret_cast<const uint4*>(st + a_rd[s2] + 4096 * i);
-  }
+  for (int ib = 0; ib < NB; ++ib) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    if (BT)
-      fb[j] = frag_tr(bs + b_rd[j] + 2048 * s2);
-    else
-      fb[j] = *reinterpret_cast<const uint4*>(bs + b_rd[s2] + 2048 * j);
+    for (int jb = 0; jb < 4; ++jb) {
+      acc[ib][jb] = mfma16(fa[ib], fb[jb], acc[ib][jb]);
+      if (ib == NB - 1) fb[jb] = rd_b<BT>(nst, bb, ns, jb);
+    }
+    fa[ib] = rd_a<AT>(nst, ab, ns, ib);
   }
 }
 
-template <int NV>
-__device__ __forceinline__ void mma(const uint4 (&fa)[4], const uint4 (&fb)[2],
-                                    f32x16 (&acc)[4][2]) {
-#pragma unroll
-  for (int i = 0; i < NV; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
-}
-
-// Per-lane state of the direct loads issued by one loading wave.
+// Per-lane state of the direct loads issued by one loading wave: instruction i
+// loads at  v[i % 2] + u + i * step + k-step offset  (the two per-lane variants
+// are the swizzles of even and odd 8-row groups of a row-major operand and are
+// equal for a transposed one).
 struct Loader {
   __amdgpu_buffer_rsrc_t a_rs, b_rs0, b_rs1;
-  uint32_t a_off[8], b_off[8];
+  uint32_t a_v0, a_v1, b_v0, b_v1;
+  uint32_t a_u, a_step, b_u, b_step;
   uint32_t a_kstride, b_kstride;
   int ksplit;
   int w;                      // loading wave 0..3
@@ -149,52 +157,46 @@ __device__ __forceinline__ void issue(uint16_t* __restrict__ dst, const Loader& 
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(L.a_rs, (lds_void*)(dst + (8 * L.w + i) * 512), 16,
-                                             L.a_off[i] + ka, 0, 0, 0);
+                                             ((i & 1) ? L.a_v1 : L.a_v0) + (L.a_u + i * L.a_step + ka),
+                                             0, 0, 0);
   const bool hi = kstep >= L.ksplit;
   const __amdgpu_buffer_rsrc_t b_rs = hi ? L.b_rs1 : L.b_rs0;
   const uint32_t kb = (uint32_t)(hi ? kstep - L.ksplit : kstep) * L.b_kstride;
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rs, (lds_void*)(dst + 16384 + (8 * L.w + i) * 512),
-                                             16, L.b_off[i] + kb, 0, 0, 0);
+                                             16, ((i & 1) ? L.b_v1 : L.b_v0) + (L.b_u + i * L.b_step + kb),
+                                             0, 0, 0);
 }
 
 #define MOE_BWD_WAIT_BARRIER() asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
-// One 64-deep k-step (the forward GEMM's schedule): fa0/fb0 hold slice 0 of
-// `cur` on entry; after the barrier that follows the last read of `cur`, the
-// loading waves refill `cur` two steps ahead, interleaved with the last
-// slice's MFMAs, and slice 0 of `nxt` is read.
-template <int NV, bool DMA, bool AT, bool BT>
+// One 64-deep k-step (the forward GEMM's schedule: two 32-deep slices): fa/fb
+// hold slice 0 of `cur` on entry; after the barrier that follows the last
+// read of `cur`, the loading waves refill `cur` two steps ahead, interleaved
+// with slice 1's MFMAs, while slice 0 of `nxt` is read.
+template <int NB, bool DMA, bool AT, bool BT>
 __device__ __forceinline__ void kstep_body(const uint16_t* __restrict__ cur,
                                            uint16_t* __restrict__ dst,
                                            const uint16_t* __restrict__ nxt, const Loader& L,
-                                           int kstep, const int (&a_rd)[4], const int (&b_rd)[4],
-                                           f32x16 (&acc)[4][2], uint4 (&fa0)[4], uint4 (&fb0)[2]) {
-  uint4 fa1[4], fb1[2];
-  frags<NV, AT, BT>(cur, 1, a_rd, b_rd, fa1, fb1);
-  mma<NV>(fa0, fb0, acc);
-  frags<NV, AT, BT>(cur, 2, a_rd, b_rd, fa0, fb0);
-  mma<NV>(fa1, fb1, acc);
-  frags<NV, AT, BT>(cur, 3, a_rd, b_rd, fa1, fb1);
-  mma<NV>(fa0, fb0, acc);
+                                           int kstep, const int (&ab)[2], const int (&bb)[2],
+                                           f32x4 (&acc)[8][4], uint4 (&fa)[8], uint4 (&fb)[4]) {
+  if (NB > 0) slice_mma<NB, AT, BT>(fa, fb, acc, cur, ab, bb, 1);
   MOE_BWD_WAIT_BARRIER();
-  if (DMA && NV == 4) {
-    frags<NV, AT, BT>(nxt, 0, a_rd, b_rd, fa0, fb0);
+  if (DMA && NB == 8) {
     issue(dst, L, kstep);
-    mma<NV>(fa1, fb1, acc);
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    slice_mma<NB, AT, BT>(fa, fb, acc, nxt, ab, bb, 0);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   } else {
     if (DMA) issue(dst, L, kstep);
     __builtin_amdgcn_sched_barrier(0);
-    frags<NV, AT, BT>(nxt, 0, a_rd, b_rd, fa0, fb0);
-    mma<NV>(fa1, fb1, acc);
+    if (NB > 0) slice_mma<NB, AT, BT>(fa, fb, acc, nxt, ab, bb, 0);
   }
 }
 
@@ -243,7 +245,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_bf16_kernel(Args p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int sm = w & 3, pw = w >> 2;
   const int wm = sm & 1, wn = sm >> 1;
-  const int l32 = lane & 31, h = lane >> 5;
   const int n0 = MODE == kSwiGLU ? nt * (kBN / 2) : nt * kBN;
   const int rows = rend - r0;
   const int tile_rows = min(rows, kBM);
@@ -253,6 +254,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_bf16_kernel(Args p) {
   L.w = w & 3;
   L.ksplit = MODE == kDX ? p.ksplit : 0x7FFFFFFF;
   const uint16_t* A = static_cast<const uint16_t*>(p.a) + (size_t)r0 * p.lda;
+  // rows past the tile's end (and, for the weight gradients, k rows past the
+  // expert's last row) lie outside the resource's range and load as zeros
   L.a_rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(A), 0,
                                              (GK ? rows : tile_rows) * p.lda * 2, kRsrcWord3);
   if (GK) {
@@ -273,90 +276,92 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_bf16_kernel(Args p) {
   }
   L.a_kstride = AT ? (uint32_t)(kBK * p.lda * 2) : (uint32_t)(kBK * 2);
   L.b_kstride = BT ? (uint32_t)(kBK * p.ldb * 2) : (uint32_t)(kBK * 2);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int ins = 8 * L.w + i;
+  {
+    // instruction ins = 8 w + i.  Row-major operand: rows 8 ins + lane / 8, chunk
+    // (lane % 8) ^ ((row / 2) % 8) = (lane % 8) ^ (4 (i % 2) + lane / 16).
+    // Transposed operand: sub-tile ins / 16 (= w / 2), k rows 4 (ins % 16) + lane / 16,
+    // chunk (lane % 16) ^ (4 (lane / 16)).
+    const int wl = L.w;
+    const int cbt = (lane & 15) ^ (4 * (lane >> 4));
     if (AT) {
-      const int q = ins >> 4, kr = 4 * (ins & 15) + (lane >> 4);
-      const int cb = (lane & 15) ^ (4 * (kr & 3));
-      L.a_off[i] = (uint32_t)((kr * p.lda + m0 + 128 * q + 8 * cb) * 2);
+      L.a_v0 = L.a_v1 = (uint32_t)(((lane >> 4) * p.lda + 8 * cbt) * 2);
+      L.a_u = (uint32_t)((32 * (wl & 1) * p.lda + m0 + 128 * (wl >> 1)) * 2);
+      L.a_step = (uint32_t)(8 * p.lda);
     } else {
-      int row = 8 * ins + (lane >> 3);
-      const int c = (lane & 7) ^ ((row >> 1) & 7);
-      row = row < tile_rows ? row : tile_rows - 1;         // rows past the end repeat the last one
-      L.a_off[i] = (uint32_t)((row * p.lda + 8 * c) * 2);
+      const int rl = lane >> 3;
+      L.a_v0 = (uint32_t)((rl * p.lda + 8 * ((lane & 7) ^ (lane >> 4))) * 2);
+      L.a_v1 = (uint32_t)((rl * p.lda + 8 * ((lane & 7) ^ (4 + (lane >> 4)))) * 2);
+      L.a_u = (uint32_t)(16 * p.lda * 8 * wl);
+      L.a_step = (uint32_t)(16 * p.lda);
     }
     if (BT) {
-      const int q = ins >> 4, kr = 4 * (ins & 15) + (lane >> 4);
-      const int cb = (lane & 15) ^ (4 * (kr & 3));
-      const int col = (MODE == kSwiGLU ? n0 : n0 + 128 * q) + 8 * cb;
-      L.b_off[i] = (uint32_t)((kr * p.ldb + col) * 2);
+      L.b_v0 = L.b_v1 = (uint32_t)(((lane >> 4) * p.ldb + 8 * cbt) * 2);
+      const int colbase = MODE == kSwiGLU ? n0 : n0 + 128 * (wl >> 1);
+      L.b_u = (uint32_t)((32 * (wl & 1) * p.ldb + colbase) * 2);
+      L.b_step = (uint32_t)(8 * p.ldb);
     } else {
-      const int nrow = 8 * ins + (lane >> 3);
-      const int c = (lane & 7) ^ ((nrow >> 1) & 7);
-      L.b_off[i] = (uint32_t)(((n0 + nrow) * p.ldb + 8 * c) * 2);
+      const int rl = lane >> 3;
+      L.b_v0 = (uint32_t)((rl * p.ldb + 8 * ((lane & 7) ^ (lane >> 4))) * 2);
+      L.b_v1 = (uint32_t)((rl * p.ldb + 8 * ((lane & 7) ^ (4 + (lane >> 4)))) * 2);
+      L.b_u = (uint32_t)((n0 + 64 * wl) * p.ldb * 2);
+      L.b_step = (uint32_t)(16 * p.ldb);
     }
   }
   if (MODE == kSwiGLU && (L.w >> 1)) L.b_rs0 = L.b_rs1;     // sub-tile 1 holds the W3 columns
 
-  // ---- fragment addresses (element offsets inside a stage)
-  int a_rd[4], b_rd[4];
+  // ---- fragment base addresses (element offsets inside a stage)
+  int ab[2], bb[2];
   {
     const int gq = lane >> 4, i16 = lane & 15;
-    const int sw = (l32 >> 1) & 7;
+    const int kr = 8 * gq + (i16 >> 2);                     // transposed reads: k row of the lane
     if (AT) {
+      // row block ib: tile rows 64 (ib / 2) + 32 wm + 16 (ib % 2); base per (ib / 2) % 2
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rb = 32 * (2 * i + wm);
-        const int q = rb >> 7, cl = rb & 127;
-        const int col = cl + 16 * (gq & 1) + 4 * (i16 & 3);
-        const int kr = 8 * (gq >> 1) + (i16 >> 2);
-        a_rd[i] = q * 8192 + kr * 128 + 8 * ((col >> 3) ^ (4 * (kr & 3))) + (col & 7);
+      for (int hb = 0; hb < 2; ++hb) {
+        const int col = 64 * hb + 32 * wm + 4 * (i16 & 3);
+        ab[hb] = kr * 128 + 8 * ((col >> 3) ^ (4 * (kr & 3))) + (col & 7);
       }
     } else {
+      const int row = 32 * wm + i16;
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) a_rd[s2] = (32 * wm + l32) * 64 + 8 * ((2 * s2 + h) ^ sw);
+      for (int s2 = 0; s2 < 2; ++s2) ab[s2] = row * 64 + 8 * ((4 * s2 + gq) ^ ((row >> 1) & 7));
     }
     if (BT) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int q = MODE == kSwiGLU ? j : wn;
         const int cb = MODE == kSwiGLU ? (wn * 64 + 32 * pw) : (64 * pw + 32 * j);
-        const int col = cb + 16 * (gq & 1) + 4 * (i16 & 3);
-        const int kr = 8 * (gq >> 1) + (i16 >> 2);
-        b_rd[j] = q * 8192 + kr * 128 + 8 * ((col >> 3) ^ (4 * (kr & 3))) + (col & 7);
+        const int col = cb + 4 * (i16 & 3);
+        bb[j] = q * 8192 + kr * 128 + 8 * ((col >> 3) ^ (4 * (kr & 3))) + (col & 7);
       }
-      b_rd[2] = b_rd[3] = 0;
     } else {
+      const int row = wn * 128 + 64 * pw + i16;
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2)
-        b_rd[s2] = (wn * 128 + 64 * pw + l32) * 64 + 8 * ((2 * s2 + h) ^ sw);
+      for (int s2 = 0; s2 < 2; ++s2) bb[s2] = row * 64 + 8 * ((4 * s2 + gq) ^ ((row >> 1) & 7));
     }
   }
 
-  f32x16 acc[4][2];
+  f32x4 acc[8][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
 
   const int nv = GK ? 4 : __builtin_amdgcn_readfirstlane(min(4, max(0, (tile_rows - 32 * wm + 63) / 64)));
 #define MOE_BWD_KLOOP(NV, D)                                                               \
   do {                                                                                     \
-    uint4 fa0[4], fb0[2];                                                                  \
-    frags<NV, AT, BT>(S0, 0, a_rd, b_rd, fa0, fb0);                                        \
+    uint4 fa[8], fb[4];                                                                    \
+    _Pragma("unroll") for (int ib = 0; ib < 2 * NV; ++ib) fa[ib] = rd_a<AT>(S0, ab, 0, ib); \
+    _Pragma("unroll") for (int jb = 0; jb < 4; ++jb) fb[jb] = rd_b<BT>(S0, bb, 0, jb);     \
     int kt = 0;                                                                            \
     for (; kt + 2 <= kl; kt += 2) {                                                        \
-      kstep_body<NV, D, AT, BT>(S0, S0, S1, L, min(kt + 2, kl - 1), a_rd, b_rd, acc, fa0,  \
-                                fb0);                                                      \
-      kstep_body<NV, D, AT, BT>(S1, S1, S0, L, min(kt + 3, kl - 1), a_rd, b_rd, acc, fa0,  \
-                                fb0);                                                      \
+      kstep_body<2 * NV, D, AT, BT>(S0, S0, S1, L, min(kt + 2, kl - 1), ab, bb, acc, fa, fb); \
+      kstep_body<2 * NV, D, AT, BT>(S1, S1, S0, L, min(kt + 3, kl - 1), ab, bb, acc, fa, fb); \
     }                                                                                      \
     if (kt < kl)                                                                           \
-      kstep_body<NV, D, AT, BT>(S0, S0, S1, L, min(kt + 2, kl - 1), a_rd, b_rd, acc, fa0,  \
-                                fb0);                                                      \
+      kstep_body<2 * NV, D, AT, BT>(S0, S0, S1, L, min(kt + 2, kl - 1), ab, bb, acc, fa, fb); \
   } while (0)
   if (kl > 0) {
     if (pw == 0) {
@@ -384,13 +389,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_bf16_kernel(Args p) {
   }
 #undef MOE_BWD_KLOOP
 
-  // ---- epilogues.  acc[i][j][r]: tile row 32 (2i + wm) + 8 (r / 4) + 4h + r % 4.
+  // ---- epilogues.  acc[ib][jb][r]: tile row 64 (ib / 2) + 32 wm + 16 (ib % 2) + 4 (lane / 16) + r,
+  // column 16 jb + lane % 16 of the wave's 64 columns (SwiGLU: jb < 2 W1, jb >= 2 the same W3 columns)
+  const int l16 = lane & 15, g4 = 4 * (lane >> 4);
   if (MODE == kSwiGLU) {
     // Stage the tile's da block (256 rows x 128 fp32 columns, 128 KB) in the
     // two LDS stages with direct loads from every wave, so that the epilogue
-    // does not wait on 64 dependent global loads per lane: after every
-    // fragment read and every refill is done, wave w loads rows 32 w .. 32 w + 31
-    // (two 512-byte rows per 1 KB instruction; rows past the tile read zeros).
+    // does not wait on dependent global loads: after every fragment read and
+    // every refill is done, wave w loads rows 32 w .. 32 w + 31 (two 512-byte
+    // rows per 1 KB instruction; rows past the tile read zeros).
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     {
       const __amdgpu_buffer_rsrc_t da_rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -407,47 +414,50 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_bf16_kernel(Args p) {
     const float* da1 = reinterpret_cast<const float*>(S1);
     uint16_t* dh = static_cast<uint16_t*>(p.dh);
     uint16_t* act = static_cast<uint16_t*>(p.act);
-    const int cl = wn * 64 + 32 * pw + l32;
-    const int col = n0 + cl;
     const int f = p.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int ib = 0; ib < 8; ++ib)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int tr = 32 * (2 * i + wm) + 8 * (r >> 2) + 4 * h + (r & 3);
+      for (int r = 0; r < 4; ++r) {
+        const int tr = 64 * (ib >> 1) + 32 * wm + 16 * (ib & 1) + g4 + r;
         const int row = r0 + tr;
         if (row < rend) {
-          const float h1 = acc[i][0][r], h3 = acc[i][1][r];
-          const float g = i < 2 ? da0[tr * 128 + cl] : da1[(tr - 128) * 128 + cl];
-          const float s = __builtin_amdgcn_rcpf(1.f + __expf(-h1));
-          const float sl = h1 * s;
-          dh[(size_t)row * 2 * f + col] = f32_to_bf16(g * h3 * (s + sl * (1.f - s)));
-          dh[(size_t)row * 2 * f + f + col] = f32_to_bf16(g * sl);
-          act[(size_t)row * f + col] = f32_to_bf16(sl * h3);
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const int cl = wn * 64 + 32 * pw + 16 * jj + l16;
+            const int col = n0 + cl;
+            const float h1 = acc[ib][jj][r], h3 = acc[ib][2 + jj][r];
+            const float g = ib < 4 ? da0[tr * 128 + cl] : da1[(tr - 128) * 128 + cl];
+            const float s = __builtin_amdgcn_rcpf(1.f + __expf(-h1));
+            const float sl = h1 * s;
+            dh[(size_t)row * 2 * f + col] = f32_to_bf16(g * h3 * (s + sl * (1.f - s)));
+            dh[(size_t)row * 2 * f + f + col] = f32_to_bf16(g * sl);
+            act[(size_t)row * f + col] = f32_to_bf16(sl * h3);
+          }
         }
       }
   } else if (MODE == kWGrad) {
     const bool low = n0 < p.nsplit;
     float* o = (low ? p.out0 : p.out1) + (size_t)e * p.o_estride;
-    const int cbase = (low ? n0 : n0 - p.nsplit) + wn * 128 + 64 * pw + l32;
+    const int cbase = (low ? n0 : n0 - p.nsplit) + wn * 128 + 64 * pw + l16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int ib = 0; ib < 8; ++ib)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + 32 * (2 * i + wm) + 8 * (r >> 2) + 4 * h + (r & 3);
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + 64 * (ib >> 1) + 32 * wm + 16 * (ib & 1) + g4 + r;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) o[(size_t)row * p.ldo + cbase + 32 * j] = acc[i][j][r];
+        for (int jb = 0; jb < 4; ++jb) o[(size_t)row * p.ldo + cbase + 16 * jb] = acc[ib][jb][r];
       }
   } else {
-    const int cbase = n0 + wn * 128 + 64 * pw + l32;
+    const int cbase = n0 + wn * 128 + 64 * pw + l16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int ib = 0; ib < 8; ++ib)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = r0 + 32 * (2 * i + wm) + 8 * (r >> 2) + 4 * h + (r & 3);
+      for (int r = 0; r < 4; ++r) {
+        const int row = r0 + 64 * (ib >> 1) + 32 * wm + 16 * (ib & 1) + g4 + r;
         if (row < rend) {
 #pragma unroll
-          for (int j = 0; j < 2; ++j) p.out0[(size_t)row * p.ldo + cbase + 32 * j] = acc[i][j][r];
+          for (int jb = 0; jb < 4; ++jb) p.out0[(size_t)row * p.ldo + cbase + 16 * jb] = acc[ib][jb][r];
         }
       }
   }

@@ -406,6 +406,30 @@ def summarize_rocprof(d, out, skip_first=0):
     print(text)
 
 
+def time_skewed(args):
+    """The skewed-routing workload under both overflow policies."""
+    import torch
+    from mixture_experts_layer_sum_amd import synth
+    ks = "skewed_zipf"
+    wsk = synth.WORKLOADS[ks]
+    log(f"generating {wsk.name}")
+    inps = synth.make_workload_inputs(ks, seed=args.seed)
+    devs = upload(inps)
+    sk = {"workload": wsk.name}
+    for pol in ("drop", "reroute"):
+        rs = time_layer(inps, devs, max(args.steps, 20), args.warmup, overflow=pol)
+        fl = layer_flops(inps, rs["A"])
+        sk[pol] = {"ms_per_step": rs["ms_per_step"],
+                   "tokens_per_s": wsk.T / (rs["ms_per_step"] * 1e-3),
+                   "routed_rows": rs["A"], "dropped_assignments": rs["dropped"],
+                   "active_experts": int((rs["kept"] > 0).sum()),
+                   "layer_tflops": fl / (rs["ms_per_step"] * 1e-3) / 1e12,
+                   "up_ms": rs["up_ms"], "down_ms": rs["down_ms"]}
+    del devs
+    torch.cuda.empty_cache()
+    return sk
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -417,6 +441,8 @@ def main():
                     help="skip the Mixtral-shaped layer with one shared expert")
     ap.add_argument("--no-skewed", action="store_true",
                     help="skip the skewed 64-expert workload (drop vs re-route)")
+    ap.add_argument("--only-skewed", action="store_true",
+                    help="time only the skewed-routing workload (both overflow policies) and exit")
     ap.add_argument("--no-main", action="store_true",
                     help="profiling aid: time only the decode-shaped layer (no JSON line)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -453,6 +479,11 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         return 1
+
+    if args.only_skewed:
+        sk = time_skewed(args)
+        log("skewed only: " + ", ".join(f"{p} {sk[p]['ms_per_step']:.3f} ms/step" for p in ("drop", "reroute")))
+        return 0
 
     if args.no_main:
         kd = "decode"
@@ -552,23 +583,7 @@ def main():
         torch.cuda.empty_cache()
 
     if not args.no_skewed:
-        ks = "skewed_zipf"
-        wsk = synth.WORKLOADS[ks]
-        log(f"generating {wsk.name}")
-        inps = synth.make_workload_inputs(ks, seed=args.seed)
-        devs = upload(inps)
-        sk = {"workload": wsk.name}
-        for pol in ("drop", "reroute"):
-            rs = time_layer(inps, devs, max(args.steps, 20), args.warmup, overflow=pol)
-            fl = layer_flops(inps, rs["A"])
-            sk[pol] = {"ms_per_step": rs["ms_per_step"],
-                       "tokens_per_s": wsk.T / (rs["ms_per_step"] * 1e-3),
-                       "routed_rows": rs["A"], "dropped_assignments": rs["dropped"],
-                       "active_experts": int((rs["kept"] > 0).sum()),
-                       "layer_tflops": fl / (rs["ms_per_step"] * 1e-3) / 1e12,
-                       "up_ms": rs["up_ms"], "down_ms": rs["down_ms"]}
-        out["skewed_overflow"] = sk
-        del devs
+        out["skewed_overflow"] = time_skewed(args)
         torch.cuda.empty_cache()
 
     if args.copy_calibration:

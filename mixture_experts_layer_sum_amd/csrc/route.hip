@@ -338,8 +338,10 @@ void router_wt_kernel(
   constexpr int ROWS = 16 * MT;
   constexpr int LD = 16 * NT + 1;
   // k-steps per batch of loads; two batches are in flight (double buffer of
-  // about 96 registers): the next batch is issued before the current one's MFMAs
-  constexpr int KB = (48 / (4 * (MT + NT))) < 1 ? 1 : (48 / (4 * (MT + NT)));
+  // about 96 registers): the next batch is issued before the current one's MFMAs.
+  // The 64-token, 64-expert tile takes two steps per batch (128 registers; 60 ->
+  // 56 us at 16384 tokens, d 4096) since its accumulators leave room for them.
+  constexpr int KB = (MT == 4 && NT == 4) ? 2 : ((48 / (4 * (MT + NT))) < 1 ? 1 : (48 / (4 * (MT + NT))));
   __shared__ float red[ROWS][LD];
   __shared__ int hist[256];
   const int tid = threadIdx.x, lane = tid & 63;

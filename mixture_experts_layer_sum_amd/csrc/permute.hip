@@ -265,42 +265,64 @@ __global__ __launch_bounds__(256) void first_round_scan_kernel(const int32_t* __
   kept1[e] = run < C ? run : C;
 }
 
-// One thread per token: proposals of its dropped slots (logits in fp32, the
-// precision the router produced them in; ties to the lower expert id).
-__global__ __launch_bounds__(256) void propose_kernel(const int32_t* __restrict__ topk_idx,
-                                                      const float* __restrict__ logits,
-                                                      const int32_t* __restrict__ rank1,
-                                                      const int32_t* __restrict__ kept1, int T,
-                                                      int N, int k, int C,
-                                                      int32_t* __restrict__ prop) {
+// One wave per token: proposals of its dropped slots.  The token's logits row
+// is read once (coalesced; fp32, the precision the router produced it in), lane
+// l holding experts l, l + 64, ...; each dropped slot, in slot order, takes the
+// expert with room that the token does not hold yet with the highest logit,
+// ties to the lower expert id (a wave-wide argmax over (logit, -id)).
+constexpr int kProposeWaves = 4;
+__global__ __launch_bounds__(64 * kProposeWaves) void propose_kernel(
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ logits,
+    const int32_t* __restrict__ rank1, const int32_t* __restrict__ kept1, int T, int N, int k,
+    int C, int32_t* __restrict__ prop) {
   __shared__ int room[256];
   for (int e = threadIdx.x; e < 256; e += blockDim.x) room[e] = (e < N) && kept1[e] < C;
   __syncthreads();
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kProposeWaves + (threadIdx.x >> 6);
   if (t >= T) return;
-  unsigned long long taken[4] = {0ull, 0ull, 0ull, 0ull};
-  for (int j = 0; j < k; ++j) {
-    const int e = topk_idx[(size_t)t * k + j];
-    if (e >= 0 && e < N) taken[e >> 6] |= 1ull << (e & 63);
+  float v[4];
+  bool ok[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int e = lane + 64 * c;
+    ok[c] = e < N && room[e];
+    v[c] = e < N ? logits[(size_t)t * N + e] : 0.f;
   }
-  const float* L = logits + (size_t)t * N;
+  for (int j = 0; j < k; ++j) {                  // the token's own experts are not candidates
+    const int e = topk_idx[(size_t)t * k + j];
+    if (e >= 0 && e < N && (e & 63) == lane) ok[e >> 6] = false;
+  }
   for (int j = 0; j < k; ++j) {
     const size_t s = (size_t)t * k + j;
     const int e0 = topk_idx[s];
     int best = -1;
-    if (e0 >= 0 && e0 < N && rank1[s] >= C) {
+    if (e0 >= 0 && e0 < N && rank1[s] >= C) {   // the same for the whole wave
       float bv = 0.f;
-      for (int e = 0; e < N; ++e) {
-        if (!room[e] || ((taken[e >> 6] >> (e & 63)) & 1ull)) continue;
-        const float v = L[e];
-        if (best < 0 || v > bv) {
-          best = e;
-          bv = v;
+      int be = 0x7FFFFFFF;                       // no candidate
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (ok[c] && (be == 0x7FFFFFFF || v[c] > bv)) {
+          bv = v[c];
+          be = lane + 64 * c;
+        }
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) {
+        const float ov = __shfl_xor(bv, m, 64);
+        const int oe = __shfl_xor(be, m, 64);
+        const bool take = oe != 0x7FFFFFFF &&
+                          (be == 0x7FFFFFFF || ov > bv || (ov == bv && oe < be));
+        if (take) {
+          bv = ov;
+          be = oe;
         }
       }
-      if (best >= 0) taken[best >> 6] |= 1ull << (best & 63);
+      if (be != 0x7FFFFFFF) {
+        best = be;
+        if ((be & 63) == lane) ok[be >> 6] = false;
+      }
     }
-    prop[s] = best;
+    if (lane == 0) prop[s] = best;
   }
 }
 
@@ -383,8 +405,9 @@ hipError_t launch_permute_reroute(const void* hidden, const int32_t* topk_idx,
                      base1, kept1);
   hipLaunchKernelGGL(rank_kernel, dim3(nch), dim3(kChunk), 0, stream, topk_idx, T, N, k, base1,
                      rank1);
-  hipLaunchKernelGGL(propose_kernel, dim3((T + 255) / 256), dim3(256), 0, stream, topk_idx,
-                     logits, rank1, kept1, T, N, k, C, prop);
+  hipLaunchKernelGGL(propose_kernel, dim3((T + kProposeWaves - 1) / kProposeWaves),
+                     dim3(64 * kProposeWaves), 0, stream, topk_idx, logits, rank1, kept1, T, N, k,
+                     C, prop);
   hipLaunchKernelGGL(chunk_hist_kernel, dim3(nch), dim3(kChunk), 0, stream, prop, T, N, k, hist2);
   hipLaunchKernelGGL(second_round_scan_kernel, dim3(1), dim3(256), 0, stream, hist2, nch, N, C,
                      kept1, base2, kept, offsets);

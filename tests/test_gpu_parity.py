@@ -155,6 +155,9 @@ REROUTE = [
     ("bf16_reroute_k4", 300, 256, 16, 4, 128, "bf16", 0.5, "skew"),
     ("bf16_reroute_no_room", 64, 256, 8, 2, 128, "bf16", 0.01, "skew"),
     ("bf16_reroute_many_chunks", 1500, 256, 16, 2, 128, "bf16", 0.75, "zipf"),
+    # more experts than a wave has lanes: each lane holds several candidates
+    ("bf16_reroute_N200", 400, 256, 200, 2, 128, "bf16", 0.8, "zipf"),
+    ("bf16_reroute_N256_k3", 300, 256, 256, 3, 128, "bf16", 0.5, "skew"),
 ]
 
 
@@ -170,6 +173,18 @@ def test_reroute_small_shapes(moe, case):
         inp = synth.make_inputs(T, d, N, k, f, dt, cf, seed, bias=b)
         rep, g, _, _ = _run(inp, f"{label}/seed{seed}", overflow="reroute")
         assert (g["kept"] <= max(1, int(np.floor(T * k / N * cf)))).all()
+
+
+@pytest.mark.parametrize("N", [8, 130])
+def test_reroute_exact_ties(moe, N):
+    """W_router = 0: every logit ties, so experts 0..k-1 overflow and each dropped
+    slot is re-routed to the lowest-id expert that has room and that the token
+    does not hold yet (ties to the lower id, also across the lanes of a wave)."""
+    inp = synth.make_inputs(64, 256, N, 2, 128, "bf16", 0.5 if N == 8 else 4.0, 3)
+    inp.w_router[:] = 0
+    rep, g, _, _ = _run(inp, f"reroute_ties_N{N}", audit=False, overflow="reroute")
+    assert (g["topk_idx"] == np.arange(2)).all()
+    assert (g["kept"][2:] > 0).any()
 
 
 def test_reroute_workload_full_size(moe):

@@ -730,7 +730,7 @@ __global__ __launch_bounds__(256) void router_dw_kernel(const void* __restrict__
     dl[t][e] = (t < nt && e < ne) ? dlog[(size_t)(t0 + t) * N + eg + e] : 0.f;
   }
   __syncthreads();
-  if (blockIdx.x == 0 && threadIdx.x < ne) {
+  if (blockIdx.x == 0 && (int)threadIdx.x < ne) {
     float s = 0.f;
     for (int t = 0; t < nt; ++t) s += dl[t][threadIdx.x];
     part_b[(size_t)chunk * N + eg + threadIdx.x] = s;

@@ -34,8 +34,9 @@
  *     are bfloat16 (raw 16-bit patterns); accumulation is fp32.  MOE_F32: all
  *     of them are fp32.  logits, topk_w, y_perm and aux are always fp32.
  *   - Limits: 1 <= k <= N <= 256; T >= 1; d and f multiples of 64; for the
- *     bf16 expert GEMMs also d a multiple of 256 and f of 128; one expert
- *     matrix (d * f elements) under 2^31 bytes; T * k < 2^31.  Outside them:
+ *     bf16 expert GEMMs also d a multiple of 256 and f of 128 and d < 2^21
+ *     (a 256-row fp32 tile of y_perm under 2^31 bytes); one expert matrix
+ *     (d * f elements) under 2^31 bytes; T * k < 2^31.  Outside them:
  *     MOE_ERR_UNSUPPORTED.
  *   - Inputs must be finite; behaviour on NaN/Inf inputs is unspecified.
  *   - Calls on one stream are ordered; calls that share outputs or workspace

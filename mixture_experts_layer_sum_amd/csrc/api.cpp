@@ -37,6 +37,9 @@ moe_status check_expert_shape(int N, int d, int f, int max_rows, moe_dtype dt) {
   if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
   if (N > kMaxExperts || d % 64 != 0 || f % 64 != 0) return MOE_ERR_UNSUPPORTED;
   if (dt == MOE_BF16 && (d % 256 != 0 || f % 128 != 0)) return MOE_ERR_UNSUPPORTED;
+  // the down projection stores a 256-row fp32 tile of y_perm through a buffer
+  // resource with 32-bit offsets
+  if (dt == MOE_BF16 && d >= (1 << 21)) return MOE_ERR_UNSUPPORTED;
   // one expert matrix is addressed through a buffer resource with a 31-bit byte range
   if (static_cast<int64_t>(d) * f * elem_bytes(dt) >= (int64_t{1} << 31)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;

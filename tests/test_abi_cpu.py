@@ -171,6 +171,8 @@ def test_fp8_entry_points_reject():
 
 
 def test_expert_matrix_size_limit():
+    # d >= 2^21: a 256-row fp32 tile of y_perm is past the 32-bit offsets of the down projection
+    assert lib.moe_expert_down(P, P, P, 8, 1 << 21, 128, 64, BF16, P, P, 1 << 40, S) == UNS
     # d * f * 2 bytes >= 2^31: one bf16 expert matrix is past the 31-bit resource range
     assert lib.moe_expert_up(P, P, P, P, 8, 32768, 32768, 64, BF16, P, S) == UNS
     assert lib.moe_expert_down(P, P, P, 8, 32768, 32768, 64, BF16, P, P, 1 << 40, S) == UNS

@@ -32,10 +32,11 @@
 // A (x_perm rows) is stored row-major and read with ds_read_b128; the
 // weights stay n-contiguous in LDS and the MFMA B operand (8 consecutive k per
 // lane) is assembled with the gfx950 transposing read ds_read_b64_tr_b16.
-// Both LDS layouts are XOR-swizzled per row so that the fragment reads are
-// bank-conflict free.  One barrier per k-step, placed after the last
-// fragment read of the current stage: the stage is refilled two steps ahead
-// while the second slice's MFMAs run.
+// Both LDS layouts are XOR-swizzled per row (the weights' also padded every
+// four k-rows) so that the fragment reads are bank-conflict free.  One
+// barrier per k-step, placed after the last fragment read of the current
+// stage: the stage is refilled two steps ahead while the second slice's MFMAs
+// run.
 // A wave's four 32-row sub-tiles are tile rows 32 (2i + wm) (the two row
 // halves interleave), so in an expert's last, partial tile both halves have
 // about the same number of real rows; sub-tiles with no real row skip their
@@ -114,10 +115,13 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kBK = 64;
+// B half of a stage: per 128-column sub-tile, 16 groups of 4 k-rows (the 1 KB
+// that one load instruction writes) each followed by 16 bytes of padding.
+constexpr int kBGroup = 4 * 128 + 8, kBSub = 16 * kBGroup, kStage = 16384 + 2 * kBSub;
 
-// Direct global -> LDS loads of one 64-deep k-step into the stage at `dst`
-// (32768 elements): A at element 0, B sub-tile q at 16384 + 8192 q.  Only the
-// four waves w = 0..3 load (8 A and 8 B instructions each).
+// Direct global -> LDS loads of one 64-deep k-step into the stage at `dst`:
+// A at element 0, B sub-tile q at 16384 + kBSub q.  Only the four waves
+// w = 0..3 load (8 A and 8 B instructions each).
 struct LoadState {
   uint32_t a_v0, a_v1, b_v;     // per-lane parts of the A (row parity 0 / 1) and B offsets
   uint32_t a_u, b_u;            // wave-uniform parts
@@ -134,7 +138,8 @@ __device__ __forceinline__ void gemm_issue(uint16_t* __restrict__ dst, __amdgpu_
                                              ((i & 1) ? L.a_v1 : L.a_v0) + (L.a_u + i * L.a_step + ka), 0, 0, 0);
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rs, (lds_void*)(dst + 16384 + (8 * w + i) * 512), 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rs, (lds_void*)(dst + 16384 + kBSub * (w >> 1) +
+                                                               kBGroup * (8 * (w & 1) + i)), 16,
                                              L.b_v + (L.b_u + i * L.b_step + kb), 0, 0, 0);
 }
 
@@ -142,12 +147,12 @@ __device__ __forceinline__ void gemm_issue(uint16_t* __restrict__ dst, __amdgpu_
 // Fragments of the 16x16x32 MFMA (lane l: row / column l % 16, k values
 // 8 (l / 16) .. +7 of a 32-deep slice).  A row block ib of slice s is one
 // ds_read_b128 at a_base[s] + 4096 (ib / 2) + 1024 (ib % 2); B column block
-// jb = 2 j + jj is two transposing reads at b_base[j] + 16 jj + 4096 s (k rows
-// +0..3 and +4..7 of the lane group).
+// jb = 2 j + jj is two transposing reads at b_base[j] + 16 jj + 8 kBGroup s
+// (k rows +0..3 and, one padded group later, +4..7 of the lane group).
 __device__ __forceinline__ uint4 rd_b(const uint16_t* __restrict__ st, int b_addr) {
   const uint16_t* p = st + 16384 + b_addr;
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p + 512));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p + kBGroup));
   const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
   return make_uint4(l2.x, l2.y, h2.x, h2.y);
 }
@@ -159,7 +164,7 @@ __device__ __forceinline__ uint4 rd_a(const uint16_t* __restrict__ st, int a_add
 __device__ __forceinline__ void rd_bs(const uint16_t* __restrict__ st, const int (&b_base)[2], int s,
                                       uint4 (&fb)[4]) {
 #pragma unroll
-  for (int jb = 0; jb < 4; ++jb) fb[jb] = rd_b(st, b_base[jb >> 1] + 16 * (jb & 1) + 4096 * s);
+  for (int jb = 0; jb < 4; ++jb) fb[jb] = rd_b(st, b_base[jb >> 1] + 16 * (jb & 1) + 8 * kBGroup * s);
 }
 
 // The 32 MFMAs of one slice for the NB row blocks that hold rows (A in fa, B
@@ -176,7 +181,7 @@ __device__ __forceinline__ void slice_mma(uint4 (&fb)[4], uint4 (&fa)[8], f32x4 
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) {
       acc[ib][jb] = mfma16(fa[ib], fb[jb], acc[ib][jb]);
-      if (ROLLB && ib == NB - 1) fb[jb] = rd_b(nst, b_base[jb >> 1] + 16 * (jb & 1) + 4096 * ns);
+      if (ROLLB && ib == NB - 1) fb[jb] = rd_b(nst, b_base[jb >> 1] + 16 * (jb & 1) + 8 * kBGroup * ns);
     }
     fa[ib] = rd_a(nst, a_base[ns], ib);
   }
@@ -256,13 +261,18 @@ __device__ __forceinline__ void gemm_step(const uint16_t* __restrict__ cur, uint
   }
 }
 
-// LDS layout of one stage (64 KB):
+// LDS layout of one stage (kStage elements, 64.5 KB):
 //   A  [256 rows][64 k]   rows of 8 x 16-byte chunks (one full 128-byte line
 //                          of x_perm per row); chunk c of row r sits at
 //                          position c ^ ((r >> 1) & 7)
 //   B  2 sub-tiles [64 k][128 n], rows of 16 chunks; chunk c of row k sits at
-//                          position c ^ (4 * (k & 3))
-// Both swizzles make the fragment reads conflict-free.
+//                          position c ^ (4 * (k & 3)); every 4 k-rows (the 1 KB
+//                          one load instruction writes) are followed by 16
+//                          bytes of padding
+// The A swizzle makes its reads conflict-free.  A 32-lane half of a transposing
+// B read covers k rows r .. r+3 and r+8 .. r+11, which share their swizzle; the
+// padding shifts the second group of rows by two 16-byte bank slots, into the
+// slots the first group leaves free.
 template <bool UP>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
     const uint16_t* __restrict__ X, const int32_t* __restrict__ offsets, int N,
@@ -272,7 +282,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
   // two 64 KB stages as separate LDS objects: the compiler tracks in-flight
   // direct loads per LDS object, so a read of one stage never waits on the
   // refill of the other
-  __shared__ __align__(1024) uint16_t S0[32768], S1[32768];
+  __shared__ __align__(1024) uint16_t S0[kStage], S1[kStage];
   __shared__ int s_last;
 
   const int nk = K / kBK;
@@ -371,7 +381,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
       const int col = cb + 4 * (i16 & 3);
       const int kr = 8 * gq + (i16 >> 2);
       const int c = (col >> 3) ^ (4 * (kr & 3));
-      b_base[j] = q * (64 * 128) + kr * 128 + 8 * c + (col & 7);
+      b_base[j] = q * kBSub + (kr >> 2) * kBGroup + (kr & 3) * 128 + 8 * c + (col & 7);
     }
   }
 

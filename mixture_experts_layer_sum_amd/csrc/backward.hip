@@ -43,6 +43,8 @@ namespace bwd {
 enum Mode { kDA = 0, kDX = 1, kSwiGLU = 2, kWGrad = 3 };
 
 constexpr int kBM = 256, kBN = 256, kBK = 64, kThreads = 512, kGroupM = 8;
+// transposed operand tile: 16-element (32-byte) pad after every 4 k-rows of 128
+constexpr int kTGroup = 4 * 128 + 8, kTSub = 16 * kTGroup, kRegion = 2 * kTSub;
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -97,7 +99,7 @@ __device__ __forceinline__ uint4 frag_tr(const uint16_t* p) {
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) i16x4*)(p));
   const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4*)(p + 512));
+      (__attribute__((address_space(3))) i16x4*)(p + kTGroup));
   const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
   return make_uint4(l2.x, l2.y, h2.x, h2.y);
 }
@@ -106,18 +108,18 @@ __device__ __forceinline__ uint4 frag_tr(const uint16_t* p) {
 // 8 (l / 16) .. +7 of a 32-deep slice s).  A row blocks ib (16 rows each) and
 // B column blocks jb (16 columns each); two base addresses per operand:
 //   row-major A:  ab[s] + 4096 (ib / 2) + 1024 (ib % 2)
-//   transposed A: ab[(ib / 2) % 2] + 8192 (ib / 4) + 16 (ib % 2) + 4096 s
+//   transposed A: ab[(ib / 2) % 2] + kTSub (ib / 4) + 16 (ib % 2) + 8 kTGroup s
 //   row-major B:  bb[s] + 1024 jb
-//   transposed B: bb[jb / 2] + 16 (jb % 2) + 4096 s
+//   transposed B: bb[jb / 2] + 16 (jb % 2) + 8 kTGroup s
 template <bool AT>
 __device__ __forceinline__ uint4 rd_a(const uint16_t* __restrict__ st, const int (&ab)[2], int s, int ib) {
-  if (AT) return frag_tr(st + ab[(ib >> 1) & 1] + 8192 * (ib >> 2) + 16 * (ib & 1) + 4096 * s);
+  if (AT) return frag_tr(st + ab[(ib >> 1) & 1] + kTSub * (ib >> 2) + 16 * (ib & 1) + 8 * kTGroup * s);
   return *reinterpret_cast<const uint4*>(st + ab[s] + 4096 * (ib >> 1) + 1024 * (ib & 1));
 }
 template <bool BT>
 __device__ __forceinline__ uint4 rd_b(const uint16_t* __restrict__ st, const int (&bb)[2], int s, int jb) {
-  const uint16_t* bs = st + 16384;
-  if (BT) return frag_tr(bs + bb[jb >> 1] + 16 * (jb & 1) + 4096 * s);
+  const uint16_t* bs = st + kRegion;
+  if (BT) return frag_tr(bs + bb[jb >> 1] + 16 * (jb & 1) + 8 * kTGroup * s);
   return *reinterpret_cast<const uint4*>(bs + bb[s] + 1024 * jb);
 }
 
@@ -152,11 +154,20 @@ struct Loader {
   int w;                      // loading wave 0..3
 };
 
+// LDS destination of load instruction ins = 8 w + i of an operand region:
+// row-major 1 KB per instruction; transposed 4 k-rows of sub-tile ins / 16,
+// each group of 4 k-rows followed by 16 bytes of padding.
+template <bool TR>
+__device__ __forceinline__ int ldst(int w, int i) {
+  return TR ? kTSub * (w >> 1) + kTGroup * (8 * (w & 1) + i) : (8 * w + i) * 512;
+}
+
+template <bool AT, bool BT>
 __device__ __forceinline__ void issue(uint16_t* __restrict__ dst, const Loader& L, int kstep) {
   const uint32_t ka = (uint32_t)kstep * L.a_kstride;
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(L.a_rs, (lds_void*)(dst + (8 * L.w + i) * 512), 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(L.a_rs, (lds_void*)(dst + ldst<AT>(L.w, i)), 16,
                                              ((i & 1) ? L.a_v1 : L.a_v0) + (L.a_u + i * L.a_step + ka),
                                              0, 0, 0);
   const bool hi = kstep >= L.ksplit;
@@ -164,7 +175,7 @@ __device__ __forceinline__ void issue(uint16_t* __restrict__ dst, const Loader& 
   const uint32_t kb = (uint32_t)(hi ? kstep - L.ksplit : kstep) * L.b_kstride;
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rs, (lds_void*)(dst + 16384 + (8 * L.w + i) * 512),
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rs, (lds_void*)(dst + kRegion + ldst<BT>(L.w, i)),
                                              16, ((i & 1) ? L.b_v1 : L.b_v0) + (L.b_u + i * L.b_step + kb),
                                              0, 0, 0);
 }
@@ -184,7 +195,7 @@ __device__ __forceinline__ void kstep_body(const uint16_t* __restrict__ cur,
   if (NB > 0) slice_mma<NB, AT, BT>(fa, fb, acc, cur, ab, bb, 1);
   MOE_BWD_WAIT_BARRIER();
   if (DMA && NB == 8) {
-    issue(dst, L, kstep);
+    issue<AT, BT>(dst, L, kstep);
     slice_mma<NB, AT, BT>(fa, fb, acc, nxt, ab, bb, 0);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -194,7 +205,7 @@ __device__ __forceinline__ void kstep_body(const uint16_t* __restrict__ cur,
     }
     __builtin_amdgcn_sched_barrier(0);
   } else {
-    if (DMA) issue(dst, L, kstep);
+    if (DMA) issue<AT, BT>(dst, L, kstep);
     __builtin_amdgcn_sched_barrier(0);
     if (NB > 0) slice_mma<NB, AT, BT>(fa, fb, acc, nxt, ab, bb, 0);
   }
@@ -204,15 +215,18 @@ __device__ __forceinline__ int clamp_off(const int32_t* offsets, int e, int max_
   return min(max(offsets[e], lo), max_rows);
 }
 
-// LDS layout of one stage (64 KB): A at element 0, B at 16384.
+// LDS layout of one stage: A region at element 0, B region at kRegion.
 //   row-major operand  [256 rows][64 k]: chunk c of row r at position c ^ ((r >> 1) & 7)
-//   transposed operand 2 x [64 k][128 cols]: chunk c of k-row kr at c ^ (4 (kr & 3))
+//   transposed operand 2 x [64 k][128 cols]: chunk c of k-row kr at c ^ (4 (kr & 3)),
+//     every 4 k-rows followed by 16 bytes of padding (a 32-lane half of a
+//     transposing read covers k rows r .. r+3 and r+8 .. r+11, which share the
+//     swizzle; the padding moves the second group to other banks)
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_bf16_kernel(Args p) {
   constexpr bool AT = MODE == kWGrad;                       // A m-contiguous
   constexpr bool BT = MODE == kSwiGLU || MODE == kWGrad;    // B n-contiguous
   constexpr bool GK = MODE == kWGrad;                       // depth = the expert's rows
-  __shared__ __align__(1024) uint16_t S0[32768], S1[32768];
+  __shared__ __align__(1024) uint16_t S0[2 * kRegion], S1[2 * kRegion];
 
   int e, r0, rend, mt, nt, m0 = 0, kl;
   if (GK) {
@@ -319,7 +333,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_bf16_kernel(Args p) {
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
         const int col = 64 * hb + 32 * wm + 4 * (i16 & 3);
-        ab[hb] = kr * 128 + 8 * ((col >> 3) ^ (4 * (kr & 3))) + (col & 7);
+        ab[hb] = (kr >> 2) * kTGroup + (kr & 3) * 128 + 8 * ((col >> 3) ^ (4 * (kr & 3))) + (col & 7);
       }
     } else {
       const int row = 32 * wm + i16;
@@ -332,7 +346,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_bf16_kernel(Args p) {
         const int q = MODE == kSwiGLU ? j : wn;
         const int cb = MODE == kSwiGLU ? (wn * 64 + 32 * pw) : (64 * pw + 32 * j);
         const int col = cb + 4 * (i16 & 3);
-        bb[j] = q * 8192 + kr * 128 + 8 * ((col >> 3) ^ (4 * (kr & 3))) + (col & 7);
+        bb[j] = q * kTSub + (kr >> 2) * kTGroup + (kr & 3) * 128 + 8 * ((col >> 3) ^ (4 * (kr & 3))) +
+                (col & 7);
       }
     } else {
       const int row = wn * 128 + 64 * pw + i16;
@@ -365,8 +380,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_bf16_kernel(Args p) {
   } while (0)
   if (kl > 0) {
     if (pw == 0) {
-      issue(S0, L, 0);
-      issue(S1, L, min(1, kl - 1));
+      issue<AT, BT>(S0, L, 0);
+      issue<AT, BT>(S1, L, min(1, kl - 1));
       asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
       switch (nv) {
         case 4: MOE_BWD_KLOOP(4, true); break;

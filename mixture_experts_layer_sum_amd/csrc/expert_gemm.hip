@@ -213,6 +213,18 @@ __device__ __forceinline__ void gemm_step(const uint16_t* __restrict__ cur, uint
     } else {
       rd_bs(cur, b_base, 1, fb1);
       slice_mma<NB, false>(fb, fa, acc, cur, a_base, b_base, 1);
+      if (NB == 8) {
+        // the compute waves as well: the next slice's B first, then one A refill
+        // after each row block's MFMAs (left alone, the scheduler reads some A
+        // blocks just before their MFMAs and waits for them)
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
   MOE_WAIT_BARRIER();
@@ -256,6 +268,15 @@ __device__ __forceinline__ void gemm_step(const uint16_t* __restrict__ cur, uint
       } else {
         rd_bs(nxt, b_base, 0, fb);
         slice_mma<NB, false>(fb1, fa, acc, nxt, a_base, b_base, 0);
+        if (NB == 8) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
   }

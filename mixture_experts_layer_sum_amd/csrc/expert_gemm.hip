@@ -49,6 +49,8 @@
 // Blocks are dealt round-robin to the 8 XCDs; each XCD gets a contiguous range
 // of the real tiles, walked 8 row tiles at a time per column tile, so the
 // blocks an XCD runs together share A rows and weight columns in its L2.
+#include <atomic>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -858,17 +860,18 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
 
 static int round8(int x) { return (x + 7) & ~7; }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; calls from several
+// host threads may query the same device concurrently, so the cache is atomic).
 static int device_cus() {
-  static int cus[64];
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cus[dev] == 0) {
-    int v = 0;
+  int v = cus[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cus[dev] = v;
+    cus[dev].store(v, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return v;
 }
 
 __global__ void zero_tickets_kernel(int32_t* __restrict__ p, int n) {

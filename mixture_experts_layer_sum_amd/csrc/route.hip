@@ -195,6 +195,10 @@ __global__ __launch_bounds__(64 * WAVES) void router_bf16_kernel(
   const int j = lane & 15, g = lane >> 4;
   const int t0 = blockIdx.x * ROWS;
   for (int i = tid; i < 256; i += 64 * WAVES) hist[i] = 0;
+  // split over k: counts are only added to by router_finish_kernel, which runs
+  // after this launch, so one block clears them here
+  if (gridDim.y > 1 && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int e = tid; e < N; e += 64 * WAVES) counts[e] = 0;
 
   const uint16_t* arow[MTR];
 #pragma unroll
@@ -564,7 +568,9 @@ hipError_t launch_route(const void* hidden, const void* w_router, const float* b
 #undef MOE_ROUTER_WT
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(zero_i32_kernel, dim3((N + 255) / 256), dim3(256), 0, stream, counts, N);
+  const int KS = bf16 ? router_kslices(T, d, N) : 1;
+  if (KS == 1)     // otherwise the first router block clears the counts
+    hipLaunchKernelGGL(zero_i32_kernel, dim3((N + 255) / 256), dim3(256), 0, stream, counts, N);
   const dim3 grid((T + kRtTok - 1) / kRtTok), block(kRtThreads);
   if (!bf16) {
     hipLaunchKernelGGL(router_f32_kernel, grid, block, 0, stream,
@@ -575,8 +581,7 @@ hipError_t launch_route(const void* hidden, const void* w_router, const float* b
   const auto* h = static_cast<const uint16_t*>(hidden);
   const auto* wr = static_cast<const uint16_t*>(w_router);
   // widest token tile the LDS allows for this N once there are enough tokens
-  // for about one block per CU; otherwise split k across blocks as well
-  const int KS = router_kslices(T, d, N);
+  // for about one block per CU; otherwise split k across blocks as well (KS)
   float* part = static_cast<float*>(ws);
 #define MOE_ROUTER(MTR, NW, WV)                                                                \
   hipLaunchKernelGGL((router_bf16_kernel<MTR, NW, WV, 1>),                                   \

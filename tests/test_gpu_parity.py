@@ -55,6 +55,10 @@ SMALL = [
     # weight-streaming paths: 32-row tiles (some experts need two), 64-row tiles
     ("bf16_rows32_two_tiles", 300, 512, 32, 2, 256, "bf16", 0.0, None),
     ("bf16_rows64", 400, 512, 20, 2, 256, "bf16", 0.0, None),
+    # up projection of the 32-row path: 256-column W1/W3 wave pairs (f % 256 == 0,
+    # three column slices) and the 128-column kernel (f % 256 == 128)
+    ("bf16_rows32_up_f768", 150, 256, 16, 2, 768, "bf16", 0.0, None),
+    ("bf16_rows32_up_f384", 150, 256, 16, 2, 384, "bf16", 0.0, None),
     # ~130 row tiles x 2 column tiles: on a 256-CU device the down projection's
     # last round (4 tiles) is split over k into 4 ranges each
     ("bf16_down_ksplit4", 16500, 512, 2, 2, 512, "bf16", 0.0, None),

@@ -179,13 +179,117 @@ void grouped_gemm_fp8_rows32_kernel(const uint16_t* __restrict__ X,
   }
 }
 
+// Up projection in wave pairs: a block of two waves owns (expert, 32 rows, 256
+// activation columns); wave 0 streams those columns' W1 codes and wave 1 their
+// W3 codes (32 lanes x 8 bytes = 256 contiguous bytes of a k-row, twice the
+// piece of the one-wave layout above), and the scaled SwiGLU halves meet in
+// LDS: wave 0 hands over its W1 sums of the upper 16 accumulator rows, wave 1
+// its W3 sums of the lower 16, and each wave finishes and stores half.
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void grouped_gemm_fp8_rows32_up2_kernel(const uint16_t* __restrict__ X,
+                                        const int32_t* __restrict__ offsets, int N,
+                                        const uint8_t* __restrict__ Q1, const uint8_t* __restrict__ Q3,
+                                        const float* __restrict__ S1, const float* __restrict__ S3,
+                                        int K, int F, int n_slices, int max_rows,
+                                        uint16_t* __restrict__ act) {
+  __shared__ float xch[2][8 * 8 * 64];      // [wave that wrote][c][half-row r][lane]
+  const int mt = blockIdx.x / n_slices, ns = blockIdx.x - mt * n_slices;
+  int e, r0, rend;
+  if (!find_tile(offsets, N, mt, 32, max_rows, e, r0, rend)) return;
+  e = __builtin_amdgcn_readfirstlane(e);
+  r0 = __builtin_amdgcn_readfirstlane(r0);
+  rend = __builtin_amdgcn_readfirstlane(rend);
+
+  const int lane = threadIdx.x & 63, i = lane & 31, h = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int col = ns * 256 + 8 * i;
+  const uint8_t* wsrc = (w == 0 ? Q1 : Q3) + (size_t)e * K * F + col + (size_t)(8 * h) * F;
+  const float* srow = (w == 0 ? S1 : S3) + (size_t)e * F + col;
+  const uint16_t* asrc = X + (size_t)min(r0 + i, rend - 1) * K + 8 * h;
+
+  f32x16 acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[c][r] = 0.f;
+
+  const size_t rstride = (size_t)F;
+  uint2 wb[2][8];
+  uint4 xa[2];
+#define MOE_F8U_LOAD(S, k0)                                                           \
+  do {                                                                               \
+    _Pragma("unroll") for (int kk = 0; kk < 8; ++kk)                                 \
+        wb[S][kk] = load_stream8(wsrc + (size_t)((k0) + kk) * rstride);              \
+    xa[S] = *reinterpret_cast<const uint4*>(asrc + (k0));                            \
+  } while (0)
+#define MOE_F8U_MMA(S)                                                                \
+  do {                                                                               \
+    uint4 rows_[8], bf[8];                                                           \
+    _Pragma("unroll") for (int kk = 0; kk < 8; ++kk) rows_[kk] = widen8(wb[S][kk]);  \
+    transpose8x8(rows_, bf);                                                         \
+    _Pragma("unroll") for (int c = 0; c < 8; ++c) acc[c] = mfma32(xa[S], bf[c], acc[c]); \
+  } while (0)
+
+  const int nk = K / 16;                        // K is a multiple of 64: nk is even
+  MOE_F8U_LOAD(0, 0);
+  for (int kt = 0; kt < nk; kt += 2) {
+    MOE_F8U_LOAD(1, (kt + 1) * 16);
+    MOE_F8U_MMA(0);
+    if (kt + 2 < nk) MOE_F8U_LOAD(0, (kt + 2) * 16);
+    MOE_F8U_MMA(1);
+  }
+#undef MOE_F8U_LOAD
+#undef MOE_F8U_MMA
+
+  float sc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) sc[c] = srow[c];
+
+  // acc[c][r]: row r0 + 8 (r / 4) + 4h + r % 4, column col + c.  Wave 0 keeps
+  // r < 8 and hands over r >= 8; wave 1 the other way round.
+  const int keep = (w == 0) ? 0 : 8;
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+      const float v = ((w == 0) ? acc[c][8 + rr] : acc[c][rr]) * sc[c];
+      xch[w][(c * 8 + rr) * 64 + lane] = v;
+    }
+  __syncthreads();
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr) {
+    float v[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float mine = ((w == 0) ? acc[c][rr] : acc[c][8 + rr]) * sc[c];
+      const float other = xch[1 - w][(c * 8 + rr) * 64 + lane];
+      const float g1 = (w == 0) ? mine : other, g3 = (w == 0) ? other : mine;
+      v[c] = g1 * __builtin_amdgcn_rcpf(1.f + __expf(-g1)) * g3;
+    }
+    const int r = keep + rr;
+    const int row = r0 + 8 * (r >> 2) + 4 * h + (r & 3);
+    if (row < rend) {
+      const uint4 pk = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                  pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+      *reinterpret_cast<uint4*>(act + (size_t)row * F + col) = pk;
+    }
+  }
+}
+
 bool fp8_rows_supported(int max_rows, int N) { return (max_rows + N - 1) / N <= 32; }
 
 hipError_t launch_expert_up_fp8(const void* x_perm, const int32_t* offsets, const uint8_t* w1q,
                                 const uint8_t* w3q, const float* s1, const float* s3, int N,
                                 int d, int f, int max_rows, void* act, hipStream_t stream) {
-  const int n_slices = f / 128;
   const int m_bound = (max_rows + 31) / 32 + N;
+  if (f % 256 == 0) {
+    const int n_slices = f / 256;
+    hipLaunchKernelGGL(grouped_gemm_fp8_rows32_up2_kernel, dim3(m_bound * n_slices), dim3(128), 0,
+                       stream, static_cast<const uint16_t*>(x_perm), offsets, N, w1q, w3q, s1, s3,
+                       d, f, n_slices, max_rows, static_cast<uint16_t*>(act));
+    return hipGetLastError();
+  }
+  const int n_slices = f / 128;
   hipLaunchKernelGGL(grouped_gemm_fp8_rows32_kernel<true>, dim3(m_bound * n_slices), dim3(64), 0,
                      stream, static_cast<const uint16_t*>(x_perm), offsets, N, w1q, w3q, s1, s3, d,
                      f, n_slices, max_rows, act);

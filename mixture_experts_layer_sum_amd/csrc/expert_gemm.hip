@@ -86,6 +86,30 @@ __device__ __forceinline__ void tile_of_logical(int logical, int m_tiles, int n_
   nt = in / gm;
 }
 
+// Row tile `mt` of the 256-row tiling, with each expert's rows spread evenly
+// over its ceil(R / 256) tiles in whole 64-row units (R rows = u units; every
+// tile gets floor(u / n) or one more), so that no tile is a sliver: a tile's
+// cost follows its 64-row blocks only while the matrix cores bound it, and a
+// tile of a few rows costs nearly a full one (it still streams its whole
+// weight slice).  rend is the tile's own end.  Wave-uniform.
+__device__ __forceinline__ bool find_tile_balanced(const int32_t* __restrict__ offsets, int N,
+                                                   int mt, int max_rows, int& e_out, int& r0,
+                                                   int& rend) {
+  int e, t0, t1;
+  if (!find_tile(offsets, N, mt, kBM, max_rows, e, t0, t1)) return false;
+  const int o0 = min(max(offsets[e], 0), max_rows);
+  const int R = t1 - o0;                       // the expert's rows (t1 is its end)
+  const int j = (t0 - o0) / kBM;               // tile index within the expert
+  const int n = (R + kBM - 1) / kBM, u = (R + 63) / 64;
+  const int q = u / n, rem = u - q * n;
+  const int start = 64 * (j * q + min(j, rem));
+  const int size = 64 * (q + (j < rem ? 1 : 0));
+  e_out = e;
+  r0 = o0 + start;
+  rend = min(o0 + start + size, t1);
+  return true;
+}
+
 // Split of the last, partial round of tiles over k.  With `total` tiles on
 // `num_cus` CUs (one block each) the last round holds r = total % num_cus
 // tiles; when that round would leave at least half of the CUs idle, each of
@@ -333,7 +357,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
   int mt, nt;
   tile_of_logical(logical, m_tiles, n_tiles, mt, nt);
   int e, r0, rend;
-  if (!find_tile(offsets, N, mt, kBM, max_rows, e, r0, rend)) return;
+  if (!find_tile_balanced(offsets, N, mt, max_rows, e, r0, rend)) return;
   e = __builtin_amdgcn_readfirstlane(e);
   r0 = __builtin_amdgcn_readfirstlane(r0);
   rend = __builtin_amdgcn_readfirstlane(rend);

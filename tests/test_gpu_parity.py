@@ -50,6 +50,8 @@ SMALL = [
     ("bf16_N256", 70, 256, 256, 2, 128, "bf16", 0.0, None),
     ("bf16_all_dropped", 64, 256, 8, 2, 128, "bf16", 0.01, "skew"),
     ("bf16_big_expert_multi_tile", 1200, 256, 2, 2, 256, "bf16", 0.0, None),
+    # 1025 rows per expert: five 256-row tiles balanced as 256, 256, 192, 192, 129 rows
+    ("bf16_balanced_row_tiles", 1025, 256, 2, 2, 256, "bf16", 0.0, None),
     ("bf16_router_ksplit", 40, 1024, 64, 2, 128, "bf16", 0.0, None),
     ("bf16_router_ksplit_N200", 50, 1024, 200, 3, 128, "bf16", 0.0, None),
     # weight-streaming paths: 32-row tiles (some experts need two), 64-row tiles

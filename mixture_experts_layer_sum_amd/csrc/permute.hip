@@ -195,6 +195,10 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restric
   const int t = blockIdx.x;
   for (int j = threadIdx.x; j < k; j += blockDim.x) srow[j] = slot_row[(size_t)t * k + j];
   __syncthreads();
+  // a token whose every slot was dropped is not read at all (block-uniform)
+  bool kept_any = false;
+  for (int j = 0; j < k; ++j) kept_any |= srow[j] >= 0;
+  if (!kept_any) return;
   const uint4* src = hidden + (size_t)t * vec_per_row;
   for (int v = threadIdx.x; v < vec_per_row; v += blockDim.x) {
     const uint4 x = src[v];

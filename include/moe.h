@@ -91,7 +91,7 @@ size_t moe_workspace_size(moe_op op, int T, int d, int N, int k, int f, moe_dtyp
  *   P1 §2.1 (a small linear layer scores every expert, the top-k scores are
  *   kept and softmax-normalised), P4 §3.1 (logits = hidden . router_w with
  *   router_w [D, E]), P4 §5.3 (equal logits rank by ascending expert id),
- *   P1 §2.3 (tokens_per_expert).
+ *   P1 §2.3 (tokens per expert).
  *
  *   hidden    [T, d]   dtype dt
  *   w_router  [d, N]   dtype dt

@@ -3,9 +3,10 @@
 //
 // cf-1.com/news/5914943 §2.1: the router is one small linear layer; the k
 // best-scoring experts are kept and their scores softmax-normalised.
-// 2kiu.com/news/2885792 §3.1: logits = einsum('bsd,de->bse', hidden, router_w).
+// 2kiu.com/news/2885792 §3.1: the logits contract the hidden dimension of the
+// tokens with the router weight matrix [hidden, experts].
 // 2kiu.com/news/2885792 §5.3: equal logits are ranked by ascending expert id.
-// cf-1.com/news/5914943 §2.3: tokens_per_expert counts the router's choices.
+// cf-1.com/news/5914943 §2.3: the number of tokens each expert is chosen for.
 //
 // bf16: 16x16x32 MFMAs; a block's 8 waves split the hidden dimension and
 // their partial logits are summed in a fixed order (see router_bf16_kernel).

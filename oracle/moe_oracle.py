@@ -82,7 +82,7 @@ def router_logits(hidden, w_router, bias=None) -> np.ndarray:
     """Router linear layer: logits[t, e] = sum_i hidden[t, i] * W_router[i, e] (+ bias[e]).
 
     P1 §2.1 (router scores every expert with one small linear layer, W_router
-    [hidden_dim, num_experts]); P4 §3.1 (the einsum 'bsd,de->bse'); optional
+    [hidden_dim, num_experts]); P4 §3.1 (the router contracts the hidden dimension with W_router); optional
     bias per P3 §4.1 (nn.Linear with bias) and P4 §5.2 (per-expert offset).
     """
     L = np.asarray(hidden, np.float64) @ np.asarray(w_router, np.float64)
@@ -116,7 +116,7 @@ def gate_weights(logits, idx) -> np.ndarray:
 
 
 def expert_counts(idx, N: int) -> np.ndarray:
-    """tokens_per_expert before any capacity drop (P1 §2.3)."""
+    """Tokens assigned to each expert before any capacity drop (P1 §2.3)."""
     return np.bincount(np.asarray(idx).ravel(), minlength=N).astype(np.int64)
 
 

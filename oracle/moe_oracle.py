@@ -20,7 +20,8 @@ Pages cited (no page has a usable title line, so each is named by its address):
 Readings of points the pages leave open (each also listed in the design notes):
 
 * gate weights are a softmax over the k selected logits (P1 §2.1, P5 §4.1);
-  P3 §4.1's "softmax over all N, keep top-k, renormalise" gives the same values;
+  P3 §4.1's order (softmax over all N experts, then keep the top k and
+  renormalise them) gives the same values;
 * ties go to the lower expert index and slot order is (logit desc, index asc)
   (P4 §5.3);
 * capacity C = floor((T*k)/N * CF) with the operation order of P4 §3.1's
@@ -36,8 +37,8 @@ Readings of points the pages leave open (each also listed in the design notes):
   pre-drop assignments and P_e the mean over tokens of the full-N softmax of
   the logits (P1 §2.3, P2 §3.2); the 0.01-style coefficient is the caller's;
 * overflow re-routing (the alternative to dropping that P3 §2.3, P4 §2.2 and
-  P5 §2.2 mention, and P5 §4.2's capacity-aware routing code sketches as
-  "mask the original choice, take the next best"): one second dispatch round after the
+  P5 §2.2 mention, and P5 §4.2's capacity-aware routing sketches in code by
+  masking the full expert and taking the next-best one): one second dispatch round after the
   capacity cut.  Each dropped assignment, in slot order within its token,
   proposes the highest-logit expert that is not among the token's top-k picks,
   not already proposed by an earlier dropped slot of the same token, and still

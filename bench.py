@@ -445,6 +445,8 @@ def main():
                     help="time only the skewed-routing workload (both overflow policies) and exit")
     ap.add_argument("--no-main", action="store_true",
                     help="profiling aid: time only the decode-shaped layer (no JSON line)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="with --no-main: the decode-shaped layer with FP8 expert weights")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward-pass object")
@@ -488,8 +490,15 @@ def main():
     if args.no_main:
         kd = "decode"
         inpd = synth.make_workload_inputs(kd, seed=args.seed)
-        rd = time_layer(inpd, upload(inpd), max(args.steps, 20), args.warmup)
-        log(f"decode only: {rd['ms_per_step']:.3f} ms/step")
+        devd = upload(inpd)
+        fp8 = None
+        if args.fp8:
+            fq = [moe.moe_quantize_fp8(devd[n]) for n in ("w1", "w3", "w2")]
+            fp8 = (fq[0][0], fq[1][0], fq[2][0], fq[0][1], fq[1][1], fq[2][1])
+            torch.cuda.synchronize()
+        rd = time_layer(inpd, devd, max(args.steps, 20), args.warmup, fp8=fp8)
+        log(f"decode only{' (fp8 weights)' if args.fp8 else ''}: {rd['ms_per_step']:.3f} ms/step, "
+            f"up {rd['up_ms']:.3f} ms, down {rd['down_ms']:.3f} ms")
         return 0
 
     key = "mixtral"

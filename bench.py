@@ -32,6 +32,10 @@ Also reported in the same line:
                 f 1536): layer time and the algorithmic bytes it must read
                 (the weights of every expert that got a token, router weights,
                 hidden and y) per second, against the HBM peak;
+  n16_cf125     the 16-expert workload (T 4096, d 2048, top-2, f 5632, bf16,
+                CF 1.25): time, tokens/s, TFLOP/s and % of the bf16 MFMA peak;
+  tiny_fp32     the tiny fp32 layer (T 64, d 128, 8 experts, f 256): microseconds
+                per layer (launch-latency bound);
   cpu_baseline  the CPU oracle on a bounded sample of the same workload.
 
 Helper modes for profiling (no timing claims):
@@ -58,6 +62,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 vector
 UP_KERNEL = "grouped_gemm_bf16_kernel<true>"
 GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_sum_amd", "csrc", "expert_gemm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "up_gemm_mixtral_T8192_traffic.json")
@@ -353,6 +358,69 @@ def write_traffic(fetch_dir, write_dir, calib_mib, cmds):
     print("\n".join(md))
 
 
+DECODE_KERNELS = {
+    "bf16 up": "grouped_gemm_bf16_rows32_up2_kernel",
+    "bf16 down": "grouped_gemm_bf16_rows32_kernel<false>",
+    "fp8 up": "grouped_gemm_fp8_rows32_up2_kernel",
+    "fp8 down": "grouped_gemm_fp8_rows32_kernel<false>",
+}
+
+
+def write_decode_traffic(fetch_dir, write_dir, calib_mib, active, cmds):
+    """HBM bytes per launch of the decode-shaped layer's weight-streaming GEMMs (bf16 and FP8
+    weights) from FETCH_SIZE / WRITE_SIZE, scaled by the calibration copy as in write_traffic."""
+    from mixture_experts_layer_sum_amd import synth
+    w = synth.WORKLOADS["decode"]
+    A = w.T * w.k                      # no capacity limit
+    algo = {"bf16 up": active * 2 * w.d * w.f * 2 + A * w.d * 2 + A * w.f * 2,
+            "bf16 down": active * w.f * w.d * 2 + A * w.f * 2 + A * w.d * 4,
+            "fp8 up": active * 2 * w.d * w.f + active * 2 * w.f * 4 + A * w.d * 2 + A * w.f * 2,
+            "fp8 down": active * w.f * w.d + active * w.d * 4 + A * w.f * 2 + A * w.d * 4}
+    weights = {"bf16 up": active * 2 * w.d * w.f * 2, "bf16 down": active * w.f * w.d * 2,
+               "fp8 up": active * 2 * w.d * w.f, "fp8 down": active * w.f * w.d}
+    calib_kib = calib_mib * 1024.0
+    per, factor = {}, {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(d, counter)
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        big = [v for v in copies if v > 0.25 * calib_kib]
+        if not big:
+            raise SystemExit(f"no calibration copy found in {d}")
+        factor[counter] = calib_kib / (sum(big) / len(big))
+        for key, kname in DECODE_KERNELS.items():
+            vals = [float(r["Counter_Value"]) for r in rows if kname in r["Kernel_Name"]]
+            if not vals:
+                raise SystemExit(f"no {kname} dispatches in {d}")
+            per[(key, counter)] = sum(vals) / len(vals)
+    md = [f"# HBM traffic of the decode-shaped layer's expert GEMMs ({w.name}, seed 0, "
+          f"{active} active experts, A = {A} routed rows)", "",
+          "Commands (repo root, on one MI355X; one counter per run):", ""]
+    md += [f"    {c}" for c in cmds]
+    md += ["", f"Calibration in the same processes: a plain {calib_mib} MiB device copy "
+           f"(`--copy-calibration {calib_mib}`); FETCH_SIZE is scaled by "
+           f"{factor['FETCH_SIZE']:.3f} and WRITE_SIZE by {factor['WRITE_SIZE']:.3f} so that the "
+           "copy reads and writes its own size.  Values are means over every dispatch of the "
+           "kernel in the run.", "",
+           "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled read GB | scaled write GB "
+           "| algorithmic GB | weight bytes GB | traffic / algorithmic |",
+           "|---|---|---|---|---|---|---|---|"]
+    for key, kname in DECODE_KERNELS.items():
+        rd = per[(key, "FETCH_SIZE")] * 1024 * factor["FETCH_SIZE"]
+        wr = per[(key, "WRITE_SIZE")] * 1024 * factor["WRITE_SIZE"]
+        md.append(f"| {key} `{kname}` | {per[(key, 'FETCH_SIZE')]:.0f} | "
+                  f"{per[(key, 'WRITE_SIZE')]:.0f} | {rd/1e9:.4f} | {wr/1e9:.4f} | "
+                  f"{algo[key]/1e9:.4f} | {weights[key]/1e9:.4f} | {(rd + wr)/algo[key]:.3f} |")
+    md += ["", "Algorithmic bytes: the weights of every active expert (bf16: 2 bytes, FP8: 1 byte "
+           "per weight, plus one fp32 scale per output column), the x_perm rows read and the "
+           "activations written (up), the activations read and the fp32 y_perm written (down).",
+           "The layer's HBM rate in bench.py's `decode` / `decode_fp8` objects is these "
+           "algorithmic bytes over the event-timed layer."]
+    out = os.path.join(ROOT, "profiles", "decode_T256_expert_gemm_hbm_traffic.md")
+    with open(out, "w") as fh:
+        fh.write("\n".join(md) + "\n")
+    print("\n".join(md))
+
+
 def summarize_rocprof(d, out, skip_first=0):
     """Short text summary of rocprofv3 csv output in directory `d`.
 
@@ -406,6 +474,42 @@ def summarize_rocprof(d, out, skip_first=0):
     print(text)
 
 
+def rates(inp, rs):
+    """Rate fields of one timed layer: tokens/s, flops and algorithmic bytes per second,
+    both roofline fractions, the routing outcome and the aux loss."""
+    ms = rs["ms_per_step"]
+    fl = layer_flops(inp, rs["A"])
+    by = layer_bytes(inp, rs["kept"])
+    tf = fl / (ms * 1e-3) / 1e12
+    gbs = by / (ms * 1e-3) / 1e9
+    return {"ms_per_step": ms, "us_per_step": 1e3 * ms, "tokens_per_s": inp.T / (ms * 1e-3),
+            "layer_tflops": tf, "pct_mfma_peak": 100.0 * tf / PEAK_BF16_TFLOPS,
+            "algorithmic_bytes": by, "GB_per_s": gbs, "pct_hbm_peak": 100.0 * gbs / PEAK_HBM_GBS,
+            "routed_rows": rs["A"], "dropped_assignments": rs["dropped"],
+            "active_experts": int((rs["kept"] > 0).sum()), "aux": rs["aux"],
+            "up_ms": rs["up_ms"], "down_ms": rs["down_ms"]}
+
+
+def time_workload(key, args, steps):
+    """One of the smaller workloads (tiny fp32, 16 experts with capacity), its own object."""
+    import torch
+    from mixture_experts_layer_sum_amd import synth
+    wk = synth.WORKLOADS[key]
+    log(f"generating {wk.name}")
+    inp = synth.make_workload_inputs(key, seed=args.seed)
+    devk = upload(inp)
+    rs = time_layer(inp, devk, steps, args.warmup)
+    out = {"workload": wk.name, "dtype": wk.dtype, "steps": steps}
+    out.update(rates(inp, rs))
+    if wk.dtype == "f32":
+        # fp32 layers run on the VALU kernels: the fp32 vector peak is the matching roofline
+        out["pct_fp32_peak"] = 100.0 * out["layer_tflops"] / PEAK_FP32_TFLOPS
+        del out["pct_mfma_peak"]
+    del devk
+    torch.cuda.empty_cache()
+    return out
+
+
 def time_skewed(args):
     """The skewed-routing workload under both overflow policies."""
     import torch
@@ -418,13 +522,7 @@ def time_skewed(args):
     sk = {"workload": wsk.name}
     for pol in ("drop", "reroute"):
         rs = time_layer(inps, devs, max(args.steps, 20), args.warmup, overflow=pol)
-        fl = layer_flops(inps, rs["A"])
-        sk[pol] = {"ms_per_step": rs["ms_per_step"],
-                   "tokens_per_s": wsk.T / (rs["ms_per_step"] * 1e-3),
-                   "routed_rows": rs["A"], "dropped_assignments": rs["dropped"],
-                   "active_experts": int((rs["kept"] > 0).sum()),
-                   "layer_tflops": fl / (rs["ms_per_step"] * 1e-3) / 1e12,
-                   "up_ms": rs["up_ms"], "down_ms": rs["down_ms"]}
+        sk[pol] = rates(inps, rs)
     del devs
     torch.cuda.empty_cache()
     return sk
@@ -447,6 +545,8 @@ def main():
                     help="profiling aid: time only the decode-shaped layer (no JSON line)")
     ap.add_argument("--fp8", action="store_true",
                     help="with --no-main: the decode-shaped layer with FP8 expert weights")
+    ap.add_argument("--no-small", action="store_true",
+                    help="skip the 16-expert (CF 1.25) and tiny fp32 workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward-pass object")
@@ -457,13 +557,30 @@ def main():
     ap.add_argument("--skip-first", type=int, default=0,
                     help="with --summarize-rocprof: warm-up dispatches per kernel left out")
     ap.add_argument("--write-traffic", nargs=2, default=None, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--decode-both", action="store_true",
+                    help="with --no-main: the decode-shaped layer with bf16, then FP8 weights")
+    ap.add_argument("--write-decode-traffic", nargs=2, default=None,
+                    metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--decode-active", type=int, default=0,
+                    help="with --write-decode-traffic: active experts of the decode run")
     args = ap.parse_args()
+
+    if args.write_decode_traffic:
+        if args.decode_active < 1:
+            raise SystemExit("--write-decode-traffic needs --decode-active (from the run's log)")
+        cmds = [f"rocprofv3 --pmc {c} -d {dr} -o run --output-format csv -- python -u "
+                f"bench.py --steps 3 --warmup 1 --no-main --decode-both "
+                f"--copy-calibration {args.copy_calibration}"
+                for c, dr in zip(("FETCH_SIZE", "WRITE_SIZE"), args.write_decode_traffic)]
+        write_decode_traffic(*args.write_decode_traffic, args.copy_calibration,
+                             args.decode_active, cmds)
+        return 0
 
     if args.write_traffic:
         # the counter runs these two commands, with -d the directories given here
         cmds = [f"rocprofv3 --pmc {c} -d {dr} -o run --output-format csv -- python -u "
                 f"bench.py --steps 2 --warmup 1 --no-decode --no-skewed --no-shared --no-backward "
-                f"--no-cpu-baseline --copy-calibration {args.copy_calibration}"
+                f"--no-small --no-cpu-baseline --copy-calibration {args.copy_calibration}"
                 for c, dr in zip(("FETCH_SIZE", "WRITE_SIZE"), args.write_traffic)]
         write_traffic(*args.write_traffic, args.copy_calibration, cmds)
         return 0
@@ -491,14 +608,20 @@ def main():
         kd = "decode"
         inpd = synth.make_workload_inputs(kd, seed=args.seed)
         devd = upload(inpd)
-        fp8 = None
-        if args.fp8:
-            fq = [moe.moe_quantize_fp8(devd[n]) for n in ("w1", "w3", "w2")]
-            fp8 = (fq[0][0], fq[1][0], fq[2][0], fq[0][1], fq[1][1], fq[2][1])
-            torch.cuda.synchronize()
-        rd = time_layer(inpd, devd, max(args.steps, 20), args.warmup, fp8=fp8)
-        log(f"decode only{' (fp8 weights)' if args.fp8 else ''}: {rd['ms_per_step']:.3f} ms/step, "
-            f"up {rd['up_ms']:.3f} ms, down {rd['down_ms']:.3f} ms")
+        variants = [False, True] if args.decode_both else [args.fp8]
+        for use_fp8 in variants:
+            fp8 = None
+            if use_fp8:
+                fq = [moe.moe_quantize_fp8(devd[n]) for n in ("w1", "w3", "w2")]
+                fp8 = (fq[0][0], fq[1][0], fq[2][0], fq[0][1], fq[1][1], fq[2][1])
+                torch.cuda.synchronize()
+            rd = time_layer(inpd, devd, max(args.steps, 20) if not args.decode_both else args.steps,
+                            args.warmup, fp8=fp8)
+            log(f"decode only{' (fp8 weights)' if use_fp8 else ''}: {rd['ms_per_step']:.3f} ms/step, "
+                f"up {rd['up_ms']:.3f} ms, down {rd['down_ms']:.3f} ms, "
+                f"active experts {int((rd['kept'] > 0).sum())}, routed rows {rd['A']}")
+        if args.copy_calibration:
+            copy_calibration(args.copy_calibration)
         return 0
 
     key = "mixtral"
@@ -594,6 +717,10 @@ def main():
     if not args.no_skewed:
         out["skewed_overflow"] = time_skewed(args)
         torch.cuda.empty_cache()
+
+    if not args.no_small:
+        out["n16_cf125"] = time_workload("n16_cf125", args, max(args.steps, 20))
+        out["tiny_fp32"] = time_workload("tiny_fp32", args, max(args.steps, 200))
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)

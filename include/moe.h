@@ -77,6 +77,19 @@ typedef enum {
 /* Human-readable name of a status code (static string). */
 const char* moe_status_string(moe_status s);
 
+/*
+ * moe_capacity -- the per-expert capacity moe_permute and moe_permute_reroute
+ * use (P4 §3.1: token slots T*k over N experts times the capacity factor,
+ * truncated; P5 §2.2: 65536 tokens, 64 experts, factor 1.2 give 1228):
+ *   C = floor(((double)T * k) / N * capacity_factor)   in IEEE double, in
+ *   that operation order, for capacity_factor > 0; C = T when
+ *   capacity_factor <= 0 (no limit) or when the formula reaches T or more
+ *   (no expert can hold more than T rows: a token picks an expert at most
+ *   once).  Host-only; touches no device.  Returns -1 for T < 1, N < 1,
+ *   k < 1, k > N or a NaN capacity_factor.
+ */
+int moe_capacity(int T, int k, int N, double capacity_factor);
+
 /* Bytes of device workspace `op` needs for these sizes (0 if none).  Returns
  * 0 for an unknown op as well.  For MOE_OP_EXPERT_FFN and MOE_OP_EXPERT_DOWN,
  * T*k is the row capacity (max_rows) of x_perm / y_perm.  The two expert ops
@@ -112,15 +125,17 @@ moe_status moe_route(const void* hidden, const void* w_router, const float* bias
 
 /*
  * moe_permute -- capacity cut and permutation into expert-contiguous rows.
- *   P4 §3.1 (capacity = int((B*S*k)/E * CF); each expert keeps its first
- *   `capacity` tokens), P5 §2.2 (worked capacity example), P1 §2.3 tip
- *   (tokens over capacity skip the MoE FFN and ride the residual), P3 §4.1
- *   (scatter tokens into per-expert queues instead of a per-expert loop).
+ *   P4 §3.1 (the capacity is the token-slot count T*k shared evenly over the
+ *   experts and scaled by the capacity factor, truncated to an integer; each
+ *   expert keeps its first `capacity` tokens), P5 §2.2 (worked capacity
+ *   example), P1 §2.3 tip (tokens over capacity skip the MoE FFN and ride the
+ *   residual), P3 §4.1 (scatter tokens into per-expert queues instead of a
+ *   per-expert loop).
  *
- *   capacity_factor > 0: C = floor((T*k)/N * capacity_factor), computed in
- *   double on the host; <= 0: no limit (C = T).  Tokens take places at an
- *   expert in token order; (t, j) is kept iff its place is < C.  Kept rows
- *   are expert-major, token-ascending within an expert.
+ *   capacity_factor > 0: C = moe_capacity(T, k, N, capacity_factor); <= 0:
+ *   no limit (C = T).  Tokens take places at an expert in token order; (t, j)
+ *   is kept iff its place is < C.  Kept rows are expert-major,
+ *   token-ascending within an expert.
  *
  *   hidden    [T, d] dtype dt
  *   topk_idx  [T, k] int32 (from moe_route; ids outside [0, N) are ignored)
@@ -133,7 +148,7 @@ moe_status moe_route(const void* hidden, const void* w_router, const float* bias
  *   ws        device workspace of moe_workspace_size(MOE_OP_PERMUTE, ...) bytes
  */
 moe_status moe_permute(const void* hidden, const int32_t* topk_idx, int T, int d, int N, int k,
-                       float capacity_factor, moe_dtype dt, void* x_perm, int32_t* perm_src,
+                       double capacity_factor, moe_dtype dt, void* x_perm, int32_t* perm_src,
                        int32_t* slot_row, int32_t* kept, int32_t* offsets, void* ws,
                        size_t ws_bytes, void* stream);
 
@@ -160,7 +175,7 @@ moe_status moe_permute(const void* hidden, const int32_t* topk_idx, int T, int d
  *   ws      moe_workspace_size(MOE_OP_PERMUTE_REROUTE, T, d, N, k, f, dt) bytes
  */
 moe_status moe_permute_reroute(const void* hidden, const int32_t* topk_idx, const float* logits,
-                               int T, int d, int N, int k, float capacity_factor, moe_dtype dt,
+                               int T, int d, int N, int k, double capacity_factor, moe_dtype dt,
                                void* x_perm, int32_t* perm_src, int32_t* slot_row, int32_t* kept,
                                int32_t* offsets, void* ws, size_t ws_bytes, void* stream);
 

@@ -45,10 +45,13 @@ moe_status check_expert_shape(int N, int d, int f, int max_rows, moe_dtype dt) {
   return MOE_OK;
 }
 
-// Capacity C = floor((T*k)/N * CF) in double, CF <= 0 meaning "no limit".
-int capacity_of(int T, int k, int N, float cf) {
-  if (!(cf > 0.f)) return T;
-  const double c = std::floor((static_cast<double>(T) * k) / N * static_cast<double>(cf));
+// Capacity C = floor((T*k)/N * CF) in double, CF <= 0 meaning "no limit".  CF
+// arrives as a double: narrowed to float, a factor such as 1.05 rounds below
+// its decimal value and C can come out one short wherever (T*k)/N * CF is a
+// whole number.
+int capacity_of(int T, int k, int N, double cf) {
+  if (!(cf > 0.0)) return T;
+  const double c = std::floor((static_cast<double>(T) * k) / N * cf);
   if (c >= static_cast<double>(T)) return T;
   return static_cast<int>(c);
 }
@@ -72,6 +75,11 @@ const char* moe_status_string(moe_status s) {
     case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP launch error";
   }
   return "unknown moe_status";
+}
+
+int moe_capacity(int T, int k, int N, double capacity_factor) {
+  if (T < 1 || N < 1 || k < 1 || k > N || std::isnan(capacity_factor)) return -1;
+  return capacity_of(T, k, N, capacity_factor);
 }
 
 size_t moe_workspace_size(moe_op op, int T, int d, int N, int k, int f, moe_dtype dt) {
@@ -118,7 +126,7 @@ moe_status moe_route(const void* hidden, const void* w_router, const float* bias
 }
 
 moe_status moe_permute(const void* hidden, const int32_t* topk_idx, int T, int d, int N, int k,
-                       float capacity_factor, moe_dtype dt, void* x_perm, int32_t* perm_src,
+                       double capacity_factor, moe_dtype dt, void* x_perm, int32_t* perm_src,
                        int32_t* slot_row, int32_t* kept, int32_t* offsets, void* ws,
                        size_t ws_bytes, void* stream) {
   if (!hidden || !topk_idx || !x_perm || !perm_src || !slot_row || !kept || !offsets)
@@ -137,7 +145,7 @@ moe_status moe_permute(const void* hidden, const int32_t* topk_idx, int T, int d
 }
 
 moe_status moe_permute_reroute(const void* hidden, const int32_t* topk_idx, const float* logits,
-                               int T, int d, int N, int k, float capacity_factor, moe_dtype dt,
+                               int T, int d, int N, int k, double capacity_factor, moe_dtype dt,
                                void* x_perm, int32_t* perm_src, int32_t* slot_row, int32_t* kept,
                                int32_t* offsets, void* ws, size_t ws_bytes, void* stream) {
   if (!hidden || !topk_idx || !logits || !x_perm || !perm_src || !slot_row || !kept || !offsets)

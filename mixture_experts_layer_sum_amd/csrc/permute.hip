@@ -1,7 +1,8 @@
 // Capacity cut and permutation into expert-contiguous rows.
 //
-// 2kiu.com/news/2885792 §3.1: capacity = int((B*S*k)/E * CF), and each expert
-// keeps only its first `capacity` tokens.  cf-1.com/news/5914943 §2.3 (tip):
+// 2kiu.com/news/2885792 §3.1: an expert's capacity is the floor of the token
+// slots (tokens x k) divided by the expert count, times the capacity factor,
+// and each expert keeps only its first `capacity` tokens.  cf-1.com/news/5914943 §2.3 (tip):
 // tokens over capacity skip the MoE FFN and ride the residual.
 // devpress.csdn.net/awstech/6a91abf4... §4.1: scatter the tokens into
 // per-expert queues in one vectorised pass instead of a loop over experts.

@@ -23,13 +23,14 @@ MOE_F32, MOE_BF16 = 0, 1
  MOE_OP_ROUTER_BACKWARD) = range(9)
 
 # Every symbol include/moe.h declares, with (restype, argtypes).
-_P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_P, _I, _F, _D, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_double, ctypes.c_size_t
 SIGNATURES = {
     "moe_status_string": (ctypes.c_char_p, [_I]),
+    "moe_capacity": (_I, [_I, _I, _I, _D]),
     "moe_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
     "moe_route": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P]),
-    "moe_permute": (_I, [_P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _Z, _P]),
-    "moe_permute_reroute": (_I, [_P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _P, _Z,
+    "moe_permute": (_I, [_P, _P, _I, _I, _I, _I, _D, _I, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "moe_permute_reroute": (_I, [_P, _P, _P, _I, _I, _I, _I, _D, _I, _P, _P, _P, _P, _P, _P, _Z,
                                  _P]),
     "moe_expert_ffn": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
     "moe_expert_up": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),

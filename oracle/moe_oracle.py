@@ -559,16 +559,19 @@ def moe_backward(hidden, w_router, w1, w3, w2, k: int, dy, capacity_factor: floa
 
 def moe_backward_sampled(hidden, w_router, w1, w3, w2, k: int, dy, capacity_factor: float = 0.0,
                          bias=None, aux_coef: float = 0.0, overflow: str = "drop", tokens=(),
-                         expert_cols=()) -> dict:
+                         expert_cols=(), router: bool = False) -> dict:
     """Entries of :func:`moe_backward` at sizes where the whole is too slow on a CPU.
 
     Routing, counts and dispatch cover every token (they are cheap); then
     * ``dhidden[t]`` for each t in ``tokens``: only the token's own slots are run
       (dX and dgate are local to a row), plus its logit gradient;
     * for each ``(e, cols)`` in ``expert_cols``: dW1_e[:, cols], dW3_e[:, cols] and
-      dW2_e[cols, :] over all of expert e's rows (local to a column of f).
+      dW2_e[cols, :] over all of expert e's rows (local to a column of f);
+    * with ``router``: dW_router and dbias in full.  They need every token's logit
+      gradient, hence every kept slot's dgate = <dy[t], FFN_e(x_t)>: one forward of
+      the experts over their rows (no expert backward).
     Returns {"dhidden": {t: [d]}, "dw": {(e, tuple(cols)): (dW1 cols, dW3 cols, dW2 rows)},
-    "topk_idx", "slot_row", "offsets"}.
+    "topk_idx", "slot_row", "offsets"} (+ "dw_router", "dbias", "dgate" with ``router``).
     """
     hidden = np.asarray(hidden)
     T, d = hidden.shape
@@ -600,4 +603,17 @@ def moe_backward_sampled(hidden, w_router, w1, w3, w2, k: int, dy, capacity_fact
         G = R["w"][tok, slot][:, None] * np.asarray(dy[tok], np.float64)
         out = swiglu_backward(np.asarray(hidden[tok], np.float64), G, w1[e], w3[e], w2[e], cols)
         res["dw"][(int(e), tuple(int(c) for c in cols))] = (out["dw1"], out["dw3"], out["dw2"])
+    if router:
+        dgate = np.zeros((T, k))
+        for e in range(R["N"]):
+            rows = np.arange(offsets[e], offsets[e + 1])
+            if rows.size == 0:
+                continue
+            tok, slot = R["row_tok"][rows], R["row_j"][rows]
+            ye = swiglu_ffn(hidden[tok], w1[e], w3[e], w2[e])
+            dgate[tok, slot] = np.sum(np.asarray(dy[tok], np.float64) * ye, axis=1)
+        dlog = _dlogits(R["L"], R["idx"], R["w"], dgate, R["counts"], T, k, aux_coef)
+        res["dw_router"] = np.asarray(hidden, np.float64).T @ dlog
+        res["dbias"] = dlog.sum(axis=0)
+        res["dgate"] = dgate
     return res

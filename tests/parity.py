@@ -166,6 +166,10 @@ def check(inp, g, sample=None, label="", audit=True, y_tol=None, overflow="drop"
     den = float(np.abs(yref[tok_ok]).max(initial=0.0))
     err = float(np.abs(ygpu[tok_ok] - yref[tok_ok]).max(initial=0.0))
     rel = err / den if den > 0 else err
+    # diagnostic only: elementwise relative error where |y_ref| >= 1e-3 max |y_ref|
+    yr_ok, yg_ok = yref[tok_ok], ygpu[tok_ok]
+    big = np.abs(yr_ok) >= 1e-3 * den
+    elem = float((np.abs(yg_ok - yr_ok)[big] / np.abs(yr_ok)[big]).max(initial=0.0))
     assert rel <= tol, f"{label}: y max rel err {rel:.3e} > {tol}"
     # tokens with every slot dropped are exactly zero (without shared experts)
     dropped = (g["slot_row"] < 0).all(1)
@@ -188,7 +192,8 @@ def check(inp, g, sample=None, label="", audit=True, y_tol=None, overflow="drop"
         assert relp <= tol, f"{label}: y_perm rel {relp:.3e}"
     aux_rel = abs(g["aux"] - ref["aux"]) / abs(ref["aux"])
     assert aux_rel <= AUX_TOL, f"{label}: aux {g['aux']} vs {ref['aux']}"
-    rep = {"label": label, "excluded_near_ties": int(excl.sum()), "y_rel": rel, "aux": g["aux"],
+    rep = {"label": label, "excluded_near_ties": int(excl.sum()), "y_rel": rel,
+           "y_elem_rel_diag": elem, "tokens_compared": int(tok_ok.sum()), "aux": g["aux"],
            "aux_ref": ref["aux"], "aux_rel": aux_rel, "rows": g["A"], "C": C,
            "dropped_assignments": int((g["slot_row"] < 0).sum()),
            "tokens_on_other_experts": int((~same_experts).sum())}

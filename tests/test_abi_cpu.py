@@ -65,7 +65,7 @@ def test_workspace_sizes():
     # the fp32 path never uses them
     assert lib.moe_workspace_size(moe.MOE_OP_EXPERT_DOWN, 64, 128, 8, 2, 256, F32) == 0
     assert lib.moe_workspace_size(moe.MOE_OP_EXPERT_DOWN, 64, 128, 8, 0, 256, BF16) == 0
-    # one fp32 [N] partial per 64 tokens
+    # one fp32 [N] partial per 16 tokens
     assert lib.moe_workspace_size(moe.MOE_OP_AUX_LOSS, 256, 128, 8, 2, 256, F32) == 16 * 8 * 4
     assert lib.moe_workspace_size(moe.MOE_OP_AUX_LOSS, 65, 128, 8, 2, 256, F32) == 5 * 8 * 4
     assert lib.moe_workspace_size(17, 64, 128, 8, 2, 256, F32) == 0
@@ -80,6 +80,33 @@ def test_workspace_sizes():
         128 * 8 * 4 + 2 * 256 * 8 * 4 + 256
     assert lib.moe_workspace_size(moe.MOE_OP_ROUTER_BACKWARD, 128, 256, 300, 2, 0, BF16) == 0
     assert lib.moe_workspace_size(moe.MOE_OP_PERMUTE, 0, 128, 8, 2, 256, F32) == 0
+
+
+def test_capacity_matches_oracle():
+    """moe_capacity (the C the permute kernels apply) equals the oracle's
+    capacity, floor((T*k)/N * CF) in double with P4 §3.1's operation order, at
+    the pages' factors (P2 §3.4's working range 1.05-1.25, P4 §3.1's 1.5) and
+    below 1, for every T below 70,000.  Narrowing the factor to fp32 before the
+    product loses a row wherever (T*k)/N * CF is a whole number (CF 1.05:
+    T 160, k 1, N 8 gives 21, fp32 gives 20), which the first asserts pin."""
+    import oracle.moe_oracle as O
+    assert lib.moe_capacity(160, 1, 8, 1.05) == O.capacity(160, 1, 8, 1.05) == 21
+    assert lib.moe_capacity(80, 2, 8, 1.05) == O.capacity(80, 2, 8, 1.05) == 21
+    assert math.floor(20 * float(ctypes.c_float(1.05).value)) == 20     # what fp32 would give
+    assert lib.moe_capacity(65536, 1, 64, 1.2) == 1228                 # P5 §2.2 worked example
+    assert lib.moe_capacity(4096, 2, 16, 1.25) == 640
+    assert lib.moe_capacity(16384, 2, 64, 1.5) == 768
+    cap = lib.moe_capacity
+    for cf in (0.7, 1.05, 1.1, 1.2, 1.25, 1.5):
+        for k in (1, 2):
+            for N in (8, 16, 64, 128):
+                bad = [T for T in range(1, 70000)
+                       if cap(T, k, N, cf) != min(O.capacity(T, k, N, cf), T)]
+                assert not bad, (cf, k, N, bad[:5])
+    # no limit, and invalid arguments
+    assert cap(300, 2, 8, 0.0) == 300 and cap(300, 2, 8, -1.0) == 300
+    assert cap(10, 2, 8, 100.0) == 10                                  # clamped to T
+    assert cap(0, 2, 8, 1.0) == -1 and cap(10, 9, 8, 1.0) == -1 and cap(10, 2, 8, math.nan) == -1
 
 
 def route(**kw):

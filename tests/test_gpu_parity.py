@@ -1,9 +1,9 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle.
 
-Small shapes are compared element by element (every token, every row); the
-five workload shapes are compared at full size in the launch configuration
-bench.py times, with routing, counts and the permutation checked for every
-token and the layer output on sampled tokens the oracle evaluates one by one.
+Small shapes are compared element by element (every token, every row); so are
+the five workload shapes at full size, in the launch configuration bench.py
+times, for two seeds: routing, counts and the permutation exact for every
+token, and the layer output on every token.
 """
 import numpy as np
 import pytest
@@ -69,6 +69,13 @@ SMALL = [
     ("bf16_router_wt_N256", 2048, 256, 256, 2, 128, "bf16", 0.0, None),
     ("bf16_router_wt_N40_k3", 2048, 256, 40, 3, 128, "bf16", 1.0, None),
     ("bf16_router_below_threshold", 2047, 256, 40, 3, 128, "bf16", 1.0, None),
+    # capacity factors whose fp32 value lies below the decimal one, at shapes where
+    # (T*k)/N * CF is a whole number (C = 21, 21, 7, 14): the capacity must follow
+    # the double formula exactly (P2 §3.4's range starts at 1.05)
+    ("bf16_cf105_T160_k1", 160, 256, 8, 1, 128, "bf16", 1.05, "skew"),
+    ("bf16_cf105_T80_k2", 80, 256, 8, 2, 128, "bf16", 1.05, "skew"),
+    ("bf16_cf07_T40_k2", 40, 256, 8, 2, 128, "bf16", 0.7, "skew"),
+    ("f32_cf07_T160_N16_k1", 160, 128, 16, 1, 128, "f32", 0.7, "skew"),
 ]
 
 
@@ -164,6 +171,10 @@ REROUTE = [
     # more experts than a wave has lanes: each lane holds several candidates
     ("bf16_reroute_N200", 400, 256, 200, 2, 128, "bf16", 0.8, "zipf"),
     ("bf16_reroute_N256_k3", 300, 256, 256, 3, 128, "bf16", 0.5, "skew"),
+    # capacity factors below their decimal value in fp32 (C = 21, 21, 7)
+    ("bf16_reroute_cf105_T160_k1", 160, 256, 8, 1, 128, "bf16", 1.05, "skew"),
+    ("bf16_reroute_cf105_T80_k2", 80, 256, 8, 2, 128, "bf16", 1.05, "skew"),
+    ("bf16_reroute_cf07_T40_k2", 40, 256, 8, 2, 128, "bf16", 0.7, "skew"),
 ]
 
 
@@ -178,7 +189,8 @@ def test_reroute_small_shapes(moe, case):
     for seed in (0, 1):
         inp = synth.make_inputs(T, d, N, k, f, dt, cf, seed, bias=b)
         rep, g, _, _ = _run(inp, f"{label}/seed{seed}", overflow="reroute")
-        assert (g["kept"] <= max(1, int(np.floor(T * k / N * cf)))).all()
+        import oracle.moe_oracle as O
+        assert (g["kept"] <= O.capacity(T, k, N, cf)).all()
 
 
 @pytest.mark.parametrize("N", [8, 130])
@@ -284,6 +296,15 @@ def _fp8_layer(moe, inp, label, sample=None):
     ref = O.moe_forward(inp.values("hidden"), inp.values("w_router"), Deq("w1"), Deq("w3"),
                         Deq("w2"), inp.k, inp.capacity_factor, inp.bias, tokens=sample)
     same = (g["topk_idx"] == ref["topk_idx"]).all(1)
+    # routing runs on the bf16 router (FP8 touches only the expert weights): a token
+    # whose picks differ from the oracle's must be a near tie of the oracle's logits
+    L32 = ref["logits"].astype(np.float32)
+    ties = parity.near_ties(L32, inp.k)
+    if inp.k > 1:
+        sel = np.take_along_axis(L32.astype(np.float64), ref["topk_idx"], 1)
+        ties = ties | (np.diff(-sel, axis=1) < parity.NEAR_TIE).any(1)
+    assert (same | ties).all(), f"{label}: routing differs on tokens that are not near ties"
+    parity.log(f"{label}: {int((~same).sum())} near-tie tokens left out of the y comparison")
     assert np.array_equal(g["slot_row"][same], ref["slot_row"][same]), label
     toks = ref["tokens"]
     ok = same[toks]
@@ -310,15 +331,15 @@ def test_fp8_decode_workload_full_size(moe):
 WORKLOADS = ["tiny_fp32", "n16_cf125", "mixtral", "skewed_zipf", "decode"]
 
 
+@pytest.mark.parametrize("seed", [0, 1])
 @pytest.mark.parametrize("key", WORKLOADS)
-def test_workload_full_size(moe, key):
-    """Full-size workload, seed 0: every token's routing and dispatch exact, y on sampled tokens."""
-    inp = synth.make_workload_inputs(key, seed=0)
-    rng = np.random.default_rng(123)
-    sample = None if inp.T <= 64 else np.sort(rng.choice(inp.T, size=48, replace=False))
-    if sample is not None:
-        # include the first and last token (ragged edges of the tiling)
-        sample = np.unique(np.concatenate([[0, inp.T - 1], sample]))
-    rep, g, dev, b = _run(inp, f"workload_{key}", sample=sample)
+def test_workload_full_size(moe, key, seed):
+    """Full-size workload, seeds 0 and 1, in the launch configuration the benchmark
+    times: every token's routing and dispatch exact, every row of x_perm a bitwise
+    copy, and y and y_perm compared with the oracle on every token and row."""
+    inp = synth.make_workload_inputs(key, seed=seed)
+    rep, g, dev, b = _run(inp, f"workload_{key}/seed{seed}", sample=None)
+    # every token is compared unless a near tie (or a capacity cascade from one) moved it
+    assert rep["tokens_compared"] + rep["excluded_near_ties"] + rep["tokens_on_other_experts"] >= inp.T
     if key == "skewed_zipf":
         assert rep["dropped_assignments"] > 0          # the Zipf bias makes capacity bite

@@ -145,8 +145,9 @@ def test_backward_is_deterministic(moe):
 def test_backward_workload_full_size(moe, key):
     """Full-size workload in the launch configuration the benchmark times: routing
     exact for every token; dhidden on sampled tokens and dW1/dW3 columns and dW2 rows
-    of sampled experts from the oracle entry by entry; dW_router and dbias checked by
-    the softmax shift invariance (each token's logit gradient sums to zero)."""
+    of sampled experts from the oracle entry by entry; dW_router and dbias in full
+    against the oracle's (every token's logit gradient: one oracle forward of the
+    experts), and by the softmax shift invariance (each row of dW_router sums to 0)."""
     import oracle.moe_oracle as O
     from tests import parity
     inp = synth.make_workload_inputs(key, seed=0)
@@ -169,7 +170,7 @@ def test_backward_workload_full_size(moe, key):
                                  parity.ExpertView(inp, "w1"), parity.ExpertView(inp, "w3"),
                                  parity.ExpertView(inp, "w2"), inp.k,
                                  synth.bf16_bits_to_f32(dy), inp.capacity_factor, inp.bias,
-                                 aux_coef=coef, tokens=toks, expert_cols=ec)
+                                 aux_coef=coef, tokens=toks, expert_cols=ec, router=True)
     assert np.array_equal(g["topk_idx"], smp["topk_idx"]), "routing differs"
     assert np.array_equal(g["slot_row"], smp["slot_row"]), "dispatch differs"
     tol = GRAD_TOL[inp.dtype]
@@ -181,9 +182,12 @@ def test_backward_workload_full_size(moe, key):
         rep[f"dw1[{e}]"] = _rel(gr.dw1[e][:, cols].cpu().numpy(), r1)
         rep[f"dw3[{e}]"] = _rel(gr.dw3[e][:, cols].cpu().numpy(), r3)
         rep[f"dw2[{e}]"] = _rel(gr.dw2[e][cols, :].cpu().numpy(), r2)
+    wr = gr.dw_router.cpu().numpy().astype(np.float64)
+    rep["dw_router"] = _rel(wr, smp["dw_router"])
+    if inp.bias is not None:
+        rep["dbias"] = _rel(gr.dbias.cpu().numpy(), smp["dbias"])
     for name, rel in rep.items():
         assert rel <= tol, f"backward_{key}: {name} max rel err {rel:.3e} > {tol}"
-    wr = gr.dw_router.cpu().numpy().astype(np.float64)
     assert np.abs(wr).max() > 0
     assert np.abs(wr.sum(1)).max() <= 1e-4 * np.abs(wr).max(), "dW_router rows do not sum to 0"
     if inp.bias is not None:

@@ -792,7 +792,10 @@ def test_backward_sampled_entries_equal_the_full_backward(overflow, cf, coef):
     ec = [(0, [0, 5, 11]), (3, [2])]
     smp = O.moe_backward_sampled(inp.hidden, inp.w_router, inp.w1, inp.w3, inp.w2, 2, dy, cf,
                                  inp.bias, aux_coef=coef, overflow=overflow, tokens=toks,
-                                 expert_cols=ec)
+                                 expert_cols=ec, router=True)
+    assert np.allclose(smp["dw_router"], full["dw_router"], rtol=1e-12, atol=1e-12)
+    assert np.allclose(smp["dbias"], full["dbias"], rtol=1e-12, atol=1e-12)
+    assert np.allclose(smp["dgate"], full["dgate"], rtol=1e-12, atol=1e-12)
     for t in toks:
         assert np.allclose(smp["dhidden"][t], full["dhidden"][t], rtol=1e-12, atol=1e-12)
     for e, cols in ec:

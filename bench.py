@@ -545,6 +545,8 @@ def main():
                     help="profiling aid: time only the decode-shaped layer (no JSON line)")
     ap.add_argument("--fp8", action="store_true",
                     help="with --no-main: the decode-shaped layer with FP8 expert weights")
+    ap.add_argument("--only-workload", default=None, choices=["n16_cf125", "tiny_fp32"],
+                    help="time only that workload (log line, no JSON line) and exit")
     ap.add_argument("--no-small", action="store_true",
                     help="skip the 16-expert (CF 1.25) and tiny fp32 workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -598,6 +600,11 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         return 1
+
+    if args.only_workload:
+        r1 = time_workload(args.only_workload, args, max(args.steps, 20))
+        log(f"{args.only_workload} only: " + json.dumps(r1))
+        return 0
 
     if args.only_skewed:
         sk = time_skewed(args)

@@ -168,7 +168,7 @@ def check(inp, g, sample=None, label="", audit=True, y_tol=None, overflow="drop"
     rel = err / den if den > 0 else err
     # diagnostic only: elementwise relative error where |y_ref| >= 1e-3 max |y_ref|
     yr_ok, yg_ok = yref[tok_ok], ygpu[tok_ok]
-    big = np.abs(yr_ok) >= 1e-3 * den
+    big = (np.abs(yr_ok) >= 1e-3 * den) & (np.abs(yr_ok) > 0)
     elem = float((np.abs(yg_ok - yr_ok)[big] / np.abs(yr_ok)[big]).max(initial=0.0))
     assert rel <= tol, f"{label}: y max rel err {rel:.3e} > {tol}"
     # tokens with every slot dropped are exactly zero (without shared experts)

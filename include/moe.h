@@ -153,6 +153,31 @@ moe_status moe_permute(const void* hidden, const int32_t* topk_idx, int T, int d
                        size_t ws_bytes, void* stream);
 
 /*
+ * moe_permute_noalloc -- moe_permute without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments, outputs,
+ * results and errors as moe_permute, bit for bit; the chunk tables moe_permute
+ * keeps in `ws` live instead in a static device array inside the library,
+ * MOE_PERMUTE_NOALLOC_SCRATCH_BYTES (4 MiB) on each device it runs on, held
+ * from the library's load until the process ends.  It allocates nothing,
+ * frees nothing and synchronises nothing (its first call on a device looks
+ * up that device's address of the array, host-side only).
+ *   Limit: moe_workspace_size(MOE_OP_PERMUTE, T, ...) = 8 * ceil(T / 256) * N
+ *   bytes must not exceed MOE_PERMUTE_NOALLOC_SCRATCH_BYTES (T * N <= 2^27
+ *   or so, e.g. 524288 tokens at 256 experts), else MOE_ERR_WORKSPACE before
+ *   anything is enqueued.
+ *   Every call on one device uses that device's one array: calls that overlap
+ *   on a device (different streams, or threads without ordering) race and
+ *   give wrong results.  Order them, e.g. on one stream.  Nothing in the
+ *   array needs to start at zero.
+ */
+#define MOE_PERMUTE_NOALLOC_SCRATCH_BYTES (4u << 20)
+moe_status moe_permute_noalloc(const void* hidden, const int32_t* topk_idx, int T, int d, int N,
+                               int k, double capacity_factor, moe_dtype dt, void* x_perm,
+                               int32_t* perm_src, int32_t* slot_row, int32_t* kept,
+                               int32_t* offsets, void* stream);
+
+/*
  * moe_permute_reroute -- as moe_permute, but assignments over capacity get
  * one second chance instead of being dropped.  P5 §4.2 (capacity-aware
  * routing: mask the over-capacity pick, take the next-best expert), P4 §2.2

@@ -144,6 +144,26 @@ moe_status moe_permute(const void* hidden, const int32_t* topk_idx, int T, int d
                                         perm_src, slot_row, kept, offsets, ws, as_stream(stream)));
 }
 
+moe_status moe_permute_noalloc(const void* hidden, const int32_t* topk_idx, int T, int d, int N,
+                               int k, double capacity_factor, moe_dtype dt, void* x_perm,
+                               int32_t* perm_src, int32_t* slot_row, int32_t* kept,
+                               int32_t* offsets, void* stream) {
+  if (!hidden || !topk_idx || !x_perm || !perm_src || !slot_row || !kept || !offsets)
+    return MOE_ERR_INVALID_ARG;
+  if (std::isnan(capacity_factor)) return MOE_ERR_INVALID_ARG;
+  moe_status s = check_tnk(T, N, k);
+  if (s != MOE_OK) return s;
+  if ((s = check_d(d)) != MOE_OK) return s;
+  if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
+  static_assert(MOE_PERMUTE_NOALLOC_SCRATCH_BYTES == moe::kPermuteNoAllocScratchBytes,
+                "header and library disagree on the static scratch size");
+  if (moe::permute_ws_bytes(T, N) > moe::kPermuteNoAllocScratchBytes) return MOE_ERR_WORKSPACE;
+  const int C = capacity_of(T, k, N, capacity_factor);
+  return hip_status(moe::launch_permute_noalloc(hidden, topk_idx, T, d, N, k, C, elem_bytes(dt),
+                                                x_perm, perm_src, slot_row, kept, offsets,
+                                                as_stream(stream)));
+}
+
 moe_status moe_permute_reroute(const void* hidden, const int32_t* topk_idx, const float* logits,
                                int T, int d, int N, int k, double capacity_factor, moe_dtype dt,
                                void* x_perm, int32_t* perm_src, int32_t* slot_row, int32_t* kept,

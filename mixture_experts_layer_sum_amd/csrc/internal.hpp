@@ -19,6 +19,13 @@ hipError_t launch_permute(const void* hidden, const int32_t* topk_idx, int T, in
                           int32_t* slot_row, int32_t* kept, int32_t* offsets, void* ws,
                           hipStream_t stream);
 
+// moe_permute_noalloc: the chunk tables live in a static device array of this size
+constexpr size_t kPermuteNoAllocScratchBytes = size_t{4} << 20;
+hipError_t launch_permute_noalloc(const void* hidden, const int32_t* topk_idx, int T, int d, int N,
+                                  int k, int C, int elem_bytes, void* x_perm, int32_t* perm_src,
+                                  int32_t* slot_row, int32_t* kept, int32_t* offsets,
+                                  hipStream_t stream);
+
 size_t permute_reroute_ws_bytes(int T, int N, int k);
 hipError_t launch_permute_reroute(const void* hidden, const int32_t* topk_idx,
                                   const float* logits, int T, int d, int N, int k, int C,

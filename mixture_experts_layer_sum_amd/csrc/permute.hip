@@ -12,6 +12,9 @@
 // histograms (integer LDS atomics, order-free), a per-expert exclusive scan
 // over chunks, and inside a chunk a 256-bit "who chose e" mask per expert
 // built with LDS atomic OR (also order-free) and read back with popcounts.
+#include <atomic>
+#include <mutex>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -456,6 +459,58 @@ hipError_t launch_permute(const void* hidden, const int32_t* topk_idx, int T, in
                      static_cast<const uint4*>(hidden), slot_row, k, vpr,
                      static_cast<uint4*>(x_perm));
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- no-allocation variant
+// moe_permute_noalloc runs the kernels above with the chunk tables in a
+// file-scope device array instead of a caller workspace, for callers that
+// cannot allocate.  Each device holds its own copy of the array from the
+// library's load until the process ends; calls that overlap on one device
+// share it and race.  Nothing in it needs clearing: chunk_hist_kernel writes
+// every entry of the histogram table and expert_scan_kernel every entry of
+// the base table before either is read.
+static __device__ __align__(256) int32_t scratch[kPermuteNoAllocScratchBytes / sizeof(int32_t)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<int32_t*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch` (the host-side name is only a
+// stand-in: passing it to a kernel would fault).  Looked up once per device,
+// with that device current, and kept.
+hipError_t scratch_of_current_device(int32_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  int32_t* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      void* q = nullptr;
+      e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (q == nullptr) return hipErrorInvalidSymbol;
+      p = static_cast<int32_t*>(q);
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_permute_noalloc(const void* hidden, const int32_t* topk_idx, int T, int d, int N,
+                                  int k, int C, int elem_bytes, void* x_perm, int32_t* perm_src,
+                                  int32_t* slot_row, int32_t* kept, int32_t* offsets,
+                                  hipStream_t stream) {
+  int32_t* ws = nullptr;
+  const hipError_t e = scratch_of_current_device(&ws);
+  if (e != hipSuccess) return e;
+  return launch_permute(hidden, topk_idx, T, d, N, k, C, elem_bytes, x_perm, perm_src, slot_row,
+                        kept, offsets, ws, stream);
 }
 
 }  // namespace moe

@@ -30,6 +30,7 @@ SIGNATURES = {
     "moe_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
     "moe_route": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _Z, _P]),
     "moe_permute": (_I, [_P, _P, _I, _I, _I, _I, _D, _I, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "moe_permute_noalloc": (_I, [_P, _P, _I, _I, _I, _I, _D, _I, _P, _P, _P, _P, _P, _P]),
     "moe_permute_reroute": (_I, [_P, _P, _P, _I, _I, _I, _I, _D, _I, _P, _P, _P, _P, _P, _P, _Z,
                                  _P]),
     "moe_expert_ffn": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
@@ -137,6 +138,25 @@ def moe_permute(hidden, topk_idx, N, capacity_factor=0.0, x_perm=None, perm_src=
     _check(_lib.moe_permute(_ptr(hidden), _ptr(topk_idx), T, d, N, k, float(capacity_factor),
                             _dt(hidden), _ptr(x_perm), _ptr(perm_src), _ptr(slot_row), _ptr(kept),
                             _ptr(offsets), _ptr(ws), ws.numel(), _stream(stream)), "moe_permute")
+    return x_perm, perm_src, slot_row, kept, offsets
+
+
+def moe_permute_noalloc(hidden, topk_idx, N, capacity_factor=0.0, x_perm=None, perm_src=None,
+                        slot_row=None, kept=None, offsets=None, stream=None):
+    """moe_permute with the library's static scratch instead of a workspace (outputs are
+    allocated here only when not given)."""
+    T, d = hidden.shape
+    k = topk_idx.shape[1]
+    dev = hidden.device
+    x_perm = _empty((T * k, d), hidden.dtype, dev, x_perm)
+    perm_src = _empty((T * k,), torch.int32, dev, perm_src)
+    slot_row = _empty((T, k), torch.int32, dev, slot_row)
+    kept = _empty((N,), torch.int32, dev, kept)
+    offsets = _empty((N + 1,), torch.int32, dev, offsets)
+    _check(_lib.moe_permute_noalloc(_ptr(hidden), _ptr(topk_idx), T, d, N, k,
+                                    float(capacity_factor), _dt(hidden), _ptr(x_perm),
+                                    _ptr(perm_src), _ptr(slot_row), _ptr(kept), _ptr(offsets),
+                                    _stream(stream)), "moe_permute_noalloc")
     return x_perm, perm_src, slot_row, kept, offsets
 
 

@@ -17,9 +17,11 @@ Also reported in the same line:
                 summary matches the current kernel source, else null;
   backward      the backward pass of the Mixtral-shaped layer (gradients of
                 <dy, y> + 0.01 * aux into hidden, the router and every expert's
-                W1/W3/W2, fp32 gradients): its time, the expert GEMMs' rate
-                (16*A*d*f flop: recompute of h1/h3, da, dx, dW1/dW3, dW2)
-                against the bf16 MFMA peak, and forward + backward per step;
+                W1/W3/W2, fp32 gradients) after a training forward that keeps
+                h1 / h3: its time, the expert GEMMs' rate (12*A*d*f flop: da
+                with the SwiGLU backward, dx, dW1/dW3, dW2) against the bf16
+                MFMA peak, the training forward, forward + backward per step,
+                and the variant that recomputes h1 / h3 instead;
   decode_fp8    the decode-shaped layer with FP8 (OCP E4M3, per-column fp32
                 scale) expert weights quantised on the GPU: bytes counted at one
                 byte per weight plus the scales;
@@ -100,14 +102,16 @@ def upload_shared(inp):
     return (t(inp.w1s), t(inp.w3s), t(inp.w2s))
 
 
-def time_layer(inp, dev, steps, warmup, overflow="drop", shared=None, fp8=None):
-    """Warm up, then time `steps` forwards; per-step HIP events bracket the GEMMs."""
+def time_layer(inp, dev, steps, warmup, overflow="drop", shared=None, fp8=None, save=False):
+    """Warm up, then time `steps` forwards; per-step HIP events bracket the GEMMs.  With
+    `save` the up projection also keeps h1 / h3 for the backward (training forward)."""
     import torch
     from mixture_experts_layer_sum_amd import moe
     T, d, N, k, f = inp.T, inp.d, inp.N, inp.k, inp.f
     ns = 0 if shared is None else shared[0].shape[0]
     b = moe.MoEBuffers(T, d, N, k, f, dev["hidden"].dtype, n_shared=ns,
-                       f_shared=None if shared is None else shared[0].shape[2])
+                       f_shared=None if shared is None else shared[0].shape[2],
+                       save_for_backward=save)
     s = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -122,7 +126,9 @@ def time_layer(inp, dev, steps, warmup, overflow="drop", shared=None, fp8=None):
                                     b.ws_permute)
         if ev:
             ev[0].record(s)
-        if fp8 is None:
+        if fp8 is None and save:
+            moe.moe_expert_up_save(b.x_perm, b.offsets, dev["w1"], dev["w3"], b.act, b.h13)
+        elif fp8 is None:
             moe.moe_expert_up(b.x_perm, b.offsets, dev["w1"], dev["w3"], b.act)
         else:
             moe.moe_expert_up_fp8(b.x_perm, b.offsets, fp8[0], fp8[1], fp8[3], fp8[4], b.act)
@@ -162,14 +168,15 @@ def time_layer(inp, dev, steps, warmup, overflow="drop", shared=None, fp8=None):
             "dropped": dropped}
 
 
-def time_backward(inp, dev, steps, warmup, coef=0.01):
+def time_backward(inp, dev, steps, warmup, coef=0.01, saved=True):
     """One forward (untimed), then `steps` backward passes; HIP events on the launch
-    stream bracket the three backward entry points of each pass."""
+    stream bracket the three backward entry points of each pass.  `saved`: the forward
+    kept h1 / h3 and the expert backward uses them (else it recomputes them)."""
     import torch
     from mixture_experts_layer_sum_amd import moe, synth
     T, d, N, k, f = inp.T, inp.d, inp.N, inp.k, inp.f
     b = moe.moe_forward(dev["hidden"], dev["w_router"], dev["w1"], dev["w3"], dev["w2"], k,
-                        inp.capacity_factor, dev["bias"])
+                        inp.capacity_factor, dev["bias"], save_for_backward=saved)
     gb = moe.MoEGradBuffers(T, d, N, k, f, dev["hidden"].dtype)
     dyh = synth.make_dy(T, d, inp.dtype, seed=11)
     dy = (torch.from_numpy(dyh.view("int16")).cuda().view(torch.bfloat16) if inp.dtype == "bf16"
@@ -183,8 +190,13 @@ def time_backward(inp, dev, steps, warmup, coef=0.01):
         moe.moe_combine_backward(dy, b.y_perm, b.slot_row, b.topk_w, gb.g_perm, gb.dgate)
         if ev:
             ev[1].record(s)
-        moe.moe_expert_backward(b.x_perm, gb.g_perm, b.offsets, dev["w1"], dev["w3"], dev["w2"],
-                                gb.dx_perm, gb.dw1, gb.dw3, gb.dw2, gb.ws_expert)
+        if saved:
+            moe.moe_expert_backward_saved(b.x_perm, gb.g_perm, b.h13, b.offsets, dev["w1"],
+                                          dev["w3"], dev["w2"], gb.dx_perm, gb.dw1, gb.dw3,
+                                          gb.dw2, gb.ws_expert)
+        else:
+            moe.moe_expert_backward(b.x_perm, gb.g_perm, b.offsets, dev["w1"], dev["w3"],
+                                    dev["w2"], gb.dx_perm, gb.dw1, gb.dw3, gb.dw2, gb.ws_expert)
         if ev:
             ev[2].record(s)
         moe.moe_router_backward(dev["hidden"], dev["w_router"], b.logits, b.topk_idx, b.topk_w,
@@ -671,10 +683,15 @@ def main():
                                 "layer_tflops": fl / (rs["ms_per_step"] * 1e-3) / 1e12}
         del sh
     if not args.no_backward:
-        log("timing the backward pass")
-        rb = time_backward(inp, dev, args.steps, args.warmup)
-        bfl = 16.0 * rb["A"] * inp.d * inp.f
+        log("timing the training forward and the backward pass")
+        rt = time_layer(inp, dev, args.steps, args.warmup, save=True)
+        rb = time_backward(inp, dev, args.steps, args.warmup, saved=True)
+        rr = time_backward(inp, dev, args.steps, args.warmup, saved=False)
+        # the expert backward's algorithmic flops: da, dx, dW2, dW1 | dW3 (12 A d f); the
+        # recompute variant adds the 4 A d f of h1 / h3 again
+        bfl = 12.0 * rb["A"] * inp.d * inp.f
         gt = bfl / (rb["expert_ms"] * 1e-3) / 1e12
+        tfwd = rt["ms_per_step"]
         out["backward"] = {"workload": w.name + "_backward_auxcoef0.01",
                            "ms_per_step": rb["ms_per_step"],
                            "tokens_per_s": inp.T / (rb["ms_per_step"] * 1e-3),
@@ -682,9 +699,15 @@ def main():
                                          "expert_backward": rb["expert_ms"],
                                          "router_backward": rb["router_ms"]},
                            "expert_gemm_tflops": gt, "expert_gemm_frac_mfma_peak": gt / PEAK_BF16_TFLOPS,
-                           "work_per_launch": f"16*A*d*f = {bfl:.4e} flop over 5 GEMM launches, A={rb['A']}",
-                           "forward_plus_backward_ms": ms + rb["ms_per_step"],
-                           "training_tokens_per_s": inp.T / ((ms + rb["ms_per_step"]) * 1e-3)}
+                           "work_per_launch": f"12*A*d*f = {bfl:.4e} flop over 4 GEMM launches "
+                                              f"(h1 / h3 saved by the forward), A={rb['A']}",
+                           "training_forward_ms": tfwd,
+                           "training_forward_up_ms": rt["up_ms"],
+                           "forward_plus_backward_ms": tfwd + rb["ms_per_step"],
+                           "training_tokens_per_s": inp.T / ((tfwd + rb["ms_per_step"]) * 1e-3),
+                           "recompute_variant": {
+                               "ms_per_step": rr["ms_per_step"], "expert_backward_ms": rr["expert_ms"],
+                               "forward_plus_backward_ms": ms + rr["ms_per_step"]}}
         torch.cuda.empty_cache()
     del dev
     torch.cuda.empty_cache()

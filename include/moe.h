@@ -71,7 +71,8 @@ typedef enum {
   MOE_OP_EXPERT_DOWN = 5,
   MOE_OP_PERMUTE_REROUTE = 6,
   MOE_OP_EXPERT_BACKWARD = 7,
-  MOE_OP_ROUTER_BACKWARD = 8
+  MOE_OP_ROUTER_BACKWARD = 8,
+  MOE_OP_EXPERT_BACKWARD_SAVED = 9
 } moe_op;
 
 /* Human-readable name of a status code (static string). */
@@ -95,8 +96,8 @@ int moe_capacity(int T, int k, int N, double capacity_factor);
  * T*k is the row capacity (max_rows) of x_perm / y_perm.  The two expert ops
  * size their k-split buffers by the compute units of the CURRENT device
  * (0 when no device is visible); query with that device current.
- * MOE_OP_EXPERT_BACKWARD: T*k is max_rows.  MOE_OP_ROUTER_BACKWARD: d and N
- * of the router, T tokens. */
+ * MOE_OP_EXPERT_BACKWARD and MOE_OP_EXPERT_BACKWARD_SAVED: T*k is max_rows.
+ * MOE_OP_ROUTER_BACKWARD: d and N of the router, T tokens. */
 size_t moe_workspace_size(moe_op op, int T, int d, int N, int k, int f, moe_dtype dt);
 
 /*
@@ -231,6 +232,16 @@ moe_status moe_expert_up(const void* x_perm, const int32_t* offsets, const void*
                          const void* w3, int N, int d, int f, int max_rows, moe_dtype dt,
                          void* act, void* stream);
 
+/* moe_expert_up for training: the same act, and also both projections
+ *   h13[r, 0:f] = x_perm[r] W1_e,  h13[r, f:2f] = x_perm[r] W3_e
+ * in dtype dt (bf16: rounded to nearest even), h13 [max_rows, 2f], for
+ * moe_expert_backward_saved, which then needs no recompute of them.  Runs the
+ * MFMA tile kernels at every batch size (they alone store h13).  Rows >=
+ * offsets[N] of h13 are not written. */
+moe_status moe_expert_up_save(const void* x_perm, const int32_t* offsets, const void* w1,
+                              const void* w3, int N, int d, int f, int max_rows, moe_dtype dt,
+                              void* act, void* h13, void* stream);
+
 /* Second grouped GEMM: y_perm[r] = act[r] W2_e, y_perm fp32.
  *   ws  moe_workspace_size(MOE_OP_EXPERT_DOWN, T, d, N, k, f, dt) bytes with
  *       T*k = max_rows (may be NULL when that size is 0).  When the tiles'
@@ -346,6 +357,23 @@ moe_status moe_expert_backward(const void* x_perm, const void* g_perm, const int
                                const void* w1, const void* w3, const void* w2, int N, int d,
                                int f, int max_rows, moe_dtype dt, float* dx_perm, float* dw1,
                                float* dw3, float* dw2, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_expert_backward_saved -- moe_expert_backward with h1 and h3 taken from
+ * the h13 [max_rows, 2f] that moe_expert_up_save stored in the forward
+ * (dtype dt) instead of recomputed from x_perm: the SwiGLU backward (dh1,
+ * dh3, a) runs in the epilogue of the da GEMM, so the backward does three
+ * grouped GEMM passes' worth of work less (12 A d f flops instead of 16).
+ * Arguments, outputs and limits otherwise as moe_expert_backward.
+ *   ws  moe_workspace_size(MOE_OP_EXPERT_BACKWARD_SAVED, T, d, N, k, f, dt)
+ *       bytes, T*k = max_rows: [dh1 | dh3] [max_rows, 2f] and a [max_rows, f]
+ *       in dtype dt, each padded to 256 bytes.
+ */
+moe_status moe_expert_backward_saved(const void* x_perm, const void* g_perm, const void* h13,
+                                     const int32_t* offsets, const void* w1, const void* w3,
+                                     const void* w2, int N, int d, int f, int max_rows,
+                                     moe_dtype dt, float* dx_perm, float* dw1, float* dw3,
+                                     float* dw2, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_router_backward -- through the softmax over the k selected logits, the

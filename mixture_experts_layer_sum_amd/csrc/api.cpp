@@ -103,6 +103,9 @@ size_t moe_workspace_size(moe_op op, int T, int d, int N, int k, int f, moe_dtyp
     case MOE_OP_EXPERT_BACKWARD:
       if (d < 1 || f < 1 || !dtype_ok(dt)) return 0;
       return moe::expert_backward_ws_bytes(d, f, T * k, dt == MOE_BF16);
+    case MOE_OP_EXPERT_BACKWARD_SAVED:
+      if (d < 1 || f < 1 || !dtype_ok(dt)) return 0;
+      return moe::expert_backward_saved_ws_bytes(d, f, T * k, dt == MOE_BF16);
     case MOE_OP_ROUTER_BACKWARD:
       if (d < 1 || N > kMaxExperts) return 0;
       return moe::router_backward_ws_bytes(T, d, N);
@@ -191,7 +194,17 @@ moe_status moe_expert_up(const void* x_perm, const int32_t* offsets, const void*
   moe_status s = check_expert_shape(N, d, f, max_rows, dt);
   if (s != MOE_OK) return s;
   return hip_status(moe::launch_expert_up(x_perm, offsets, w1, w3, N, d, f, max_rows,
-                                          dt == MOE_BF16, act, as_stream(stream)));
+                                          dt == MOE_BF16, act, nullptr, as_stream(stream)));
+}
+
+moe_status moe_expert_up_save(const void* x_perm, const int32_t* offsets, const void* w1,
+                              const void* w3, int N, int d, int f, int max_rows, moe_dtype dt,
+                              void* act, void* h13, void* stream) {
+  if (!x_perm || !offsets || !w1 || !w3 || !act || !h13) return MOE_ERR_INVALID_ARG;
+  moe_status s = check_expert_shape(N, d, f, max_rows, dt);
+  if (s != MOE_OK) return s;
+  return hip_status(moe::launch_expert_up(x_perm, offsets, w1, w3, N, d, f, max_rows,
+                                          dt == MOE_BF16, act, h13, as_stream(stream)));
 }
 
 moe_status moe_expert_down(const void* act, const int32_t* offsets, const void* w2, int N, int d,
@@ -218,7 +231,7 @@ moe_status moe_expert_ffn(const void* x_perm, const int32_t* offsets, const void
   if (ws_bytes < need_act + need_down) return MOE_ERR_WORKSPACE;
   if (!ws) return MOE_ERR_INVALID_ARG;
   hipError_t e = moe::launch_expert_up(x_perm, offsets, w1, w3, N, d, f, max_rows, dt == MOE_BF16,
-                                       ws, as_stream(stream));
+                                       ws, nullptr, as_stream(stream));
   if (e != hipSuccess) return MOE_ERR_HIP;
   void* down_ws = need_down > 0 ? static_cast<char*>(ws) + need_act : nullptr;
   return hip_status(moe::launch_expert_down(ws, offsets, w2, N, d, f, max_rows, dt == MOE_BF16,
@@ -320,6 +333,28 @@ moe_status moe_expert_backward(const void* x_perm, const void* g_perm, const int
   return hip_status(moe::launch_expert_backward(x_perm, g_perm, offsets, w1, w3, w2, N, d, f,
                                                 max_rows, dt == MOE_BF16, dx_perm, dw1, dw3, dw2,
                                                 ws, as_stream(stream)));
+}
+
+moe_status moe_expert_backward_saved(const void* x_perm, const void* g_perm, const void* h13,
+                                     const int32_t* offsets, const void* w1, const void* w3,
+                                     const void* w2, int N, int d, int f, int max_rows,
+                                     moe_dtype dt, float* dx_perm, float* dw1, float* dw3,
+                                     float* dw2, void* ws, size_t ws_bytes, void* stream) {
+  if (!x_perm || !g_perm || !h13 || !offsets || !w1 || !w3 || !w2 || !dx_perm || !dw1 || !dw3 ||
+      !dw2)
+    return MOE_ERR_INVALID_ARG;
+  moe_status s = check_expert_shape(N, d, f, max_rows, dt);
+  if (s != MOE_OK) return s;
+  if (dt == MOE_BF16 && (f % 256 != 0 ||
+                         static_cast<int64_t>(max_rows) * f >= (int64_t{1} << 29) ||
+                         static_cast<int64_t>(max_rows) * d >= (int64_t{1} << 30)))
+    return MOE_ERR_UNSUPPORTED;
+  const size_t need = moe::expert_backward_saved_ws_bytes(d, f, max_rows, dt == MOE_BF16);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (!ws) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_expert_backward_saved(x_perm, g_perm, h13, offsets, w1, w3, w2, N,
+                                                      d, f, max_rows, dt == MOE_BF16, dx_perm,
+                                                      dw1, dw3, dw2, ws, as_stream(stream)));
 }
 
 moe_status moe_router_backward(const void* hidden, const void* w_router, const float* logits,

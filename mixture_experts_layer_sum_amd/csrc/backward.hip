@@ -40,7 +40,9 @@
 namespace moe {
 namespace bwd {
 
-enum Mode { kDA = 0, kDX = 1, kSwiGLU = 2, kWGrad = 3 };
+// kDAS: the da GEMM with the SwiGLU backward in its epilogue, from the h1 / h3
+// the forward saved (moe_expert_backward_saved): no recompute GEMM
+enum Mode { kDA = 0, kDX = 1, kSwiGLU = 2, kWGrad = 3, kDAS = 4 };
 
 constexpr int kBM = 256, kBN = 256, kBK = 64, kThreads = 512, kGroupM = 8;
 // transposed operand tile: 16-element (32-byte) pad after every 4 k-rows of 128
@@ -70,6 +72,7 @@ struct Args {
   int ldo, nsplit;
   long long o_estride;      // WGrad: elements between experts' outputs
   const float* da;          // SwiGLU: da [rows, f] (input)
+  const void* h13;          // DAS: [h1 | h3] [rows, 2f] saved by the forward (input)
   void* dh;                 // SwiGLU: [dh1 | dh3] [rows, 2f] (output)
   void* act;                // SwiGLU: a [rows, f] (output)
   int f;
@@ -451,6 +454,71 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_bf16_kernel(Args p) {
           }
         }
       }
+  } else if (MODE == kDAS) {
+    // acc = da for tile rows x f-columns n0 .. n0 + 255.  Four passes of 64 tile rows
+    // (row blocks ib = 2 pass, 2 pass + 1):
+    //  1. the rows' saved [h1 256 | h3 256] (bf16, 1 KB) come into S0 by direct loads
+    //     from every wave (8 rows each, one row per 1 KB instruction: lanes 0..31 read
+    //     the h1 piece, 32..63 the h3 piece; rows past the tile read zeros);
+    //  2. each lane turns its h1, h3 and da into dh1, dh3 (written over h1, h3 in S0)
+    //     and a (into S1, 512-byte rows plus 16 bytes of padding);
+    //  3. the block writes the rows' dh1, dh3 and a pieces (512 bytes each) to global
+    //     memory with 16-byte stores (2-byte stores from the accumulators' lanes cost a
+    //     quarter of this GEMM).
+    constexpr int kActE = 264;
+    const int f = p.f;
+    const __amdgpu_buffer_rsrc_t h_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(static_cast<const uint16_t*>(p.h13) + (size_t)r0 * 2 * f), 0,
+        tile_rows * 2 * f * 2, kRsrcWord3);
+    const uint32_t hv = (uint32_t)((((lane >> 5) ? f : 0) + n0 + 8 * (lane & 31)) * 2);
+    uint16_t* dh = static_cast<uint16_t*>(p.dh);
+    uint16_t* act = static_cast<uint16_t*>(p.act);
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            h_rs, (lds_void*)(S0 + (8 * w + i) * 512), 16, hv,
+            (uint32_t)((64 * pass + 8 * w + i) * 2 * f * 2), 0, 0);
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+      for (int ib = 2 * pass; ib < 2 * pass + 2; ++ib)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int lr = 32 * wm + 16 * (ib & 1) + g4 + r;        // row within the pass
+          uint16_t* hrow = S0 + lr * 512;
+          uint16_t* arow = S1 + lr * kActE;
+#pragma unroll
+          for (int jb = 0; jb < 4; ++jb) {
+            const int cl = wn * 128 + 64 * pw + 16 * jb + l16;
+            const float h1 = bf16_to_f32(hrow[cl]), h3 = bf16_to_f32(hrow[256 + cl]);
+            const float g = acc[ib][jb][r];
+            const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-h1));
+            const float sl = h1 * sg;
+            hrow[cl] = f32_to_bf16(g * h3 * (sg + sl * (1.f - sg)));
+            hrow[256 + cl] = f32_to_bf16(g * sl);
+            arow[cl] = f32_to_bf16(sl * h3);
+          }
+        }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      // wave w: rows 8 w .. 8 w + 7 of the pass, 24 (row, piece) pairs, two per
+      // instruction (32 lanes x 16 bytes each)
+#pragma unroll
+      for (int i = 0; i < 12; ++i) {
+        const int idx = 2 * i + (lane >> 5);
+        const int prow = 8 * w + idx / 3, seg = idx % 3;
+        const int row = r0 + 64 * pass + prow;
+        const int c8 = 8 * (lane & 31);
+        const uint16_t* src = seg == 2 ? S1 + prow * kActE + c8 : S0 + prow * 512 + 256 * seg + c8;
+        const uint4 v = *reinterpret_cast<const uint4*>(src);
+        if (row < rend) {
+          uint16_t* dst = seg == 2 ? act + (size_t)row * f + n0
+                                   : dh + (size_t)row * 2 * f + (seg == 1 ? f : 0) + n0;
+          *reinterpret_cast<uint4*>(dst + c8) = v;
+        }
+      }
+    }
   } else if (MODE == kWGrad) {
     const bool low = n0 < p.nsplit;
     float* o = (low ? p.out0 : p.out1) + (size_t)e * p.o_estride;
@@ -570,7 +638,18 @@ __global__ __launch_bounds__(256) void bwd_gemm_f32_kernel(Args p) {
       }
       const int row = r0 + mloc;
       if (row >= rend) continue;
-      if (MODE == kSwiGLU) {
+      if (MODE == kDAS) {
+        const int f = p.f;
+        const float* hs = static_cast<const float*>(p.h13);
+        const float h1 = hs[(size_t)row * 2 * f + col], h3 = hs[(size_t)row * 2 * f + f + col];
+        const float g = c0[i][j];
+        const float s = 1.f / (1.f + expf(-h1));
+        const float sl = h1 * s;
+        float* dh = static_cast<float*>(p.dh);
+        dh[(size_t)row * 2 * f + col] = g * h3 * (s + sl * (1.f - s));
+        dh[(size_t)row * 2 * f + f + col] = g * sl;
+        static_cast<float*>(p.act)[(size_t)row * f + col] = sl * h3;
+      } else if (MODE == kSwiGLU) {
         const int f = p.f;
         const float h1 = c0[i][j], h3 = c1[i][j];
         const float g = p.da[(size_t)row * f + col];
@@ -877,6 +956,58 @@ hipError_t launch_expert_backward(const void* x_perm, const void* g_perm, const 
   gemm<kWGrad>(s, bf16, stream);
 
   // [dW1_e | dW3_e] = x_e^T [dh1_e | dh3_e]  ([d, rows] x [rows, 2f])
+  s = a;
+  s.a = x_perm; s.lda = d;
+  s.b0 = dh; s.b1 = dh; s.ldb = 2 * f;
+  s.M = d; s.Nn = 2 * f; s.out0 = dw1; s.out1 = dw3; s.ldo = f; s.nsplit = f;
+  s.o_estride = (long long)d * f;
+  gemm<kWGrad>(s, bf16, stream);
+  return hipGetLastError();
+}
+
+size_t expert_backward_saved_ws_bytes(int d, int f, int max_rows, bool bf16) {
+  (void)d;
+  const size_t rows = (size_t)max_rows, eb = bf16 ? 2 : 4;
+  return bwd::pad256(rows * 2 * f * eb) + bwd::pad256(rows * f * eb);
+}
+
+hipError_t launch_expert_backward_saved(const void* x_perm, const void* g_perm, const void* h13,
+                                        const int32_t* offsets, const void* w1, const void* w3,
+                                        const void* w2, int N, int d, int f, int max_rows,
+                                        bool bf16, float* dx_perm, float* dw1, float* dw3,
+                                        float* dw2, void* ws, hipStream_t stream) {
+  using namespace bwd;
+  const size_t rows = (size_t)max_rows, eb = bf16 ? 2 : 4;
+  void* dh = ws;
+  void* act = static_cast<char*>(ws) + pad256(rows * 2 * f * eb);
+  Args a{};
+  a.offsets = offsets;
+  a.n_exp = N;
+  a.max_rows = max_rows;
+
+  // da = g W2_e^T, and in the same epilogue dh1, dh3, a from the saved h1 / h3
+  Args s = a;
+  s.a = g_perm; s.lda = d;
+  s.b0 = w2; s.b1 = w2; s.ldb = d; s.b_estride = (long long)f * d;
+  s.K = d; s.Nn = f; s.h13 = h13; s.dh = dh; s.act = act; s.f = f;
+  gemm<kDAS>(s, bf16, stream);
+
+  // dx = [dh1 | dh3] [W1_e | W3_e]^T
+  s = a;
+  s.a = dh; s.lda = 2 * f;
+  s.b0 = w1; s.b1 = w3; s.ldb = f; s.b_estride = (long long)d * f;
+  s.K = 2 * f; s.ksplit = f / kBK; s.Nn = d; s.out0 = dx_perm; s.ldo = d;
+  gemm<kDX>(s, bf16, stream);
+
+  // dW2_e = a_e^T g_e
+  s = a;
+  s.a = act; s.lda = f;
+  s.b0 = g_perm; s.b1 = g_perm; s.ldb = d;
+  s.M = f; s.Nn = d; s.out0 = dw2; s.out1 = dw2; s.ldo = d; s.nsplit = d;
+  s.o_estride = (long long)f * d;
+  gemm<kWGrad>(s, bf16, stream);
+
+  // [dW1_e | dW3_e] = x_e^T [dh1_e | dh3_e]
   s = a;
   s.a = x_perm; s.lda = d;
   s.b0 = dh; s.b1 = dh; s.ldb = 2 * f;

@@ -325,7 +325,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
     const uint16_t* __restrict__ X, const int32_t* __restrict__ offsets, int N,
     const uint16_t* __restrict__ Wa, const uint16_t* __restrict__ Wb, int K, int Nout,
     int n_tiles, int max_rows, void* __restrict__ out, float* __restrict__ part,
-    int32_t* __restrict__ tickets, int num_cus, int dp_grid) {
+    int32_t* __restrict__ tickets, int num_cus, int dp_grid, uint16_t* __restrict__ h13) {
   // two 64 KB stages as separate LDS objects: the compiler tracks in-flight
   // direct loads per LDS object, so a read of one stage never waits on the
   // refill of the other
@@ -533,7 +533,54 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
   // ---- epilogue: block (ib, jb), lane l, element r is row
   // 64 (ib >> 1) + 32 wm + 16 (ib & 1) + 4 (l >> 4) + r, column 16 (jb & 1) + (l & 15)
   // of the wave's column group jb >> 1
-  if (UP) {
+  if (UP && h13) {
+    // training: the tile's act and both projections ([h1 | h3] per row of h13) leave
+    // through LDS so that they are written as 256-byte row pieces by 16-byte stores
+    // (three 2-byte stores per element straight from the accumulators cost about a
+    // tenth of the kernel).  Two passes of 128 tile rows; a row holds
+    // [act 128 | h1 128 | h3 128] bf16 and 16 bytes of padding (784 bytes: the four
+    // row groups of a write, 4 rows apart, start 16 banks apart); rows 0..63 in S0,
+    // 64..127 in S1.
+    constexpr int kRowE = 392;
+    uint16_t* act = static_cast<uint16_t*>(out);
+    const int g4 = 4 * (lane >> 4), l16 = lane & 15;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+      for (int ib = 4 * pass; ib < 4 * pass + 4; ++ib)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int lr = 64 * (ib >> 1) + 32 * wm + 16 * (ib & 1) + g4 + r - 128 * pass;
+          uint16_t* lrow = (lr < 64 ? S0 : S1) + (lr & 63) * kRowE;
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const int c = wn * 64 + 32 * pw + 16 * jj + l16;
+            const float h1 = acc[ib][jj][r], h3 = acc[ib][2 + jj][r];
+            const float gv = h1 * __builtin_amdgcn_rcpf(1.f + __expf(-h1)) * h3;
+            lrow[c] = f32_to_bf16(gv);
+            lrow[128 + c] = f32_to_bf16(h1);
+            lrow[256 + c] = f32_to_bf16(h3);
+          }
+        }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      // wave w writes rows 16 w .. 16 w + 15 of the pass: 48 (row, piece) pairs, four
+      // per instruction (16 lanes x 16 bytes each)
+#pragma unroll
+      for (int i = 0; i < 12; ++i) {
+        const int idx = 4 * i + (lane >> 4);
+        const int prow = 16 * w + idx / 3, seg = idx % 3;
+        const int row = r0 + 128 * pass + prow;
+        const uint16_t* lrow = (prow < 64 ? S0 : S1) + (prow & 63) * kRowE;
+        const uint4 v = *reinterpret_cast<const uint4*>(lrow + 128 * seg + 8 * l16);
+        if (row < rend) {
+          uint16_t* dst = seg == 0 ? act + (size_t)row * Nout + n0
+                                   : h13 + (size_t)row * 2 * Nout + (seg == 2 ? Nout : 0) + n0;
+          *reinterpret_cast<uint4*>(dst + 8 * l16) = v;
+        }
+      }
+    }
+  } else if (UP) {
     uint16_t* act = static_cast<uint16_t*>(out);
 #pragma unroll
     for (int ib = 0; ib < 8; ++ib)
@@ -921,7 +968,7 @@ template <bool UP>
 __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
     const float* __restrict__ X, const int32_t* __restrict__ offsets, int N,
     const float* __restrict__ Wa, const float* __restrict__ Wb, int K, int Nout, int n_tiles,
-    int max_rows, float* __restrict__ out) {
+    int max_rows, float* __restrict__ out, float* __restrict__ h13) {
   __shared__ float As[kFBK][kFBM + 1];
   __shared__ float B1[kFBK][kFBN];
   __shared__ float B3[kFBK][kFBN];
@@ -972,6 +1019,10 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
     for (int j = 0; j < 4; ++j) {
       const int col = n0 + tx * 4 + j;
       float v = c1[i][j];
+      if (UP && h13) {
+        h13[(size_t)row * 2 * Nout + col] = v;
+        h13[(size_t)row * 2 * Nout + Nout + col] = c3[i][j];
+      }
       if (UP) v = v / (1.f + expf(-v)) * c3[i][j];
       out[(size_t)row * Nout + col] = v;
     }
@@ -1014,8 +1065,9 @@ size_t expert_down_ws_bytes(int N, int d, int f, int max_rows, bool bf16) {
 
 hipError_t launch_expert_up(const void* x_perm, const int32_t* offsets, const void* w1,
                             const void* w3, int N, int d, int f, int max_rows, bool bf16,
-                            void* act, hipStream_t stream) {
-  if (bf16 && rows_mt(max_rows, N) > 0) {
+                            void* act, void* h13, hipStream_t stream) {
+  // with h13 (training) the tile kernels run at every batch size: only they store h1 / h3
+  if (bf16 && !h13 && rows_mt(max_rows, N) > 0) {
     launch_rows<true>(rows_mt(max_rows, N), x_perm, offsets, N, w1, w3, d, f, max_rows, act, stream);
   } else if (bf16) {
     const int n_tiles = f / (kBN / 2);
@@ -1025,14 +1077,14 @@ hipError_t launch_expert_up(const void* x_perm, const int32_t* offsets, const vo
                        static_cast<const uint16_t*>(x_perm), offsets, N,
                        static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w3), d, f,
                        n_tiles, max_rows, act, static_cast<float*>(nullptr),
-                       static_cast<int32_t*>(nullptr), 0, grid);
+                       static_cast<int32_t*>(nullptr), 0, grid, static_cast<uint16_t*>(h13));
   } else {
     const int n_tiles = f / kFBN;
     const int mt_bound = (max_rows + kFBM - 1) / kFBM + N;
     hipLaunchKernelGGL(grouped_gemm_f32_kernel<true>, dim3(mt_bound * n_tiles), dim3(256), 0,
                        stream, static_cast<const float*>(x_perm), offsets, N,
                        static_cast<const float*>(w1), static_cast<const float*>(w3), d, f, n_tiles,
-                       max_rows, static_cast<float*>(act));
+                       max_rows, static_cast<float*>(act), static_cast<float*>(h13));
   }
   return hipGetLastError();
 }
@@ -1061,14 +1113,14 @@ hipError_t launch_expert_down(const void* act, const int32_t* offsets, const voi
                        static_cast<const uint16_t*>(act), offsets, N,
                        static_cast<const uint16_t*>(w2), static_cast<const uint16_t*>(nullptr), f,
                        d, n_tiles, max_rows, static_cast<void*>(y_perm), part, tickets, cus,
-                       dp_grid);
+                       dp_grid, static_cast<uint16_t*>(nullptr));
   } else {
     const int n_tiles = d / kFBN;
     const int mt_bound = (max_rows + kFBM - 1) / kFBM + N;
     hipLaunchKernelGGL(grouped_gemm_f32_kernel<false>, dim3(mt_bound * n_tiles), dim3(256), 0,
                        stream, static_cast<const float*>(act), offsets, N,
                        static_cast<const float*>(w2), static_cast<const float*>(nullptr), f, d,
-                       n_tiles, max_rows, y_perm);
+                       n_tiles, max_rows, y_perm, static_cast<float*>(nullptr));
   }
   return hipGetLastError();
 }

@@ -33,9 +33,10 @@ hipError_t launch_permute_reroute(const void* hidden, const int32_t* topk_idx,
                                   int32_t* slot_row, int32_t* kept, int32_t* offsets, void* ws,
                                   hipStream_t stream);
 
+// h13: NULL, or [max_rows, 2f] in the layer dtype: h1 = x W1 then h3 = x W3 per row
 hipError_t launch_expert_up(const void* x_perm, const int32_t* offsets, const void* w1,
                             const void* w3, int N, int d, int f, int max_rows, bool bf16,
-                            void* act, hipStream_t stream);
+                            void* act, void* h13, hipStream_t stream);
 size_t expert_down_ws_bytes(int N, int d, int f, int max_rows, bool bf16);   // current device
 hipError_t launch_expert_down(const void* act, const int32_t* offsets, const void* w2, int N,
                               int d, int f, int max_rows, bool bf16, float* y_perm, void* ws,
@@ -63,6 +64,12 @@ hipError_t launch_combine_backward(const void* dy, const float* y_perm, const in
                                    const float* topk_w, int T, int d, int k, bool bf16,
                                    void* g_perm, float* dgate, hipStream_t stream);
 size_t expert_backward_ws_bytes(int d, int f, int max_rows, bool bf16);
+size_t expert_backward_saved_ws_bytes(int d, int f, int max_rows, bool bf16);
+hipError_t launch_expert_backward_saved(const void* x_perm, const void* g_perm, const void* h13,
+                                        const int32_t* offsets, const void* w1, const void* w3,
+                                        const void* w2, int N, int d, int f, int max_rows,
+                                        bool bf16, float* dx_perm, float* dw1, float* dw3,
+                                        float* dw2, void* ws, hipStream_t stream);
 hipError_t launch_expert_backward(const void* x_perm, const void* g_perm, const int32_t* offsets,
                                   const void* w1, const void* w3, const void* w2, int N, int d,
                                   int f, int max_rows, bool bf16, float* dx_perm, float* dw1,

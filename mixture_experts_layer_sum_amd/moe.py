@@ -20,7 +20,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16 = 0, 1
 (MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_EXPERT_FFN, MOE_OP_COMBINE, MOE_OP_AUX_LOSS,
  MOE_OP_EXPERT_DOWN, MOE_OP_PERMUTE_REROUTE, MOE_OP_EXPERT_BACKWARD,
- MOE_OP_ROUTER_BACKWARD) = range(9)
+ MOE_OP_ROUTER_BACKWARD, MOE_OP_EXPERT_BACKWARD_SAVED) = range(10)
 
 # Every symbol include/moe.h declares, with (restype, argtypes).
 _P, _I, _F, _D, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_double, ctypes.c_size_t
@@ -35,6 +35,7 @@ SIGNATURES = {
                                  _P]),
     "moe_expert_ffn": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
     "moe_expert_up": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
+    "moe_expert_up_save": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P]),
     "moe_expert_down": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _Z, _P]),
     "moe_quantize_fp8": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
     "moe_expert_up_fp8": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
@@ -44,6 +45,8 @@ SIGNATURES = {
     "moe_combine_backward": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
     "moe_expert_backward": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P,
                                  _Z, _P]),
+    "moe_expert_backward_saved": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P,
+                                       _P, _P, _Z, _P]),
     "moe_router_backward": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _F, _I, _I, _I, _I,
                                  _I, _P, _P, _P, _P, _Z, _P]),
 }
@@ -190,6 +193,18 @@ def moe_expert_up(x_perm, offsets, w1, w3, act=None, stream=None):
     return act
 
 
+def moe_expert_up_save(x_perm, offsets, w1, w3, act=None, h13=None, stream=None):
+    """moe_expert_up that also stores h13 = [x W1 | x W3] per row for the backward."""
+    max_rows, d = x_perm.shape
+    N, _, f = w1.shape
+    act = _empty((max_rows, f), x_perm.dtype, x_perm.device, act)
+    h13 = _empty((max_rows, 2 * f), x_perm.dtype, x_perm.device, h13)
+    _check(_lib.moe_expert_up_save(_ptr(x_perm), _ptr(offsets), _ptr(w1), _ptr(w3), N, d, f,
+                                   max_rows, _dt(x_perm), _ptr(act), _ptr(h13), _stream(stream)),
+           "moe_expert_up_save")
+    return act, h13
+
+
 def moe_expert_down(act, offsets, w2, y_perm=None, ws=None, stream=None):
     max_rows, f = act.shape
     N, _, d = w2.shape
@@ -273,7 +288,8 @@ def moe_aux_loss(logits, counts, k, aux=None, ws=None, stream=None):
 class MoEBuffers:
     """Every output and workspace of one layer forward, allocated once."""
 
-    def __init__(self, T, d, N, k, f, dtype, device="cuda", n_shared=0, f_shared=None):
+    def __init__(self, T, d, N, k, f, dtype, device="cuda", n_shared=0, f_shared=None,
+                 save_for_backward=False):
         self.T, self.d, self.N, self.k, self.f, self.dtype = T, d, N, k, f, dtype
         e = lambda shape, dt: torch.empty(shape, dtype=dt, device=device)  # noqa: E731
         self.logits = e((T, N), torch.float32)
@@ -286,6 +302,8 @@ class MoEBuffers:
         self.kept = e((N,), torch.int32)
         self.offsets = e((N + 1,), torch.int32)
         self.act = e((T * k, f), dtype)
+        # training: [x W1 | x W3] per routed row, kept for moe_expert_backward_saved
+        self.h13 = e((T * k, 2 * f), dtype) if save_for_backward else None
         self.y_perm = e((T * k, d), torch.float32)
         self.y = e((T, d), dtype)
         self.aux = e((1,), torch.float32)
@@ -307,7 +325,7 @@ class MoEBuffers:
 
 def moe_forward(hidden, w_router, w1, w3, w2, k, capacity_factor=0.0, bias=None,
                 bufs: Optional[MoEBuffers] = None, stream=None, overflow="drop", shared=None,
-                fp8=None):
+                fp8=None, save_for_backward=False):
     """Run the five steps on the current stream.  Returns the MoEBuffers holding every result.
 
     ``y`` excludes the residual: the layer output with residual is hidden + y.
@@ -316,16 +334,23 @@ def moe_forward(hidden, w_router, w1, w3, w2, k, capacity_factor=0.0, bias=None,
     token passes through, added with weight 1.
     ``fp8`` is None or (w1q, w3q, w2q, s1, s3, s2) from moe_quantize_fp8: the expert GEMMs
     then read the FP8 codes (w1, w3, w2 are only used for their shapes).
+    ``save_for_backward`` (bf16 / fp32 weights): the up projection also keeps
+    h13 = [x W1 | x W3] (moe_expert_up_save), which moe_backward then uses instead of
+    recomputing it; with ``bufs`` given, they must have been built with it.
     """
     if overflow not in ("drop", "reroute"):
         raise ValueError(f"unknown overflow policy {overflow!r}")
     T, d = hidden.shape
     N, _, f = w1.shape
     ns = 0 if shared is None else shared[0].shape[0]
+    if save_for_backward and fp8 is not None:
+        raise ValueError("save_for_backward needs bf16 / fp32 expert weights")
     if bufs is None:
         bufs = MoEBuffers(T, d, N, k, f, hidden.dtype, hidden.device, ns,
-                          None if shared is None else shared[0].shape[2])
+                          None if shared is None else shared[0].shape[2], save_for_backward)
     b = bufs
+    if save_for_backward and b.h13 is None:
+        raise ValueError("bufs were built without save_for_backward")
     moe_route(hidden, w_router, k, bias, b.logits, b.topk_idx, b.topk_w, b.counts, b.ws_route,
               stream)
     if overflow == "drop":
@@ -334,8 +359,12 @@ def moe_forward(hidden, w_router, w1, w3, w2, k, capacity_factor=0.0, bias=None,
     else:
         moe_permute_reroute(hidden, b.topk_idx, b.logits, N, capacity_factor, b.x_perm, b.perm_src,
                             b.slot_row, b.kept, b.offsets, b.ws_permute, stream)
+    b.saved = bool(save_for_backward)
     if fp8 is None:
-        moe_expert_up(b.x_perm, b.offsets, w1, w3, b.act, stream)
+        if save_for_backward:
+            moe_expert_up_save(b.x_perm, b.offsets, w1, w3, b.act, b.h13, stream)
+        else:
+            moe_expert_up(b.x_perm, b.offsets, w1, w3, b.act, stream)
         moe_expert_down(b.act, b.offsets, w2, b.y_perm, b.ws_down, stream)
     else:
         w1q, w3q, w2q, s1, s3, s2 = fp8
@@ -380,6 +409,26 @@ def moe_expert_backward(x_perm, g_perm, offsets, w1, w3, w2, dx_perm=None, dw1=N
                                     _ptr(w2), N, d, f, max_rows, _dt(x_perm), _ptr(dx_perm),
                                     _ptr(dw1), _ptr(dw3), _ptr(dw2), _ptr(ws), ws.numel(),
                                     _stream(stream)), "moe_expert_backward")
+    return dx_perm, dw1, dw3, dw2
+
+
+def moe_expert_backward_saved(x_perm, g_perm, h13, offsets, w1, w3, w2, dx_perm=None, dw1=None,
+                              dw3=None, dw2=None, ws=None, stream=None):
+    max_rows, d = x_perm.shape
+    N, _, f = w1.shape
+    dev = x_perm.device
+    dx_perm = _empty((max_rows, d), torch.float32, dev, dx_perm)
+    dw1 = _empty((N, d, f), torch.float32, dev, dw1)
+    dw3 = _empty((N, d, f), torch.float32, dev, dw3)
+    dw2 = _empty((N, f, d), torch.float32, dev, dw2)
+    if ws is None:
+        ws = torch.empty(max(1, workspace_size(MOE_OP_EXPERT_BACKWARD_SAVED, max_rows, d, N, 1, f,
+                                               x_perm.dtype)), dtype=torch.uint8, device=dev)
+    _check(_lib.moe_expert_backward_saved(_ptr(x_perm), _ptr(g_perm), _ptr(h13), _ptr(offsets),
+                                          _ptr(w1), _ptr(w3), _ptr(w2), N, d, f, max_rows,
+                                          _dt(x_perm), _ptr(dx_perm), _ptr(dw1), _ptr(dw3),
+                                          _ptr(dw2), _ptr(ws), ws.numel(), _stream(stream)),
+           "moe_expert_backward_saved")
     return dx_perm, dw1, dw3, dw2
 
 
@@ -441,7 +490,7 @@ def moe_backward(hidden, w_router, w1, w3, w2, dy, fwd: MoEBuffers, aux_coef=0.0
                  grads: Optional[MoEGradBuffers] = None, want_dbias=True, stream=None,
                  shared=None):
     """Gradients of <dy, y> + aux_coef * aux for the batch `fwd` holds (moe_forward's
-    buffers of the same call).  Returns the MoEGradBuffers (dhidden, dw_router, dbias,
+    buffers of the same call; when that forward saved h13, the expert backward uses it).  Returns the MoEGradBuffers (dhidden, dw_router, dbias,
     dw1, dw3, dw2 in fp32; with ``shared`` = (w1s, w3s, w2s) also dw1s, dw3s, dw2s)."""
     T, d = hidden.shape
     N, _, f = w1.shape
@@ -461,8 +510,12 @@ def moe_backward(hidden, w_router, w1, w3, w2, dy, fwd: MoEBuffers, aux_coef=0.0
                                 stream)
         dx_shared = g.dx_shared
     moe_combine_backward(dy, fwd.y_perm, fwd.slot_row, fwd.topk_w, g.g_perm, g.dgate, stream)
-    moe_expert_backward(fwd.x_perm, g.g_perm, fwd.offsets, w1, w3, w2, g.dx_perm, g.dw1, g.dw3,
-                        g.dw2, g.ws_expert, stream)
+    if getattr(fwd, "saved", False):
+        moe_expert_backward_saved(fwd.x_perm, g.g_perm, fwd.h13, fwd.offsets, w1, w3, w2,
+                                  g.dx_perm, g.dw1, g.dw3, g.dw2, g.ws_expert, stream)
+    else:
+        moe_expert_backward(fwd.x_perm, g.g_perm, fwd.offsets, w1, w3, w2, g.dx_perm, g.dw1,
+                            g.dw3, g.dw2, g.ws_expert, stream)
     moe_router_backward(hidden, w_router, fwd.logits, fwd.topk_idx, fwd.topk_w, fwd.counts,
                         g.dgate, g.dx_perm, fwd.slot_row, aux_coef, g.dhidden, g.dw_router,
                         g.dbias, want_dbias, g.ws_router, stream, dx_shared)

@@ -39,26 +39,48 @@ def _rel(gpu, ref):
     return err / den if den > 0 else err
 
 
-def run_backward(moe, inp, coef, overflow="drop", label=""):
+def _forward(moe, inp, dev, overflow, saved):
+    from tests import parity
+    sh = (dev["w1s"], dev["w3s"], dev["w2s"]) if inp.n_shared else None
+    b = moe.moe_forward(dev["hidden"], dev["w_router"], dev["w1"], dev["w3"], dev["w2"], inp.k,
+                        inp.capacity_factor, dev["bias"], overflow=overflow, shared=sh,
+                        save_for_backward=saved)
+    torch.cuda.synchronize()
+    return parity.host_results(b), b
+
+
+def run_backward(moe, inp, coef, overflow="drop", label="", modes=("recompute", "saved")):
+    """Both expert-backward paths (h1 / h3 recomputed, or saved by the forward) against
+    one oracle backward."""
     import oracle.moe_oracle as O
     from tests import parity
     parity.log(f"{label}: T={inp.T} d={inp.d} N={inp.N} k={inp.k} f={inp.f} {inp.dtype} "
                f"cf={inp.capacity_factor} aux_coef={coef} overflow={overflow}")
     dev = parity.to_device(inp)
-    g, b = parity.run_gpu(inp, dev, overflow=overflow)
     dy = synth.make_dy(inp.T, inp.d, inp.dtype, seed=11)
     sh = (dev["w1s"], dev["w3s"], dev["w2s"]) if inp.n_shared else None
-    gr = moe.moe_backward(dev["hidden"], dev["w_router"], dev["w1"], dev["w3"], dev["w2"],
-                          _dev(dy, inp.dtype), b, coef, want_dbias=inp.bias is not None,
-                          shared=sh)
-    torch.cuda.synchronize()
     dyv = synth.bf16_bits_to_f32(dy) if inp.dtype == "bf16" else dy
-    ref = O.moe_backward(inp.values("hidden"), inp.values("w_router"),
-                         parity.ExpertView(inp, "w1"), parity.ExpertView(inp, "w3"),
-                         parity.ExpertView(inp, "w2"), inp.k, dyv, inp.capacity_factor, inp.bias,
-                         aux_coef=coef, overflow=overflow,
-                         shared=(inp.values("w1s"), inp.values("w3s"), inp.values("w2s"))
-                         if inp.n_shared else None)
+    ref = None
+    reps = {}
+    for mode in modes:
+        g, b = _forward(moe, inp, dev, overflow, mode == "saved")
+        gr = moe.moe_backward(dev["hidden"], dev["w_router"], dev["w1"], dev["w3"], dev["w2"],
+                              _dev(dy, inp.dtype), b, coef, want_dbias=inp.bias is not None,
+                              shared=sh)
+        torch.cuda.synchronize()
+        if ref is None:
+            ref = O.moe_backward(inp.values("hidden"), inp.values("w_router"),
+                                 parity.ExpertView(inp, "w1"), parity.ExpertView(inp, "w3"),
+                                 parity.ExpertView(inp, "w2"), inp.k, dyv, inp.capacity_factor,
+                                 inp.bias, aux_coef=coef, overflow=overflow,
+                                 shared=(inp.values("w1s"), inp.values("w3s"), inp.values("w2s"))
+                                 if inp.n_shared else None)
+        reps[mode] = _compare(inp, g, gr, ref, f"{label}/{mode}")
+    return reps
+
+
+def _compare(inp, g, gr, ref, label):
+    from tests import parity
     # the gradients are taken at one routing: it must be the oracle's
     assert np.array_equal(g["topk_idx"], ref["topk_idx"]), f"{label}: routing differs"
     assert np.array_equal(g["slot_row"], ref["slot_row"]), f"{label}: dispatch differs"
@@ -125,13 +147,14 @@ def test_backward_small(moe, case):
     run_backward(moe, inp, coef, overflow, label)
 
 
-def test_backward_is_deterministic(moe):
+@pytest.mark.parametrize("saved", [False, True])
+def test_backward_is_deterministic(moe, saved):
     inp = synth.make_inputs(500, 256, 8, 2, 256, "bf16", 1.0, 3)
     from tests import parity
     dev = parity.to_device(inp)
     outs = []
     for _ in range(2):
-        _, b = parity.run_gpu(inp, dev)
+        _, b = _forward(moe, inp, dev, "drop", saved)
         dy = _dev(synth.make_dy(inp.T, inp.d, "bf16", 5), "bf16")
         gr = moe.moe_backward(dev["hidden"], dev["w_router"], dev["w1"], dev["w3"], dev["w2"], dy,
                               b, 0.01)
@@ -141,56 +164,104 @@ def test_backward_is_deterministic(moe):
         assert torch.equal(a, c)
 
 
+def test_up_save_stores_both_projections(moe):
+    """moe_expert_up_save: act as moe_expert_up, and h13 = [x W1 | x W3] per row against
+    the oracle's fp64 products (bf16: one rounding of an fp32 sum)."""
+    import oracle.moe_oracle as O
+    from tests import parity
+    for dt, T, N in (("bf16", 300, 8), ("bf16", 37, 64), ("f32", 100, 8)):
+        inp = synth.make_inputs(T, 256 if dt == "bf16" else 128, N, 2, 256, dt, 0.0, 2)
+        dev = parity.to_device(inp)
+        g, b = _forward(moe, inp, dev, "drop", True)
+        act2 = moe.moe_expert_up(b.x_perm, b.offsets, dev["w1"], dev["w3"])
+        torch.cuda.synchronize()
+        A = g["A"]
+        h13 = b.h13[:A].float().cpu().numpy().astype(np.float64)
+        hv = inp.values("hidden")
+        f = inp.f
+        src = g["perm_src"]
+        h1 = np.zeros((A, f))
+        h3 = np.zeros((A, f))
+        off = g["offsets"]
+        for e in range(N):
+            rows = np.arange(off[e], off[e + 1])
+            if rows.size:
+                x = hv[src[rows]].astype(np.float64)
+                h1[rows] = x @ inp.expert_values("w1", e).astype(np.float64)
+                h3[rows] = x @ inp.expert_values("w3", e).astype(np.float64)
+        tol = 2e-2 if dt == "bf16" else 1e-5
+        assert _rel(h13[:, :f], h1) <= tol and _rel(h13[:, f:], h3) <= tol, dt
+        a1 = b.act[:A].float().cpu().numpy()
+        a2 = act2[:A].float().cpu().numpy()
+        assert _rel(a1, a2) <= (1e-2 if dt == "bf16" else 1e-6), dt
+        ref = O.moe_forward(hv, inp.values("w_router"), parity.ExpertView(inp, "w1"),
+                            parity.ExpertView(inp, "w3"), parity.ExpertView(inp, "w2"), inp.k)
+        assert _rel(g["y"], ref["y"]) <= parity.Y_TOL[dt], dt
+
+
 @pytest.mark.parametrize("key", ["mixtral", "skewed_zipf"])
 def test_backward_workload_full_size(moe, key):
-    """Full-size workload in the launch configuration the benchmark times: routing
-    exact for every token; dhidden on sampled tokens and dW1/dW3 columns and dW2 rows
-    of sampled experts from the oracle entry by entry; dW_router and dbias in full
-    against the oracle's (every token's logit gradient: one oracle forward of the
-    experts), and by the softmax shift invariance (each row of dW_router sums to 0)."""
+    """Full-size workload in the launch configuration the benchmark times, with h1 / h3
+    recomputed and with them saved by the forward: routing exact for every token;
+    dhidden on sampled tokens and dW1/dW3 columns and dW2 rows of sampled experts from
+    the oracle entry by entry; dW_router and dbias in full against the oracle's (every
+    token's logit gradient: one oracle forward of the experts), and by the softmax shift
+    invariance (each row of dW_router sums to 0)."""
     import oracle.moe_oracle as O
     from tests import parity
     inp = synth.make_workload_inputs(key, seed=0)
     coef = 0.01
-    parity.log(f"backward_{key}: forward + backward on the GPU")
     dev = parity.to_device(inp)
-    g, b = parity.run_gpu(inp, dev)
     dy = synth.make_dy(inp.T, inp.d, inp.dtype, seed=11)
-    gr = moe.moe_backward(dev["hidden"], dev["w_router"], dev["w1"], dev["w3"], dev["w2"],
-                          _dev(dy, inp.dtype), b, coef, want_dbias=inp.bias is not None)
-    torch.cuda.synchronize()
     T, N, f = inp.T, inp.N, inp.f
     toks = [0, 1, T // 2 + 1, T - 1]
-    rows = np.diff(g["offsets"])
-    busiest, idlest = int(rows.argmax()), int(rows.argmin())
-    ec = [(busiest, [0, 1, f // 2 + 3, f - 1]), (idlest, [5, f - 2])]
-    parity.log(f"backward_{key}: oracle on tokens {toks}, experts/columns {ec}, "
-               f"rows per expert {rows.min()}..{rows.max()}")
+    got = {}
+    for mode in ("recompute", "saved"):
+        parity.log(f"backward_{key}/{mode}: forward + backward on the GPU")
+        g, b = _forward(moe, inp, dev, "drop", mode == "saved")
+        gr = moe.moe_backward(dev["hidden"], dev["w_router"], dev["w1"], dev["w3"], dev["w2"],
+                              _dev(dy, inp.dtype), b, coef, want_dbias=inp.bias is not None)
+        torch.cuda.synchronize()
+        rows = np.diff(g["offsets"])
+        busiest, idlest = int(rows.argmax()), int(rows.argmin())
+        ec = [(busiest, [0, 1, f // 2 + 3, f - 1]), (idlest, [5, f - 2])]
+        got[mode] = {"g": g, "ec": ec, "dh": gr.dhidden[toks].cpu().numpy(),
+                     "dw": {(e, tuple(c)): (gr.dw1[e][:, c].cpu().numpy(),
+                                             gr.dw3[e][:, c].cpu().numpy(),
+                                             gr.dw2[e][c, :].cpu().numpy()) for e, c in ec},
+                     "dw_router": gr.dw_router.cpu().numpy().astype(np.float64),
+                     "dbias": gr.dbias.cpu().numpy().astype(np.float64)
+                     if inp.bias is not None else None}
+        del gr, b
+        torch.cuda.empty_cache()
+    ec = got["recompute"]["ec"]
+    assert ec == got["saved"]["ec"]
+    parity.log(f"backward_{key}: oracle on tokens {toks}, experts/columns {ec}")
     smp = O.moe_backward_sampled(inp.values("hidden"), inp.values("w_router"),
                                  parity.ExpertView(inp, "w1"), parity.ExpertView(inp, "w3"),
                                  parity.ExpertView(inp, "w2"), inp.k,
                                  synth.bf16_bits_to_f32(dy), inp.capacity_factor, inp.bias,
                                  aux_coef=coef, tokens=toks, expert_cols=ec, router=True)
-    assert np.array_equal(g["topk_idx"], smp["topk_idx"]), "routing differs"
-    assert np.array_equal(g["slot_row"], smp["slot_row"]), "dispatch differs"
     tol = GRAD_TOL[inp.dtype]
-    dh = gr.dhidden[toks].cpu().numpy()
     ref = np.stack([smp["dhidden"][t] for t in toks])
-    rep = {"dhidden": _rel(dh, ref)}
-    for e, cols in ec:
-        r1, r3, r2 = smp["dw"][(e, tuple(cols))]
-        rep[f"dw1[{e}]"] = _rel(gr.dw1[e][:, cols].cpu().numpy(), r1)
-        rep[f"dw3[{e}]"] = _rel(gr.dw3[e][:, cols].cpu().numpy(), r3)
-        rep[f"dw2[{e}]"] = _rel(gr.dw2[e][cols, :].cpu().numpy(), r2)
-    wr = gr.dw_router.cpu().numpy().astype(np.float64)
-    rep["dw_router"] = _rel(wr, smp["dw_router"])
-    if inp.bias is not None:
-        rep["dbias"] = _rel(gr.dbias.cpu().numpy(), smp["dbias"])
-    for name, rel in rep.items():
-        assert rel <= tol, f"backward_{key}: {name} max rel err {rel:.3e} > {tol}"
-    assert np.abs(wr).max() > 0
-    assert np.abs(wr.sum(1)).max() <= 1e-4 * np.abs(wr).max(), "dW_router rows do not sum to 0"
-    if inp.bias is not None:
-        db = gr.dbias.cpu().numpy().astype(np.float64)
-        assert abs(db.sum()) <= 1e-4 * np.abs(db).max()
-    parity.log(f"backward_{key}: rel errors {rep}")
+    for mode, r in got.items():
+        assert np.array_equal(r["g"]["topk_idx"], smp["topk_idx"]), "routing differs"
+        assert np.array_equal(r["g"]["slot_row"], smp["slot_row"]), "dispatch differs"
+        rep = {"dhidden": _rel(r["dh"], ref)}
+        for e, cols in ec:
+            r1, r3, r2 = smp["dw"][(e, tuple(cols))]
+            d1, d3, d2 = r["dw"][(e, tuple(cols))]
+            rep[f"dw1[{e}]"] = _rel(d1, r1)
+            rep[f"dw3[{e}]"] = _rel(d3, r3)
+            rep[f"dw2[{e}]"] = _rel(d2, r2)
+        wr = r["dw_router"]
+        rep["dw_router"] = _rel(wr, smp["dw_router"])
+        if inp.bias is not None:
+            rep["dbias"] = _rel(r["dbias"], smp["dbias"])
+        for name, rel in rep.items():
+            assert rel <= tol, f"backward_{key}/{mode}: {name} max rel err {rel:.3e} > {tol}"
+        assert np.abs(wr).max() > 0
+        assert np.abs(wr.sum(1)).max() <= 1e-4 * np.abs(wr).max(), "dW_router rows do not sum to 0"
+        if inp.bias is not None:
+            assert abs(r["dbias"].sum()) <= 1e-4 * np.abs(r["dbias"]).max()
+        parity.log(f"backward_{key}/{mode}: rel errors {rep}")

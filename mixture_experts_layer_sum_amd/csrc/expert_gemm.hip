@@ -115,11 +115,17 @@ __device__ __forceinline__ bool find_tile_balanced(const int32_t* __restrict__ o
 // tiles; when that round would leave at least half of the CUs idle, each of
 // its r tiles is cut into `segs` k-ranges run by separate blocks (segs <= 4,
 // each range at least two k-steps).  Returns the number of tiles computed
-// whole (the first n_dp logical tiles).
+// whole (the first n_dp logical tiles).  Only deep tiles are split: the few
+// CUs of an unsplit last round run at a much higher clock under the chip's
+// power limit, so for K = 5632 (88 k-steps, 48 tail tiles) the whole tiles
+// finished sooner (272 us) than four ranges each (331 us), while for
+// K = 14336 (224 k-steps, the same 48 tail tiles) the split won (1671 against
+// 1780 us).
 constexpr int kMaxSegs = 4;
+constexpr int kMinSplitSteps = 128;
 __device__ __forceinline__ int split_plan(int total, int nk, int num_cus, int& segs) {
   segs = 1;
-  if (num_cus <= 0) return total;
+  if (num_cus <= 0 || nk < kMinSplitSteps) return total;
   const int r = total % num_cus;
   if (r == 0 || 2 * r > num_cus) return total;
   int s = num_cus / r;
@@ -962,7 +968,10 @@ static void launch_rows(int mt, const void* x, const int32_t* offsets, int N, co
 }
 
 // ---------------------------------------------------------------- fp32 (VALU)
-constexpr int kFBM = 64, kFBN = 64, kFBK = 16;
+// 64-deep k chunks: each thread has 16 loads of A and 16 (+16) of the weights in
+// flight per chunk, so that a small layer (a few chunks per block) waits on memory
+// a few times rather than K / 16 times.  The k order of every sum is unchanged.
+constexpr int kFBM = 64, kFBN = 64, kFBK = 64;
 
 template <bool UP>
 __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
@@ -980,15 +989,23 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
   const size_t wexp = (size_t)e * K * Nout;
   float c1[4][4] = {}, c3[4][4] = {};
   for (int k0 = 0; k0 < K; k0 += kFBK) {
+    float va[16], vb1[16], vb3[16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int item = tid + 256 * i;           // 64 rows x 16 k
-      const int row = item >> 4, kk = item & 15;
+    for (int i = 0; i < 16; ++i) {
+      const int item = tid + 256 * i;           // 64 rows x 64 k
+      const int row = item >> 6, kk = item & 63;
       const int gr = r0 + row;
-      As[kk][row] = gr < rend ? X[(size_t)gr * K + k0 + kk] : 0.f;
-      const int kr = item >> 6, col = item & 63;  // 16 k x 64 cols
-      B1[kr][col] = Wa[wexp + (size_t)(k0 + kr) * Nout + n0 + col];
-      if (UP) B3[kr][col] = Wb[wexp + (size_t)(k0 + kr) * Nout + n0 + col];
+      va[i] = gr < rend ? X[(size_t)gr * K + k0 + kk] : 0.f;
+      const int kr = item >> 6, col = item & 63;  // 64 k x 64 cols
+      vb1[i] = Wa[wexp + (size_t)(k0 + kr) * Nout + n0 + col];
+      vb3[i] = UP ? Wb[wexp + (size_t)(k0 + kr) * Nout + n0 + col] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int item = tid + 256 * i;
+      As[item & 63][item >> 6] = va[i];
+      B1[item >> 6][item & 63] = vb1[i];
+      if (UP) B3[item >> 6][item & 63] = vb3[i];
     }
     __syncthreads();
 #pragma unroll

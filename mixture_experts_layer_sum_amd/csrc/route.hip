@@ -523,8 +523,16 @@ __global__ __launch_bounds__(kRtThreads) void router_f32_kernel(
     const int t = t0 + r;
     float s = 0.f;
     if (t < T) {
+      // four independent partial sums over q mod 4 (d is a multiple of 64), so that
+      // the loads of an unrolled stretch are in flight together instead of one
+      // dependent multiply-add at a time (47 -> 36 us for 64 tokens, d 128, 8 experts)
       const float* h = hidden + (size_t)t * d;
-      for (int q = 0; q < d; ++q) s = fmaf(h[q], wr[(size_t)q * N + e], s);
+      float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int q = 0; q < d; q += 4)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) s4[u] = fmaf(h[q + u], wr[(size_t)(q + u) * N + e], s4[u]);
+      s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
       s += bias ? bias[e] : 0.f;
       logits[(size_t)t * N + e] = s;
     }

@@ -323,6 +323,72 @@ __global__ __launch_bounds__(64 * WAVES) void router_bf16_kernel(
 constexpr int kRtBigT = 2048;
 constexpr int kRtBigWaves = 8;
 
+// Top-k + softmax + histogram of ROWS tokens by the block's 512 threads, LPT =
+// 512 / ROWS lanes per token (a power of two, inside one wave): lane s of a
+// token holds the logits of experts s, s + LPT, ... (NW / LPT of them, NW = the
+// padded expert count), and k rounds each take the best untaken expert, larger
+// logit first and lower id among equal ones, by a butterfly over the token's
+// lanes.  The token's first lane writes the k picks and their softmax weights.
+template <int ROWS, int NW>
+__device__ __forceinline__ void topk_lanes(const float* red, int ld, int t0, int nt, int N, int k,
+                                           int32_t* __restrict__ topk_idx,
+                                           float* __restrict__ topk_w, int* hist) {
+  constexpr int LPT = 64 * kRtBigWaves / ROWS;
+  constexpr int VPL = NW / LPT > 0 ? NW / LPT : 1;
+  const int tid = threadIdx.x;
+  const int r = tid / LPT, sl = tid % LPT;
+  const bool live = r < nt;
+  float v[VPL];
+  unsigned taken = 0;
+#pragma unroll
+  for (int c = 0; c < VPL; ++c) {
+    const int e = sl + LPT * c;
+    v[c] = (live && e < N) ? red[r * ld + e] : 0.f;
+    if (e >= N) taken |= 1u << c;
+  }
+  float sv[kTopkThread];
+  int si[kTopkThread];
+#pragma unroll
+  for (int jj = 0; jj < kTopkThread; ++jj) {
+    if (jj >= k) break;
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int c = 0; c < VPL; ++c) {
+      if (!(taken & (1u << c)) && (be == 0x7fffffff || v[c] > bv)) {
+        bv = v[c];
+        be = sl + LPT * c;
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < LPT; m <<= 1) {
+      const float ov = __shfl_xor(bv, m, 64);
+      const int oe = __shfl_xor(be, m, 64);
+      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+    }
+    if (be % LPT == sl) taken |= 1u << (be / LPT);
+    sv[jj] = bv;
+    si[jj] = be;
+  }
+  if (live && sl == 0) {
+    const float vmax = sv[0];
+    float s = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < kTopkThread; ++jj)
+      if (jj < k) s += __expf(sv[jj] - vmax);
+    const float inv = 1.f / s;
+    const int t = t0 + r;
+#pragma unroll
+    for (int jj = 0; jj < kTopkThread; ++jj) {
+      if (jj < k) {
+        topk_idx[(size_t)t * k + jj] = si[jj];
+        topk_w[(size_t)t * k + jj] = __expf(sv[jj] - vmax) * inv;
+        atomicAdd(&hist[si[jj]], 1);
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void router_prep_kernel(const uint16_t* __restrict__ wr, int d,
                                                           int N, int N16, uint16_t* __restrict__ wt,
                                                           int32_t* __restrict__ counts) {
@@ -347,7 +413,10 @@ void router_wt_kernel(
   // The 64-token, 64-expert tile takes two steps per batch (128 registers; 60 ->
   // 56 us at 16384 tokens, d 4096) since its accumulators leave room for them.
   constexpr int KB = (MT == 4 && NT == 4) ? 2 : ((48 / (4 * (MT + NT))) < 1 ? 1 : (48 / (4 * (MT + NT))));
-  __shared__ float red[ROWS][LD];
+  // per-wave partial tiles while they fit in LDS (64 tokens x 64 experts, 32 x 128,
+  // 16 x 256); wider tiles add the waves' partials into one tile a wave at a time
+  constexpr bool kPerWave = MT * NT <= 16;
+  __shared__ float red[kPerWave ? kRtBigWaves : 1][ROWS][LD];
   __shared__ int hist[256];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -404,35 +473,52 @@ void router_wt_kernel(
   }
 #undef MOE_RT_LOAD
 #undef MOE_RT_MMA
-  // acc[m][et][r]: expert 16 et + 4g + r, token 16 m + j.  The waves add their
-  // partial logits into one LDS tile in wave order (fixed order).
-  for (int ww = 0; ww < kRtBigWaves; ++ww) {
-    if (w == ww) {
+  // acc[m][et][r]: expert 16 et + 4g + r, token 16 m + j.  Each wave writes its
+  // partial logits to a tile of its own; one pass then adds the eight tiles in
+  // wave order (a fixed order, the same sum as adding them one wave at a time).
+  if (kPerWave) {
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int et = 0; et < NT; ++et)
+      for (int et = 0; et < NT; ++et)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float& dst = red[16 * m + j][16 * et + 4 * g + r];
-            dst = ww == 0 ? acc[m][et][r] : dst + acc[m][et][r];
-          }
-    }
+        for (int r = 0; r < 4; ++r)
+          red[kPerWave ? w : 0][16 * m + j][16 * et + 4 * g + r] = acc[m][et][r];
     __syncthreads();
+  } else {
+    for (int ww = 0; ww < kRtBigWaves; ++ww) {
+      if (w == ww) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int et = 0; et < NT; ++et)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              float& dst = red[0][16 * m + j][16 * et + 4 * g + r];
+              dst = ww == 0 ? acc[m][et][r] : dst + acc[m][et][r];
+            }
+      }
+      __syncthreads();
+    }
   }
   const int nt = min(ROWS, T - t0);
   for (int i = tid; i < ROWS * N; i += 64 * kRtBigWaves) {
     const int r = i / N, e = i - r * N;
-    const float v = red[r][e] + ((bias != nullptr) ? bias[e] : 0.f);
-    red[r][e] = v;
+    float v = red[0][r][e];
+    if (kPerWave) {
+#pragma unroll
+      for (int ww = 1; ww < kRtBigWaves; ++ww) v += red[kPerWave ? ww : 0][r][e];
+    }
+    v += (bias != nullptr) ? bias[e] : 0.f;
+    red[0][r][e] = v;
     if (r < nt) logits[(size_t)(t0 + r) * N + e] = v;
   }
   __syncthreads();
   if (k <= kTopkThread) {
-    if (tid < nt) topk_thread(&red[tid][0], t0 + tid, N, k, topk_idx, topk_w, hist);
+    topk_lanes<ROWS, 16 * NT>(&red[0][0][0], LD, t0, nt, N, k, topk_idx, topk_w, hist);
   } else {
     for (int r = w; r < nt; r += kRtBigWaves)
-      topk_row(&red[r][0], t0 + r, N, k, topk_idx, topk_w, hist);
+      topk_row(&red[0][r][0], t0 + r, N, k, topk_idx, topk_w, hist);
   }
   __syncthreads();
   for (int e = tid; e < N; e += 64 * kRtBigWaves)

@@ -110,6 +110,110 @@ __device__ __forceinline__ bool find_tile_balanced(const int32_t* __restrict__ o
   return true;
 }
 
+// Heaviest-first order of the balanced row tiles.  A balanced tile holds 1..4
+// units of 64 rows (an expert with R rows has n = ceil(R / 256) tiles and
+// u = ceil(R / 64) units: its first u % n tiles hold floor(u / n) + 1 units,
+// the rest floor(u / n)).  When the grid is short and the tiles differ,
+// dispatching them in order of units (4 first; ties by expert, then tile)
+// lets the CUs that finish a lighter tile early take the next light one
+// instead of the grid ending on a round of heavy tiles, and dealing tile b to
+// XCD b % 8 spreads the heavy tiles evenly over the XCDs (the grouped order
+// hands whole groups of row tiles to one XCD).  Measured: skewed routing with
+// re-routing (36 experts, 992 tiles) up 461 -> 437 us, down 244 -> 239 us;
+// 16 experts with K = 5632 (304 down tiles) 277 -> 267 us.  A light tile
+// costs nearly as much as a full one (its two-stage load pipeline waits on
+// memory latency either way), so 16 skewed experts with 416 tiles gain nothing.
+//
+// lpt_classes: the number of row tiles of each weight w = 1..4 (cls[w - 1]).
+__device__ __forceinline__ void lpt_classes(const int32_t* __restrict__ offsets, int N,
+                                            int max_rows, int (&cls)[4]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) cls[w] = 0;
+  for (int b = 0; b < N; b += 64) {
+    const int e = b + lane;
+    int c[4] = {0, 0, 0, 0};
+    if (e < N) {
+      const int o0 = min(max(offsets[e], 0), max_rows);
+      const int o1 = min(max(offsets[e + 1], o0), max_rows);
+      const int R = o1 - o0;
+      if (R > 0) {
+        const int n = (R + kBM - 1) / kBM, u = (R + 63) / 64;
+        const int q = u / n, rem = u - q * n;
+#pragma unroll
+        for (int w = 1; w <= 4; ++w) c[w - 1] = (q + 1 == w ? rem : 0) + (q == w ? n - rem : 0);
+      }
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      int v = c[w];
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+      cls[w] += v;
+    }
+  }
+}
+
+// Row tile number s of the heaviest-first order (cls from lpt_classes): its
+// expert and rows [r0, rend), the same rows find_tile_balanced gives that tile.
+__device__ __forceinline__ bool find_tile_lpt(const int32_t* __restrict__ offsets, int N, int s,
+                                              int max_rows, const int (&cls)[4], int& e_out,
+                                              int& r0, int& rend) {
+  int w = 4;
+  while (w > 0 && s >= cls[w - 1]) {
+    s -= cls[w - 1];
+    --w;
+  }
+  if (w == 0) return false;
+  const int lane = threadIdx.x & 63;
+  int before = 0;
+  for (int b = 0; b < N; b += 64) {
+    const int e = b + lane;
+    int o0 = 0, o1 = 0, q = 0, rem = 0, cnt = 0;
+    if (e < N) {
+      o0 = min(max(offsets[e], 0), max_rows);
+      o1 = min(max(offsets[e + 1], o0), max_rows);
+      const int R = o1 - o0;
+      if (R > 0) {
+        const int n = (R + kBM - 1) / kBM, u = (R + 63) / 64;
+        q = u / n;
+        rem = u - q * n;
+        cnt = (q + 1 == w ? rem : 0) + (q == w ? n - rem : 0);
+      }
+    }
+    int inc = cnt;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const int v = __shfl_up(inc, m, 64);
+      if (lane >= m) inc += v;
+    }
+    const int tot = __shfl(inc, 63, 64);
+    if (s < before + tot) {
+      const unsigned long long bal = __ballot(before + inc > s);
+      const int L = __ffsll(static_cast<long long>(bal)) - 1;
+      const int idx = s - before - __shfl(inc - cnt, L, 64);
+      const int qL = __shfl(q, L, 64), remL = __shfl(rem, L, 64), oL = __shfl(o0, L, 64);
+      const int j = (w == qL + 1 ? 0 : remL) + idx;          // tile within the expert
+      const int start = 64 * (j * qL + min(j, remL));
+      e_out = b + L;
+      r0 = oL + start;
+      rend = min(oL + start + 64 * (qL + (j < remL ? 1 : 0)), __shfl(o1, L, 64));
+      return true;
+    }
+    before += tot;
+  }
+  return false;
+}
+
+// Heaviest-first dispatch is used when some row tile is light and the grid
+// is at most this many rounds of the CUs; longer grids keep the grouped,
+// XCD-contiguous order, whose L2 reuse matters more than the last round
+// (16 experts, K = 2048, 1672 tiles: 390 us grouped, 404 us heaviest-first).
+#ifndef MOE_LPT_ROUNDS
+#define MOE_LPT_ROUNDS 4
+#endif
+constexpr int kLptRounds = MOE_LPT_ROUNDS;
+
 // Split of the last, partial round of tiles over k.  With `total` tiles on
 // `num_cus` CUs (one block each) the last round holds r = total % num_cus
 // tiles; when that round would leave at least half of the CUs idle, each of
@@ -339,15 +443,25 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
   __shared__ int s_last;
 
   const int nk = K / kBK;
-  const int m_tiles = count_tiles(offsets, N, kBM, max_rows);
+  int cls[4];
+  lpt_classes(offsets, N, max_rows, cls);
+  const int m_tiles = cls[0] + cls[1] + cls[2] + cls[3];
   const int total = m_tiles * n_tiles;
-  int segs;
-  const int n_dp = split_plan(total, nk, num_cus, segs);
+  // heaviest-first: block b computes tile b (row tile b / n_tiles of that
+  // order, column tile b % n_tiles), so XCD b % 8 gets every eighth tile
+  const bool lpt = num_cus > 0 && cls[3] != m_tiles && total <= kLptRounds * num_cus;
+  int segs = 1;
+  const int n_dp = (UP || lpt || !tickets) ? total : split_plan(total, nk, num_cus, segs);
   // blocks [0, dp_grid) compute whole tiles; the rest compute k-ranges of the
   // last n_sk tiles (block j: tile n_dp + j / segs, range j % segs)
   int logical, kb = 0, kl = nk, slot = -1;
   if ((int)blockIdx.x < dp_grid) {
-    if (!dp_logical(n_dp, logical)) return;
+    if (lpt) {
+      logical = blockIdx.x;
+      if (logical >= total) return;
+    } else if (!dp_logical(n_dp, logical)) {
+      return;
+    }
   } else {
     const int j = blockIdx.x - dp_grid;
     if (j >= (total - n_dp) * segs) return;
@@ -360,10 +474,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
   kb = __builtin_amdgcn_readfirstlane(kb);
   kl = __builtin_amdgcn_readfirstlane(kl);
   slot = __builtin_amdgcn_readfirstlane(slot);
-  int mt, nt;
-  tile_of_logical(logical, m_tiles, n_tiles, mt, nt);
-  int e, r0, rend;
-  if (!find_tile_balanced(offsets, N, mt, max_rows, e, r0, rend)) return;
+  int mt, nt, e, r0, rend;
+  if (lpt) {
+    mt = logical / n_tiles;
+    nt = logical - mt * n_tiles;
+    if (!find_tile_lpt(offsets, N, mt, max_rows, cls, e, r0, rend)) return;
+  } else {
+    tile_of_logical(logical, m_tiles, n_tiles, mt, nt);
+    if (!find_tile_balanced(offsets, N, mt, max_rows, e, r0, rend)) return;
+  }
   e = __builtin_amdgcn_readfirstlane(e);
   r0 = __builtin_amdgcn_readfirstlane(r0);
   rend = __builtin_amdgcn_readfirstlane(rend);
@@ -1094,7 +1213,8 @@ hipError_t launch_expert_up(const void* x_perm, const int32_t* offsets, const vo
                        static_cast<const uint16_t*>(x_perm), offsets, N,
                        static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w3), d, f,
                        n_tiles, max_rows, act, static_cast<float*>(nullptr),
-                       static_cast<int32_t*>(nullptr), 0, grid, static_cast<uint16_t*>(h13));
+                       static_cast<int32_t*>(nullptr), device_cus(), grid,
+                       static_cast<uint16_t*>(h13));
   } else {
     const int n_tiles = f / kFBN;
     const int mt_bound = (max_rows + kFBM - 1) / kFBM + N;
@@ -1116,11 +1236,11 @@ hipError_t launch_expert_down(const void* act, const int32_t* offsets, const voi
     const int n_tiles = d / kBN;
     const int mt_bound = (max_rows + kBM - 1) / kBM + N;
     const int dp_grid = round8(mt_bound * n_tiles);
-    const int cus = ws ? device_cus() : 0;
-    float* part = static_cast<float*>(ws);
+    const int cus = device_cus();
+    float* part = cus > 0 ? static_cast<float*>(ws) : nullptr;
     int32_t* tickets = nullptr;
     int grid = dp_grid;
-    if (cus > 0) {
+    if (part) {
       tickets = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + partial_bytes(cus));
       hipLaunchKernelGGL(zero_tickets_kernel, dim3((cus + 255) / 256), dim3(256), 0, stream,
                          tickets, cus);

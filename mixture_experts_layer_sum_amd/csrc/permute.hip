@@ -132,34 +132,42 @@ __global__ __launch_bounds__(kChunk) void place_kernel(const int32_t* __restrict
     }
 }
 
-// All of the above in one block when every token fits in one chunk (T <= 256,
-// decode-sized batches): histogram, capacity, exclusive scan and places.
+// All of the above, and the copy of the rows, in one launch when every token
+// fits in one chunk (T <= 256, decode-sized batches).  Block t (one per token)
+// builds the whole chunk's histogram, capacity cut, exclusive scan and
+// per-expert masks in LDS (the same values in every block: the inputs are a
+// few KB and the work is integer and order-free), then places its own token's
+// slots and copies its hidden row into them; block 0 also writes kept and
+// offsets.  One launch instead of a dispatch block followed by a copy grid.
 __global__ __launch_bounds__(kChunk) void permute_one_chunk_kernel(
     const int32_t* __restrict__ topk_idx, int T, int N, int k, int C, int32_t* __restrict__ kept,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ slot_row, int32_t* __restrict__ perm_src) {
+    int32_t* __restrict__ offsets, int32_t* __restrict__ slot_row, int32_t* __restrict__ perm_src,
+    const uint4* __restrict__ hidden, int vec_per_row, uint4* __restrict__ x_perm) {
   __shared__ unsigned long long mask[256][4];
   __shared__ int h[256];
   __shared__ int sk[256];
   __shared__ int off[256];
+  __shared__ int srow[256];
   const int tid = threadIdx.x;
   mask[tid][0] = mask[tid][1] = mask[tid][2] = mask[tid][3] = 0ull;
   h[tid] = 0;
   __syncthreads();
-  const int t = tid;
-  const int word = tid >> 6;
-  const unsigned long long bit = 1ull << (tid & 63);
-  if (t < T)
-    for (int j = 0; j < k; ++j) {
-      const int e = topk_idx[(size_t)t * k + j];
-      if (e >= 0 && e < N) {
-        atomicAdd(&h[e], 1);
-        atomicOr(&mask[e][word], bit);
+  {
+    const int t = tid;
+    const int word = t >> 6;
+    const unsigned long long bit = 1ull << (t & 63);
+    if (t < T)
+      for (int j = 0; j < k; ++j) {
+        const int e = topk_idx[(size_t)t * k + j];
+        if (e >= 0 && e < N) {
+          atomicAdd(&h[e], 1);
+          atomicOr(&mask[e][word], bit);
+        }
       }
-    }
+  }
   __syncthreads();
   const int e = tid;
   const int kp = (e < N) ? (h[e] < C ? h[e] : C) : 0;
-  if (e < N) kept[e] = kp;
   sk[e] = kp;
   __syncthreads();
   for (int s = 1; s < 256; s <<= 1) {     // inclusive Hillis-Steele scan
@@ -169,24 +177,46 @@ __global__ __launch_bounds__(kChunk) void permute_one_chunk_kernel(
     __syncthreads();
   }
   off[e] = sk[e] - kp;
-  if (e < N) offsets[e] = sk[e] - kp;
-  if (e == N - 1) offsets[N] = sk[e];
-  __syncthreads();
-  if (t < T)
-    for (int j = 0; j < k; ++j) {
-      const int ex = topk_idx[(size_t)t * k + j];
-      int row = -1;
-      if (ex >= 0 && ex < N) {
-        int place = 0;
-        for (int q = 0; q < word; ++q) place += __popcll(mask[ex][q]);
-        place += __popcll(mask[ex][word] & (bit - 1ull));
-        if (place < C) {
-          row = off[ex] + place;
-          perm_src[row] = t;
-        }
-      }
-      slot_row[(size_t)t * k + j] = row;
+  if (blockIdx.x == 0) {
+    if (e < N) {
+      kept[e] = kp;
+      offsets[e] = sk[e] - kp;
     }
+    if (e == N - 1) offsets[N] = sk[e];
+  }
+  __syncthreads();
+  // this block's token: its slots' rows
+  const int t = blockIdx.x;
+  const int word = t >> 6;
+  const unsigned long long bit = 1ull << (t & 63);
+  for (int j = tid; j < k; j += kChunk) {
+    const int ex = topk_idx[(size_t)t * k + j];
+    int row = -1;
+    if (ex >= 0 && ex < N) {
+      int place = 0;
+      for (int q = 0; q < word; ++q) place += __popcll(mask[ex][q]);
+      place += __popcll(mask[ex][word] & (bit - 1ull));
+      if (place < C) {
+        row = off[ex] + place;
+        perm_src[row] = t;
+      }
+    }
+    slot_row[(size_t)t * k + j] = row;
+    if (j < 256) srow[j] = row;
+  }
+  __syncthreads();
+  const int kk = k < 256 ? k : 256;
+  bool kept_any = false;
+  for (int j = 0; j < kk; ++j) kept_any |= srow[j] >= 0;
+  if (!kept_any) return;
+  const uint4* src = hidden + (size_t)t * vec_per_row;
+  for (int v = tid; v < vec_per_row; v += kChunk) {
+    const uint4 x = src[v];
+    for (int j = 0; j < kk; ++j) {
+      const int r = srow[j];
+      if (r >= 0) x_perm[(size_t)r * vec_per_row + v] = x;
+    }
+  }
 }
 
 // Copy hidden[t] into each of its kept rows of x_perm.  One block per token,
@@ -441,9 +471,13 @@ hipError_t launch_permute(const void* hidden, const int32_t* topk_idx, int T, in
                           int32_t* slot_row, int32_t* kept, int32_t* offsets, void* ws,
                           hipStream_t stream) {
   const int nch = (T + kChunk - 1) / kChunk;
+  const int vpr = (d * elem_bytes) / 16;
   if (nch == 1) {
-    hipLaunchKernelGGL(permute_one_chunk_kernel, dim3(1), dim3(kChunk), 0, stream, topk_idx, T, N,
-                       k, C, kept, offsets, slot_row, perm_src);
+    if (T == 0) return hipGetLastError();
+    hipLaunchKernelGGL(permute_one_chunk_kernel, dim3(T), dim3(kChunk), 0, stream, topk_idx, T, N,
+                       k, C, kept, offsets, slot_row, perm_src, static_cast<const uint4*>(hidden),
+                       vpr, static_cast<uint4*>(x_perm));
+    return hipGetLastError();
   } else {
     int32_t* hist = static_cast<int32_t*>(ws);
     int32_t* base = hist + static_cast<size_t>(nch) * N;
@@ -454,7 +488,6 @@ hipError_t launch_permute(const void* hidden, const int32_t* topk_idx, int T, in
     hipLaunchKernelGGL(place_kernel, dim3(nch), dim3(kChunk), 0, stream, topk_idx, T, N, k, C,
                        base, offsets, slot_row, perm_src);
   }
-  const int vpr = (d * elem_bytes) / 16;
   hipLaunchKernelGGL(gather_rows_kernel, dim3(T), dim3(256), 0, stream,
                      static_cast<const uint4*>(hidden), slot_row, k, vpr,
                      static_cast<uint4*>(x_perm));

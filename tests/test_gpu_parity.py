@@ -61,10 +61,14 @@ SMALL = [
     # three column slices) and the 128-column kernel (f % 256 == 128)
     ("bf16_rows32_up_f768", 150, 256, 16, 2, 768, "bf16", 0.0, None),
     ("bf16_rows32_up_f384", 150, 256, 16, 2, 384, "bf16", 0.0, None),
-    # ~130 row tiles x 2 column tiles: on a 256-CU device the down projection's
-    # last round (4 tiles) is split over k into 4 ranges each (f = 8192: only tiles
-    # of at least 128 k-steps are split)
-    ("bf16_down_ksplit4", 16500, 512, 2, 2, 8192, "bf16", 0.0, None),
+    # 132 full row tiles x 2 column tiles = 264 tiles: on a 256-CU device the down
+    # projection's last round (8 tiles) is split over k into 4 ranges each (f = 8192:
+    # only tiles of at least 128 k-steps are split; every tile holds 256 rows, so the
+    # grouped tile order applies rather than the heaviest-first one)
+    ("bf16_down_ksplit4", 16896, 512, 2, 2, 8192, "bf16", 0.0, None),
+    # short grids of unequal tiles run heaviest first: 7 experts of ~1400, ~1000,
+    # ~300 and 47..71 rows (row tiles of 4, 3, 2 and 1 units of 64 rows)
+    ("bf16_heaviest_first_mix", 1500, 256, 7, 2, 512, "bf16", 0.0, "skew"),
     # the large-batch router (>= 2048 tokens): 256 experts (16 expert tiles), 40 experts
     # (tiles padded to 4) with k = 3 and a capacity cut, and one token below the threshold
     ("bf16_router_wt_N256", 2048, 256, 256, 2, 128, "bf16", 0.0, None),

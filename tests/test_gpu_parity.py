@@ -320,17 +320,25 @@ def _fp8_layer(moe, inp, label, sample=None):
     return rel
 
 
-@pytest.mark.parametrize("shape", [(37, 256, 16, 2, 256), (200, 512, 32, 2, 384), (1, 256, 8, 2, 128)])
+@pytest.mark.parametrize("shape", [
+    (37, 256, 16, 2, 256, None), (200, 512, 32, 2, 384, None), (1, 256, 8, 2, 128, None),
+    (37, 512, 16, 2, 512, None), (1, 512, 8, 2, 512, None),
+    # skewed routing: experts 0..2 take several 32-row tiles each
+    (60, 1024, 16, 2, 1024, "skew")])
 def test_fp8_layer_small(moe, shape):
-    T, d, N, k, f = shape
+    T, d, N, k, f, bias = shape
+    b = None
+    if bias == "skew":
+        b = np.zeros(N, np.float32)
+        b[:3] = [3.0, 2.0, 1.0]
     for seed in (0, 1):
-        inp = synth.make_inputs(T, d, N, k, f, "bf16", 0.0, seed)
+        inp = synth.make_inputs(T, d, N, k, f, "bf16", 0.0, seed, bias=b)
         _fp8_layer(moe, inp, f"fp8_T{T}_d{d}_N{N}_f{f}/seed{seed}")
 
 
 def test_fp8_decode_workload_full_size(moe):
     inp = synth.make_workload_inputs("decode", seed=0)
-    _fp8_layer(moe, inp, "fp8_decode_T256", sample=np.array([0, 97, 180, 255]))
+    _fp8_layer(moe, inp, "fp8_decode_T256", sample=np.arange(0, 256, 8))
 
 
 WORKLOADS = ["tiny_fp32", "n16_cf125", "mixtral", "skewed_zipf", "decode"]

@@ -1237,7 +1237,11 @@ hipError_t launch_expert_down(const void* act, const int32_t* offsets, const voi
     const int mt_bound = (max_rows + kBM - 1) / kBM + N;
     const int dp_grid = round8(mt_bound * n_tiles);
     const int cus = device_cus();
-    float* part = cus > 0 ? static_cast<float*>(ws) : nullptr;
+    // the last round is split over k only for tiles of at least kMinSplitSteps
+    // k-steps: for shallower ones the tickets are never used, so they are not
+    // cleared and no range blocks are launched
+    const bool may_split = f / kBK >= kMinSplitSteps;
+    float* part = (cus > 0 && may_split) ? static_cast<float*>(ws) : nullptr;
     int32_t* tickets = nullptr;
     int grid = dp_grid;
     if (part) {

@@ -418,11 +418,15 @@ void router_wt_kernel(
   constexpr bool kPerWave = MT * NT <= 16;
   __shared__ float red[kPerWave ? kRtBigWaves : 1][ROWS][LD];
   __shared__ int hist[256];
+  __shared__ float sbias[256];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 15, g = lane >> 4;
   const int t0 = blockIdx.x * ROWS;
   for (int i = tid; i < 256; i += 64 * kRtBigWaves) hist[i] = 0;
+  // the bias is read here, under the k-loop, rather than once per logit in the
+  // epilogue (where each read would wait out a memory latency of its own)
+  for (int i = tid; i < N; i += 64 * kRtBigWaves) sbias[i] = (bias != nullptr) ? bias[i] : 0.f;
 
   const int nks = d / 32;
   const int ks0 = w * nks / kRtBigWaves, ks1 = (w + 1) * nks / kRtBigWaves;
@@ -509,7 +513,7 @@ void router_wt_kernel(
 #pragma unroll
       for (int ww = 1; ww < kRtBigWaves; ++ww) v += red[kPerWave ? ww : 0][r][e];
     }
-    v += (bias != nullptr) ? bias[e] : 0.f;
+    v += sbias[e];
     red[0][r][e] = v;
     if (r < nt) logits[(size_t)(t0 + r) * N + e] = v;
   }

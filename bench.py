@@ -193,7 +193,7 @@ def time_backward(inp, dev, steps, warmup, coef=0.01, saved=True):
         if saved:
             moe.moe_expert_backward_saved(b.x_perm, gb.g_perm, b.h13, b.offsets, dev["w1"],
                                           dev["w3"], dev["w2"], gb.dx_perm, gb.dw1, gb.dw3,
-                                          gb.dw2, gb.ws_expert)
+                                          gb.dw2, gb.ws_expert, act=b.act)
         else:
             moe.moe_expert_backward(b.x_perm, gb.g_perm, b.offsets, dev["w1"], dev["w3"],
                                     dev["w2"], gb.dx_perm, gb.dw1, gb.dw3, gb.dw2, gb.ws_expert)

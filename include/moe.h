@@ -362,18 +362,24 @@ moe_status moe_expert_backward(const void* x_perm, const void* g_perm, const int
  * moe_expert_backward_saved -- moe_expert_backward with h1 and h3 taken from
  * the h13 [max_rows, 2f] that moe_expert_up_save stored in the forward
  * (dtype dt) instead of recomputed from x_perm: the SwiGLU backward (dh1,
- * dh3, a) runs in the epilogue of the da GEMM, so the backward does three
- * grouped GEMM passes' worth of work less (12 A d f flops instead of 16).
+ * dh3) runs in the epilogue of the da GEMM, so the backward does 12 A d f
+ * flops instead of 16 (no recompute GEMM).
+ *   act  NULL, or the forward's activations [max_rows, f] (dtype dt; the
+ *        `act` moe_expert_up_save wrote): dW2 = act^T g then uses the very
+ *        values the forward multiplied by W2, and the epilogue neither
+ *        recomputes nor writes a.  With NULL, a = silu(h1) h3 is recomputed
+ *        from h13 into the workspace.
  * Arguments, outputs and limits otherwise as moe_expert_backward.
  *   ws  moe_workspace_size(MOE_OP_EXPERT_BACKWARD_SAVED, T, d, N, k, f, dt)
  *       bytes, T*k = max_rows: [dh1 | dh3] [max_rows, 2f] and a [max_rows, f]
  *       in dtype dt, each padded to 256 bytes.
  */
 moe_status moe_expert_backward_saved(const void* x_perm, const void* g_perm, const void* h13,
-                                     const int32_t* offsets, const void* w1, const void* w3,
-                                     const void* w2, int N, int d, int f, int max_rows,
-                                     moe_dtype dt, float* dx_perm, float* dw1, float* dw3,
-                                     float* dw2, void* ws, size_t ws_bytes, void* stream);
+                                     const void* act, const int32_t* offsets, const void* w1,
+                                     const void* w3, const void* w2, int N, int d, int f,
+                                     int max_rows, moe_dtype dt, float* dx_perm, float* dw1,
+                                     float* dw3, float* dw2, void* ws, size_t ws_bytes,
+                                     void* stream);
 
 /*
  * moe_router_backward -- through the softmax over the k selected logits, the

@@ -336,10 +336,11 @@ moe_status moe_expert_backward(const void* x_perm, const void* g_perm, const int
 }
 
 moe_status moe_expert_backward_saved(const void* x_perm, const void* g_perm, const void* h13,
-                                     const int32_t* offsets, const void* w1, const void* w3,
-                                     const void* w2, int N, int d, int f, int max_rows,
-                                     moe_dtype dt, float* dx_perm, float* dw1, float* dw3,
-                                     float* dw2, void* ws, size_t ws_bytes, void* stream) {
+                                     const void* act, const int32_t* offsets, const void* w1,
+                                     const void* w3, const void* w2, int N, int d, int f,
+                                     int max_rows, moe_dtype dt, float* dx_perm, float* dw1,
+                                     float* dw3, float* dw2, void* ws, size_t ws_bytes,
+                                     void* stream) {
   if (!x_perm || !g_perm || !h13 || !offsets || !w1 || !w3 || !w2 || !dx_perm || !dw1 || !dw3 ||
       !dw2)
     return MOE_ERR_INVALID_ARG;
@@ -352,9 +353,10 @@ moe_status moe_expert_backward_saved(const void* x_perm, const void* g_perm, con
   const size_t need = moe::expert_backward_saved_ws_bytes(d, f, max_rows, dt == MOE_BF16);
   if (ws_bytes < need) return MOE_ERR_WORKSPACE;
   if (!ws) return MOE_ERR_INVALID_ARG;
-  return hip_status(moe::launch_expert_backward_saved(x_perm, g_perm, h13, offsets, w1, w3, w2, N,
-                                                      d, f, max_rows, dt == MOE_BF16, dx_perm,
-                                                      dw1, dw3, dw2, ws, as_stream(stream)));
+  return hip_status(moe::launch_expert_backward_saved(x_perm, g_perm, h13, act, offsets, w1, w3,
+                                                      w2, N, d, f, max_rows, dt == MOE_BF16,
+                                                      dx_perm, dw1, dw3, dw2, ws,
+                                                      as_stream(stream)));
 }
 
 moe_status moe_router_backward(const void* hidden, const void* w_router, const float* logits,

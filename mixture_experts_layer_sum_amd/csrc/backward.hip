@@ -34,6 +34,8 @@
 // are staged k-row-major and read with the transposing ds_read_b64_tr_b16.
 // The weight gradients' depth ends at the expert's last row: the buffer
 // resource stops there, so the loads past it return zeros.
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -461,12 +463,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_bf16_kernel(Args p) {
     //     from every wave (8 rows each, one row per 1 KB instruction: lanes 0..31 read
     //     the h1 piece, 32..63 the h3 piece; rows past the tile read zeros);
     //  2. each lane turns its h1, h3 and da into dh1, dh3 (written over h1, h3 in S0)
-    //     and a (into S1, 512-byte rows plus 16 bytes of padding);
-    //  3. the block writes the rows' dh1, dh3 and a pieces (512 bytes each) to global
+    //     and, unless the caller passed the forward's activations, a (into S1,
+    //     512-byte rows plus 16 bytes of padding);
+    //  3. the block writes the rows' dh1, dh3 (and a) pieces (512 bytes each) to global
     //     memory with 16-byte stores (2-byte stores from the accumulators' lanes cost a
     //     quarter of this GEMM).
     constexpr int kActE = 264;
     const int f = p.f;
+    const bool want_act = p.act != nullptr;      // block-uniform
     const __amdgpu_buffer_rsrc_t h_rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(static_cast<const uint16_t*>(p.h13) + (size_t)r0 * 2 * f), 0,
         tile_rows * 2 * f * 2, kRsrcWord3);
@@ -498,26 +502,34 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_bf16_kernel(Args p) {
             const float sl = h1 * sg;
             hrow[cl] = f32_to_bf16(g * h3 * (sg + sl * (1.f - sg)));
             hrow[256 + cl] = f32_to_bf16(g * sl);
-            arow[cl] = f32_to_bf16(sl * h3);
+            if (want_act) arow[cl] = f32_to_bf16(sl * h3);
           }
         }
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      // wave w: rows 8 w .. 8 w + 7 of the pass, 24 (row, piece) pairs, two per
-      // instruction (32 lanes x 16 bytes each)
+      // wave w: rows 8 w .. 8 w + 7 of the pass, 24 (row, piece) pairs (16 without
+      // a), two per instruction (32 lanes x 16 bytes each)
+      auto store_pieces = [&](auto pieces_c) {
+        constexpr int pieces = decltype(pieces_c)::value;
 #pragma unroll
-      for (int i = 0; i < 12; ++i) {
-        const int idx = 2 * i + (lane >> 5);
-        const int prow = 8 * w + idx / 3, seg = idx % 3;
-        const int row = r0 + 64 * pass + prow;
-        const int c8 = 8 * (lane & 31);
-        const uint16_t* src = seg == 2 ? S1 + prow * kActE + c8 : S0 + prow * 512 + 256 * seg + c8;
-        const uint4 v = *reinterpret_cast<const uint4*>(src);
-        if (row < rend) {
-          uint16_t* dst = seg == 2 ? act + (size_t)row * f + n0
-                                   : dh + (size_t)row * 2 * f + (seg == 1 ? f : 0) + n0;
-          *reinterpret_cast<uint4*>(dst + c8) = v;
+        for (int i = 0; i < 4 * pieces; ++i) {
+          const int idx = 2 * i + (lane >> 5);
+          const int prow = 8 * w + idx / pieces, seg = idx % pieces;
+          const int row = r0 + 64 * pass + prow;
+          const int c8 = 8 * (lane & 31);
+          const uint16_t* src =
+              seg == 2 ? S1 + prow * kActE + c8 : S0 + prow * 512 + 256 * seg + c8;
+          const uint4 v = *reinterpret_cast<const uint4*>(src);
+          if (row < rend) {
+            uint16_t* dst = seg == 2 ? act + (size_t)row * f + n0
+                                     : dh + (size_t)row * 2 * f + (seg == 1 ? f : 0) + n0;
+            *reinterpret_cast<uint4*>(dst + c8) = v;
+          }
         }
-      }
+      };
+      if (want_act)
+        store_pieces(std::integral_constant<int, 3>{});
+      else
+        store_pieces(std::integral_constant<int, 2>{});
     }
   } else if (MODE == kWGrad) {
     const bool low = n0 < p.nsplit;
@@ -648,7 +660,7 @@ __global__ __launch_bounds__(256) void bwd_gemm_f32_kernel(Args p) {
         float* dh = static_cast<float*>(p.dh);
         dh[(size_t)row * 2 * f + col] = g * h3 * (s + sl * (1.f - s));
         dh[(size_t)row * 2 * f + f + col] = g * sl;
-        static_cast<float*>(p.act)[(size_t)row * f + col] = sl * h3;
+        if (p.act) static_cast<float*>(p.act)[(size_t)row * f + col] = sl * h3;
       } else if (MODE == kSwiGLU) {
         const int f = p.f;
         const float h1 = c0[i][j], h3 = c1[i][j];
@@ -972,14 +984,17 @@ size_t expert_backward_saved_ws_bytes(int d, int f, int max_rows, bool bf16) {
 }
 
 hipError_t launch_expert_backward_saved(const void* x_perm, const void* g_perm, const void* h13,
-                                        const int32_t* offsets, const void* w1, const void* w3,
+                                        const void* act_in, const int32_t* offsets,
+                                        const void* w1, const void* w3,
                                         const void* w2, int N, int d, int f, int max_rows,
                                         bool bf16, float* dx_perm, float* dw1, float* dw3,
                                         float* dw2, void* ws, hipStream_t stream) {
   using namespace bwd;
   const size_t rows = (size_t)max_rows, eb = bf16 ? 2 : 4;
   void* dh = ws;
-  void* act = static_cast<char*>(ws) + pad256(rows * 2 * f * eb);
+  // the forward's activations when the caller has them, else recomputed here
+  void* act_ws = static_cast<char*>(ws) + pad256(rows * 2 * f * eb);
+  const void* act = act_in ? act_in : act_ws;
   Args a{};
   a.offsets = offsets;
   a.n_exp = N;
@@ -989,7 +1004,7 @@ hipError_t launch_expert_backward_saved(const void* x_perm, const void* g_perm, 
   Args s = a;
   s.a = g_perm; s.lda = d;
   s.b0 = w2; s.b1 = w2; s.ldb = d; s.b_estride = (long long)f * d;
-  s.K = d; s.Nn = f; s.h13 = h13; s.dh = dh; s.act = act; s.f = f;
+  s.K = d; s.Nn = f; s.h13 = h13; s.dh = dh; s.act = act_in ? nullptr : act_ws; s.f = f;
   gemm<kDAS>(s, bf16, stream);
 
   // dx = [dh1 | dh3] [W1_e | W3_e]^T

@@ -66,7 +66,8 @@ hipError_t launch_combine_backward(const void* dy, const float* y_perm, const in
 size_t expert_backward_ws_bytes(int d, int f, int max_rows, bool bf16);
 size_t expert_backward_saved_ws_bytes(int d, int f, int max_rows, bool bf16);
 hipError_t launch_expert_backward_saved(const void* x_perm, const void* g_perm, const void* h13,
-                                        const int32_t* offsets, const void* w1, const void* w3,
+                                        const void* act_in, const int32_t* offsets,
+                                        const void* w1, const void* w3,
                                         const void* w2, int N, int d, int f, int max_rows,
                                         bool bf16, float* dx_perm, float* dw1, float* dw3,
                                         float* dw2, void* ws, hipStream_t stream);

@@ -45,8 +45,8 @@ SIGNATURES = {
     "moe_combine_backward": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
     "moe_expert_backward": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P,
                                  _Z, _P]),
-    "moe_expert_backward_saved": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P,
-                                       _P, _P, _Z, _P]),
+    "moe_expert_backward_saved": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P,
+                                       _P, _P, _P, _Z, _P]),
     "moe_router_backward": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _F, _I, _I, _I, _I,
                                  _I, _P, _P, _P, _P, _Z, _P]),
 }
@@ -413,7 +413,8 @@ def moe_expert_backward(x_perm, g_perm, offsets, w1, w3, w2, dx_perm=None, dw1=N
 
 
 def moe_expert_backward_saved(x_perm, g_perm, h13, offsets, w1, w3, w2, dx_perm=None, dw1=None,
-                              dw3=None, dw2=None, ws=None, stream=None):
+                              dw3=None, dw2=None, ws=None, stream=None, act=None):
+    """``act``: the forward's activations [max_rows, f] (None: recomputed from h13)."""
     max_rows, d = x_perm.shape
     N, _, f = w1.shape
     dev = x_perm.device
@@ -424,8 +425,9 @@ def moe_expert_backward_saved(x_perm, g_perm, h13, offsets, w1, w3, w2, dx_perm=
     if ws is None:
         ws = torch.empty(max(1, workspace_size(MOE_OP_EXPERT_BACKWARD_SAVED, max_rows, d, N, 1, f,
                                                x_perm.dtype)), dtype=torch.uint8, device=dev)
-    _check(_lib.moe_expert_backward_saved(_ptr(x_perm), _ptr(g_perm), _ptr(h13), _ptr(offsets),
-                                          _ptr(w1), _ptr(w3), _ptr(w2), N, d, f, max_rows,
+    _check(_lib.moe_expert_backward_saved(_ptr(x_perm), _ptr(g_perm), _ptr(h13), _ptr(act),
+                                          _ptr(offsets), _ptr(w1), _ptr(w3), _ptr(w2), N, d, f,
+                                          max_rows,
                                           _dt(x_perm), _ptr(dx_perm), _ptr(dw1), _ptr(dw3),
                                           _ptr(dw2), _ptr(ws), ws.numel(), _stream(stream)),
            "moe_expert_backward_saved")
@@ -512,7 +514,8 @@ def moe_backward(hidden, w_router, w1, w3, w2, dy, fwd: MoEBuffers, aux_coef=0.0
     moe_combine_backward(dy, fwd.y_perm, fwd.slot_row, fwd.topk_w, g.g_perm, g.dgate, stream)
     if getattr(fwd, "saved", False):
         moe_expert_backward_saved(fwd.x_perm, g.g_perm, fwd.h13, fwd.offsets, w1, w3, w2,
-                                  g.dx_perm, g.dw1, g.dw3, g.dw2, g.ws_expert, stream)
+                                  g.dx_perm, g.dw1, g.dw3, g.dw2, g.ws_expert, stream,
+                                  act=fwd.act)
     else:
         moe_expert_backward(fwd.x_perm, g.g_perm, fwd.offsets, w1, w3, w2, g.dx_perm, g.dw1,
                             g.dw3, g.dw2, g.ws_expert, stream)

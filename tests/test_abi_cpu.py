@@ -269,17 +269,21 @@ def test_backward_entry_points_reject():
                                    S) == WS
     # backward with saved h1 / h3: null h13; bf16 f not a multiple of 256; workspace of
     # [dh1 | dh3] + a only (no da), one byte short; null workspace
-    assert lib.moe_expert_backward_saved(P, P, NUL, P, P, P, P, 8, 256, 256, 64, BF16, P, P, P, P,
-                                         P, big, S) == INV
-    assert lib.moe_expert_backward_saved(P, P, P, P, P, P, P, 8, 256, 384, 64, BF16, P, P, P, P,
-                                         P, big, S) == UNS
+    assert lib.moe_expert_backward_saved(P, P, NUL, P, P, P, P, P, 8, 256, 256, 64, BF16, P, P, P,
+                                         P, P, big, S) == INV
+    assert lib.moe_expert_backward_saved(P, P, P, P, P, P, P, P, 8, 256, 384, 64, BF16, P, P, P,
+                                         P, P, big, S) == UNS
     rows, f = 64 * 2, 256
     wss = lib.moe_workspace_size(moe.MOE_OP_EXPERT_BACKWARD_SAVED, 64, 128, 8, 2, f, BF16)
     assert wss == rows * 2 * f * 2 + rows * f * 2
-    assert lib.moe_expert_backward_saved(P, P, P, P, P, P, P, 8, 256, 256, rows, BF16, P, P, P, P,
-                                         P, wss - 1, S) == WS
-    assert lib.moe_expert_backward_saved(P, P, P, P, P, P, P, 8, 256, 256, rows, BF16, P, P, P, P,
-                                         NUL, wss, S) == INV
+    assert lib.moe_expert_backward_saved(P, P, P, P, P, P, P, P, 8, 256, 256, rows, BF16, P, P, P,
+                                         P, P, wss - 1, S) == WS
+    assert lib.moe_expert_backward_saved(P, P, P, P, P, P, P, P, 8, 256, 256, rows, BF16, P, P, P,
+                                         P, NUL, wss, S) == INV
+    # the forward's activations are optional (NULL: recomputed): a null act alone is accepted
+    # up to the workspace check
+    assert lib.moe_expert_backward_saved(P, P, P, NUL, P, P, P, P, 8, 256, 256, rows, BF16, P, P,
+                                         P, P, P, wss - 1, S) == WS
     # up projection that keeps h13: null h13; unsupported dtype
     assert lib.moe_expert_up_save(P, P, P, P, 8, 256, 256, 64, BF16, P, NUL, S) == INV
     assert lib.moe_expert_up_save(P, P, P, P, 8, 256, 256, 64, 5, P, P, S) == UNS

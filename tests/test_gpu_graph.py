@@ -95,7 +95,7 @@ def test_training_step_graph_replays_match_eager(moe):
         moe.moe_aux_loss(b.logits, b.counts, k, b.aux, b.ws_aux)
         moe.moe_combine_backward(dy, b.y_perm, b.slot_row, b.topk_w, gb.g_perm, gb.dgate)
         moe.moe_expert_backward_saved(b.x_perm, gb.g_perm, b.h13, b.offsets, w1, w3, w2,
-                                      gb.dx_perm, gb.dw1, gb.dw3, gb.dw2, gb.ws_expert)
+                                      gb.dx_perm, gb.dw1, gb.dw3, gb.dw2, gb.ws_expert, act=b.act)
         moe.moe_router_backward(h, wr, b.logits, b.topk_idx, b.topk_w, b.counts, gb.dgate,
                                 gb.dx_perm, b.slot_row, 0.01, gb.dhidden, gb.dw_router, gb.dbias,
                                 True, gb.ws_router)

@@ -49,9 +49,11 @@ def _forward(moe, inp, dev, overflow, saved):
     return parity.host_results(b), b
 
 
-def run_backward(moe, inp, coef, overflow="drop", label="", modes=("recompute", "saved")):
-    """Both expert-backward paths (h1 / h3 recomputed, or saved by the forward) against
-    one oracle backward."""
+def run_backward(moe, inp, coef, overflow="drop", label="",
+                 modes=("recompute", "saved", "saved_recompute_act")):
+    """The expert-backward paths against one oracle backward: h1 / h3 recomputed; saved
+    by the forward, with dW2 from the forward's activations; saved, with the activations
+    recomputed from h1 / h3 (moe_expert_backward_saved with act = NULL)."""
     import oracle.moe_oracle as O
     from tests import parity
     parity.log(f"{label}: T={inp.T} d={inp.d} N={inp.N} k={inp.k} f={inp.f} {inp.dtype} "
@@ -63,7 +65,9 @@ def run_backward(moe, inp, coef, overflow="drop", label="", modes=("recompute", 
     ref = None
     reps = {}
     for mode in modes:
-        g, b = _forward(moe, inp, dev, overflow, mode == "saved")
+        g, b = _forward(moe, inp, dev, overflow, mode.startswith("saved"))
+        if mode == "saved_recompute_act":
+            b.act = None        # moe_backward then passes no activations
         gr = moe.moe_backward(dev["hidden"], dev["w_router"], dev["w1"], dev["w3"], dev["w2"],
                               _dev(dy, inp.dtype), b, coef, want_dbias=inp.bias is not None,
                               shared=sh)

@@ -349,7 +349,12 @@ moe_status moe_combine_backward(const void* dy, const float* y_perm, const int32
  *   w2 [N, f, d] dtype dt.
  *   ws  moe_workspace_size(MOE_OP_EXPERT_BACKWARD, T, d, N, k, f, dt) bytes,
  *       T*k = max_rows: da [max_rows, f] fp32, [dh1 | dh3] [max_rows, 2f] and
- *       a [max_rows, f] in dtype dt, each padded to 256 bytes.
+ *       a [max_rows, f] in dtype dt, each padded to 256 bytes, and for bf16
+ *       one fp32 256 x 256 tile and one counter per compute unit of the
+ *       current device: when the dx GEMM's last round of tiles would leave
+ *       most compute units idle, those tiles are split over k and their
+ *       partial tiles meet there, summed in a fixed order (results do not
+ *       depend on scheduling).  Calls that share `ws` must be ordered.
  *   Limits: those of moe_expert_ffn; for bf16 f a multiple of 256,
  *   max_rows * f < 2^29 and max_rows * d < 2^30.
  */
@@ -372,7 +377,8 @@ moe_status moe_expert_backward(const void* x_perm, const void* g_perm, const int
  * Arguments, outputs and limits otherwise as moe_expert_backward.
  *   ws  moe_workspace_size(MOE_OP_EXPERT_BACKWARD_SAVED, T, d, N, k, f, dt)
  *       bytes, T*k = max_rows: [dh1 | dh3] [max_rows, 2f] and a [max_rows, f]
- *       in dtype dt, each padded to 256 bytes.
+ *       in dtype dt, each padded to 256 bytes, and (bf16) the dx GEMM's k-split
+ *       tiles and counters as for moe_expert_backward.
  */
 moe_status moe_expert_backward_saved(const void* x_perm, const void* g_perm, const void* h13,
                                      const void* act, const int32_t* offsets, const void* w1,

@@ -78,6 +78,12 @@ struct Args {
   void* dh;                 // SwiGLU: [dh1 | dh3] [rows, 2f] (output)
   void* act;                // SwiGLU: a [rows, f] (output)
   int f;
+  // DX: the last round's tiles split over k (partial tiles and one ticket per
+  // compute unit in the workspace); null tickets: no split
+  float* part;
+  int32_t* tickets;
+  int num_cus;
+  int dp_grid;              // blocks [0, dp_grid) compute whole tiles
 };
 
 __device__ __forceinline__ bool dp_logical(int total, int& logical) {
@@ -156,6 +162,7 @@ struct Loader {
   uint32_t a_u, a_step, b_u, b_step;
   uint32_t a_kstride, b_kstride;
   int ksplit;
+  int kbase;                  // first k-step of this block's range
   int w;                      // loading wave 0..3
 };
 
@@ -169,6 +176,7 @@ __device__ __forceinline__ int ldst(int w, int i) {
 
 template <bool AT, bool BT>
 __device__ __forceinline__ void issue(uint16_t* __restrict__ dst, const Loader& L, int kstep) {
+  kstep += L.kbase;
   const uint32_t ka = (uint32_t)kstep * L.a_kstride;
 #pragma unroll
   for (int i = 0; i < 8; ++i)
@@ -226,14 +234,37 @@ __device__ __forceinline__ int clamp_off(const int32_t* offsets, int e, int max_
 //     every 4 k-rows followed by 16 bytes of padding (a 32-lane half of a
 //     transposing read covers k rows r .. r+3 and r+8 .. r+11, which share the
 //     swizzle; the padding moves the second group to other banks)
+// Split of the last round of tiles over k (dx only: 1088 tiles of 448 k-steps
+// at the Mixtral counts leave a last round of 64 tiles on 256 CUs): when the
+// last round would leave at least half of the CUs idle, each of its r tiles is
+// cut into up to 4 k-ranges run by separate blocks, and the last block of a
+// tile to take its ticket sums the partial tiles in range order (the forward
+// down projection's scheme; results do not depend on which block finishes
+// last).  Only tiles of at least 128 k-steps are split.  Returns the number of
+// tiles computed whole.
+constexpr int kMaxSegs = 4, kMinSplitSteps = 128;
+__device__ __forceinline__ int split_plan(int total, int nk, int num_cus, int& segs) {
+  segs = 1;
+  if (num_cus <= 0 || nk < kMinSplitSteps) return total;
+  const int r = total % num_cus;
+  if (r == 0 || 2 * r > num_cus) return total;
+  int sg = num_cus / r;
+  sg = sg < kMaxSegs ? sg : kMaxSegs;
+  sg = sg < nk / 2 ? sg : nk / 2;
+  if (sg < 2) return total;
+  segs = sg;
+  return total - r;
+}
+
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_bf16_kernel(Args p) {
   constexpr bool AT = MODE == kWGrad;                       // A m-contiguous
   constexpr bool BT = MODE == kSwiGLU || MODE == kWGrad;    // B n-contiguous
   constexpr bool GK = MODE == kWGrad;                       // depth = the expert's rows
   __shared__ __align__(1024) uint16_t S0[2 * kRegion], S1[2 * kRegion];
+  __shared__ int s_last;
 
-  int e, r0, rend, mt, nt, m0 = 0, kl;
+  int e, r0, rend, mt, nt, m0 = 0, kl, kb = 0, slot = -1, segs = 1;
   if (GK) {
     const int m_tiles = p.M / kBM;
     const int tpe = m_tiles * p.n_tiles;
@@ -247,12 +278,29 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_bf16_kernel(Args p) {
     kl = (rend - r0 + kBK - 1) / kBK;
   } else {
     const int m_tiles = count_tiles(p.offsets, p.n_exp, kBM, p.max_rows);
+    const int total = m_tiles * p.n_tiles;
+    const int nk = p.K / kBK;
+    const int n_dp = (MODE == kDX && p.tickets) ? split_plan(total, nk, p.num_cus, segs) : total;
+    // blocks [0, dp_grid) compute whole tiles; the rest compute k-ranges of the
+    // last tiles (block j: tile n_dp + j / segs, range j % segs)
     int logical;
-    if (!dp_logical(m_tiles * p.n_tiles, logical)) return;
+    kl = nk;
+    if (MODE != kDX || (int)blockIdx.x < p.dp_grid) {
+      if (!dp_logical(n_dp, logical)) return;
+    } else {
+      const int j = blockIdx.x - p.dp_grid;
+      if (j >= (total - n_dp) * segs) return;
+      logical = n_dp + j / segs;
+      const int seg = j % segs;
+      kb = seg * nk / segs;
+      kl = (seg + 1) * nk / segs - kb;
+      slot = j;
+    }
     tile_of_logical(logical, m_tiles, p.n_tiles, mt, nt);
     if (!find_tile(p.offsets, p.n_exp, mt, kBM, p.max_rows, e, r0, rend)) return;
-    kl = p.K / kBK;
   }
+  kb = __builtin_amdgcn_readfirstlane(kb);
+  slot = __builtin_amdgcn_readfirstlane(slot);
   e = __builtin_amdgcn_readfirstlane(e);
   r0 = __builtin_amdgcn_readfirstlane(r0);
   rend = __builtin_amdgcn_readfirstlane(rend);
@@ -272,6 +320,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_bf16_kernel(Args p) {
   Loader L;
   L.w = w & 3;
   L.ksplit = MODE == kDX ? p.ksplit : 0x7FFFFFFF;
+  L.kbase = kb;
   const uint16_t* A = static_cast<const uint16_t*>(p.a) + (size_t)r0 * p.lda;
   // rows past the tile's end (and, for the weight gradients, k rows past the
   // expert's last row) lie outside the resource's range and load as zeros
@@ -408,6 +457,53 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_bf16_kernel(Args p) {
     }
   }
 #undef MOE_BWD_KLOOP
+
+  // ---- dx k-range blocks: store the partial tile; the last of a tile's
+  // blocks to take its ticket sums all of the tile's partials in range order
+  // and goes on to the normal epilogue
+  if (MODE == kDX && slot >= 0) {
+    const __amdgpu_buffer_rsrc_t mine = __builtin_amdgcn_make_buffer_rsrc(
+        p.part + (size_t)slot * (kBM * kBN), 0, kBM * kBN * 4, kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = acc[i][j][r];
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), mine, tid * 4,
+                                                ((i * 4 + j) * 4 + r) * kThreads * 4, 0);
+        }
+    // every wave's stores are done before the barrier; one wave then makes the
+    // block's tile visible device-wide and takes the ticket
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const int tile_sk = slot / segs;
+    if (tid == 0) {
+      __threadfence();
+      const int last = atomicAdd(&p.tickets[tile_sk], 1) == segs - 1;
+      if (last) __threadfence();       // acquire the other blocks' partial tiles
+      s_last = last;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    const __amdgpu_buffer_rsrc_t all = __builtin_amdgcn_make_buffer_rsrc(
+        p.part + (size_t)tile_sk * segs * (kBM * kBN), 0, segs * kBM * kBN * 4, kRsrcWord3);
+    for (int q = 0; q < segs; ++q) {
+      const int qo = q * kBM * kBN * 4;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float v = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(all, tid * 4,
+                                                            qo + ((i * 4 + j) * 4 + r) * kThreads * 4, 0));
+            acc[i][j][r] = q == 0 ? v : acc[i][j][r] + v;
+          }
+    }
+  }
 
   // ---- epilogues.  acc[ib][jb][r]: tile row 64 (ib / 2) + 32 wm + 16 (ib % 2) + 4 (lane / 16) + r,
   // column 16 jb + lane % 16 of the wave's 64 columns (SwiGLU: jb < 2 W1, jb >= 2 the same W3 columns)
@@ -877,7 +973,31 @@ __global__ __launch_bounds__(256) void router_dw_reduce_kernel(const float* __re
 }
 
 static int round8(int x) { return (x + 7) & ~7; }
+
 static size_t pad256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+__global__ void zero_i32_kernel(int32_t* __restrict__ q, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) q[i] = 0;
+}
+
+// Workspace of the dx GEMM's k-split: one fp32 256 x 256 partial tile and one
+// ticket per compute unit (0 bytes without a device, e.g. on a CPU-only host).
+size_t split_ws_bytes() {
+  const int cus = device_cus();
+  if (cus <= 0) return 0;
+  return pad256((size_t)cus * kBM * kBN * sizeof(float)) + pad256((size_t)cus * sizeof(int32_t));
+}
+
+// Point the dx GEMM's arguments at the split workspace that starts at `base`.
+void set_split(Args& s, void* base) {
+  const int cus = device_cus();
+  if (cus <= 0 || !base) return;
+  s.part = static_cast<float*>(base);
+  s.tickets = reinterpret_cast<int32_t*>(static_cast<char*>(base) +
+                                         pad256((size_t)cus * kBM * kBN * sizeof(float)));
+  s.num_cus = cus;
+}
 
 template <int MODE>
 static void gemm(const Args& a, bool bf16, hipStream_t stream) {
@@ -890,6 +1010,12 @@ static void gemm(const Args& a, bool bf16, hipStream_t stream) {
     } else {
       const int mt_bound = (a.max_rows + kBM - 1) / kBM + a.n_exp;
       grid = round8(mt_bound * b.n_tiles);
+    }
+    b.dp_grid = grid;
+    if (MODE == kDX && a.tickets) {
+      hipLaunchKernelGGL(zero_i32_kernel, dim3((a.num_cus + 255) / 256), dim3(256), 0, stream,
+                         a.tickets, a.num_cus);
+      grid += round8(a.num_cus);
     }
     hipLaunchKernelGGL(bwd_gemm_bf16_kernel<MODE>, dim3(grid), dim3(kThreads), 0, stream, b);
   } else {
@@ -907,7 +1033,8 @@ static void gemm(const Args& a, bool bf16, hipStream_t stream) {
 size_t expert_backward_ws_bytes(int d, int f, int max_rows, bool bf16) {
   (void)d;
   const size_t rows = (size_t)max_rows, eb = bf16 ? 2 : 4;
-  return bwd::pad256(rows * f * 4) + bwd::pad256(rows * 2 * f * eb) + bwd::pad256(rows * f * eb);
+  return bwd::pad256(rows * f * 4) + bwd::pad256(rows * 2 * f * eb) + bwd::pad256(rows * f * eb) +
+         (bf16 ? bwd::split_ws_bytes() : 0);
 }
 
 hipError_t launch_combine_backward(const void* dy, const float* y_perm, const int32_t* slot_row,
@@ -957,6 +1084,7 @@ hipError_t launch_expert_backward(const void* x_perm, const void* g_perm, const 
   s.a = dh; s.lda = 2 * f;
   s.b0 = w1; s.b1 = w3; s.ldb = f; s.b_estride = (long long)d * f;
   s.K = 2 * f; s.ksplit = f / kBK; s.Nn = d; s.out0 = dx_perm; s.ldo = d;
+  if (bf16) set_split(s, static_cast<char*>(act) + pad256(rows * f * eb));
   gemm<kDX>(s, bf16, stream);
 
   // dW2_e = a_e^T g_e  ([f, rows] x [rows, d])
@@ -980,7 +1108,8 @@ hipError_t launch_expert_backward(const void* x_perm, const void* g_perm, const 
 size_t expert_backward_saved_ws_bytes(int d, int f, int max_rows, bool bf16) {
   (void)d;
   const size_t rows = (size_t)max_rows, eb = bf16 ? 2 : 4;
-  return bwd::pad256(rows * 2 * f * eb) + bwd::pad256(rows * f * eb);
+  return bwd::pad256(rows * 2 * f * eb) + bwd::pad256(rows * f * eb) +
+         (bf16 ? bwd::split_ws_bytes() : 0);
 }
 
 hipError_t launch_expert_backward_saved(const void* x_perm, const void* g_perm, const void* h13,
@@ -1012,6 +1141,7 @@ hipError_t launch_expert_backward_saved(const void* x_perm, const void* g_perm, 
   s.a = dh; s.lda = 2 * f;
   s.b0 = w1; s.b1 = w3; s.ldb = f; s.b_estride = (long long)d * f;
   s.K = 2 * f; s.ksplit = f / kBK; s.Nn = d; s.out0 = dx_perm; s.ldo = d;
+  if (bf16) set_split(s, static_cast<char*>(act_ws) + pad256(rows * f * eb));
   gemm<kDX>(s, bf16, stream);
 
   // dW2_e = a_e^T g_e

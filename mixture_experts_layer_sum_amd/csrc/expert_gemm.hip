@@ -1169,7 +1169,7 @@ static int round8(int x) { return (x + 7) & ~7; }
 
 // Compute units of the current device (cached per device; calls from several
 // host threads may query the same device concurrently, so the cache is atomic).
-static int device_cus() {
+int device_cus() {
   static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;

@@ -65,6 +65,9 @@ hipError_t launch_combine_backward(const void* dy, const float* y_perm, const in
                                    void* g_perm, float* dgate, hipStream_t stream);
 size_t expert_backward_ws_bytes(int d, int f, int max_rows, bool bf16);
 size_t expert_backward_saved_ws_bytes(int d, int f, int max_rows, bool bf16);
+// Compute units of the current device (0 if there is none).
+int device_cus();
+
 hipError_t launch_expert_backward_saved(const void* x_perm, const void* g_perm, const void* h13,
                                         const void* act_in, const int32_t* offsets,
                                         const void* w1, const void* w3,

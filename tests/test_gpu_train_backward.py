@@ -129,6 +129,10 @@ SMALL = [
     ("bf16_N256", 70, 256, 256, 2, 256, "bf16", 0.0, None, 0.01, "drop"),
     ("f32_k_eq_N", 40, 64, 4, 4, 64, "f32", 0.0, None, 0.1, "drop"),
     ("bf16_d512_f768", 300, 512, 8, 2, 768, "bf16", 1.25, None, 0.01, "drop"),
+    # f = 4096: the dx GEMM is 2f = 8192 deep (128 k-steps) and its 4 tiles fill a few of
+    # the CUs, so each tile is split over k into 4 ranges whose partials meet in the
+    # workspace
+    ("bf16_dx_ksplit", 300, 256, 2, 2, 4096, "bf16", 0.0, None, 0.01, "drop"),
     # shared experts: every token, weight 1; two of them, and one with all routed slots dropped
     ("f32_two_shared", 100, 128, 8, 2, 128, "f32", 1.0, None, 0.01, "drop", 2, 64),
     ("bf16_shared", 400, 256, 8, 2, 256, "bf16", 1.0, "skew", 0.01, "drop", 1, 512),

@@ -20,6 +20,7 @@
  * P4 §5.1):
  *   through the combine                                           moe_combine_backward
  *   through both grouped GEMMs (dx, dW1, dW3, dW2)               moe_expert_backward
+ *   (or with h1, h3 kept by the forward's moe_expert_up_save)     moe_expert_backward_saved
  *   through the softmax, the aux loss and the router linear       moe_router_backward
  *
  * Conventions shared by every entry point:

@@ -16,7 +16,10 @@
 //   da       : da[r] = g[r] W2_e^T                              (grouped, NT)
 //   swiglu   : recompute h1, h3; dh1 = da * h3 * silu'(h1), dh3 = da * silu(h1),
 //              a = silu(h1) * h3                                 (grouped, NN)
-//   dx       : dx[r] = dh1[r] W1_e^T + dh3[r] W3_e^T              (grouped, NT, K = 2f)
+//              (with h1, h3 saved by the forward: in the da GEMM's epilogue, and a
+//              is the forward's own activation when the caller passes it)
+//   dx       : dx[r] = dh1[r] W1_e^T + dh3[r] W3_e^T              (grouped, NT, K = 2f;
+//              a sparse last round of deep tiles is split over k)
 //   weights  : dW2_e = a_e^T g_e;  [dW1_e | dW3_e] = x_e^T [dh1_e | dh3_e]
 //                                                   (per expert, k = the expert's rows)
 //   router   : dlogit = softmax-over-k Jacobian of dgate + aux_coef * d aux / d logits;
@@ -228,12 +231,6 @@ __device__ __forceinline__ int clamp_off(const int32_t* offsets, int e, int max_
   return min(max(offsets[e], lo), max_rows);
 }
 
-// LDS layout of one stage: A region at element 0, B region at kRegion.
-//   row-major operand  [256 rows][64 k]: chunk c of row r at position c ^ ((r >> 1) & 7)
-//   transposed operand 2 x [64 k][128 cols]: chunk c of k-row kr at c ^ (4 (kr & 3)),
-//     every 4 k-rows followed by 16 bytes of padding (a 32-lane half of a
-//     transposing read covers k rows r .. r+3 and r+8 .. r+11, which share the
-//     swizzle; the padding moves the second group to other banks)
 // Split of the last round of tiles over k (dx only: 1088 tiles of 448 k-steps
 // at the Mixtral counts leave a last round of 64 tiles on 256 CUs): when the
 // last round would leave at least half of the CUs idle, each of its r tiles is
@@ -256,6 +253,12 @@ __device__ __forceinline__ int split_plan(int total, int nk, int num_cus, int& s
   return total - r;
 }
 
+// LDS layout of one stage: A region at element 0, B region at kRegion.
+//   row-major operand  [256 rows][64 k]: chunk c of row r at position c ^ ((r >> 1) & 7)
+//   transposed operand 2 x [64 k][128 cols]: chunk c of k-row kr at c ^ (4 (kr & 3)),
+//     every 4 k-rows followed by 16 bytes of padding (a 32-lane half of a
+//     transposing read covers k rows r .. r+3 and r+8 .. r+11, which share the
+//     swizzle; the padding moves the second group to other banks)
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_bf16_kernel(Args p) {
   constexpr bool AT = MODE == kWGrad;                       // A m-contiguous

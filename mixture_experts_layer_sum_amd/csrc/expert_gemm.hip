@@ -208,11 +208,9 @@ __device__ __forceinline__ bool find_tile_lpt(const int32_t* __restrict__ offset
 // Heaviest-first dispatch is used when some row tile is light and the grid
 // is at most this many rounds of the CUs; longer grids keep the grouped,
 // XCD-contiguous order, whose L2 reuse matters more than the last round
-// (16 experts, K = 2048, 1672 tiles: 390 us grouped, 404 us heaviest-first).
-#ifndef MOE_LPT_ROUNDS
-#define MOE_LPT_ROUNDS 4
-#endif
-constexpr int kLptRounds = MOE_LPT_ROUNDS;
+// (16 experts, K = 2048, 1672 tiles: 390 us grouped, 404 us heaviest-first;
+// Mixtral counts, 7504 tiles: 3.09 ms grouped, 3.20 ms heaviest-first).
+constexpr int kLptRounds = 4;
 
 // Split of the last, partial round of tiles over k.  With `total` tiles on
 // `num_cus` CUs (one block each) the last round holds r = total % num_cus

@@ -55,6 +55,7 @@ constexpr int kTGroup = 4 * 128 + 8, kTSub = 16 * kTGroup, kRegion = 2 * kTSub;
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 // One GEMM launch.  Row indices r are rows of the expert-contiguous order.
@@ -558,15 +559,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_bf16_kernel(Args p) {
   } else if (MODE == kDAS) {
     // acc = da for tile rows x f-columns n0 .. n0 + 255.  Four passes of 64 tile rows
     // (row blocks ib = 2 pass, 2 pass + 1):
-    //  1. the rows' saved [h1 256 | h3 256] (bf16, 1 KB) come into S0 by direct loads
+    //  1. the rows' saved [h1 256 | h3 256] (bf16, 1 KB) come into LDS by direct loads
     //     from every wave (8 rows each, one row per 1 KB instruction: lanes 0..31 read
     //     the h1 piece, 32..63 the h3 piece; rows past the tile read zeros);
-    //  2. each lane turns its h1, h3 and da into dh1, dh3 (written over h1, h3 in S0)
-    //     and, unless the caller passed the forward's activations, a (into S1,
-    //     512-byte rows plus 16 bytes of padding);
+    //  2. each lane turns its h1, h3 and da into dh1, dh3 (written over h1, h3) and,
+    //     unless the caller passed the forward's activations, a (into S1, 512-byte
+    //     rows plus 16 bytes of padding);
     //  3. the block writes the rows' dh1, dh3 (and a) pieces (512 bytes each) to global
     //     memory with 16-byte stores (2-byte stores from the accumulators' lanes cost a
     //     quarter of this GEMM).
+    // Without a, the passes alternate between the two stages and the next pass's
+    // rows load while the current pass computes and stores; with a, S1 holds the
+    // a rows and every pass loads into S0 after the previous pass's stores.
     constexpr int kActE = 264;
     const int f = p.f;
     const bool want_act = p.act != nullptr;      // block-uniform
@@ -574,28 +578,45 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_bf16_kernel(Args p) {
         const_cast<uint16_t*>(static_cast<const uint16_t*>(p.h13) + (size_t)r0 * 2 * f), 0,
         tile_rows * 2 * f * 2, kRsrcWord3);
     const uint32_t hv = (uint32_t)((((lane >> 5) ? f : 0) + n0 + 8 * (lane & 31)) * 2);
-    uint16_t* dh = static_cast<uint16_t*>(p.dh);
+    // stores past the tile's last row fall outside the range and are dropped, so
+    // every wave issues the same number of stores per pass
+    const __amdgpu_buffer_rsrc_t dh_rs = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<uint16_t*>(p.dh) + (size_t)r0 * 2 * f, 0, tile_rows * 2 * f * 2, kRsrcWord3);
     uint16_t* act = static_cast<uint16_t*>(p.act);
-#pragma unroll
-    for (int pass = 0; pass < 4; ++pass) {
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    auto load_pass = [&](uint16_t* buf, int pass) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            h_rs, (lds_void*)(S0 + (8 * w + i) * 512), 16, hv,
+            h_rs, (lds_void*)(buf + (8 * w + i) * 512), 16, hv,
             (uint32_t)((64 * pass + 8 * w + i) * 2 * f * 2), 0, 0);
-      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+    // every h1 / h3 of the lane is read before the first dh is written over them,
+    // so the reads issue back to back instead of each waiting out the LDS latency
+    auto compute_pass = [&](uint16_t* hbuf, int pass) {
+      uint16_t hv[2][4][4][2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int jb = 0; jb < 4; ++jb) {
+            const int lr = 32 * wm + 16 * b + g4 + r;
+            const int cl = wn * 128 + 64 * pw + 16 * jb + l16;
+            hv[b][r][jb][0] = hbuf[lr * 512 + cl];
+            hv[b][r][jb][1] = hbuf[lr * 512 + 256 + cl];
+          }
 #pragma unroll
       for (int ib = 2 * pass; ib < 2 * pass + 2; ++ib)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int lr = 32 * wm + 16 * (ib & 1) + g4 + r;        // row within the pass
-          uint16_t* hrow = S0 + lr * 512;
+          uint16_t* hrow = hbuf + lr * 512;
           uint16_t* arow = S1 + lr * kActE;
 #pragma unroll
           for (int jb = 0; jb < 4; ++jb) {
             const int cl = wn * 128 + 64 * pw + 16 * jb + l16;
-            const float h1 = bf16_to_f32(hrow[cl]), h3 = bf16_to_f32(hrow[256 + cl]);
+            const float h1 = bf16_to_f32(hv[ib & 1][r][jb][0]);
+            const float h3 = bf16_to_f32(hv[ib & 1][r][jb][1]);
             const float g = acc[ib][jb][r];
             const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-h1));
             const float sl = h1 * sg;
@@ -604,31 +625,66 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_bf16_kernel(Args p) {
             if (want_act) arow[cl] = f32_to_bf16(sl * h3);
           }
         }
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      // wave w: rows 8 w .. 8 w + 7 of the pass, 24 (row, piece) pairs (16 without
-      // a), two per instruction (32 lanes x 16 bytes each)
-      auto store_pieces = [&](auto pieces_c) {
-        constexpr int pieces = decltype(pieces_c)::value;
+    };
+    // wave w: rows 8 w .. 8 w + 7 of the pass, 24 (row, piece) pairs (16 without
+    // a), two per instruction (32 lanes x 16 bytes each)
+    auto store_pieces = [&](const uint16_t* hbuf, int pass, auto pieces_c) {
+      constexpr int pieces = decltype(pieces_c)::value;
 #pragma unroll
-        for (int i = 0; i < 4 * pieces; ++i) {
-          const int idx = 2 * i + (lane >> 5);
-          const int prow = 8 * w + idx / pieces, seg = idx % pieces;
-          const int row = r0 + 64 * pass + prow;
-          const int c8 = 8 * (lane & 31);
-          const uint16_t* src =
-              seg == 2 ? S1 + prow * kActE + c8 : S0 + prow * 512 + 256 * seg + c8;
-          const uint4 v = *reinterpret_cast<const uint4*>(src);
-          if (row < rend) {
-            uint16_t* dst = seg == 2 ? act + (size_t)row * f + n0
-                                     : dh + (size_t)row * 2 * f + (seg == 1 ? f : 0) + n0;
-            *reinterpret_cast<uint4*>(dst + c8) = v;
-          }
+      for (int i = 0; i < 4 * pieces; ++i) {
+        const int idx = 2 * i + (lane >> 5);
+        const int prow = 8 * w + idx / pieces, seg = idx % pieces;
+        const int trow = 64 * pass + prow;
+        const int c8 = 8 * (lane & 31);
+        const uint16_t* src =
+            seg == 2 ? S1 + prow * kActE + c8 : hbuf + prow * 512 + 256 * seg + c8;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+        if (seg == 2) {
+          if (r0 + trow < rend)
+            *reinterpret_cast<u32x4*>(act + (size_t)(r0 + trow) * f + n0 + c8) = v;
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b128(
+              v, dh_rs, (uint32_t)(((size_t)trow * 2 * f + (seg == 1 ? f : 0) + n0 + c8) * 2), 0, 0);
         }
-      };
-      if (want_act)
-        store_pieces(std::integral_constant<int, 3>{});
-      else
-        store_pieces(std::integral_constant<int, 2>{});
+      }
+    };
+    if (want_act) {
+#pragma unroll
+      for (int pass = 0; pass < 4; ++pass) {
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        load_pass(S0, pass);
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        compute_pass(S0, pass);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        store_pieces(S0, pass, std::integral_constant<int, 3>{});
+      }
+    } else {
+      // vector-memory operations of one wave, in issue order: L0 L1 | st0 L2 | st1 L3 |
+      // st2 | st3 (Lp: 8 loads of pass p, stp: 8 stores of pass p); each wait lets the
+      // operations issued after the pass's loads stay in flight
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      load_pass(S0, 0);
+      load_pass(S1, 1);
+      asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+      compute_pass(S0, 0);
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      store_pieces(S0, 0, std::integral_constant<int, 2>{});
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      load_pass(S0, 2);
+      asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+      compute_pass(S1, 1);
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      store_pieces(S1, 1, std::integral_constant<int, 2>{});
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      load_pass(S1, 3);
+      asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+      compute_pass(S0, 2);
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      store_pieces(S0, 2, std::integral_constant<int, 2>{});
+      asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+      compute_pass(S1, 3);
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      store_pieces(S1, 3, std::integral_constant<int, 2>{});
     }
   } else if (MODE == kWGrad) {
     const bool low = n0 < p.nsplit;

@@ -630,15 +630,23 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_gemm_bf16_kernel(Args p) {
     // a), two per instruction (32 lanes x 16 bytes each)
     auto store_pieces = [&](const uint16_t* hbuf, int pass, auto pieces_c) {
       constexpr int pieces = decltype(pieces_c)::value;
+      u32x4 pv[4 * pieces];      // every piece is read before the first store is issued
+#pragma unroll
+      for (int i = 0; i < 4 * pieces; ++i) {
+        const int idx = 2 * i + (lane >> 5);
+        const int prow = 8 * w + idx / pieces, seg = idx % pieces;
+        const int c8 = 8 * (lane & 31);
+        const uint16_t* src =
+            seg == 2 ? S1 + prow * kActE + c8 : hbuf + prow * 512 + 256 * seg + c8;
+        pv[i] = *reinterpret_cast<const u32x4*>(src);
+      }
 #pragma unroll
       for (int i = 0; i < 4 * pieces; ++i) {
         const int idx = 2 * i + (lane >> 5);
         const int prow = 8 * w + idx / pieces, seg = idx % pieces;
         const int trow = 64 * pass + prow;
         const int c8 = 8 * (lane & 31);
-        const uint16_t* src =
-            seg == 2 ? S1 + prow * kActE + c8 : hbuf + prow * 512 + 256 * seg + c8;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+        const u32x4 v = pv[i];
         if (seg == 2) {
           if (r0 + trow < rend)
             *reinterpret_cast<u32x4*>(act + (size_t)(r0 + trow) * f + n0 + c8) = v;

@@ -669,7 +669,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
     const int g4 = 4 * (lane >> 4), l16 = lane & 15;
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      // before the first pass the k-loop's last refills must have landed; before
+      // the second only the LDS reads of the first pass's stores (the stores
+      // themselves stay in flight)
+      if (pass == 0)
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
       for (int ib = 4 * pass; ib < 4 * pass + 4; ++ib)
 #pragma unroll
@@ -689,13 +695,20 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16_kernel(
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       // wave w writes rows 16 w .. 16 w + 15 of the pass: 48 (row, piece) pairs, four
       // per instruction (16 lanes x 16 bytes each)
+      uint4 pv[12];       // every piece is read before the first store is issued
+#pragma unroll
+      for (int i = 0; i < 12; ++i) {
+        const int idx = 4 * i + (lane >> 4);
+        const int prow = 16 * w + idx / 3, seg = idx % 3;
+        const uint16_t* lrow = (prow < 64 ? S0 : S1) + (prow & 63) * kRowE;
+        pv[i] = *reinterpret_cast<const uint4*>(lrow + 128 * seg + 8 * l16);
+      }
 #pragma unroll
       for (int i = 0; i < 12; ++i) {
         const int idx = 4 * i + (lane >> 4);
         const int prow = 16 * w + idx / 3, seg = idx % 3;
         const int row = r0 + 128 * pass + prow;
-        const uint16_t* lrow = (prow < 64 ? S0 : S1) + (prow & 63) * kRowE;
-        const uint4 v = *reinterpret_cast<const uint4*>(lrow + 128 * seg + 8 * l16);
+        const uint4 v = pv[i];
         if (row < rend) {
           uint16_t* dst = seg == 0 ? act + (size_t)row * Nout + n0
                                    : h13 + (size_t)row * 2 * Nout + (seg == 2 ? Nout : 0) + n0;

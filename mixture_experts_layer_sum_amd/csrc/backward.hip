@@ -936,10 +936,13 @@ __global__ __launch_bounds__(256) void router_dlogit_kernel(
   }
 }
 
-// dhidden for 32 tokens x 256 columns per block: the router term
-// dlogit[t] W_router^T (W_router is [d, N]), plus the token's slot rows of dx
-// in slot order, plus the shared experts' dx rows in shared-expert order.
-constexpr int kDxTok = 32;
+// dhidden for 8 tokens x 1024 columns per block (4 adjacent columns per
+// thread, 16-byte loads and stores): the router term dlogit[t] W_router^T
+// (W_router is [d, N]), plus the token's slot rows of dx in slot order, plus the
+// shared experts' dx rows in shared-expert order.  The slot rows of 8 tokens
+// are loaded together (a dropped slot reads row 0 and discards it), so that a
+// thread keeps 8 loads in flight instead of waiting on each.
+constexpr int kDxTok = 8, kDxGroup = 8;
 template <bool BF16>
 __global__ __launch_bounds__(256) void router_dx_kernel(
     const void* __restrict__ w_router, const float* __restrict__ dlog,
@@ -956,86 +959,184 @@ __global__ __launch_bounds__(256) void router_dx_kernel(
   for (int i = threadIdx.x; i < kDxTok * k; i += 256)
     sr[i] = i < nt * k ? slot_row[(size_t)t0 * k + i] : -1;
   __syncthreads();
-  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (c >= d) return;
-  float acc[kDxTok];
+  float4 acc[kDxTok];
 #pragma unroll
-  for (int t = 0; t < kDxTok; ++t) acc[t] = 0.f;
-  for (int e = 0; e < N; ++e) {
-    const float wv = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(w_router)[(size_t)c * N + e])
-                          : static_cast<const float*>(w_router)[(size_t)c * N + e];
+  for (int t = 0; t < kDxTok; ++t) acc[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto w_at = [&](int i, int e) {
+    return BF16 ? bf16_to_f32(static_cast<const uint16_t*>(w_router)[(size_t)(c + i) * N + e])
+                : static_cast<const float*>(w_router)[(size_t)(c + i) * N + e];
+  };
+  auto fma_e = [&](int e, const float (&wv)[4]) {
 #pragma unroll
-    for (int t = 0; t < kDxTok; ++t) acc[t] = fmaf(dl[t * N + e], wv, acc[t]);
+    for (int t = 0; t < kDxTok; ++t) {
+      const float g = dl[t * N + e];
+      acc[t].x = fmaf(g, wv[0], acc[t].x);
+      acc[t].y = fmaf(g, wv[1], acc[t].y);
+      acc[t].z = fmaf(g, wv[2], acc[t].z);
+      acc[t].w = fmaf(g, wv[3], acc[t].w);
+    }
+  };
+  // experts in order; the weights of 8 experts are loaded before their products
+  int e = 0;
+  for (; e + 8 <= N; e += 8) {
+    float wv[8][4];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wv[q][i] = w_at(i, e + q);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) fma_e(e + q, wv[q]);
+  }
+  for (; e < N; ++e) {
+    float wv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[i] = w_at(i, e);
+    fma_e(e, wv);
   }
 #pragma unroll
-  for (int t = 0; t < kDxTok; ++t) {
-    if (t < nt) {
-      float v = acc[t];
-      for (int j = 0; j < k; ++j) {
-        const int r = sr[t * k + j];
-        if (r >= 0) v += dx_perm[(size_t)r * d + c];
+  for (int t0g = 0; t0g < kDxTok; t0g += kDxGroup) {
+    for (int j = 0; j < k; ++j) {
+      float4 v[kDxGroup];
+#pragma unroll
+      for (int t = 0; t < kDxGroup; ++t) {
+        const int r = sr[(t0g + t) * k + j];
+        v[t] = *reinterpret_cast<const float4*>(dx_perm + (size_t)max(r, 0) * d + c);
       }
-      for (int q = 0; q < n_shared; ++q) v += dx_shared[((size_t)q * T + t0 + t) * d + c];
-      dhidden[(size_t)(t0 + t) * d + c] = v;
+#pragma unroll
+      for (int t = 0; t < kDxGroup; ++t) {
+        if (sr[(t0g + t) * k + j] >= 0) {
+          float4& a = acc[t0g + t];
+          a.x += v[t].x; a.y += v[t].y; a.z += v[t].z; a.w += v[t].w;
+        }
+      }
     }
+    for (int q = 0; q < n_shared; ++q) {
+#pragma unroll
+      for (int t = 0; t < kDxGroup; ++t) {
+        if (t0g + t < nt) {
+          const float4 v = *reinterpret_cast<const float4*>(
+              dx_shared + ((size_t)q * T + t0 + t0g + t) * d + c);
+          float4& a = acc[t0g + t];
+          a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kDxGroup; ++t)
+      if (t0g + t < nt)
+        *reinterpret_cast<float4*>(dhidden + (size_t)(t0 + t0g + t) * d + c) = acc[t0g + t];
   }
 }
 
 // Partial dW_router = hidden^T dlogit over one chunk of 64 tokens, for 256
-// columns and a group of up to 16 experts per block; the first column block
-// also writes the chunk's partial dbias.
-constexpr int kDwTok = 64, kDwE = 16;
-template <bool BF16>
+// columns (one per thread) and a group of up to EG experts per block (EG = 8
+// when N <= 8, else 16), tokens in order (the hidden values of 16 tokens are
+// loaded before their products), stored expert-major ([chunk][N][d], coalesced
+// over the columns); the first column block also writes the chunk's partial
+// dbias.
+constexpr int kDwTok = 64;
+template <bool BF16, int EG>
 __global__ __launch_bounds__(256) void router_dw_kernel(const void* __restrict__ hidden,
                                                         const float* __restrict__ dlog, int T,
                                                         int d, int N, float* __restrict__ part_w,
                                                         float* __restrict__ part_b) {
-  __shared__ float dl[kDwTok][kDwE];
-  const int chunk = blockIdx.y, eg = blockIdx.z * kDwE;
+  __shared__ float4 dl[kDwTok][EG / 4];
+  const int chunk = blockIdx.y, eg = blockIdx.z * EG;
   const int t0 = chunk * kDwTok, nt = min(kDwTok, T - t0);
-  const int ne = min(kDwE, N - eg);
-  for (int i = threadIdx.x; i < kDwTok * kDwE; i += 256) {
-    const int t = i / kDwE, e = i % kDwE;
-    dl[t][e] = (t < nt && e < ne) ? dlog[(size_t)(t0 + t) * N + eg + e] : 0.f;
+  const int ne = min(EG, N - eg);
+  float* dls = reinterpret_cast<float*>(dl);
+  for (int i = threadIdx.x; i < kDwTok * EG; i += 256) {
+    const int t = i / EG, e = i % EG;
+    dls[i] = (t < nt && e < ne) ? dlog[(size_t)(t0 + t) * N + eg + e] : 0.f;
   }
   __syncthreads();
   if (blockIdx.x == 0 && (int)threadIdx.x < ne) {
     float s = 0.f;
-    for (int t = 0; t < nt; ++t) s += dl[t][threadIdx.x];
+    for (int t = 0; t < nt; ++t) s += dls[t * EG + threadIdx.x];
     part_b[(size_t)chunk * N + eg + threadIdx.x] = s;
   }
   const int c = blockIdx.x * 256 + threadIdx.x;
   if (c >= d) return;
-  float acc[kDwE];
+  float acc[EG];
 #pragma unroll
-  for (int e = 0; e < kDwE; ++e) acc[e] = 0.f;
-  for (int t = 0; t < nt; ++t) {
-    const float hv = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(hidden)[(size_t)(t0 + t) * d + c])
-                          : static_cast<const float*>(hidden)[(size_t)(t0 + t) * d + c];
+  for (int e = 0; e < EG; ++e) acc[e] = 0.f;
+  for (int tb = 0; tb < nt; tb += 16) {
+    float hv[16];
 #pragma unroll
-    for (int e = 0; e < kDwE; ++e) acc[e] = fmaf(hv, dl[t][e], acc[e]);
+    for (int u = 0; u < 16; ++u) {
+      const int t = min(tb + u, nt - 1);            // rows past the chunk: dl is 0 there
+      hv[u] = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(hidden)[(size_t)(t0 + t) * d + c])
+                   : static_cast<const float*>(hidden)[(size_t)(t0 + t) * d + c];
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+#pragma unroll
+      for (int e4 = 0; e4 < EG / 4; ++e4) {
+        const float4 g = dl[tb + u][e4];
+        acc[4 * e4 + 0] = fmaf(hv[u], g.x, acc[4 * e4 + 0]);
+        acc[4 * e4 + 1] = fmaf(hv[u], g.y, acc[4 * e4 + 1]);
+        acc[4 * e4 + 2] = fmaf(hv[u], g.z, acc[4 * e4 + 2]);
+        acc[4 * e4 + 3] = fmaf(hv[u], g.w, acc[4 * e4 + 3]);
+      }
   }
-  float* o = part_w + ((size_t)chunk * d + c) * N + eg;
-  for (int e = 0; e < ne; ++e) o[e] = acc[e];
+#pragma unroll
+  for (int e = 0; e < EG; ++e)
+    if (e < ne) part_w[((size_t)chunk * N + eg + e) * d + c] = acc[e];
 }
 
-// Sum of the chunk partials in chunk order (deterministic).
-__global__ __launch_bounds__(256) void router_dw_reduce_kernel(const float* __restrict__ part_w,
-                                                               const float* __restrict__ part_b,
-                                                               int n_chunks, int d, int N,
-                                                               float* __restrict__ dw,
-                                                               float* __restrict__ dbias) {
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  const size_t dn = (size_t)d * N;
+// Sum of the chunk partials in a fixed order (deterministic): a block owns 256
+// consecutive elements of the expert-major partials (4 columns of one expert per
+// lane, 16-byte loads); wave g sums the chunks of its contiguous eighth of the
+// chunk range in chunk order, then the eight wave sums are added in wave order
+// and written to dW_router [d, N].  The first N threads of block 0 sum dbias in
+// chunk order.
+constexpr int kDwRedWaves = 8;
+__global__ __launch_bounds__(64 * kDwRedWaves) void router_dw_reduce_kernel(
+    const float* __restrict__ part_w, const float* __restrict__ part_b, int n_chunks, int d,
+    int N, float* __restrict__ dw, float* __restrict__ dbias) {
+  __shared__ float4 red[kDwRedWaves][64];
+  const int lane = threadIdx.x & 63, g = threadIdx.x >> 6;
+  const size_t dn = (size_t)d * N;                      // a multiple of 4
+  const size_t i = ((size_t)blockIdx.x * 64 + lane) * 4;  // expert i / d, columns i % d ..
+  const int q0 = g * n_chunks / kDwRedWaves, q1 = (g + 1) * n_chunks / kDwRedWaves;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
   if (i < dn) {
-    float s = 0.f;
-    for (int q = 0; q < n_chunks; ++q) s += part_w[(size_t)q * dn + i];
-    dw[i] = s;
+    int q = q0;
+    for (; q + 8 <= q1; q += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4*>(part_w + (size_t)(q + u) * dn + i);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w;
+      }
+    }
+    for (; q < q1; ++q) {
+      const float4 v = *reinterpret_cast<const float4*>(part_w + (size_t)q * dn + i);
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
   }
-  if (dbias && i < (size_t)N) {
-    float s = 0.f;
-    for (int q = 0; q < n_chunks; ++q) s += part_b[(size_t)q * N + i];
-    dbias[i] = s;
+  red[g][lane] = s;
+  __syncthreads();
+  if (g == 0 && i < dn) {
+    float4 t = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < kDwRedWaves; ++w) {
+      const float4 v = red[w][lane];
+      t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
+    }
+    const int e = (int)(i / d), c = (int)(i % d);
+    dw[(size_t)c * N + e] = t.x;
+    dw[(size_t)(c + 1) * N + e] = t.y;
+    dw[(size_t)(c + 2) * N + e] = t.z;
+    dw[(size_t)(c + 3) * N + e] = t.w;
+  }
+  if (dbias && blockIdx.x == 0 && (int)threadIdx.x < N) {
+    float sb = 0.f;
+    for (int q = 0; q < n_chunks; ++q) sb += part_b[(size_t)q * N + threadIdx.x];
+    dbias[threadIdx.x] = sb;
   }
 }
 
@@ -1251,7 +1352,7 @@ hipError_t launch_router_backward(const void* hidden, const void* w_router, cons
                                            pad256((size_t)chunks * d * N * 4));
   hipLaunchKernelGGL(router_dlogit_kernel, dim3((T + 255) / 256), dim3(256), 0, stream, logits,
                      topk_idx, topk_w, counts, dgate, aux_coef, T, N, k, dlog);
-  const dim3 gx((d + 255) / 256, (T + kDxTok - 1) / kDxTok);
+  const dim3 gx((d + 1023) / 1024, (T + kDxTok - 1) / kDxTok);
   const size_t shx = (size_t)kDxTok * (N + k) * 4;
   if (bf16)
     hipLaunchKernelGGL(router_dx_kernel<true>, gx, dim3(256), shx, stream, w_router, dlog, dx_perm,
@@ -1259,16 +1360,24 @@ hipError_t launch_router_backward(const void* hidden, const void* w_router, cons
   else
     hipLaunchKernelGGL(router_dx_kernel<false>, gx, dim3(256), shx, stream, w_router, dlog,
                        dx_perm, slot_row, dx_shared, n_shared, T, d, N, k, dhidden);
-  const dim3 gw((d + 255) / 256, chunks, (N + kDwE - 1) / kDwE);
-  if (bf16)
-    hipLaunchKernelGGL(router_dw_kernel<true>, gw, dim3(256), 0, stream, hidden, dlog, T, d, N,
-                       part_w, part_b);
+  const int eg_w = N <= 8 ? 8 : 16;
+  const dim3 gw((d + 255) / 256, chunks, (N + eg_w - 1) / eg_w);
+  if (bf16 && eg_w == 8)
+    hipLaunchKernelGGL((router_dw_kernel<true, 8>), gw, dim3(256), 0, stream, hidden, dlog, T, d,
+                       N, part_w, part_b);
+  else if (bf16)
+    hipLaunchKernelGGL((router_dw_kernel<true, 16>), gw, dim3(256), 0, stream, hidden, dlog, T, d,
+                       N, part_w, part_b);
+  else if (eg_w == 8)
+    hipLaunchKernelGGL((router_dw_kernel<false, 8>), gw, dim3(256), 0, stream, hidden, dlog, T, d,
+                       N, part_w, part_b);
   else
-    hipLaunchKernelGGL(router_dw_kernel<false>, gw, dim3(256), 0, stream, hidden, dlog, T, d, N,
-                       part_w, part_b);
+    hipLaunchKernelGGL((router_dw_kernel<false, 16>), gw, dim3(256), 0, stream, hidden, dlog, T,
+                       d, N, part_w, part_b);
   const size_t dn = (size_t)d * N;
-  hipLaunchKernelGGL(router_dw_reduce_kernel, dim3((unsigned)((dn + 255) / 256)), dim3(256), 0,
-                     stream, part_w, part_b, chunks, d, N, dw_router, dbias);
+  hipLaunchKernelGGL(router_dw_reduce_kernel, dim3((unsigned)((dn + 255) / 256)),
+                     dim3(64 * kDwRedWaves), 0, stream, part_w, part_b, chunks, d, N, dw_router,
+                     dbias);
   return hipGetLastError();
 }
 

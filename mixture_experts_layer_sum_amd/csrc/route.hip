@@ -429,7 +429,13 @@ void router_wt_kernel(
   for (int i = tid; i < N; i += 64 * kRtBigWaves) sbias[i] = (bias != nullptr) ? bias[i] : 0.f;
 
   const int nks = d / 32;
-  const int ks0 = w * nks / kRtBigWaves, ks1 = (w + 1) * nks / kRtBigWaves;
+  // k-range q of 8 (q/8 .. (q+1)/8 of d) for this wave; the assignment rotates with
+  // the block's place on its XCD (blocks go to the XCDs in turn), so that the
+  // XCD's blocks do not all read the same part of WT at the same time.  The
+  // partial of range q goes to slot q and the slots are summed in range order,
+  // so the sum does not depend on the rotation.
+  const int q = (w + (int)(blockIdx.x >> 3)) & (kRtBigWaves - 1);
+  const int ks0 = q * nks / kRtBigWaves, ks1 = (q + 1) * nks / kRtBigWaves;
   const uint16_t* brow[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) brow[m] = hidden + (size_t)min(t0 + 16 * m + j, T - 1) * d + 8 * g;
@@ -478,8 +484,8 @@ void router_wt_kernel(
 #undef MOE_RT_LOAD
 #undef MOE_RT_MMA
   // acc[m][et][r]: expert 16 et + 4g + r, token 16 m + j.  Each wave writes its
-  // partial logits to a tile of its own; one pass then adds the eight tiles in
-  // wave order (a fixed order, the same sum as adding them one wave at a time).
+  // partial logits to the tile of its k-range; one pass then adds the eight tiles
+  // in range order (a fixed order, the same sum as adding them one range at a time).
   if (kPerWave) {
 #pragma unroll
     for (int m = 0; m < MT; ++m)
@@ -487,11 +493,11 @@ void router_wt_kernel(
       for (int et = 0; et < NT; ++et)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          red[kPerWave ? w : 0][16 * m + j][16 * et + 4 * g + r] = acc[m][et][r];
+          red[kPerWave ? q : 0][16 * m + j][16 * et + 4 * g + r] = acc[m][et][r];
     __syncthreads();
   } else {
     for (int ww = 0; ww < kRtBigWaves; ++ww) {
-      if (w == ww) {
+      if (q == ww) {
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll

@@ -1098,58 +1098,70 @@ static void launch_rows(int mt, const void* x, const int32_t* offsets, int N, co
 }
 
 // ---------------------------------------------------------------- fp32 (VALU)
-// 64-deep k chunks: each thread has 16 loads of A and 16 (+16) of the weights in
-// flight per chunk, so that a small layer (a few chunks per block) waits on memory
-// a few times rather than K / 16 times.  The k order of every sum is unchanged.
-constexpr int kFBM = 64, kFBN = 64, kFBK = 64;
+// 64-deep k chunks: each thread has BM / 4 loads of A and 16 (+16) of the weights
+// in flight per chunk, so that a small layer (a few chunks per block) waits on
+// memory a few times rather than K / 16 times.  The k order of every sum is
+// unchanged.  Tiles of BM = 64 rows, or 16 when the experts average at most 16
+// rows: the arithmetic of a 64-row tile runs on the waves that hold its rows,
+// so a tile with 16 real rows would leave three of its four waves idle.
+constexpr int kFBN = 64, kFBK = 64;
 
-template <bool UP>
+template <bool UP, int BM>
 __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
     const float* __restrict__ X, const int32_t* __restrict__ offsets, int N,
     const float* __restrict__ Wa, const float* __restrict__ Wb, int K, int Nout, int n_tiles,
     int max_rows, float* __restrict__ out, float* __restrict__ h13) {
-  __shared__ float As[kFBK][kFBM + 1];
+  constexpr int RPT = BM / 16;                  // rows per thread
+  __shared__ float As[kFBK][BM + 1];
   __shared__ float B1[kFBK][kFBN];
   __shared__ float B3[kFBK][kFBN];
   const int mt = blockIdx.x / n_tiles, nt = blockIdx.x % n_tiles;
   int e, r0, rend;
-  if (!find_tile(offsets, N, mt, kFBM, max_rows, e, r0, rend)) return;
+  if (!find_tile(offsets, N, mt, BM, max_rows, e, r0, rend)) return;
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const int n0 = nt * kFBN;
   const size_t wexp = (size_t)e * K * Nout;
-  float c1[4][4] = {}, c3[4][4] = {};
+  float c1[RPT][4] = {}, c3[RPT][4] = {};
   for (int k0 = 0; k0 < K; k0 += kFBK) {
-    float va[16], vb1[16], vb3[16];
+    float va[BM / 4], vb1[16], vb3[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int item = tid + 256 * i;           // 64 rows x 64 k
+    for (int i = 0; i < BM / 4; ++i) {
+      const int item = tid + 256 * i;           // BM rows x 64 k
       const int row = item >> 6, kk = item & 63;
       const int gr = r0 + row;
       va[i] = gr < rend ? X[(size_t)gr * K + k0 + kk] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int item = tid + 256 * i;
       const int kr = item >> 6, col = item & 63;  // 64 k x 64 cols
       vb1[i] = Wa[wexp + (size_t)(k0 + kr) * Nout + n0 + col];
       vb3[i] = UP ? Wb[wexp + (size_t)(k0 + kr) * Nout + n0 + col] : 0.f;
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < BM / 4; ++i) {
       const int item = tid + 256 * i;
       As[item & 63][item >> 6] = va[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int item = tid + 256 * i;
       B1[item >> 6][item & 63] = vb1[i];
       if (UP) B3[item >> 6][item & 63] = vb3[i];
     }
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < kFBK; ++kk) {
-      float a[4], b1[4], b3[4];
+      float a[RPT], b1[4], b3[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+      for (int i = 0; i < RPT; ++i) a[i] = As[kk][ty * RPT + i];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         b1[j] = B1[kk][tx * 4 + j];
         if (UP) b3[j] = B3[kk][tx * 4 + j];
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < RPT; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           c1[i][j] = fmaf(a[i], b1[j], c1[i][j]);
@@ -1159,8 +1171,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
     __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = r0 + ty * 4 + i;
+  for (int i = 0; i < RPT; ++i) {
+    const int row = r0 + ty * RPT + i;
     if (row >= rend) continue;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -1173,6 +1185,25 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(
       if (UP) v = v / (1.f + expf(-v)) * c3[i][j];
       out[(size_t)row * Nout + col] = v;
     }
+  }
+}
+
+// Row tile of the fp32 kernel: 16 rows when the experts average at most 16.
+static bool f32_small_tiles(int max_rows, int N) { return (max_rows + N - 1) / N <= 16; }
+
+template <bool UP>
+static void launch_f32(const float* x, const int32_t* offsets, int N, const float* wa,
+                       const float* wb, int K, int Nout, int max_rows, float* out, float* h13,
+                       hipStream_t stream) {
+  const int n_tiles = Nout / kFBN;
+  if (f32_small_tiles(max_rows, N)) {
+    const int mt_bound = (max_rows + 15) / 16 + N;
+    hipLaunchKernelGGL((grouped_gemm_f32_kernel<UP, 16>), dim3(mt_bound * n_tiles), dim3(256), 0,
+                       stream, x, offsets, N, wa, wb, K, Nout, n_tiles, max_rows, out, h13);
+  } else {
+    const int mt_bound = (max_rows + 63) / 64 + N;
+    hipLaunchKernelGGL((grouped_gemm_f32_kernel<UP, 64>), dim3(mt_bound * n_tiles), dim3(256), 0,
+                       stream, x, offsets, N, wa, wb, K, Nout, n_tiles, max_rows, out, h13);
   }
 }
 
@@ -1227,12 +1258,9 @@ hipError_t launch_expert_up(const void* x_perm, const int32_t* offsets, const vo
                        static_cast<int32_t*>(nullptr), device_cus(), grid,
                        static_cast<uint16_t*>(h13));
   } else {
-    const int n_tiles = f / kFBN;
-    const int mt_bound = (max_rows + kFBM - 1) / kFBM + N;
-    hipLaunchKernelGGL(grouped_gemm_f32_kernel<true>, dim3(mt_bound * n_tiles), dim3(256), 0,
-                       stream, static_cast<const float*>(x_perm), offsets, N,
-                       static_cast<const float*>(w1), static_cast<const float*>(w3), d, f, n_tiles,
-                       max_rows, static_cast<float*>(act), static_cast<float*>(h13));
+    launch_f32<true>(static_cast<const float*>(x_perm), offsets, N, static_cast<const float*>(w1),
+                     static_cast<const float*>(w3), d, f, max_rows, static_cast<float*>(act),
+                     static_cast<float*>(h13), stream);
   }
   return hipGetLastError();
 }
@@ -1267,12 +1295,8 @@ hipError_t launch_expert_down(const void* act, const int32_t* offsets, const voi
                        d, n_tiles, max_rows, static_cast<void*>(y_perm), part, tickets, cus,
                        dp_grid, static_cast<uint16_t*>(nullptr));
   } else {
-    const int n_tiles = d / kFBN;
-    const int mt_bound = (max_rows + kFBM - 1) / kFBM + N;
-    hipLaunchKernelGGL(grouped_gemm_f32_kernel<false>, dim3(mt_bound * n_tiles), dim3(256), 0,
-                       stream, static_cast<const float*>(act), offsets, N,
-                       static_cast<const float*>(w2), static_cast<const float*>(nullptr), f, d,
-                       n_tiles, max_rows, y_perm, static_cast<float*>(nullptr));
+    launch_f32<false>(static_cast<const float*>(act), offsets, N, static_cast<const float*>(w2),
+                      nullptr, f, d, max_rows, y_perm, nullptr, stream);
   }
   return hipGetLastError();
 }

@@ -641,6 +641,78 @@ __global__ __launch_bounds__(kRtThreads) void router_f32_kernel(
     if (hist[e]) atomicAdd(&counts[e], hist[e]);
 }
 
+// fp32 router for up to 32 experts: one wave per token, so that a batch of a
+// few dozen tokens still spreads over as many CUs and keeps many loads in
+// flight (the 64-token-per-block kernel above runs a 64-token batch in one
+// block, each thread through chains of dependent loads).  Lane l accumulates
+// the token's products for every expert over the hidden positions l, l + 64,
+// ... (the loads of U positions issued before their products), the 64 lane sums
+// of each expert are added by a butterfly (every lane ends with the same
+// bits), and the token's top-k runs on its logits in LDS.
+constexpr int kRfWaves = 4, kRfMaxN = 32;
+template <int NE>
+__global__ __launch_bounds__(64 * kRfWaves) void router_f32_wave_kernel(
+    const float* __restrict__ hidden, const float* __restrict__ wr, const float* __restrict__ bias,
+    int T, int d, int N, int k, float* __restrict__ logits, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, int32_t* __restrict__ counts) {
+  constexpr int U = NE <= 16 ? 4 : 2;
+  __shared__ float lg[kRfWaves][NE];
+  __shared__ int hist[256];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int t = blockIdx.x * kRfWaves + w;              // wave-uniform
+  for (int i = tid; i < 256; i += 64 * kRfWaves) hist[i] = 0;
+  if (t < T) {
+    float acc[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) acc[e] = 0.f;
+    const float* h = hidden + (size_t)t * d;
+    int q = lane;                                       // d is a multiple of 64
+    for (; q + 64 * (U - 1) < d; q += 64 * U) {
+      float hv[U], wv[U][NE];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        hv[u] = h[q + 64 * u];
+#pragma unroll
+        for (int e = 0; e < NE; ++e) wv[u][e] = e < N ? wr[(size_t)(q + 64 * u) * N + e] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < NE; ++e) acc[e] = fmaf(hv[u], wv[u][e], acc[e]);
+    }
+    for (; q < d; q += 64) {
+      const float hv = h[q];
+#pragma unroll
+      for (int e = 0; e < NE; ++e)
+        acc[e] = fmaf(hv, e < N ? wr[(size_t)q * N + e] : 0.f, acc[e]);
+    }
+    float mine = 0.f;                                   // lane e keeps expert e's logit
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      float v = acc[e];
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+      if (e == lane) mine = v;
+    }
+    if (lane < N) {
+      mine += bias ? bias[lane] : 0.f;
+      lg[w][lane] = mine;
+      logits[(size_t)t * N + lane] = mine;
+    }
+  }
+  __syncthreads();
+  if (t < T) {
+    if (k <= kTopkThread) {
+      if (lane == 0) topk_thread(lg[w], t, N, k, topk_idx, topk_w, hist);
+    } else {
+      topk_row(lg[w], t, N, k, topk_idx, topk_w, hist);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < N; e += 64 * kRfWaves)
+    if (hist[e]) atomicAdd(&counts[e], hist[e]);
+}
+
 hipError_t launch_route(const void* hidden, const void* w_router, const float* bias, int T, int d,
                         int N, int k, bool bf16, float* logits, int32_t* topk_idx, float* topk_w,
                         int32_t* counts, void* ws, hipStream_t stream) {
@@ -678,9 +750,21 @@ hipError_t launch_route(const void* hidden, const void* w_router, const float* b
     hipLaunchKernelGGL(zero_i32_kernel, dim3((N + 255) / 256), dim3(256), 0, stream, counts, N);
   const dim3 grid((T + kRtTok - 1) / kRtTok), block(kRtThreads);
   if (!bf16) {
-    hipLaunchKernelGGL(router_f32_kernel, grid, block, 0, stream,
-                       static_cast<const float*>(hidden), static_cast<const float*>(w_router),
-                       bias, T, d, N, k, logits, topk_idx, topk_w, counts);
+    const auto* hf = static_cast<const float*>(hidden);
+    const auto* wf = static_cast<const float*>(w_router);
+    const dim3 gw((T + kRfWaves - 1) / kRfWaves), bw(64 * kRfWaves);
+    if (N <= 8)
+      hipLaunchKernelGGL(router_f32_wave_kernel<8>, gw, bw, 0, stream, hf, wf, bias, T, d, N, k,
+                         logits, topk_idx, topk_w, counts);
+    else if (N <= 16)
+      hipLaunchKernelGGL(router_f32_wave_kernel<16>, gw, bw, 0, stream, hf, wf, bias, T, d, N, k,
+                         logits, topk_idx, topk_w, counts);
+    else if (N <= kRfMaxN)
+      hipLaunchKernelGGL(router_f32_wave_kernel<32>, gw, bw, 0, stream, hf, wf, bias, T, d, N, k,
+                         logits, topk_idx, topk_w, counts);
+    else
+      hipLaunchKernelGGL(router_f32_kernel, grid, block, 0, stream, hf, wf, bias, T, d, N, k,
+                         logits, topk_idx, topk_w, counts);
     return hipGetLastError();
   }
   const auto* h = static_cast<const uint16_t*>(hidden);

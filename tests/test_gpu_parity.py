@@ -81,6 +81,12 @@ SMALL = [
     ("bf16_cf105_T80_k2", 80, 256, 8, 2, 128, "bf16", 1.05, "skew"),
     ("bf16_cf07_T40_k2", 40, 256, 8, 2, 128, "bf16", 0.7, "skew"),
     ("f32_cf07_T160_N16_k1", 160, 128, 16, 1, 128, "f32", 0.7, "skew"),
+    # the fp32 router: one wave per token up to 32 experts (24 experts: the 32-wide
+    # accumulator set; k = 20: the token's top-k by the whole wave), the 64-token
+    # block beyond 32 experts
+    ("f32_router_N24", 100, 128, 24, 2, 128, "f32", 0.0, None),
+    ("f32_router_N24_k20", 40, 64, 24, 20, 64, "f32", 0.0, None),
+    ("f32_router_N40_k3", 90, 128, 40, 3, 128, "f32", 1.0, "skew"),
 ]
 
 

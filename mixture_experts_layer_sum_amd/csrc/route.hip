@@ -603,7 +603,9 @@ size_t route_ws_bytes(int T, int d, int N) {
   return ks > 1 ? static_cast<size_t>(ks) * T * N * sizeof(float) : 0;
 }
 
-// fp32: the same epilogue after a plain fp32 dot product per (token, expert).
+// fp32 routers of more than 32 experts (router_f32_wave_kernel below takes the
+// rest): 64 tokens per block, the same epilogue after a plain fp32 dot product
+// per (token, expert).
 __global__ __launch_bounds__(kRtThreads) void router_f32_kernel(
     const float* __restrict__ hidden, const float* __restrict__ wr, const float* __restrict__ bias,
     int T, int d, int N, int k, float* __restrict__ logits, int32_t* __restrict__ topk_idx,

@@ -196,6 +196,92 @@ __global__ __launch_bounds__(kAuxFinal) void aux_final_kernel(const float* __res
   if (tid == 0) aux[0] = term[0] * static_cast<float>(N);
 }
 
+// Batches of at most 64 tokens (four 16-token partials) in one launch: waves
+// 4b .. 4b + 3 of a 1024-thread block compute partial b exactly as block b of
+// aux_partial_kernel does, the partials stay in LDS, and the block then runs
+// aux_final_kernel's fixed-order folds on them, so the result is bit for bit
+// that of the two-launch form.
+constexpr int kAuxSmallT = 4 * kAuxTok;
+__global__ __launch_bounds__(kAuxFinal) void aux_small_kernel(const float* __restrict__ logits,
+                                                              int T, const int32_t* __restrict__ counts,
+                                                              int N, int k, float* __restrict__ aux) {
+  constexpr int TPW = kAuxTok / 4;
+  __shared__ float red[16][256];
+  __shared__ float part[4][256];
+  __shared__ double fold[kAuxFinal];
+  __shared__ float term[256];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nb = (T + kAuxTok - 1) / kAuxTok;
+  {
+    const int b = w >> 2, wi = w & 3;
+    const int tb = b * kAuxTok + wi * TPW;
+    float v[TPW][4];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int t = tb + i;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int e = lane + 64 * c;
+        v[i][c] = (t < T && e < N) ? logits[(size_t)t * N + e] : -INFINITY;
+      }
+    }
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      if (tb + i >= T) break;
+      float m = fmaxf(fmaxf(v[i][0], v[i][1]), fmaxf(v[i][2], v[i][3]));
+      m = wave_max(m);
+      float s = 0.f;
+      float p[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        p[c] = (lane + 64 * c < N) ? __expf(v[i][c] - m) : 0.f;
+        s += p[c];
+      }
+      s = wave_sum(s);
+      const float inv = 1.f / s;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] += p[c] * inv;
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) red[w][lane + 64 * c] = acc[c];
+  }
+  __syncthreads();
+  for (int i = tid; i < 4 * 256; i += kAuxFinal) {
+    const int b = i >> 8, e = i & 255;
+    part[b][e] = ((red[4 * b][e] + red[4 * b + 1][e]) + red[4 * b + 2][e]) + red[4 * b + 3][e];
+  }
+  __syncthreads();
+  int np2 = 1;
+  while (np2 < N) np2 <<= 1;
+  const int G = kAuxFinal / np2;
+  const int e = tid % np2, g = tid / np2;
+  double s = 0.0;
+  if (e < N)
+    for (int b = g; b < nb; b += G) s += part[b][e];
+  fold[tid] = s;
+  __syncthreads();
+  for (int h = G / 2; h >= 1; h >>= 1) {
+    if (g < h) fold[tid] += fold[tid + h * np2];
+    __syncthreads();
+  }
+  if (tid < np2) {
+    float t = 0.f;
+    if (tid < N) {
+      const double P = fold[tid] / T;
+      const double fe = static_cast<double>(counts[tid]) / (static_cast<double>(T) * k);
+      t = static_cast<float>(fe * P);
+    }
+    term[tid] = t;
+  }
+  __syncthreads();
+  for (int h = np2 / 2; h >= 1; h >>= 1) {
+    if (tid < h) term[tid] += term[tid + h];
+    __syncthreads();
+  }
+  if (tid == 0) aux[0] = term[0] * static_cast<float>(N);
+}
+
 size_t aux_ws_bytes(int T, int N) {
   const size_t nb = (static_cast<size_t>(T) + kAuxTok - 1) / kAuxTok;
   return nb * static_cast<size_t>(N) * sizeof(float);
@@ -203,6 +289,11 @@ size_t aux_ws_bytes(int T, int N) {
 
 hipError_t launch_aux(const float* logits, const int32_t* counts, int T, int N, int k, float* aux,
                       void* ws, hipStream_t stream) {
+  if (T <= kAuxSmallT) {
+    hipLaunchKernelGGL(aux_small_kernel, dim3(1), dim3(kAuxFinal), 0, stream, logits, T, counts, N,
+                       k, aux);
+    return hipGetLastError();
+  }
   const int nb = (T + kAuxTok - 1) / kAuxTok;
   float* part = static_cast<float*>(ws);
   hipLaunchKernelGGL(aux_partial_kernel, dim3(nb), dim3(256), 0, stream, logits, T, N, part);

@@ -104,12 +104,14 @@ def test_small_shapes(moe, case):
         _run(inp, f"{label}/seed{seed}")
 
 
-def test_uniform_router_exact_ties(moe):
-    """W_router = 0: every logit ties; lower ids win on both sides, aux is exactly 1."""
+@pytest.mark.parametrize("T", [64, 128])
+def test_uniform_router_exact_ties(moe, T):
+    """W_router = 0: every logit ties; lower ids win on both sides, aux is exactly 1
+    (T = 64: the one-launch aux loss, T = 128: partial sums and a final pass)."""
     for dt in ("bf16", "f32"):
-        inp = synth.make_inputs(128, 256, 8, 2, 128, dt, 1.25, 3)
+        inp = synth.make_inputs(T, 256, 8, 2, 128, dt, 1.25, 3)
         inp.w_router[:] = 0
-        rep, g, _, _ = _run(inp, f"uniform_router_{dt}", audit=False)
+        rep, g, _, _ = _run(inp, f"uniform_router_{dt}_T{T}", audit=False)
         assert (g["topk_idx"] == np.arange(2)).all()
         assert np.all(g["topk_w"] == 0.5)
         assert g["aux"] == 1.0

@@ -25,9 +25,12 @@
  *
  * Conventions shared by every entry point:
  *   - Every pointer argument is a DEVICE pointer owned by the caller, to a
- *     contiguous row-major array; the library never allocates, frees, keeps
- *     or synchronises.  `stream` is a hipStream_t passed as void* (NULL = the
- *     null stream); all work is enqueued on it asynchronously.
+ *     contiguous row-major array, 16-byte aligned (the kernels use 16-byte
+ *     accesses; hipMalloc and torch allocations are 256-byte aligned; a
+ *     misaligned pointer is MOE_ERR_INVALID_ARG); the library never
+ *     allocates, frees, keeps or synchronises.  `stream` is a hipStream_t
+ *     passed as void* (NULL = the null stream); all work is enqueued on it
+ *     asynchronously.
  *   - Argument errors are detected on the host before anything is enqueued
  *     and leave every output untouched.  MOE_ERR_HIP reports a launch error;
  *     a fault inside a kernel surfaces at the caller's next synchronisation.
@@ -55,7 +58,7 @@ extern "C" {
 
 typedef enum {
   MOE_OK = 0,
-  MOE_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, k outside [1, N], NaN capacity factor */
+  MOE_ERR_INVALID_ARG = 1, /* null or misaligned pointer, non-positive size, k outside [1, N], NaN capacity factor */
   MOE_ERR_UNSUPPORTED = 2, /* shape or dtype outside the limits above */
   MOE_ERR_WORKSPACE = 3,   /* workspace smaller than moe_workspace_size() */
   MOE_ERR_HIP = 4          /* HIP launch error */

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <initializer_list>
 
 #include "internal.hpp"
 
@@ -16,6 +17,15 @@ inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 inline bool dtype_ok(moe_dtype dt) { return dt == MOE_F32 || dt == MOE_BF16; }
 inline int elem_bytes(moe_dtype dt) { return dt == MOE_BF16 ? 2 : 4; }
 inline moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Every device buffer must be 16-byte aligned: the kernels read and write them
+// with 16-byte vector and buffer accesses (hipMalloc and torch allocations are
+// 256-byte aligned).  Null pointers pass here; the null checks are separate.
+inline bool aligned16(std::initializer_list<const void*> ps) {
+  for (const void* q : ps)
+    if (reinterpret_cast<uintptr_t>(q) & 15) return false;
+  return true;
+}
 
 // Shared shape checks.  Order: invalid (nonsense) arguments first, then
 // unsupported-but-meaningful ones.
@@ -116,6 +126,7 @@ size_t moe_workspace_size(moe_op op, int T, int d, int N, int k, int f, moe_dtyp
 moe_status moe_route(const void* hidden, const void* w_router, const float* bias, int T, int d,
                      int N, int k, moe_dtype dt, float* logits, int32_t* topk_idx, float* topk_w,
                      int32_t* counts, void* ws, size_t ws_bytes, void* stream) {
+  if (!aligned16({hidden, w_router, bias, logits, topk_idx, topk_w, counts, ws})) return MOE_ERR_INVALID_ARG;
   if (!hidden || !w_router || !logits || !topk_idx || !topk_w || !counts) return MOE_ERR_INVALID_ARG;
   moe_status s = check_tnk(T, N, k);
   if (s != MOE_OK) return s;
@@ -132,6 +143,7 @@ moe_status moe_permute(const void* hidden, const int32_t* topk_idx, int T, int d
                        double capacity_factor, moe_dtype dt, void* x_perm, int32_t* perm_src,
                        int32_t* slot_row, int32_t* kept, int32_t* offsets, void* ws,
                        size_t ws_bytes, void* stream) {
+  if (!aligned16({hidden, topk_idx, x_perm, perm_src, slot_row, kept, offsets, ws})) return MOE_ERR_INVALID_ARG;
   if (!hidden || !topk_idx || !x_perm || !perm_src || !slot_row || !kept || !offsets)
     return MOE_ERR_INVALID_ARG;
   if (std::isnan(capacity_factor)) return MOE_ERR_INVALID_ARG;
@@ -151,6 +163,7 @@ moe_status moe_permute_noalloc(const void* hidden, const int32_t* topk_idx, int 
                                int k, double capacity_factor, moe_dtype dt, void* x_perm,
                                int32_t* perm_src, int32_t* slot_row, int32_t* kept,
                                int32_t* offsets, void* stream) {
+  if (!aligned16({hidden, topk_idx, x_perm, perm_src, slot_row, kept, offsets})) return MOE_ERR_INVALID_ARG;
   if (!hidden || !topk_idx || !x_perm || !perm_src || !slot_row || !kept || !offsets)
     return MOE_ERR_INVALID_ARG;
   if (std::isnan(capacity_factor)) return MOE_ERR_INVALID_ARG;
@@ -171,6 +184,7 @@ moe_status moe_permute_reroute(const void* hidden, const int32_t* topk_idx, cons
                                int T, int d, int N, int k, double capacity_factor, moe_dtype dt,
                                void* x_perm, int32_t* perm_src, int32_t* slot_row, int32_t* kept,
                                int32_t* offsets, void* ws, size_t ws_bytes, void* stream) {
+  if (!aligned16({hidden, topk_idx, logits, x_perm, perm_src, slot_row, kept, offsets, ws})) return MOE_ERR_INVALID_ARG;
   if (!hidden || !topk_idx || !logits || !x_perm || !perm_src || !slot_row || !kept || !offsets)
     return MOE_ERR_INVALID_ARG;
   if (std::isnan(capacity_factor)) return MOE_ERR_INVALID_ARG;
@@ -190,6 +204,7 @@ moe_status moe_permute_reroute(const void* hidden, const int32_t* topk_idx, cons
 moe_status moe_expert_up(const void* x_perm, const int32_t* offsets, const void* w1,
                          const void* w3, int N, int d, int f, int max_rows, moe_dtype dt,
                          void* act, void* stream) {
+  if (!aligned16({x_perm, offsets, w1, w3, act})) return MOE_ERR_INVALID_ARG;
   if (!x_perm || !offsets || !w1 || !w3 || !act) return MOE_ERR_INVALID_ARG;
   moe_status s = check_expert_shape(N, d, f, max_rows, dt);
   if (s != MOE_OK) return s;
@@ -200,6 +215,7 @@ moe_status moe_expert_up(const void* x_perm, const int32_t* offsets, const void*
 moe_status moe_expert_up_save(const void* x_perm, const int32_t* offsets, const void* w1,
                               const void* w3, int N, int d, int f, int max_rows, moe_dtype dt,
                               void* act, void* h13, void* stream) {
+  if (!aligned16({x_perm, offsets, w1, w3, act, h13})) return MOE_ERR_INVALID_ARG;
   if (!x_perm || !offsets || !w1 || !w3 || !act || !h13) return MOE_ERR_INVALID_ARG;
   moe_status s = check_expert_shape(N, d, f, max_rows, dt);
   if (s != MOE_OK) return s;
@@ -210,6 +226,7 @@ moe_status moe_expert_up_save(const void* x_perm, const int32_t* offsets, const 
 moe_status moe_expert_down(const void* act, const int32_t* offsets, const void* w2, int N, int d,
                            int f, int max_rows, moe_dtype dt, float* y_perm, void* ws,
                            size_t ws_bytes, void* stream) {
+  if (!aligned16({act, offsets, w2, y_perm, ws})) return MOE_ERR_INVALID_ARG;
   if (!act || !offsets || !w2 || !y_perm) return MOE_ERR_INVALID_ARG;
   moe_status s = check_expert_shape(N, d, f, max_rows, dt);
   if (s != MOE_OK) return s;
@@ -223,6 +240,7 @@ moe_status moe_expert_down(const void* act, const int32_t* offsets, const void* 
 moe_status moe_expert_ffn(const void* x_perm, const int32_t* offsets, const void* w1,
                           const void* w3, const void* w2, int N, int d, int f, int max_rows,
                           moe_dtype dt, float* y_perm, void* ws, size_t ws_bytes, void* stream) {
+  if (!aligned16({x_perm, offsets, w1, w3, w2, y_perm, ws})) return MOE_ERR_INVALID_ARG;
   if (!x_perm || !offsets || !w1 || !w3 || !w2 || !y_perm) return MOE_ERR_INVALID_ARG;
   moe_status s = check_expert_shape(N, d, f, max_rows, dt);
   if (s != MOE_OK) return s;
@@ -240,6 +258,7 @@ moe_status moe_expert_ffn(const void* x_perm, const int32_t* offsets, const void
 
 moe_status moe_quantize_fp8(const void* w, moe_dtype dt, int N, int K, int M, uint8_t* q,
                             float* scale, void* stream) {
+  if (!aligned16({w, q, scale})) return MOE_ERR_INVALID_ARG;
   if (!w || !q || !scale) return MOE_ERR_INVALID_ARG;
   if (N < 1 || K < 1 || M < 1) return MOE_ERR_INVALID_ARG;
   if (!dtype_ok(dt)) return MOE_ERR_UNSUPPORTED;
@@ -260,6 +279,7 @@ static moe_status check_fp8_shape(int N, int d, int f, int max_rows) {
 moe_status moe_expert_up_fp8(const void* x_perm, const int32_t* offsets, const uint8_t* w1q,
                              const uint8_t* w3q, const float* s1, const float* s3, int N, int d,
                              int f, int max_rows, void* act, void* stream) {
+  if (!aligned16({x_perm, offsets, w1q, w3q, s1, s3, act})) return MOE_ERR_INVALID_ARG;
   if (!x_perm || !offsets || !w1q || !w3q || !s1 || !s3 || !act) return MOE_ERR_INVALID_ARG;
   moe_status s = check_fp8_shape(N, d, f, max_rows);
   if (s != MOE_OK) return s;
@@ -270,6 +290,7 @@ moe_status moe_expert_up_fp8(const void* x_perm, const int32_t* offsets, const u
 moe_status moe_expert_down_fp8(const void* act, const int32_t* offsets, const uint8_t* w2q,
                                const float* s2, int N, int d, int f, int max_rows, float* y_perm,
                                void* stream) {
+  if (!aligned16({act, offsets, w2q, s2, y_perm})) return MOE_ERR_INVALID_ARG;
   if (!act || !offsets || !w2q || !s2 || !y_perm) return MOE_ERR_INVALID_ARG;
   moe_status s = check_fp8_shape(N, d, f, max_rows);
   if (s != MOE_OK) return s;
@@ -280,6 +301,7 @@ moe_status moe_expert_down_fp8(const void* act, const int32_t* offsets, const ui
 moe_status moe_combine(const float* y_perm, const int32_t* slot_row, const float* topk_w,
                        const float* y_shared, int n_shared, int T, int d, int k, moe_dtype dt,
                        void* y, void* stream) {
+  if (!aligned16({y_perm, slot_row, topk_w, y_shared, y})) return MOE_ERR_INVALID_ARG;
   if (!y_perm || !slot_row || !topk_w || !y) return MOE_ERR_INVALID_ARG;
   if (T < 1 || k < 1 || n_shared < 0 || (n_shared > 0 && !y_shared)) return MOE_ERR_INVALID_ARG;
   if (k > kMaxExperts) return MOE_ERR_UNSUPPORTED;
@@ -292,6 +314,7 @@ moe_status moe_combine(const float* y_perm, const int32_t* slot_row, const float
 
 moe_status moe_aux_loss(const float* logits, const int32_t* counts, int T, int N, int k,
                         float* aux, void* ws, size_t ws_bytes, void* stream) {
+  if (!aligned16({logits, counts, aux, ws})) return MOE_ERR_INVALID_ARG;
   if (!logits || !counts || !aux) return MOE_ERR_INVALID_ARG;
   moe_status s = check_tnk(T, N, k);
   if (s != MOE_OK) return s;
@@ -303,6 +326,7 @@ moe_status moe_aux_loss(const float* logits, const int32_t* counts, int T, int N
 moe_status moe_combine_backward(const void* dy, const float* y_perm, const int32_t* slot_row,
                                 const float* topk_w, int T, int d, int k, moe_dtype dt,
                                 void* g_perm, float* dgate, void* stream) {
+  if (!aligned16({dy, y_perm, slot_row, topk_w, g_perm, dgate})) return MOE_ERR_INVALID_ARG;
   if (!dy || !y_perm || !slot_row || !topk_w || !g_perm || !dgate) return MOE_ERR_INVALID_ARG;
   if (T < 1 || k < 1) return MOE_ERR_INVALID_ARG;
   if (k > kMaxExperts || static_cast<int64_t>(T) * k >= (int64_t{1} << 31)) return MOE_ERR_UNSUPPORTED;
@@ -317,6 +341,7 @@ moe_status moe_expert_backward(const void* x_perm, const void* g_perm, const int
                                const void* w1, const void* w3, const void* w2, int N, int d,
                                int f, int max_rows, moe_dtype dt, float* dx_perm, float* dw1,
                                float* dw3, float* dw2, void* ws, size_t ws_bytes, void* stream) {
+  if (!aligned16({x_perm, g_perm, offsets, w1, w3, w2, dx_perm, dw1, dw3, dw2, ws})) return MOE_ERR_INVALID_ARG;
   if (!x_perm || !g_perm || !offsets || !w1 || !w3 || !w2 || !dx_perm || !dw1 || !dw3 || !dw2)
     return MOE_ERR_INVALID_ARG;
   moe_status s = check_expert_shape(N, d, f, max_rows, dt);
@@ -341,6 +366,7 @@ moe_status moe_expert_backward_saved(const void* x_perm, const void* g_perm, con
                                      int max_rows, moe_dtype dt, float* dx_perm, float* dw1,
                                      float* dw3, float* dw2, void* ws, size_t ws_bytes,
                                      void* stream) {
+  if (!aligned16({x_perm, g_perm, h13, act, offsets, w1, w3, w2, dx_perm, dw1, dw3, dw2, ws})) return MOE_ERR_INVALID_ARG;
   if (!x_perm || !g_perm || !h13 || !offsets || !w1 || !w3 || !w2 || !dx_perm || !dw1 || !dw3 ||
       !dw2)
     return MOE_ERR_INVALID_ARG;
@@ -366,6 +392,7 @@ moe_status moe_router_backward(const void* hidden, const void* w_router, const f
                                float aux_coef, int T, int d, int N, int k, moe_dtype dt,
                                float* dhidden, float* dw_router, float* dbias, void* ws,
                                size_t ws_bytes, void* stream) {
+  if (!aligned16({hidden, w_router, logits, topk_idx, topk_w, counts, dgate, dx_perm, slot_row, dx_shared, dhidden, dw_router, dbias, ws})) return MOE_ERR_INVALID_ARG;
   if (!hidden || !w_router || !logits || !topk_idx || !topk_w || !counts || !dgate || !dx_perm ||
       !slot_row || !dhidden || !dw_router)
     return MOE_ERR_INVALID_ARG;

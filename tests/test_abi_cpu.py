@@ -167,6 +167,21 @@ def test_expert_ffn_rejects(kw, status):
     assert ffn(**kw) == status
 
 
+M = ctypes.c_void_p(4096 + 8)      # fake device address, 8-byte but not 16-byte aligned
+
+
+@pytest.mark.parametrize("call,names", [
+    (route, ["hidden", "w_router", "bias", "logits", "topk_idx", "topk_w", "counts", "ws"]),
+    (permute, ["hidden", "topk_idx", "x_perm", "perm_src", "slot_row", "kept", "offsets", "ws"]),
+    (ffn, ["x_perm", "offsets", "w1", "w3", "w2", "y_perm", "ws"]),
+], ids=["route", "permute", "expert_ffn"])
+def test_misaligned_pointers_rejected(call, names):
+    """Every device buffer must be 16-byte aligned (the kernels use 16-byte
+    accesses); a misaligned one is an argument error caught before any launch."""
+    for name in names:
+        assert call(**{name: M}) == INV, name
+
+
 def reroute(**kw):
     a = dict(hidden=P, topk_idx=P, logits=P, T=64, d=128, N=8, k=2, cf=1.0, dt=BF16, x_perm=P,
              perm_src=P, slot_row=P, kept=P, offsets=P, ws=P, ws_bytes=1 << 20, stream=S)

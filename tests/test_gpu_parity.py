@@ -206,6 +206,48 @@ def test_reroute_small_shapes(moe, case):
         assert (g["kept"] <= O.capacity(T, k, N, cf)).all()
 
 
+def _random_configs(n=24, seed=20261203):
+    """Seeded draws across the documented limits: 1 to 256 experts (one expert, k = N
+    and odd counts included), token counts that are not multiples of any tile, both
+    dtypes, capacity factors with and without drops, both overflow policies.  The
+    weight count N*d*f stays small enough for the oracle to finish in seconds."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dt = "bf16" if rng.random() < 0.75 else "f32"
+        N = int(rng.choice([1, 2, 3, 5, 8, 13, 16, 31, 64, 100, 256]))
+        if dt == "bf16":
+            d = int(rng.choice([256, 512, 768])) if N <= 16 else 256
+            f = int(rng.choice([128, 256, 384, 512])) if N <= 16 else int(rng.choice([128, 256]))
+        else:
+            d = int(rng.choice([64, 128, 192, 256])) if N <= 16 else 64
+            f = int(rng.choice([64, 128, 192])) if N <= 16 else 64
+        k = int(rng.integers(1, min(N, 6) + 1))
+        T = int(rng.integers(1, 800))
+        cf = float(rng.choice([0.0, 0.5, 0.9, 1.0, 1.05, 1.25, 2.0]))
+        bias = str(rng.choice(["none", "skew", "zipf"]))
+        overflow = "reroute" if (cf > 0 and rng.random() < 0.35) else "drop"
+        out.append((f"rand{i:02d}_{dt}_T{T}_d{d}_N{N}_k{k}_f{f}_cf{cf}_{bias}_{overflow}",
+                    T, d, N, k, f, dt, cf, bias, overflow, i))
+    return out
+
+
+RANDOM = _random_configs()
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=[c[0] for c in RANDOM])
+def test_random_configs(moe, case):
+    label, T, d, N, k, f, dt, cf, bias, overflow, seed = case
+    b = None
+    if bias == "zipf":
+        b = synth.zipf_bias(N)
+    elif bias == "skew":
+        b = np.zeros(N, np.float32)
+        b[: min(3, N)] = [3.0, 2.0, 1.0][: min(3, N)]
+    inp = synth.make_inputs(T, d, N, k, f, dt, cf, 100 + seed, bias=b)
+    _run(inp, label, overflow=overflow)
+
+
 @pytest.mark.parametrize("N", [8, 130])
 def test_reroute_exact_ties(moe, N):
     """W_router = 0: every logit ties, so experts 0..k-1 overflow and each dropped

@@ -155,6 +155,47 @@ def test_backward_small(moe, case):
     run_backward(moe, inp, coef, overflow, label)
 
 
+def _random_configs(n=12, seed=20261204):
+    """Seeded draws across the backward's limits (bf16: d a multiple of 256 and f of
+    256; fp32: multiples of 64): 1 to 64 experts, k up to 4 (k = N included), token
+    counts that are no multiple of a tile, both overflow policies, with and without
+    the aux term and a router bias."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dt = "bf16" if rng.random() < 0.7 else "f32"
+        N = int(rng.choice([1, 2, 3, 5, 8, 13, 16, 31, 64]))
+        if dt == "bf16":
+            d = int(rng.choice([256, 512]))
+            f = int(rng.choice([256, 512])) if N <= 16 else 256
+        else:
+            d = int(rng.choice([64, 128, 192]))
+            f = int(rng.choice([64, 128, 192])) if N <= 16 else 64
+        k = int(rng.integers(1, min(N, 4) + 1))
+        T = int(rng.integers(1, 600))
+        cf = float(rng.choice([0.0, 0.8, 1.0, 1.25]))
+        bias = str(rng.choice(["none", "skew"]))
+        coef = float(rng.choice([0.0, 0.01, 0.1]))
+        overflow = "reroute" if (cf > 0 and rng.random() < 0.35) else "drop"
+        out.append((f"rand{i:02d}_{dt}_T{T}_d{d}_N{N}_k{k}_f{f}_cf{cf}_{bias}_aux{coef}_{overflow}",
+                    T, d, N, k, f, dt, cf, bias, coef, overflow, i))
+    return out
+
+
+RANDOM = _random_configs()
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=[c[0] for c in RANDOM])
+def test_backward_random_configs(moe, case):
+    label, T, d, N, k, f, dt, cf, bias, coef, overflow, seed = case
+    b = None
+    if bias == "skew":
+        b = np.zeros(N, np.float32)
+        b[: min(3, N)] = [1.5, 1.0, 0.5][: min(3, N)]
+    inp = synth.make_inputs(T, d, N, k, f, dt, cf, 200 + seed, bias=b)
+    run_backward(moe, inp, coef, overflow, label)
+
+
 @pytest.mark.parametrize("saved", [False, True])
 def test_backward_is_deterministic(moe, saved):
     inp = synth.make_inputs(500, 256, 8, 2, 256, "bf16", 1.0, 3)

@@ -319,17 +319,19 @@ __global__ __launch_bounds__(64 * kProposeWaves) void propose_kernel(
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * kProposeWaves + (threadIdx.x >> 6);
   if (t >= T) return;
+  // bit c of `ok`: expert lane + 64 c is still a candidate (a mask rather than an
+  // array, which the dynamic index below would put in scratch memory)
   float v[4];
-  bool ok[4];
+  unsigned ok = 0;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int e = lane + 64 * c;
-    ok[c] = e < N && room[e];
+    if (e < N && room[e]) ok |= 1u << c;
     v[c] = e < N ? logits[(size_t)t * N + e] : 0.f;
   }
   for (int j = 0; j < k; ++j) {                  // the token's own experts are not candidates
     const int e = topk_idx[(size_t)t * k + j];
-    if (e >= 0 && e < N && (e & 63) == lane) ok[e >> 6] = false;
+    if (e >= 0 && e < N && (e & 63) == lane) ok &= ~(1u << (e >> 6));
   }
   for (int j = 0; j < k; ++j) {
     const size_t s = (size_t)t * k + j;
@@ -340,7 +342,7 @@ __global__ __launch_bounds__(64 * kProposeWaves) void propose_kernel(
       int be = 0x7FFFFFFF;                       // no candidate
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        if (ok[c] && (be == 0x7FFFFFFF || v[c] > bv)) {
+        if (((ok >> c) & 1u) && (be == 0x7FFFFFFF || v[c] > bv)) {
           bv = v[c];
           be = lane + 64 * c;
         }
@@ -357,7 +359,7 @@ __global__ __launch_bounds__(64 * kProposeWaves) void propose_kernel(
       }
       if (be != 0x7FFFFFFF) {
         best = be;
-        if ((be & 63) == lane) ok[be >> 6] = false;
+        if ((be & 63) == lane) ok &= ~(1u << (be >> 6));
       }
     }
     if (lane == 0) prop[s] = best;

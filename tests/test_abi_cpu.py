@@ -319,3 +319,24 @@ def test_backward_entry_points_reject():
     assert lib.moe_router_backward(*a) == INV
     a = list(args); a[10] = -1; a[9] = P
     assert lib.moe_router_backward(*a) == INV
+
+
+def test_plain_c_caller(tmp_path):
+    """include/moe.h compiles as strict C99 and a C program linked against the library
+    gets the documented capacities and argument errors (tests/c_abi_check.c)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler on this host")
+    libdir = os.path.dirname(moe.LIB_PATH)
+    libname = os.path.basename(moe.LIB_PATH)
+    assert libname.startswith("lib") and libname.endswith(".so")
+    exe = tmp_path / "c_abi_check"
+    subprocess.run([cc, "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror",
+                    "-I", os.path.join(ROOT, "include"), os.path.join(ROOT, "tests", "c_abi_check.c"),
+                    "-L", libdir, "-l" + libname[3:-3], "-Wl,-rpath," + libdir, "-o", str(exe)],
+                   check=True, capture_output=True, text=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert "0 failure(s)" in out.stdout
